@@ -1,0 +1,542 @@
+// Host task-graph builder: operators -> tiles -> tasks, events, per-worker
+// queues; graph checks; a host-thread simulator of the device protocol.
+//
+// Sources (web pages on Mirage Persistent Kernel, "MPK"):
+//   P1 "Mirage Persistent Kernel: Fusing Multi-GPU LLM Inference into One
+//      Kernel Launch" (hysenlabs.com, English review)
+//   P4 "Mirage Persistent Kernel：把 LLM 推理压进单个 GPU 内核" (hysenlabs.com, Chinese review)
+//   P5 "Mirage Persistent Kernel kompiliert LLM-Inferenz in einen Persistent
+//      Kernel" (hysenlabs.com, German review)
+//
+// The pages describe a compiler that turns a chain of fused operators into
+// tasks which on-GPU schedulers hand to workers (P1 "How MPK Works"; P4
+// "工作机制"), and advise that each operator's thread-block count be a multiple
+// of the worker count so no worker idles (P1 "The API"; P5 "Grenzen der
+// README-Aussagen").  Here each operator is split into at most one tile per
+// worker CU (256 on MI355X), tiles become tasks, every operator owns one
+// monotonic event counter, and each worker gets a static queue of its tasks
+// in operator order.  A task waits until its producers' events reach
+// count * (iteration + 1) (or count * iteration for reads of the previous
+// iteration's tokens/step), so counters are never reset inside a run.
+#include <algorithm>
+#include <memory>
+#include <atomic>
+#include <chrono>
+#include <cstring>
+#include <random>
+#include <set>
+#include <thread>
+
+#include "graph.hpp"
+
+static thread_local std::string g_err;
+
+int mpk_fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+void mpk_clear_error() { g_err.clear(); }
+
+extern "C" const char* mpk_last_error(void) { return g_err.c_str(); }
+
+int mpk_attn_splits(int num_workers, int batch, int nkv, int max_seq) {
+  int ns = num_workers / std::max(1, batch * nkv);
+  int by_len = (max_seq + 15) / 16;  // at least ~16 positions per split at full length
+  ns = std::min(ns, by_len);
+  return std::max(1, ns);
+}
+
+namespace {
+
+struct Shape {
+  int dtype;
+  int ndim;
+  int64_t d[4];
+};
+
+std::string tname(const mpk_graph_s* g, int id) {
+  if (id < 0 || id >= (int)g->tensors.size()) return "#" + std::to_string(id);
+  const std::string& n = g->names[id];
+  return n.empty() ? "#" + std::to_string(id) : n;
+}
+
+int check_tensor(const mpk_graph_s* g, int id, int dtype, std::initializer_list<int64_t> dims,
+                 const char* what, int op) {
+  if (id < 0 || id >= (int)g->tensors.size())
+    return mpk_fail(MPK_ERR_INVALID_ARG, "op " + std::to_string(op) + ": " + what + " tensor id " +
+                                             std::to_string(id) + " out of range");
+  const mpk_tensor& t = g->tensors[id];
+  if (t.dtype != dtype)
+    return mpk_fail(MPK_ERR_DTYPE, "op " + std::to_string(op) + ": " + what + " (" + tname(g, id) +
+                                       ") has the wrong dtype");
+  if ((int)dims.size() != t.ndim)
+    return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(op) + ": " + what + " (" + tname(g, id) +
+                                       ") has " + std::to_string(t.ndim) + " dims, expected " +
+                                       std::to_string(dims.size()));
+  int i = 0;
+  for (int64_t want : dims) {
+    if (want >= 0 && t.dims[i] != want)
+      return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(op) + ": " + what + " (" + tname(g, id) +
+                                         ") dim " + std::to_string(i) + " is " +
+                                         std::to_string(t.dims[i]) + ", expected " +
+                                         std::to_string(want));
+    ++i;
+  }
+  if (t.dev_ptr && ((uintptr_t)t.dev_ptr & 15))
+    return mpk_fail(MPK_ERR_ALIGN, "tensor " + tname(g, id) + " is not 16-byte aligned");
+  return MPK_OK;
+}
+
+}  // namespace
+
+extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg* launch,
+                               const mpk_tensor* tensors, int32_t n_tensors, const mpk_op* ops,
+                               int32_t n_ops, const mpk_meta* meta, mpk_graph_t* out) {
+  mpk_clear_error();
+  if (!model || !launch || !tensors || !ops || !meta || !out || n_tensors <= 0 || n_ops <= 0)
+    return mpk_fail(MPK_ERR_INVALID_ARG, "mpk_build_graph: NULL argument or empty table");
+  *out = nullptr;
+  auto g = new mpk_graph_s();
+  std::unique_ptr<mpk_graph_s> guard(g);
+  g->model = *model;
+  g->launch = *launch;
+  g->meta = *meta;
+  g->tensors.assign(tensors, tensors + n_tensors);
+  for (auto& t : g->tensors) {
+    g->names.push_back(t.name ? t.name : "");
+    t.name = nullptr;
+  }
+  g->ops.assign(ops, ops + n_ops);
+  const mpk_model_cfg& M = g->model;
+  if (M.num_layers <= 0 || M.hidden <= 0 || M.n_q_heads <= 0 || M.n_kv_heads <= 0 ||
+      M.head_dim <= 0 || M.ffn <= 0 || M.vocab <= 0 || M.max_seq <= 0 || M.max_batch <= 0 ||
+      !(M.rms_eps >= 0.f) || !(M.rope_theta > 0.f))
+    return mpk_fail(MPK_ERR_INVALID_ARG, "model config has a non-positive field");
+  if (M.n_q_heads % M.n_kv_heads)
+    return mpk_fail(MPK_ERR_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (M.head_dim % 16 || M.head_dim > 128 || M.head_dim < 16)
+    return mpk_fail(MPK_ERR_SHAPE, "head_dim must be a multiple of 16 in [16, 128]");
+  if (M.n_q_heads / M.n_kv_heads > MPK_NW)
+    return mpk_fail(MPK_ERR_SHAPE, "more than 8 query heads per kv head");
+
+  // ---- worker / scheduler split (P1 "How MPK Works", restated for CUs) ----
+  mpk_launch_cfg& Lc = g->launch;
+  if (Lc.num_cus <= 0) return mpk_fail(MPK_ERR_INVALID_ARG, "launch.num_cus must be set (> 0)");
+  if (Lc.sched_mode == MPK_SCHED_CORESIDENT) {
+    int w = Lc.num_workers ? Lc.num_workers : Lc.num_cus;
+    if (w != Lc.num_cus)
+      return mpk_fail(MPK_ERR_SPLIT, "co-resident mode needs num_workers == CU count (" +
+                                         std::to_string(Lc.num_cus) + ")");
+    if (Lc.num_schedulers != 0 && Lc.num_schedulers != w)
+      return mpk_fail(MPK_ERR_SPLIT, "co-resident mode carries one scheduler wavefront per worker");
+    g->num_workers = w;
+  } else if (Lc.sched_mode == MPK_SCHED_DEDICATED) {
+    if (Lc.num_workers <= 0 || Lc.num_schedulers <= 0 || Lc.num_schedulers % 4 ||
+        Lc.num_workers + Lc.num_schedulers / 4 != Lc.num_cus)
+      return mpk_fail(MPK_ERR_SPLIT, "dedicated mode needs num_workers + num_schedulers/4 == "
+                                     "CU count with num_schedulers a positive multiple of 4");
+    g->num_workers = Lc.num_workers;
+  } else {
+    return mpk_fail(MPK_ERR_INVALID_ARG, "unknown sched_mode");
+  }
+  const int W = g->num_workers;
+
+  // ---- meta tensors ----
+  const int B = meta->num_requests;
+  if (B <= 0 || B > M.max_batch || B > MPK_MAX_BATCH)
+    return mpk_fail(MPK_ERR_SHAPE, "num_requests must be in [1, min(max_batch, 8)]");
+  int rc;
+  if ((rc = check_tensor(g, meta->tokens, MPK_I32, {B, -1}, "tokens", -1))) return rc;
+  if ((rc = check_tensor(g, meta->step, MPK_I32, {B}, "step", -1))) return rc;
+  if ((rc = check_tensor(g, meta->prompt_len, MPK_I32, {B}, "prompt_len", -1))) return rc;
+  for (int id : {meta->tokens, meta->step, meta->prompt_len})
+    if (!g->tensors[id].dev_ptr)
+      return mpk_fail(MPK_ERR_INVALID_ARG, "meta tensors must be attached caller memory");
+
+  const int H = M.hidden, d = M.head_dim, nq = M.n_q_heads, nkv = M.n_kv_heads;
+  const int qkv_w = (nq + 2 * nkv) * d;
+  g->producer.assign(n_tensors, -1);
+  g->embed_src.assign(n_tensors, -1);
+  g->dops.assign(n_ops, mpk_dev_op{});
+  std::vector<std::vector<int>> reads(n_ops);  // f32 activations read
+  std::vector<int> reads_meta(n_ops, 0);
+  int lm_op = -1;
+
+  auto set_producer = [&](int op, int t) -> int {
+    if (t < 0 || t >= n_tensors) return mpk_fail(MPK_ERR_INVALID_ARG, "output tensor id out of range");
+    if (g->producer[t] != -1)
+      return mpk_fail(MPK_ERR_GRAPH, "tensor " + tname(g, t) + " has two producers");
+    g->producer[t] = op;
+    return MPK_OK;
+  };
+  auto act_read = [&](int op, int t) {
+    if (g->embed_src[t] >= 0) reads_meta[op] = 1;
+    else reads[op].push_back(t);
+  };
+  const int64_t LDS_FLOATS = (MPK_LDS_BYTES - 8192) / 4;
+
+  for (int i = 0; i < n_ops; ++i) {
+    const mpk_op& o = g->ops[i];
+    mpk_dev_op& D = g->dops[i];
+    switch (o.kind) {
+      case MPK_OP_EMBED: {
+        if ((rc = check_tensor(g, o.in[0], MPK_BF16, {M.vocab, H}, "E", i))) return rc;
+        if ((rc = check_tensor(g, o.out[0], MPK_F32, {B, H}, "x", i))) return rc;
+        if ((rc = set_producer(i, o.out[0]))) return rc;
+        g->embed_src[o.out[0]] = o.in[0];
+        D.kind = 0;
+        break;
+      }
+      case MPK_OP_RMSNORM_LINEAR:
+      case MPK_OP_LINEAR_RESIDUAL:
+      case MPK_OP_RMSNORM_GATEUP:
+      case MPK_OP_LMHEAD_ARGMAX: {
+        const mpk_tensor& X = g->tensors[o.in[0] >= 0 && o.in[0] < n_tensors ? o.in[0] : 0];
+        if (o.in[0] < 0 || o.in[0] >= n_tensors || X.ndim != 2)
+          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": x must be [B, K]");
+        const int K = (int)X.dims[1];
+        if ((rc = check_tensor(g, o.in[0], MPK_F32, {B, K}, "x", i))) return rc;
+        if (K % 8) return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": K must be a multiple of 8");
+        const int nseg = (K + MPK_SEG - 1) / MPK_SEG;
+        if ((int64_t)B * nseg * MPK_SEG > LDS_FLOATS && (int64_t)B * ((K + 511) / 512) * 512 > LDS_FLOATS)
+          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) +
+                                             ": num_requests * K does not fit the LDS staging buffer");
+        act_read(i, o.in[0]);
+        D.kind = MPK_TK_GEMV;
+        D.K = K;
+        D.nseg = nseg;
+        D.x_embed = g->embed_src[o.in[0]] >= 0;
+        D.has_norm = o.kind != MPK_OP_LINEAR_RESIDUAL;
+        if (D.has_norm && (rc = check_tensor(g, o.in[1], MPK_BF16, {K}, "gain", i))) return rc;
+        int N = 0;
+        if (o.kind == MPK_OP_RMSNORM_LINEAR) {
+          int rows[3] = {0, 0, 0};
+          for (int w = 0; w < 3; ++w) {
+            int id = o.in[2 + w];
+            if (id < 0) {
+              if (w == 0) return mpk_fail(MPK_ERR_INVALID_ARG, "rmsnorm_linear needs W0");
+              continue;
+            }
+            if ((rc = check_tensor(g, id, MPK_BF16, {-1, K}, "W", i))) return rc;
+            rows[w] = (int)g->tensors[id].dims[0];
+          }
+          D.N0 = rows[0], D.N1 = rows[1], D.N2 = rows[2];
+          N = rows[0] + rows[1] + rows[2];
+          if ((rc = check_tensor(g, o.out[0], MPK_F32, {B, N}, "y", i))) return rc;
+          D.epi = MPK_EPI_STORE;
+        } else if (o.kind == MPK_OP_LINEAR_RESIDUAL) {
+          if ((rc = check_tensor(g, o.in[1], MPK_BF16, {-1, K}, "W", i))) return rc;
+          N = (int)g->tensors[o.in[1]].dims[0];
+          D.N0 = N;
+          if ((rc = check_tensor(g, o.in[2], MPK_F32, {B, N}, "residual", i))) return rc;
+          if ((rc = check_tensor(g, o.out[0], MPK_F32, {B, N}, "y", i))) return rc;
+          act_read(i, o.in[2]);
+          D.res_embed = g->embed_src[o.in[2]] >= 0;
+          D.epi = MPK_EPI_RESID;
+        } else if (o.kind == MPK_OP_RMSNORM_GATEUP) {
+          if ((rc = check_tensor(g, o.in[2], MPK_BF16, {-1, K}, "Wg", i))) return rc;
+          int F = (int)g->tensors[o.in[2]].dims[0];
+          if ((rc = check_tensor(g, o.in[3], MPK_BF16, {F, K}, "Wu", i))) return rc;
+          if ((rc = check_tensor(g, o.out[0], MPK_F32, {B, F}, "m", i))) return rc;
+          D.N0 = F, D.N1 = F;
+          D.pairs = 1;
+          N = 2 * F;
+          D.epi = MPK_EPI_SILU;
+        } else {
+          if (lm_op >= 0) return mpk_fail(MPK_ERR_GRAPH, "more than one LM head operator");
+          lm_op = i;
+          if ((rc = check_tensor(g, o.in[2], MPK_BF16, {M.vocab, K}, "E", i))) return rc;
+          N = M.vocab;
+          D.N0 = N;
+          if (o.out[0] >= 0) {
+            if ((rc = check_tensor(g, o.out[0], MPK_F32, {-1, B, M.vocab}, "logits", i))) return rc;
+            D.logits_iters = g->tensors[o.out[0]].dims[0];
+          }
+          D.epi = MPK_EPI_ARGMAX;
+          D.kind = MPK_TK_LMHEAD;
+          reads_meta[i] = 1;
+        }
+        if (o.kind != MPK_OP_LMHEAD_ARGMAX || o.out[0] >= 0)
+          if ((rc = set_producer(i, o.out[0]))) return rc;
+        D.n_out = o.kind == MPK_OP_RMSNORM_GATEUP ? N / 2 : N;
+        // tiling: every worker wavefront must get >= 2 weight blocks per tile
+        const int a = D.pairs ? 2 : 1;
+        const int U = N / a;
+        const int per_wave_units = (2 + a * nseg - 1) / (a * nseg);
+        const int min_units = MPK_NW * per_wave_units;
+        int T = o.num_tiles > 0 ? o.num_tiles : std::max(1, std::min(W, U / min_units));
+        if (T > W || U / T < min_units)
+          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": " + std::to_string(U) +
+                                             " rows cannot give " + std::to_string(T) +
+                                             " tiles of >= " + std::to_string(min_units) + " rows");
+        D.ntiles = T;
+        if (D.epi == MPK_EPI_RESID && (int64_t)B * ((U + T - 1) / T) * a > 512)
+          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) +
+                                             ": residual rows per tile x num_requests exceed 512");
+        break;
+      }
+      case MPK_OP_ATTENTION: {
+        if ((rc = check_tensor(g, o.in[0], MPK_F32, {B, qkv_w}, "qkv", i))) return rc;
+        if ((rc = check_tensor(g, o.in[1], MPK_BF16, {d}, "q_norm", i))) return rc;
+        if ((rc = check_tensor(g, o.in[2], MPK_BF16, {d}, "k_norm", i))) return rc;
+        if ((rc = check_tensor(g, o.in[3], MPK_BF16, {B, nkv, M.max_seq, d}, "kcache", i))) return rc;
+        if ((rc = check_tensor(g, o.in[4], MPK_BF16, {B, nkv, M.max_seq, d}, "vcache", i))) return rc;
+        if (!g->tensors[o.in[3]].dev_ptr || !g->tensors[o.in[4]].dev_ptr)
+          return mpk_fail(MPK_ERR_INVALID_ARG, "KV caches must be attached caller memory");
+        if ((rc = check_tensor(g, o.out[0], MPK_F32, {B, nq * d}, "o", i))) return rc;
+        if ((rc = set_producer(i, o.out[0]))) return rc;
+        act_read(i, o.in[0]);
+        reads_meta[i] = 1;
+        D.kind = MPK_TK_ATTN;
+        D.nq = nq, D.nkv = nkv, D.d = d, D.S = M.max_seq;
+        D.nsplit = mpk_attn_splits(W, B, nkv, M.max_seq);
+        D.ntiles = B * nkv * D.nsplit;
+        break;
+      }
+      default:
+        return mpk_fail(MPK_ERR_INVALID_ARG, "op " + std::to_string(i) + ": unknown kind");
+    }
+  }
+  // activations must come from earlier operators
+  for (int i = 0; i < n_ops; ++i)
+    for (int t : reads[i]) {
+      int p = g->producer[t];
+      if (p >= i)
+        return mpk_fail(MPK_ERR_GRAPH, "op " + std::to_string(i) + " reads " + tname(g, t) +
+                                           " before its producer op " + std::to_string(p));
+    }
+  // ---- events and dependencies ----
+  std::vector<int> op_ev(n_ops, -1);
+  for (int i = 0; i < n_ops; ++i) {
+    if (g->dops[i].kind == 0) continue;
+    op_ev[i] = (int)g->ev_count.size();
+    const mpk_dev_op& D = g->dops[i];
+    int cnt = D.kind == MPK_TK_GEMV ? D.ntiles : D.kind == MPK_TK_ATTN ? B * D.nkv : 1;
+    g->ev_count.push_back(cnt);
+    g->ev_op.push_back(i);
+    g->dops[i].event = op_ev[i];
+  }
+  int sink = -1;
+  for (int i = n_ops - 1; i >= 0; --i)
+    if (g->dops[i].kind) {
+      sink = i;
+      break;
+    }
+  if (sink < 0) return mpk_fail(MPK_ERR_GRAPH, "graph has no operator with work");
+  if (lm_op >= 0 && lm_op != sink)
+    return mpk_fail(MPK_ERR_GRAPH, "the LM head operator must be the last operator");
+  g->sink = sink;
+  // same-iteration ancestors
+  std::vector<std::set<int>> direct(n_ops), anc(n_ops);
+  for (int i = 0; i < n_ops; ++i) {
+    if (!g->dops[i].kind) continue;
+    for (int t : reads[i]) {
+      int p = g->producer[t];
+      if (p >= 0 && g->dops[p].kind) direct[i].insert(p);
+    }
+    for (int p : direct[i]) {
+      anc[i].insert(p);
+      anc[i].insert(anc[p].begin(), anc[p].end());
+    }
+  }
+  for (int i = 0; i < n_ops; ++i)
+    if (g->dops[i].kind && i != sink && !anc[sink].count(i))
+      return mpk_fail(MPK_ERR_GRAPH, "op " + std::to_string(i) +
+                                         " is not an ancestor of the last operator");
+  // previous-iteration edge: readers of tokens/step (through the embedding or
+  // directly) and every operator without producers wait for the sink.
+  std::vector<int> has_prev(n_ops, 0), needs_prev(n_ops, 0);
+  for (int i = 0; i < n_ops; ++i) {
+    if (!g->dops[i].kind) continue;
+    needs_prev[i] = (reads_meta[i] && lm_op >= 0) || direct[i].empty();
+    has_prev[i] = needs_prev[i];
+    for (int p : anc[i]) has_prev[i] |= has_prev[p];
+  }
+  std::vector<std::vector<std::pair<int, int>>> deps(n_ops);  // (op, prev)
+  for (int i = 0; i < n_ops; ++i) {
+    if (!g->dops[i].kind) continue;
+    for (int p : direct[i]) {
+      bool implied = false;
+      for (int q : direct[i])
+        if (q != p && anc[q].count(p)) implied = true;
+      if (!implied) deps[i].push_back({p, 0});
+    }
+    if (needs_prev[i]) {
+      bool implied = false;
+      for (int q : direct[i])
+        if (has_prev[q]) implied = true;
+      if (!implied) deps[i].push_back({sink, 1});
+    }
+    if ((int)deps[i].size() > MPK_MAX_DEPS)
+      return mpk_fail(MPK_ERR_GRAPH, "op " + std::to_string(i) + " has more than 3 direct producers");
+  }
+  // ---- tasks ----
+  g->op_first_task.assign(n_ops, 0);
+  g->op_ntasks.assign(n_ops, 0);
+  for (int i = 0; i < n_ops; ++i) {
+    mpk_dev_op& D = g->dops[i];
+    g->op_first_task[i] = (int)g->tasks.size();
+    if (!D.kind) continue;
+    g->op_ntasks[i] = D.ntiles;
+    for (int t = 0; t < D.ntiles; ++t) {
+      mpk_dev_task T{};
+      T.kind = D.kind;
+      T.op = i;
+      T.tile = t;
+      T.worker = (int)(((int64_t)t * W) / D.ntiles);
+      T.split = -1;
+      if (D.kind == MPK_TK_ATTN) {
+        int per_req = D.nkv * D.nsplit;
+        T.row0 = t / per_req;                   // request
+        T.nrows = (t % per_req) / D.nsplit;     // kv head
+        T.split = t % D.nsplit;
+        T.last_only = 1;
+      } else {
+        const int a = D.pairs ? 2 : 1;
+        const int U = (D.N0 + D.N1 + D.N2) / a;
+        int u0 = (int)((int64_t)t * U / D.ntiles), u1 = (int)((int64_t)(t + 1) * U / D.ntiles);
+        T.row0 = u0 * a;
+        T.nrows = (u1 - u0) * a;
+        T.last_only = D.kind == MPK_TK_LMHEAD;
+      }
+      T.n_deps = (int)deps[i].size();
+      for (int k = 0; k < MPK_MAX_DEPS; ++k) T.dep_ev[k] = T.dep_cnt[k] = T.dep_prev[k] = -1;
+      for (int k = 0; k < T.n_deps; ++k) {
+        T.dep_ev[k] = op_ev[deps[i][k].first];
+        T.dep_cnt[k] = g->ev_count[T.dep_ev[k]];
+        T.dep_prev[k] = deps[i][k].second;
+      }
+      T.out_ev = op_ev[i];
+      g->tasks.push_back(T);
+      mpk_task_info I{};
+      I.op = i, I.tile = t, I.worker = T.worker, I.row0 = T.row0, I.nrows = T.nrows, I.split = T.split;
+      for (int k = 0; k < MPK_MAX_DEPS; ++k) {
+        I.dep_event[k] = T.dep_ev[k];
+        I.dep_count[k] = T.dep_cnt[k];
+        I.dep_prev[k] = T.dep_prev[k];
+      }
+      I.out_event = T.out_ev;
+      g->info.push_back(I);
+    }
+  }
+  // ---- per-worker queues in operator order ----
+  std::vector<std::vector<int>> q(W);
+  for (size_t k = 0; k < g->tasks.size(); ++k) q[g->tasks[k].worker].push_back((int)k);
+  g->qlen.assign(W, 0);
+  g->max_queue = 1;
+  for (int w = 0; w < W; ++w) {
+    g->qlen[w] = (int)q[w].size();
+    g->max_queue = std::max(g->max_queue, g->qlen[w]);
+  }
+  g->queues.assign((size_t)W * g->max_queue, mpk_dev_qentry{-1, -1});
+  g->queue_ids.assign((size_t)W * g->max_queue, -1);
+  for (int w = 0; w < W; ++w) {
+    const int n = g->qlen[w];
+    for (int k = 0; k < n; ++k) {
+      int nx = -1;
+      for (int j = 1; j <= n; ++j) {
+        int kk = k + j;
+        const mpk_dev_task& T = g->tasks[q[w][kk % n]];
+        if (T.kind == MPK_TK_GEMV || T.kind == MPK_TK_LMHEAD) {
+          nx = kk;
+          break;
+        }
+      }
+      g->queues[(size_t)w * g->max_queue + k] = mpk_dev_qentry{q[w][k], nx};
+      g->queue_ids[(size_t)w * g->max_queue + k] = q[w][k];
+    }
+  }
+  *out = guard.release();
+  return MPK_OK;
+}
+
+extern "C" int mpk_get_graph_info(mpk_graph_t g, mpk_graph_info* info) {
+  mpk_clear_error();
+  if (!g || !info) return mpk_fail(MPK_ERR_INVALID_ARG, "NULL argument");
+  info->num_tasks = (int)g->tasks.size();
+  info->num_events = (int)g->ev_count.size();
+  info->num_workers = g->num_workers;
+  info->max_queue = g->max_queue;
+  info->num_ops = (int)g->ops.size();
+  info->sink_op = g->sink;
+  info->tasks = g->info.data();
+  info->event_count = g->ev_count.data();
+  info->event_op = g->ev_op.data();
+  info->queue_len = g->qlen.data();
+  info->queues = g->queue_ids.data();
+  return MPK_OK;
+}
+
+extern "C" void mpk_destroy_graph(mpk_graph_t g) { delete g; }
+
+// ---- host-thread simulation of the device protocol ----------------------
+extern "C" int mpk_simulate(mpk_graph_t g, int32_t n_iter, uint32_t seed, int32_t jitter_us,
+                            int32_t timeout_ms, mpk_trace_record* trace) {
+  mpk_clear_error();
+  if (!g || n_iter <= 0 || !trace || jitter_us < 0 || timeout_ms <= 0)
+    return mpk_fail(MPK_ERR_INVALID_ARG, "mpk_simulate: bad argument");
+  const int W = g->num_workers, NT = (int)g->tasks.size();
+  std::vector<std::atomic<uint32_t>> ev(g->ev_count.size());
+  for (auto& e : ev) e.store(0);
+  // last-arriver groups: attention (op, request, kv head); LM head (op)
+  std::vector<std::atomic<uint32_t>> grp(NT);
+  for (auto& e : grp) e.store(0);
+  std::atomic<uint32_t> ticket{0};
+  std::atomic<int> failed{0};
+  for (int64_t i = 0; i < (int64_t)n_iter * NT; ++i) trace[i] = mpk_trace_record{-1, -1, 0, 0, 0, 0, 0, 0};
+  auto t0 = std::chrono::steady_clock::now();
+  auto now_ns = [&] {
+    return (uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(
+               std::chrono::steady_clock::now() - t0).count();
+  };
+  auto worker = [&](int w) {
+    std::mt19937 rng(seed * 7919u + (uint32_t)w);
+    for (int s = 0; s < n_iter && !failed.load(); ++s) {
+      for (int k = 0; k < g->qlen[w]; ++k) {
+        const mpk_dev_task& T = g->tasks[g->queues[(size_t)w * g->max_queue + k].task];
+        int tid = g->queues[(size_t)w * g->max_queue + k].task;
+        auto start = std::chrono::steady_clock::now();
+        for (int d = 0; d < T.n_deps; ++d) {
+          uint32_t target = (uint32_t)T.dep_cnt[d] * (uint32_t)(s + 1 - T.dep_prev[d]);
+          while (ev[T.dep_ev[d]].load(std::memory_order_acquire) < target) {
+            if (failed.load()) return;
+            if (std::chrono::steady_clock::now() - start > std::chrono::milliseconds(timeout_ms)) {
+              failed.store(1);
+              return;
+            }
+            std::this_thread::yield();
+          }
+        }
+        mpk_trace_record& R = trace[(int64_t)s * NT + tid];
+        R.task = tid;
+        R.iteration = s;
+        R.start_ticket = ticket.fetch_add(1);
+        R.t_start = now_ns();
+        R.hw_id = (uint32_t)w;
+        if (jitter_us) std::this_thread::sleep_for(std::chrono::microseconds(rng() % (jitter_us + 1)));
+        bool signal = true;
+        const mpk_dev_op& D = g->dops[T.op];
+        if (T.last_only) {
+          int group, size;
+          if (T.kind == MPK_TK_ATTN) {
+            group = g->op_first_task[T.op] + (T.row0 * D.nkv + T.nrows) * D.nsplit;
+            size = D.nsplit;
+          } else {
+            group = g->op_first_task[T.op];
+            size = D.ntiles;
+          }
+          uint32_t old = grp[group].fetch_add(1, std::memory_order_acq_rel);
+          signal = (old % (uint32_t)size) == (uint32_t)size - 1;
+        }
+        R.end_ticket = ticket.fetch_add(1);
+        R.t_end = now_ns();
+        if (signal) ev[T.out_ev].fetch_add(1, std::memory_order_release);
+      }
+    }
+  };
+  std::vector<std::thread> th;
+  for (int w = 0; w < W; ++w) th.emplace_back(worker, w);
+  for (auto& t : th) t.join();
+  if (failed.load()) return mpk_fail(MPK_ERR_DEVICE_TIMEOUT, "simulated dependency wait timed out");
+  return MPK_OK;
+}

@@ -1,0 +1,118 @@
+/*
+ * Internal tables shared by the host graph builder (builder.cpp) and the
+ * device runtime (runtime.hip).  Plain structs, identical layout on both
+ * sides.
+ */
+#ifndef MPK_INTERNAL_H
+#define MPK_INTERNAL_H
+
+#include <stdint.h>
+
+#include "mpk.h"
+
+#define MPK_NW 8                        /* worker wavefronts per workgroup */
+#define MPK_THREADS (64 * (MPK_NW + 1)) /* + one scheduler wavefront */
+#define MPK_SEG 4096                    /* columns of one weight block */
+#define MPK_BU 8                        /* 16-byte-per-lane units per block */
+#define MPK_MAX_DEPS 3
+#define MPK_ATTN_SUB 1024               /* positions scored per pass of an attention task */
+#define MPK_LDS_BYTES (96 * 1024)       /* dynamic LDS per workgroup (forces one per CU) */
+#define MPK_MAX_BATCH 8
+
+enum { MPK_TK_GEMV = 1, MPK_TK_ATTN = 2, MPK_TK_LMHEAD = 3 };
+enum { MPK_EPI_STORE = 0, MPK_EPI_RESID = 1, MPK_EPI_SILU = 2, MPK_EPI_ARGMAX = 3 };
+
+/* One operator as the device sees it. */
+typedef struct {
+  int32_t kind;      /* MPK_TK_* */
+  int32_t epi;       /* MPK_EPI_* for GEMV / LMHEAD */
+  int32_t K;         /* input width */
+  int32_t nseg;      /* ceil(K / MPK_SEG) */
+  int32_t N0, N1, N2;/* rows of W0, W1, W2 */
+  int32_t pairs;     /* 1: virtual rows interleave (gate, up) */
+  int32_t x_embed;   /* 1: x[r] is E[tokens[r][step[r]]] */
+  int32_t res_embed; /* 1: residual[r] is E[tokens[r][step[r]]] */
+  int32_t has_norm;  /* 1: x is RMS-normalised with `gain` */
+  int32_t event;     /* event this operator's tasks signal */
+  int32_t n_out;     /* width of y (per request) */
+  int32_t ntiles;    /* tasks of this operator */
+  /* attention */
+  int32_t nq, nkv, d, nsplit, S;
+  int32_t pad0;
+  const float* x;
+  const uint16_t* gain;
+  const uint16_t* W0;
+  const uint16_t* W1;
+  const uint16_t* W2;
+  const float* resid;
+  float* y;
+  const uint16_t* E; /* embedding rows for x_embed / res_embed */
+  const uint16_t* qn;
+  const uint16_t* kn;
+  uint16_t* kc;
+  uint16_t* vc;
+  float* part;       /* attention split partials; LM head per-tile (value, index) */
+  uint32_t* tickets; /* attention: [B * nkv]; LM head: [1] */
+  float* logits;     /* LM head: optional [iters][B][V] */
+  int64_t logits_iters;
+} mpk_dev_op;
+
+/* One task (a tile of an operator). */
+typedef struct {
+  int32_t kind;
+  int32_t op;
+  int32_t tile;
+  int32_t worker;
+  int32_t row0, nrows; /* GEMV: virtual rows; ATTN: request, kv head */
+  int32_t split;       /* ATTN split */
+  int32_t n_deps;
+  int32_t dep_ev[MPK_MAX_DEPS];
+  int32_t dep_cnt[MPK_MAX_DEPS];
+  int32_t dep_prev[MPK_MAX_DEPS];
+  int32_t out_ev;
+  int32_t last_only;   /* 1: only the last arriver of the tile group signals */
+  int32_t pad[2];
+} mpk_dev_task;
+
+/* Per queue entry: task id and the queue position of the next task that
+ * streams weights (to prefetch), or -1. Positions >= queue length wrap into
+ * the next iteration. */
+typedef struct {
+  int32_t task;
+  int32_t next_stream;
+} mpk_dev_qentry;
+
+typedef struct {
+  int32_t code;      /* mpk_status_t of the device side */
+  int32_t iteration;
+  int32_t task;
+  int32_t abort_req; /* host-written stop request */
+} mpk_dev_status;
+
+typedef struct {
+  const mpk_dev_task* tasks;
+  const mpk_dev_op* ops;
+  const mpk_dev_qentry* queues; /* [num_workers][qstride] */
+  const mpk_dev_qentry* single_q; /* [n_tasks]: {task, -1} (one-launch-per-operator path) */
+  const int32_t* qlen;          /* [num_workers] */
+  uint32_t* events;
+  int32_t* tokens;
+  int32_t* step;
+  const int32_t* prompt_len;
+  const float* rope_cos;        /* [max_seq][d/2] */
+  const float* rope_sin;
+  mpk_dev_status* status;
+  mpk_trace_record* trace;      /* NULL = off */
+  uint32_t* ticket_ctr;
+  uint64_t timeout_ticks;       /* s_memrealtime ticks (100 MHz) */
+  int32_t qstride;
+  int32_t n_iter;
+  int32_t n_tasks;
+  int32_t B;
+  int32_t tokens_width;
+  int32_t rope_half;
+  float rms_eps;
+  int32_t vocab;
+} mpk_kparams;
+
+#endif

@@ -1,0 +1,241 @@
+"""Host-side tests of the C ABI: exported symbols, argument validation, the
+task-graph builder's tiling, events and queues, and the dependency protocol
+run on host threads (no GPU: the builder never touches device memory, so the
+"device" pointers here are placeholders)."""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+import persistent_task_runtime_amd as mpk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mpk.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "mpk.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|void|const char\s*\*)\s*(mpk_[a-z_]+)\s*\(", hdr, re.M))
+    assert declared == set(mpk.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+class FakePtrs(dict):
+    """Distinct 256-byte-aligned placeholder addresses per name."""
+
+    def __missing__(self, key):
+        v = 0x7F0000000000 + (len(self) + 1) * 0x1000000
+        self[key] = v
+        return v
+
+
+def build(shape, B=1, tokens_width=64, max_seq=64, num_cus=256, layers=None, logits_iters=0,
+          with_embedding=True, with_lm_head=True, launch=None):
+    ptrs = FakePtrs()
+    spec, meta = mpk.qwen3_graph(shape, B, ptrs, tokens_width, max_seq, layers=layers,
+                                 logits_iters=logits_iters, with_embedding=with_embedding,
+                                 with_lm_head=with_lm_head, x_in_ptr=ptrs["x_in"])
+    g = mpk.mpk_build_graph(mpk.model_cfg(shape, B, max_seq), launch or mpk.launch_cfg(num_cus),
+                            spec.c_tensors(), spec.ops, meta)
+    return g, spec
+
+
+def info_arrays(g):
+    info = mpk.mpk_get_graph_info(g)
+    tasks = [info.tasks[i] for i in range(info.num_tasks)]
+    ev_cnt = [info.event_count[i] for i in range(info.num_events)]
+    ev_op = [info.event_op[i] for i in range(info.num_events)]
+    qlen = [info.queue_len[w] for w in range(info.num_workers)]
+    queues = [[info.queues[w * info.max_queue + k] for k in range(qlen[w])] for w in range(info.num_workers)]
+    return info, tasks, ev_cnt, ev_op, queues
+
+
+def test_full_model_tiles_fill_every_cu():
+    g, spec = build(synth.QWEN3_8B, tokens_width=551, max_seq=551)
+    try:
+        info, tasks, ev_cnt, ev_op, queues = info_arrays(g)
+        per_op = {}
+        for t in tasks:
+            per_op.setdefault(t.op, []).append(t)
+        kinds = [o.kind for o in spec.ops]
+        # every operator with work has exactly one tile / task per CU
+        for i, k in enumerate(kinds):
+            if k == mpk.MPK_OP_EMBED:
+                assert i not in per_op
+                continue
+            assert len(per_op[i]) == 256, (i, k, len(per_op[i]))
+            assert sorted(t.worker for t in per_op[i]) == list(range(256))
+        # row split of the named shapes (P1 "The API": blocks a multiple of the workers)
+        rows = {mpk.MPK_OP_RMSNORM_LINEAR: 24, mpk.MPK_OP_RMSNORM_GATEUP: 96}
+        for i, k in enumerate(kinds):
+            if k in rows:
+                assert {t.nrows for t in per_op[i]} == {rows[k]}
+            if k == mpk.MPK_OP_LINEAR_RESIDUAL:
+                assert {t.nrows for t in per_op[i]} == {16}
+            if k == mpk.MPK_OP_LMHEAD_ARGMAX:
+                assert {t.nrows for t in per_op[i]} == {593, 594}
+                assert sum(t.nrows for t in per_op[i]) == 151936
+        # 36 layers x 5 operators + LM head, in operator order on every queue
+        assert all(len(q) == 36 * 5 + 1 for q in queues)
+        for q in queues:
+            ops = [tasks[t].op for t in q]
+            assert ops == sorted(ops)
+        assert info.sink_op == len(spec.ops) - 1
+        # attention: 8 kv heads x 32 splits at batch 1
+        attn = [t for t in tasks if kinds[t.op] == mpk.MPK_OP_ATTENTION and t.op == 2]
+        assert sorted((t.nrows, t.split) for t in attn) == [(j, c) for j in range(8) for c in range(32)]
+        # event counts: tiles (GEMV), merges per (request, kv head) (attention), 1 (LM head)
+        for e, (c, op) in enumerate(zip(ev_cnt, ev_op)):
+            k = kinds[op]
+            want = {mpk.MPK_OP_ATTENTION: 8, mpk.MPK_OP_LMHEAD_ARGMAX: 1}.get(k, 256)
+            assert c == want
+    finally:
+        mpk.mpk_destroy_graph(g)
+
+
+def test_dependencies_follow_the_decoder_chain():
+    g, spec = build(synth.TINY)
+    try:
+        info, tasks, ev_cnt, ev_op, queues = info_arrays(g)
+        kinds = [o.kind for o in spec.ops]
+        deps = {}
+        for t in tasks:
+            d = tuple(sorted((ev_op[t.dep_event[k]], t.dep_prev[k]) for k in range(3) if t.dep_event[k] >= 0))
+            deps.setdefault(t.op, set()).add(d)
+        assert all(len(v) == 1 for v in deps.values())
+        deps = {k: next(iter(v)) for k, v in deps.items()}
+        sink = info.sink_op
+        # op 0 is the (task-less) embedding; layer 0 QKV waits for the previous iteration's LM head
+        assert deps[1] == ((sink, 1),)
+        for i in range(1, len(kinds) - 1):
+            if i > 1:
+                assert deps[i] == ((i - 1, 0),), (i, deps[i])
+        assert deps[sink] == ((sink - 1, 0),)
+    finally:
+        mpk.mpk_destroy_graph(g)
+
+
+def test_simulated_protocol_respects_every_edge_under_jitter():
+    shape = synth.TINY
+    g, spec = build(shape, num_cus=32, tokens_width=16, max_seq=16)
+    try:
+        info, tasks, ev_cnt, ev_op, queues = info_arrays(g)
+        n_iter = 3
+        tr = mpk.mpk_simulate(g, n_iter, seed=7, jitter_us=200, timeout_ms=20000)
+        assert (tr["task"] >= 0).all(), "every task ran in every iteration"
+        NT = info.num_tasks
+        tr = tr.reshape(n_iter, NT)
+        kinds = [o.kind for o in spec.ops]
+        by_op = {}
+        for i, t in enumerate(tasks):
+            by_op.setdefault(t.op, []).append(i)
+        # edges derived from the decoder's operator order, not from the builder tables
+        chain = [i for i, k in enumerate(kinds) if k != mpk.MPK_OP_EMBED]
+        for s in range(n_iter):
+            for a, b in zip(chain, chain[1:]):
+                end_a = max(tr[s, i]["end_ticket"] for i in by_op[a])
+                start_b = min(tr[s, i]["start_ticket"] for i in by_op[b])
+                assert end_a < start_b, (s, a, b)
+            if s:
+                end_lm = max(tr[s - 1, i]["end_ticket"] for i in by_op[chain[-1]])
+                start_first = min(tr[s, i]["start_ticket"] for i in by_op[chain[0]])
+                assert end_lm < start_first
+    finally:
+        mpk.mpk_destroy_graph(g)
+
+
+def test_split_rule_checked_for_cus():
+    # P1 "How MPK Works": workers + (local + remote schedulers) / 4 = #SMs; the
+    # pages' example GPU has 108 SMs (P4 "工作机制").
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_numbers.json")))
+    n = gold["a100_sm_count"]["value"]
+    ok = mpk.launch_cfg(n, sched_mode=mpk.MPK_SCHED_DEDICATED, num_workers=n - 8, num_schedulers=32)
+    g, _ = build(synth.TINY, launch=ok, num_cus=n)
+    mpk.mpk_destroy_graph(g)
+    for nw, ns in ((n - 8, 30), (n - 7, 32), (n, 4)):
+        bad = mpk.launch_cfg(n, sched_mode=mpk.MPK_SCHED_DEDICATED, num_workers=nw, num_schedulers=ns)
+        with pytest.raises(mpk.MPKError) as e:
+            build(synth.TINY, launch=bad, num_cus=n)
+        assert e.value.code == mpk.MPK_ERR_SPLIT
+    # co-resident mode: one scheduler wavefront per worker CU
+    with pytest.raises(mpk.MPKError) as e:
+        build(synth.TINY, launch=mpk.launch_cfg(256, num_workers=200))
+    assert e.value.code == mpk.MPK_ERR_SPLIT
+
+
+def test_shape_and_graph_errors_are_reported():
+    shape = synth.TINY
+    ptrs = FakePtrs()
+    spec, meta = mpk.qwen3_graph(shape, 1, ptrs, 64, 64)
+    mcfg, lcfg = mpk.model_cfg(shape, 1, 64), mpk.launch_cfg(256)
+    # wrong dtype
+    t = spec.c_tensors()
+    t[spec.index["l0.wq"]].dtype = mpk.MPK_F32
+    with pytest.raises(mpk.MPKError) as e:
+        mpk.mpk_build_graph(mcfg, lcfg, t, spec.ops, meta)
+    assert e.value.code == mpk.MPK_ERR_DTYPE
+    # wrong shape
+    t = spec.c_tensors()
+    t[spec.index["l1.wo"]].dims[1] = 255
+    with pytest.raises(mpk.MPKError) as e:
+        mpk.mpk_build_graph(mcfg, lcfg, t, spec.ops, meta)
+    assert e.value.code == mpk.MPK_ERR_SHAPE
+    # misaligned attached pointer
+    t = spec.c_tensors()
+    t[spec.index["l0.wk"]].dev_ptr = ptrs["l0.wk"] + 2
+    with pytest.raises(mpk.MPKError) as e:
+        mpk.mpk_build_graph(mcfg, lcfg, t, spec.ops, meta)
+    assert e.value.code == mpk.MPK_ERR_ALIGN
+    # operator reading an activation before its producer
+    ops = list(spec.ops)
+    ops[1], ops[2] = ops[2], ops[1]
+    with pytest.raises(mpk.MPKError) as e:
+        mpk.mpk_build_graph(mcfg, lcfg, spec.c_tensors(), ops, meta)
+    assert e.value.code == mpk.MPK_ERR_GRAPH
+    # LM head not last
+    ops = list(spec.ops)
+    ops.append(ops[1])
+    with pytest.raises(mpk.MPKError) as e:
+        mpk.mpk_build_graph(mcfg, lcfg, spec.c_tensors(), ops, meta)
+    assert e.value.code in (mpk.MPK_ERR_GRAPH,)
+    # too many tiles for the rows
+    ops = list(spec.ops)
+    ops[1].num_tiles = 256
+    with pytest.raises(mpk.MPKError) as e:
+        mpk.mpk_build_graph(mcfg, lcfg, spec.c_tensors(), ops, meta)
+    assert e.value.code == mpk.MPK_ERR_SHAPE
+    assert "tiles" in mpk.mpk_last_error()
+
+
+def test_null_arguments_are_rejected(lib):
+    import ctypes
+
+    assert lib.mpk_run_steps(None, 1, None) == mpk.MPK_ERR_INVALID_ARG
+    assert lib.mpk_get_status(None, None, None, None) == mpk.MPK_ERR_INVALID_ARG
+    out = ctypes.c_void_p()
+    assert lib.mpk_compile(None, 0, ctypes.byref(out)) == mpk.MPK_ERR_INVALID_ARG
+    assert lib.mpk_build_graph(None, None, None, 0, None, 0, None, ctypes.byref(out)) == mpk.MPK_ERR_INVALID_ARG
+    assert "NULL" in mpk.mpk_last_error()
+    lib.mpk_destroy_exec(None)
+    lib.mpk_destroy_graph(None)
+
+
+def test_single_layer_graph_without_embedding_or_lm_head():
+    sh = synth.ModelShape(1, 4096, 32, 8, 128, 12288, 151936)
+    g, spec = build(sh, tokens_width=514, max_seq=513, with_embedding=False, with_lm_head=False)
+    try:
+        info, tasks, ev_cnt, ev_op, queues = info_arrays(g)
+        assert info.sink_op == len(spec.ops) - 1
+        first = [t for t in tasks if t.op == 0]
+        # no producer: waits for the previous iteration's last operator
+        assert {(ev_op[t.dep_event[0]], t.dep_prev[0]) for t in first} == {(info.sink_op, 1)}
+    finally:
+        mpk.mpk_destroy_graph(g)
