@@ -1,0 +1,168 @@
+"""Benchmark: greedy decode of the Qwen3-8B-shaped model at batch 1 on one
+MI355X through the persistent kernel.
+
+Workload: 36 layers (hidden 4096, 32 q / 8 kv heads of 128, FFN 12288) and a
+tied 151936-row embedding / LM head, seeded N(0, 0.02) bf16 weights, a
+39-token seeded prompt and greedy decoding (the pages' Figure 1 workload:
+39-token prompt, 512 generated tokens).  A step is one decode iteration:
+every layer, the LM head, the argmax and the step/tokens advance for the one
+request.  The warm-up steps ingest the prompt (untimed); the timed steps are
+the generating ones (defaults: 38 warm-up, 512 timed).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms/token decode latency at batch 1 (Qwen3-8B shape) + % of HBM roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_position(sh) -> int:
+    """bf16 K and V of one position over all layers."""
+    return sh.layers * sh.n_kv * sh.head_dim * 2 * 2
+
+
+def iteration_bytes(sh, p: int) -> int:
+    """Algorithmic HBM bytes of one decode iteration at position p (batch 1):
+    every weight byte once (the embedding is a one-row gather, the tied LM head
+    is streamed whole), the K/V rows of positions < p read, the K/V row of p
+    written, the embedding row read."""
+    return sh.streamed_weight_bytes() + kv_bytes_per_position(sh) * (p + 1) + 2 * sh.hidden
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=38)
+    ap.add_argument("--per-op-steps", type=int, default=64)
+    ap.add_argument("--cpu-iters", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-op", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import persistent_task_runtime_amd as mpk
+    from persistent_task_runtime_amd import runner
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    sh = synth.QWEN3_8B
+    P = 39
+    K, W = args.steps, args.warmup
+    total = W + K
+    width = max(P + 512 + 1, total + 2)
+    w = synth.Workload("qwen3_8b", sh, 1, n_iter=total, tokens_width=width,
+                       prompt_len=np.array([P], np.int32), step0=np.zeros(1, np.int32))
+    t0 = time.time()
+    weights = synth.make_model(sh, seed=0)
+    log("weights generated in %.1f s" % (time.time() - t0))
+    model = runner.DeviceModel(sh, weights=weights)
+    torch.cuda.synchronize()
+    log("uploaded %.2f GB in %.1f s" % (model.bytes() / 1e9, time.time() - t0))
+
+    stream = torch.cuda.current_stream()
+    sess = runner.Session(w, model, max_seq=width)
+    if W:
+        sess.run(W)
+        torch.cuda.synchronize()
+        sess.check_status()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    sess.run(K)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sess.check_status()
+    ms = e0.elapsed_time(e1)
+    ms_tok = ms / K
+    step_now = int(sess.step.cpu()[0])
+    assert step_now == total, (step_now, total)
+    toks = sess.tokens.cpu().numpy()[0]
+    assert (toks[: total + 1] >= 0).all()
+    alg_bytes = sum(iteration_bytes(sh, W + i) for i in range(K))
+    achieved = alg_bytes / (ms / 1e3) / 1e9
+    bound_ms = alg_bytes / K / (HBM_PEAK_GBS * 1e9) * 1e3
+    log("persistent: %.4f ms/token, %.1f GB/s algorithmic (%.1f%% of %.0f GB/s)"
+        % (ms_tok, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
+    sess.close()
+
+    per_op = None
+    if not args.no_per_op:
+        Kp = min(args.per_op_steps, K)
+        s2 = runner.Session(w, model, max_seq=width)
+        s2.run(W, per_op=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        s2.run(Kp, per_op=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s2.check_status()
+        per_op = e0.elapsed_time(e1) / Kp
+        log("one launch per operator: %.4f ms/token over %d steps" % (per_op, Kp))
+        s2.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        n_cpu = args.cpu_iters
+        om = oracle.Model(sh, weights)
+        st = oracle.State(sh, synth.make_tokens(w), w.step0, w.prompt_len, n_cpu + 1)
+        t1 = time.time()
+        oracle.decode(om, st, n_cpu, want_logits=False)
+        dt = time.time() - t1
+        cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+        cpu = {"value": dt / n_cpu * 1e3, "unit": "ms/token", "cores": cores, "kind": "oracle",
+               "sample": "%d greedy decode iterations (positions 0-%d) of the same model and prompt, "
+                         "fp64 C oracle, OpenMP over output rows" % (n_cpu, n_cpu - 1)}
+        log("cpu oracle: %.1f ms/token on %d threads" % (cpu["value"], cores))
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_tok, 5),
+        "unit": "ms/token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_tok, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_batch1_prompt39_greedy", "layers": sh.layers,
+                   "hidden": sh.hidden, "q_heads": sh.n_q, "kv_heads": sh.n_kv, "head_dim": sh.head_dim,
+                   "ffn": sh.ffn, "vocab": sh.vocab, "tied_lm_head": True, "batch": 1,
+                   "prompt_tokens": P, "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "bound_ms_per_token": round(bound_ms, 5),
+        "frac_of_bound": round(bound_ms / ms_tok, 4),
+        "per_op_ms_per_token": round(per_op, 5) if per_op else None,
+        "speedup_vs_per_op": round(per_op / ms_tok, 3) if per_op else None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
