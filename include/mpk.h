@@ -89,7 +89,8 @@ typedef struct {
   int32_t num_workers;     /* 0 = num_cus */
   int32_t num_schedulers;  /* see sched_mode */
   int32_t sched_mode;      /* MPK_SCHED_* */
-  int32_t trace;           /* 1 = record one trace record per executed task */
+  int32_t trace;           /* 1 = one trace record per executed task, with global ordering
+                              tickets; 2 = the same without tickets (timestamps only, lighter) */
   int32_t reserved;
   uint64_t spin_timeout_ns; /* device watchdog per dependency wait; 0 = 2 s */
 } mpk_launch_cfg;
@@ -210,6 +211,7 @@ typedef struct {
   uint64_t t_end;
   uint32_t hw_id;        /* HW_ID hardware register of the scheduler wave */
   uint32_t xcc_id;       /* XCC_ID hardware register */
+  uint64_t t_ready;      /* inputs staged, weight stream about to be consumed (GEMV tasks; else 0) */
 } mpk_trace_record;
 
 int mpk_read_trace(mpk_exec_t exec, void* host_buf, size_t bytes, size_t* written);

@@ -80,7 +80,7 @@ class mpk_meta(ctypes.Structure):
 class mpk_trace_record(ctypes.Structure):
     _fields_ = [("task", c_i32), ("iteration", c_i32), ("start_ticket", c_u32),
                 ("end_ticket", c_u32), ("t_start", c_u64), ("t_end", c_u64),
-                ("hw_id", c_u32), ("xcc_id", c_u32)]
+                ("hw_id", c_u32), ("xcc_id", c_u32), ("t_ready", c_u64)]
 
 
 class mpk_task_info(ctypes.Structure):
@@ -99,7 +99,7 @@ class mpk_graph_info(ctypes.Structure):
 
 TRACE_DTYPE_FIELDS = [("task", "<i4"), ("iteration", "<i4"), ("start_ticket", "<u4"),
                       ("end_ticket", "<u4"), ("t_start", "<u8"), ("t_end", "<u8"),
-                      ("hw_id", "<u4"), ("xcc_id", "<u4")]
+                      ("hw_id", "<u4"), ("xcc_id", "<u4"), ("t_ready", "<u8")]
 
 
 class MPKError(RuntimeError):

@@ -40,8 +40,10 @@ void mpk_clear_error() { g_err.clear(); }
 extern "C" const char* mpk_last_error(void) { return g_err.c_str(); }
 
 int mpk_attn_splits(int num_workers, int batch, int nkv, int max_seq) {
+  // Enough splits that one split holds at most ~128 positions at full
+  // length, but no more tasks than workers.
   int ns = num_workers / std::max(1, batch * nkv);
-  int by_len = (max_seq + 15) / 16;  // at least ~16 positions per split at full length
+  int by_len = (max_seq + 127) / 128;
   ns = std::min(ns, by_len);
   return std::max(1, ns);
 }
@@ -173,7 +175,6 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
     if (g->embed_src[t] >= 0) reads_meta[op] = 1;
     else reads[op].push_back(t);
   };
-  const int64_t LDS_FLOATS = (MPK_LDS_BYTES - 8192) / 4;
 
   for (int i = 0; i < n_ops; ++i) {
     const mpk_op& o = g->ops[i];
@@ -198,9 +199,13 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
         if ((rc = check_tensor(g, o.in[0], MPK_F32, {B, K}, "x", i))) return rc;
         if (K % 8) return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": K must be a multiple of 8");
         const int nseg = (K + MPK_SEG - 1) / MPK_SEG;
-        if ((int64_t)B * nseg * MPK_SEG > LDS_FLOATS && (int64_t)B * ((K + 511) / 512) * 512 > LDS_FLOATS)
-          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) +
-                                             ": num_requests * K does not fit the LDS staging buffer");
+        {
+          // columns are split over the 8 worker wavefronts in 512-column units
+          const int upr = (K + 511) / 512;
+          if (!((upr % MPK_NW == 0 && upr / MPK_NW <= 3) || (MPK_NW % upr == 0)))
+            return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": K = " + std::to_string(K) +
+                                               " must give 1, 2, 4, 8, 16 or 24 units of 512 columns");
+        }
         act_read(i, o.in[0]);
         D.kind = MPK_TK_GEMV;
         D.K = K;
@@ -270,9 +275,12 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
                                              " rows cannot give " + std::to_string(T) +
                                              " tiles of >= " + std::to_string(min_units) + " rows");
         D.ntiles = T;
-        if (D.epi == MPK_EPI_RESID && (int64_t)B * ((U + T - 1) / T) * a > 512)
+        if (D.kind == MPK_TK_GEMV && (int64_t)B * ((U + T - 1) / T) * a > 512)
           return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) +
-                                             ": residual rows per tile x num_requests exceed 512");
+                                             ": rows per tile x num_requests exceed 512");
+        if ((int64_t)B * ((U + T - 1) / T) * a * 32 > (B == 1 ? 28 * 1024 : 40 * 1024))
+          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) +
+                                             ": rows per tile x num_requests exceed the partial-sum buffer");
         break;
       }
       case MPK_OP_ATTENTION: {
@@ -305,55 +313,73 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
         return mpk_fail(MPK_ERR_GRAPH, "op " + std::to_string(i) + " reads " + tname(g, t) +
                                            " before its producer op " + std::to_string(p));
     }
-  // ---- events and dependencies ----
-  std::vector<int> op_ev(n_ops, -1);
-  for (int i = 0; i < n_ops; ++i) {
+  // ---- internal argmax operator after the LM head ----
+  // The LM head's tiles each publish a (max, index) pair; one argmax task
+  // reduces them, writes the token and advances step (the iteration's end).
+  int NA = n_ops;
+  if (lm_op >= 0) {
+    mpk_dev_op A{};
+    A.kind = MPK_TK_ARGMAX;
+    A.ntiles = 1;
+    A.N0 = g->dops[lm_op].N0;
+    g->dops.push_back(A);
+    g->argmax_op = NA;
+    reads.emplace_back();
+    reads_meta.push_back(1);
+    ++NA;
+  }
+  // ---- events: one flag per producer task (per merge group for attention) ----
+  std::vector<int> op_ev(NA, -1);
+  for (int i = 0; i < NA; ++i) {
     if (g->dops[i].kind == 0) continue;
     op_ev[i] = (int)g->ev_count.size();
     const mpk_dev_op& D = g->dops[i];
-    int cnt = D.kind == MPK_TK_GEMV ? D.ntiles : D.kind == MPK_TK_ATTN ? B * D.nkv : 1;
+    int cnt = D.kind == MPK_TK_ATTN ? B * D.nkv : D.ntiles;
     g->ev_count.push_back(cnt);
     g->ev_op.push_back(i);
+    g->ev_base.push_back(g->n_flags);
+    g->n_flags += cnt;
     g->dops[i].event = op_ev[i];
   }
   int sink = -1;
-  for (int i = n_ops - 1; i >= 0; --i)
+  for (int i = NA - 1; i >= 0; --i)
     if (g->dops[i].kind) {
       sink = i;
       break;
     }
   if (sink < 0) return mpk_fail(MPK_ERR_GRAPH, "graph has no operator with work");
-  if (lm_op >= 0 && lm_op != sink)
+  if (lm_op >= 0 && lm_op != n_ops - 1)
     return mpk_fail(MPK_ERR_GRAPH, "the LM head operator must be the last operator");
   g->sink = sink;
   // same-iteration ancestors
-  std::vector<std::set<int>> direct(n_ops), anc(n_ops);
-  for (int i = 0; i < n_ops; ++i) {
+  std::vector<std::set<int>> direct(NA), anc(NA);
+  for (int i = 0; i < NA; ++i) {
     if (!g->dops[i].kind) continue;
     for (int t : reads[i]) {
       int p = g->producer[t];
       if (p >= 0 && g->dops[p].kind) direct[i].insert(p);
     }
+    if (i == g->argmax_op) direct[i].insert(lm_op);
     for (int p : direct[i]) {
       anc[i].insert(p);
       anc[i].insert(anc[p].begin(), anc[p].end());
     }
   }
-  for (int i = 0; i < n_ops; ++i)
+  for (int i = 0; i < NA; ++i)
     if (g->dops[i].kind && i != sink && !anc[sink].count(i))
       return mpk_fail(MPK_ERR_GRAPH, "op " + std::to_string(i) +
                                          " is not an ancestor of the last operator");
   // previous-iteration edge: readers of tokens/step (through the embedding or
   // directly) and every operator without producers wait for the sink.
-  std::vector<int> has_prev(n_ops, 0), needs_prev(n_ops, 0);
-  for (int i = 0; i < n_ops; ++i) {
+  std::vector<int> has_prev(NA, 0), needs_prev(NA, 0);
+  for (int i = 0; i < NA; ++i) {
     if (!g->dops[i].kind) continue;
-    needs_prev[i] = (reads_meta[i] && lm_op >= 0) || direct[i].empty();
+    needs_prev[i] = (reads_meta[i] && lm_op >= 0 && i != g->argmax_op) || direct[i].empty();
     has_prev[i] = needs_prev[i];
     for (int p : anc[i]) has_prev[i] |= has_prev[p];
   }
-  std::vector<std::vector<std::pair<int, int>>> deps(n_ops);  // (op, prev)
-  for (int i = 0; i < n_ops; ++i) {
+  std::vector<std::vector<std::pair<int, int>>> deps(NA);  // (op, prev)
+  for (int i = 0; i < NA; ++i) {
     if (!g->dops[i].kind) continue;
     for (int p : direct[i]) {
       bool implied = false;
@@ -371,9 +397,9 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
       return mpk_fail(MPK_ERR_GRAPH, "op " + std::to_string(i) + " has more than 3 direct producers");
   }
   // ---- tasks ----
-  g->op_first_task.assign(n_ops, 0);
-  g->op_ntasks.assign(n_ops, 0);
-  for (int i = 0; i < n_ops; ++i) {
+  g->op_first_task.assign(NA, 0);
+  g->op_ntasks.assign(NA, 0);
+  for (int i = 0; i < NA; ++i) {
     mpk_dev_op& D = g->dops[i];
     g->op_first_task[i] = (int)g->tasks.size();
     if (!D.kind) continue;
@@ -385,37 +411,41 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
       T.tile = t;
       T.worker = (int)(((int64_t)t * W) / D.ntiles);
       T.split = -1;
+      T.out_flag = g->ev_base[op_ev[i]] + t;
       if (D.kind == MPK_TK_ATTN) {
         int per_req = D.nkv * D.nsplit;
         T.row0 = t / per_req;                   // request
         T.nrows = (t % per_req) / D.nsplit;     // kv head
         T.split = t % D.nsplit;
         T.last_only = 1;
+        T.out_flag = g->ev_base[op_ev[i]] + T.row0 * D.nkv + T.nrows;
+      } else if (D.kind == MPK_TK_ARGMAX) {
+        T.worker = 0;
+        T.row0 = 0;
+        T.nrows = D.N0;
       } else {
         const int a = D.pairs ? 2 : 1;
         const int U = (D.N0 + D.N1 + D.N2) / a;
         int u0 = (int)((int64_t)t * U / D.ntiles), u1 = (int)((int64_t)(t + 1) * U / D.ntiles);
         T.row0 = u0 * a;
         T.nrows = (u1 - u0) * a;
-        T.last_only = D.kind == MPK_TK_LMHEAD;
       }
       T.n_deps = (int)deps[i].size();
-      for (int k = 0; k < MPK_MAX_DEPS; ++k) T.dep_ev[k] = T.dep_cnt[k] = T.dep_prev[k] = -1;
-      for (int k = 0; k < T.n_deps; ++k) {
-        T.dep_ev[k] = op_ev[deps[i][k].first];
-        T.dep_cnt[k] = g->ev_count[T.dep_ev[k]];
-        T.dep_prev[k] = deps[i][k].second;
-      }
-      T.out_ev = op_ev[i];
-      g->tasks.push_back(T);
+      for (int k = 0; k < MPK_MAX_DEPS; ++k) T.dep_base[k] = T.dep_n[k] = T.dep_prev[k] = -1;
       mpk_task_info I{};
-      I.op = i, I.tile = t, I.worker = T.worker, I.row0 = T.row0, I.nrows = T.nrows, I.split = T.split;
-      for (int k = 0; k < MPK_MAX_DEPS; ++k) {
-        I.dep_event[k] = T.dep_ev[k];
-        I.dep_count[k] = T.dep_cnt[k];
-        I.dep_prev[k] = T.dep_prev[k];
+      for (int k = 0; k < MPK_MAX_DEPS; ++k) I.dep_event[k] = I.dep_count[k] = I.dep_prev[k] = -1;
+      for (int k = 0; k < T.n_deps; ++k) {
+        const int e = op_ev[deps[i][k].first];
+        T.dep_base[k] = g->ev_base[e];
+        T.dep_n[k] = g->ev_count[e];
+        T.dep_prev[k] = deps[i][k].second;
+        I.dep_event[k] = e;
+        I.dep_count[k] = g->ev_count[e];
+        I.dep_prev[k] = deps[i][k].second;
       }
-      I.out_event = T.out_ev;
+      g->tasks.push_back(T);
+      I.op = i, I.tile = t, I.worker = T.worker, I.row0 = T.row0, I.nrows = T.nrows, I.split = T.split;
+      I.out_event = op_ev[i];
       g->info.push_back(I);
     }
   }
@@ -457,7 +487,7 @@ extern "C" int mpk_get_graph_info(mpk_graph_t g, mpk_graph_info* info) {
   info->num_events = (int)g->ev_count.size();
   info->num_workers = g->num_workers;
   info->max_queue = g->max_queue;
-  info->num_ops = (int)g->ops.size();
+  info->num_ops = (int)g->dops.size();
   info->sink_op = g->sink;
   info->tasks = g->info.data();
   info->event_count = g->ev_count.data();
@@ -476,14 +506,14 @@ extern "C" int mpk_simulate(mpk_graph_t g, int32_t n_iter, uint32_t seed, int32_
   if (!g || n_iter <= 0 || !trace || jitter_us < 0 || timeout_ms <= 0)
     return mpk_fail(MPK_ERR_INVALID_ARG, "mpk_simulate: bad argument");
   const int W = g->num_workers, NT = (int)g->tasks.size();
-  std::vector<std::atomic<uint32_t>> ev(g->ev_count.size());
-  for (auto& e : ev) e.store(0);
-  // last-arriver groups: attention (op, request, kv head); LM head (op)
+  std::vector<std::atomic<uint32_t>> flags(g->n_flags);
+  for (auto& e : flags) e.store(0);
+  // last-arriver groups of attention: (op, request, kv head)
   std::vector<std::atomic<uint32_t>> grp(NT);
   for (auto& e : grp) e.store(0);
   std::atomic<uint32_t> ticket{0};
   std::atomic<int> failed{0};
-  for (int64_t i = 0; i < (int64_t)n_iter * NT; ++i) trace[i] = mpk_trace_record{-1, -1, 0, 0, 0, 0, 0, 0};
+  for (int64_t i = 0; i < (int64_t)n_iter * NT; ++i) trace[i] = mpk_trace_record{-1, -1, 0, 0, 0, 0, 0, 0, 0};
   auto t0 = std::chrono::steady_clock::now();
   auto now_ns = [&] {
     return (uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(
@@ -493,18 +523,20 @@ extern "C" int mpk_simulate(mpk_graph_t g, int32_t n_iter, uint32_t seed, int32_
     std::mt19937 rng(seed * 7919u + (uint32_t)w);
     for (int s = 0; s < n_iter && !failed.load(); ++s) {
       for (int k = 0; k < g->qlen[w]; ++k) {
-        const mpk_dev_task& T = g->tasks[g->queues[(size_t)w * g->max_queue + k].task];
-        int tid = g->queues[(size_t)w * g->max_queue + k].task;
+        const int tid = g->queues[(size_t)w * g->max_queue + k].task;
+        const mpk_dev_task& T = g->tasks[tid];
         auto start = std::chrono::steady_clock::now();
         for (int d = 0; d < T.n_deps; ++d) {
-          uint32_t target = (uint32_t)T.dep_cnt[d] * (uint32_t)(s + 1 - T.dep_prev[d]);
-          while (ev[T.dep_ev[d]].load(std::memory_order_acquire) < target) {
-            if (failed.load()) return;
-            if (std::chrono::steady_clock::now() - start > std::chrono::milliseconds(timeout_ms)) {
-              failed.store(1);
-              return;
+          const uint32_t target = (uint32_t)(s + 1 - T.dep_prev[d]);
+          for (int f = T.dep_base[d]; f < T.dep_base[d] + T.dep_n[d]; ++f) {
+            while (flags[f].load(std::memory_order_acquire) < target) {
+              if (failed.load()) return;
+              if (std::chrono::steady_clock::now() - start > std::chrono::milliseconds(timeout_ms)) {
+                failed.store(1);
+                return;
+              }
+              std::this_thread::yield();
             }
-            std::this_thread::yield();
           }
         }
         mpk_trace_record& R = trace[(int64_t)s * NT + tid];
@@ -517,20 +549,13 @@ extern "C" int mpk_simulate(mpk_graph_t g, int32_t n_iter, uint32_t seed, int32_
         bool signal = true;
         const mpk_dev_op& D = g->dops[T.op];
         if (T.last_only) {
-          int group, size;
-          if (T.kind == MPK_TK_ATTN) {
-            group = g->op_first_task[T.op] + (T.row0 * D.nkv + T.nrows) * D.nsplit;
-            size = D.nsplit;
-          } else {
-            group = g->op_first_task[T.op];
-            size = D.ntiles;
-          }
-          uint32_t old = grp[group].fetch_add(1, std::memory_order_acq_rel);
-          signal = (old % (uint32_t)size) == (uint32_t)size - 1;
+          const int group = g->op_first_task[T.op] + (T.row0 * D.nkv + T.nrows) * D.nsplit;
+          const uint32_t old = grp[group].fetch_add(1, std::memory_order_acq_rel);
+          signal = (old % (uint32_t)D.nsplit) == (uint32_t)D.nsplit - 1;
         }
         R.end_ticket = ticket.fetch_add(1);
         R.t_end = now_ns();
-        if (signal) ev[T.out_ev].fetch_add(1, std::memory_order_release);
+        if (signal) flags[T.out_flag].store((uint32_t)(s + 1), std::memory_order_release);
       }
     }
   };

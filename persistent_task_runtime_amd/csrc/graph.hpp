@@ -24,7 +24,9 @@ struct mpk_graph_s {
   std::vector<int> op_first_task, op_ntasks;
   std::vector<mpk_dev_task> tasks;
   std::vector<mpk_task_info> info;
-  std::vector<int> ev_count, ev_op;
+  std::vector<int> ev_count, ev_op, ev_base;  // per event: producers (flags), operator, first flag
+  int n_flags = 0;
+  int argmax_op = -1;                           // internal operator appended after the LM head
   std::vector<int> qlen;
   int max_queue = 0;
   std::vector<mpk_dev_qentry> queues;  // [num_workers][max_queue]

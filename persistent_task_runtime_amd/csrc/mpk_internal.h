@@ -15,11 +15,11 @@
 #define MPK_SEG 4096                    /* columns of one weight block */
 #define MPK_BU 8                        /* 16-byte-per-lane units per block */
 #define MPK_MAX_DEPS 3
-#define MPK_ATTN_SUB 1024               /* positions scored per pass of an attention task */
+#define MPK_ATTN_SUB 512                /* positions scored per pass of an attention task */
 #define MPK_LDS_BYTES (96 * 1024)       /* dynamic LDS per workgroup (forces one per CU) */
 #define MPK_MAX_BATCH 8
 
-enum { MPK_TK_GEMV = 1, MPK_TK_ATTN = 2, MPK_TK_LMHEAD = 3 };
+enum { MPK_TK_GEMV = 1, MPK_TK_ATTN = 2, MPK_TK_LMHEAD = 3, MPK_TK_ARGMAX = 4 };
 enum { MPK_EPI_STORE = 0, MPK_EPI_RESID = 1, MPK_EPI_SILU = 2, MPK_EPI_ARGMAX = 3 };
 
 /* One operator as the device sees it. */
@@ -57,7 +57,9 @@ typedef struct {
   int64_t logits_iters;
 } mpk_dev_op;
 
-/* One task (a tile of an operator). */
+/* One task (a tile of an operator).  Completion is published as an
+ * iteration stamp (iteration + 1) in the task's flag; a dependency on an
+ * operator is satisfied when all of that operator's flags reach the stamp. */
 typedef struct {
   int32_t kind;
   int32_t op;
@@ -66,12 +68,12 @@ typedef struct {
   int32_t row0, nrows; /* GEMV: virtual rows; ATTN: request, kv head */
   int32_t split;       /* ATTN split */
   int32_t n_deps;
-  int32_t dep_ev[MPK_MAX_DEPS];
-  int32_t dep_cnt[MPK_MAX_DEPS];
-  int32_t dep_prev[MPK_MAX_DEPS];
-  int32_t out_ev;
-  int32_t last_only;   /* 1: only the last arriver of the tile group signals */
-  int32_t pad[2];
+  int32_t dep_base[MPK_MAX_DEPS]; /* first flag of the producer operator */
+  int32_t dep_n[MPK_MAX_DEPS];    /* number of flags of the producer operator */
+  int32_t dep_prev[MPK_MAX_DEPS]; /* 1: wait for the previous iteration's stamp */
+  int32_t out_flag;    /* flag this task stamps (attention: its group's last arriver) */
+  int32_t last_only;   /* 1: only the last arriver of the tile group stamps */
+  int32_t pad[1];
 } mpk_dev_task;
 
 /* Per queue entry: task id and the queue position of the next task that
@@ -95,7 +97,7 @@ typedef struct {
   const mpk_dev_qentry* queues; /* [num_workers][qstride] */
   const mpk_dev_qentry* single_q; /* [n_tasks]: {task, -1} (one-launch-per-operator path) */
   const int32_t* qlen;          /* [num_workers] */
-  uint32_t* events;
+  uint32_t* flags;               /* [n_flags] iteration stamps */
   int32_t* tokens;
   int32_t* step;
   const int32_t* prompt_len;
@@ -103,6 +105,7 @@ typedef struct {
   const float* rope_sin;
   mpk_dev_status* status;
   mpk_trace_record* trace;      /* NULL = off */
+  int32_t trace_tickets;        /* 1: also take global tickets (slower) */
   uint32_t* ticket_ctr;
   uint64_t timeout_ticks;       /* s_memrealtime ticks (100 MHz) */
   int32_t qstride;
@@ -113,6 +116,7 @@ typedef struct {
   int32_t rope_half;
   float rms_eps;
   int32_t vocab;
+  int32_t pos0[MPK_MAX_BATCH];  /* step[r] at launch: position of request r in iteration s is pos0[r] + s */
 } mpk_kparams;
 
 #endif

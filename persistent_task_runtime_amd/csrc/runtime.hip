@@ -147,17 +147,66 @@ DEV uint32_t hwreg_xcc_id() {
 // flight.  The compiler does not model the LDS writes of global_load_lds, so
 // the ring's consumer waits explicitly; the memory clobber keeps the LDS read
 // of the slot after the wait.
+// LDS reads inside the weight stream are written in asm, each block waiting
+// for its own reads: the compiler cannot tell LDS reads from the DMA'd ring
+// slots and would otherwise wait for every ring load in flight before any
+// LDS read it sees.
+DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lptr_t)(void*)p; }
+
+DEV u32x4 lds_read_u32x4(uint32_t a) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+
+// Two float4 at byte address a and a + 1024.
+DEV void lds_read_2f4(uint32_t a, f32x4& x0, f32x4& x1) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(x0), "=v"(x1)
+               : "v"(a)
+               : "memory");
+}
+
+DEV float lds_read_f32(uint32_t a) {
+  float v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+
 template <int N>
 DEV void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Device-scope ("sc1") accesses.  Every value one task hands to another task
+// on another CU (activations, attention partials, K/V rows, tokens, step,
+// completion flags) is written with device-scope stores and read with
+// device-scope loads: these go to the point of coherence shared by all XCDs,
+// so no L2 write-back or invalidate is needed to pass data between CUs.  A
+// producer stamps its flag only after s_waitcnt vmcnt(0) has seen all its
+// device-scope stores complete; a consumer issues its device-scope loads only
+// after it has seen every producer flag.
+DEV float ld_dev(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV int ld_devi(const int32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV uint32_t ld_devu(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV void st_devi(int32_t* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV void st_devu(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// all vector-memory operations of this wavefront complete (the scheduler
+// wavefront issues no weight loads, so this waits only for its own stores)
+DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // LDS layout (bytes)
 //   [0, 2048)                 control words, reductions, 1/rms, tile argmax
+//   [LDS_OUT, +4096)          task outputs staged for the scheduler wavefront
 //   [LDS_X, +XS)              staged activations x (or attention scratch)
-//   [LDS_RES, +2048)          staged residual rows of the tile
-//   [LDS_RING, +NW*R*1024)    weight rings, R units of 1 KB per wavefront
+//   [RES, +2048)              staged residual rows of the tile
+//   [RING, +NW*R*1024)        weight rings, R units of 1 KB per wavefront
 // x is staged permuted so each 16-byte LDS read is lane-contiguous:
 //   column k -> unit u = k / 512, lane l = (k % 512) / 8, half h = (k % 8) / 4
 //   offset (floats) = u * 512 + h * 256 + l * 4 + (k % 4)
@@ -166,26 +215,44 @@ DEV void vm_wait() {
 #define LDS_RED 256                      // [16][8] floats: per-wave partials
 #define LDS_INV (LDS_RED + 16 * 8 * 4)   // [8] floats
 #define LDS_BEST (LDS_INV + 64)          // [8 waves][8] (float) + [8][8] (int)
-#define LDS_X 2048
+#define LDS_POS (LDS_BEST + 512)         // [8] int: step[r] of the current iteration
+#define LDS_OUT 2048
+#define LDS_OUT_FLOATS 1024
+#define LDS_X (LDS_OUT + LDS_OUT_FLOATS * 4)
 #define LDS_RES_BYTES 2048
 
 template <int NB>
 struct Lay {
-  static constexpr int XS = 49152 * NB;                    // staged x bytes
-  static constexpr int RES = LDS_X + XS;                   // residual rows
-  static constexpr int RING = RES + LDS_RES_BYTES;         // weight rings
-  static constexpr int R = NB == 1 ? 12 : 6;               // ring units per wavefront
+  static constexpr int XS = 49152 * NB;             // staged x bytes
+  static constexpr int RES = LDS_X + XS;            // residual rows
+  static constexpr int RING = RES + LDS_RES_BYTES;  // weight rings
+  static constexpr int R = NB == 1 ? 12 : 6;        // ring units per wavefront
   static constexpr int TOTAL = RING + MPK_NW * R * 1024;
 };
 static_assert(Lay<1>::TOTAL <= 160 * 1024, "LDS budget");
 static_assert(Lay<2>::TOTAL <= 160 * 1024, "LDS budget");
 
+DEV void lds_write_f32(uint32_t a, float v) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(v) : "memory");
+}
+
 DEV int xperm(int k) { return (k & ~511) + ((k & 4) << 6) + (((k & 511) >> 3) << 2) + (k & 3); }
 
+// Position of request b in the current iteration (read once per iteration
+// by the scheduler wavefront into LDS_POS).
+DEV int cur_pos(const char* smem, int b) { return __builtin_amdgcn_readfirstlane(reinterpret_cast<const volatile int*>(smem + LDS_POS)[b]); }
+
+// Scheduler wavefront: positions of iteration s into LDS_POS (uniform
+// indices into the kernel-argument array).
+DEV void set_positions(const mpk_kparams& P, char* smem, int s, int lane) {
+  if (lane == 0)
+    for (int b = 0; b < P.B; ++b) reinterpret_cast<volatile int*>(smem + LDS_POS)[b] = P.pos0[b] + s;
+}
+
 // Token id consumed by request b in this iteration.
-DEV int cur_token(const mpk_kparams& P, int b) {
-  const int p = gldi(P.step + b);
-  const int t = gldi(P.tokens + (int64_t)b * P.tokens_width + p);
+DEV int cur_token(const mpk_kparams& P, const char* smem, int b) {
+  const int p = cur_pos(smem, b);
+  const int t = ld_devi(P.tokens + (int64_t)b * P.tokens_width + p);
   return t < 0 ? 0 : (t >= P.vocab ? P.vocab - 1 : t);  // ids are checked on the host; stay in bounds
 }
 
@@ -197,14 +264,6 @@ DEV int cur_token(const mpk_kparams& P, int b) {
 //   units of 512 bf16 (1 KB, 16 bytes per lane); a wavefront's sequence is
 //   its rows in order, each row's units in order.
 // ---------------------------------------------------------------------------
-DEV const uint16_t* row_ptr(cop& D, int vrow) {
-  if (D.pairs) return ((vrow & 1) ? D.W1 : D.W0) + (int64_t)(vrow >> 1) * D.K;
-  if (vrow < D.N0) return D.W0 + (int64_t)vrow * D.K;
-  vrow -= D.N0;
-  if (vrow < D.N1) return D.W1 + (int64_t)vrow * D.K;
-  return D.W2 + (int64_t)(vrow - D.N1) * D.K;
-}
-
 DEV int units_per_row(cop& D) { return (D.K + 511) >> 9; }
 
 DEV int wave_units(cop& D, ctask& T, int wave) {
@@ -232,25 +291,39 @@ struct Issuer {
 };
 
 DEV void issuer_row(Issuer& I, int wave) {
+  // Select among loaded pointer values (not among field addresses: a
+  // variable-index field access would keep the issuer in scratch memory).
+  const uint16_t* w0 = unip(I.W0);
+  const uint16_t* w1 = unip(I.W1);
+  const uint16_t* w2 = unip(I.W2);
   int vrow = I.row0 + (wave + MPK_NW * I.kk) * I.a + I.rr;
-  const uint16_t* r;
+  const uint16_t* base;
+  int r;
   if (I.pairs) {
-    r = ((vrow & 1) ? I.W1 : I.W0) + (int64_t)(vrow >> 1) * I.K;
+    base = (vrow & 1) ? w1 : w0;
+    r = vrow >> 1;
   } else if (vrow < I.N0) {
-    r = I.W0 + (int64_t)vrow * I.K;
+    base = w0;
+    r = vrow;
   } else if (vrow - I.N0 < I.N1) {
-    r = I.W1 + (int64_t)(vrow - I.N0) * I.K;
+    base = w1;
+    r = vrow - I.N0;
   } else {
-    r = I.W2 + (int64_t)(vrow - I.N0 - I.N1) * I.K;
+    base = w2;
+    r = vrow - I.N0 - I.N1;
   }
-  I.row = unip(r);
+  I.row = unip(base + (int64_t)r * I.K);
 }
 
 // Point the issuer at the first stream task at or after queue position k of
 // iteration s that gives this wave at least one unit.
 DEV void issuer_seek(Issuer& I, const mpk_kparams& P, cqent* Q, int qlen, int s, int k, int wave) {
   int found = 0;
+  s = uni(s);
+  k = uni(k);
+  qlen = uni(qlen);
   for (int guard = 0; guard < 2 * qlen + 2 && !found; ++guard) {
+    k = uni(k);
     if (k >= qlen) {
       k = uni(k - qlen);
       s = uni(s + 1);
@@ -354,8 +427,7 @@ DEV void ring_fill(Issuer& I, RingState& S, char* ring_wave, const mpk_kparams& 
 // compute 1 / rms per request, and stage the tile's residual rows.  All
 // waves take part in the barriers.
 template <int NB>
-DEV void stage_x(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid,
-                 bool sched) {
+DEV void stage_x(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, bool sched) {
   float* xs = reinterpret_cast<float*>(smem + LDS_X);
   float* res = reinterpret_cast<float*>(smem + Lay<NB>::RES);
   float* red = reinterpret_cast<float*>(smem + LDS_RED);
@@ -370,7 +442,7 @@ DEV void stage_x(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid,
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const uint16_t* erow = nullptr;
-      if (D.x_embed) erow = D.E + (int64_t)cur_token(P, b) * K;
+      if (D.x_embed) erow = D.E + (int64_t)cur_token(P, smem, b) * K;
       for (int k = tid * 4; k < Kpad; k += MPK_NW * 64 * 4) {
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         if (k < K) {
@@ -378,8 +450,8 @@ DEV void stage_x(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid,
             const u32x2 e = gldv<u32x2>(erow + k);
             v[0] = bf16lo(e.x), v[1] = bf16hi(e.x), v[2] = bf16lo(e.y), v[3] = bf16hi(e.y);
           } else {
-            const f32x4 f = gldv<f32x4>(D.x + (int64_t)b * K + k);
-            v[0] = f.x, v[1] = f.y, v[2] = f.z, v[3] = f.w;
+            const float* xp = D.x + (int64_t)b * K + k;
+            v[0] = ld_dev(xp), v[1] = ld_dev(xp + 1), v[2] = ld_dev(xp + 2), v[3] = ld_dev(xp + 3);
           }
           if (D.has_norm) {
             const u32x2 gg = gldv<u32x2>(D.gain + k);
@@ -397,8 +469,8 @@ DEV void stage_x(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid,
         for (int i = tid; i < T.nrows; i += MPK_NW * 64) {
           const int row = T.row0 + i;
           float r;
-          if (D.res_embed) r = bf16f(gld16(D.E + (int64_t)cur_token(P, b) * D.n_out + row));
-          else r = gld(D.resid + (int64_t)b * D.n_out + row);
+          if (D.res_embed) r = bf16f(gld16(D.E + (int64_t)cur_token(P, smem, b) * D.n_out + row));
+          else r = ld_dev(D.resid + (int64_t)b * D.n_out + row);
           res[b * T.nrows + i] = r;
         }
       }
@@ -426,24 +498,36 @@ DEV void stage_x(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid,
 
 DEV float silu(float g) { return g / (1.0f + expf(-g)); }
 
+DEV void unpack8(const u32x4 w, float (&f)[8]) {
+  f[0] = bf16lo(w.x), f[1] = bf16hi(w.x), f[2] = bf16lo(w.y), f[3] = bf16hi(w.y);
+  f[4] = bf16lo(w.z), f[5] = bf16hi(w.z), f[6] = bf16lo(w.w), f[7] = bf16hi(w.w);
+}
+
 // ---------------------------------------------------------------------------
 // GEMV-type task: rmsnorm_linear (EPI_STORE), linear + residual (EPI_RESID),
 // rmsnorm + gate/up + SiLU-mul (EPI_SILU), final norm + LM head + tile argmax
-// (EPI_ARGMAX).  Returns true when the task's completion must be signalled.
+// (EPI_ARGMAX).  Row results are staged in LDS (LDS_OUT); the scheduler
+// wavefront publishes them after the task.
 // ---------------------------------------------------------------------------
 template <int NB>
-DEV bool gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I,
-                   RingState& RS, cqent* Q, int qlen, int s, char* smem, int tid,
-                   bool sched) {
+DEV void gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I, RingState& RS, cqent* Q, int qlen,
+                   int s, char* smem, int tid, bool sched) {
   constexpr int R = Lay<NB>::R;
   stage_x<NB>(P, D, T, smem, tid, sched);
+  if (sched && P.trace && (tid & 63) == 0)
+    P.trace[(int64_t)s * P.n_tasks + (&T - tasks_of(P))].t_ready = clock_now();
   const int EPI = D.epi;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const float* xs = reinterpret_cast<const float*>(smem + LDS_X);
   const float* res = reinterpret_cast<const float*>(smem + Lay<NB>::RES);
-  const float* inv = reinterpret_cast<const float*>(smem + LDS_INV);
+  float* outs = reinterpret_cast<float*>(smem + LDS_OUT);
+  const float* inv_lds = reinterpret_cast<const float*>(smem + LDS_INV);
+  float inv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) inv[b] = inv_lds[b];
   char* ring_wave = smem + Lay<NB>::RING + wave * R * 1024;
   const int Kpad = ((D.K + 511) / 512) * 512;
+  const int n_out_tile = D.pairs ? T.nrows / 2 : T.nrows;
   float best_v[NB];
   int best_i[NB];
 #pragma unroll
@@ -458,14 +542,14 @@ DEV bool gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I,
     for (int b = 0; b < NB; ++b) acc[b] = 0.f, gate[b] = 0.f;
     for (int i = 0; i < n; ++i) {
       wait_head<R>(RS.inflight);
-      const u32x4 w = *reinterpret_cast<const u32x4*>(ring_wave + RS.head * 1024 + lane * 16);
+      const u32x4 w = lds_read_u32x4(lds_addr(ring_wave) + RS.head * 1024 + lane * 16);
       const float wf[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
                            bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
       const int base = u * 512 + lane * 4;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float4 x0 = *reinterpret_cast<const float4*>(xs + b * Kpad + base);
-        const float4 x1 = *reinterpret_cast<const float4*>(xs + b * Kpad + base + 256);
+        f32x4 x0, x1;
+        lds_read_2f4(lds_addr(xs) + (uint32_t)(b * Kpad + base) * 4u, x0, x1);
         float sacc = acc[b];
         sacc = fmaf(wf[0], x0.x, sacc);
         sacc = fmaf(wf[1], x0.y, sacc);
@@ -483,20 +567,23 @@ DEV bool gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I,
       ring_top_up<R>(I, RS, ring_wave, P, Q, qlen, wave, lane);
       if (++u == upr) {
         u = 0;
-        const int vrow = T.row0 + (wave + MPK_NW * kk) * a + rr;
+        const int lrow = (wave + MPK_NW * kk) * a + rr;  // row within the tile
+        const int vrow = T.row0 + lrow;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const float sum = wave_sum(acc[b]);
           acc[b] = 0.f;
+          // LDS traffic inside the weight stream stays in asm (see lds_read_u32x4)
           if (EPI == MPK_EPI_STORE) {
-            if (lane == 0) gst(D.y + (int64_t)b * D.n_out + vrow, sum * inv[b]);
+            if (lane == 0) lds_write_f32(lds_addr(outs + b * n_out_tile + lrow), sum * inv[b]);
           } else if (EPI == MPK_EPI_RESID) {
-            if (lane == 0) gst(D.y + (int64_t)b * D.n_out + vrow, res[b * T.nrows + (vrow - T.row0)] + sum);
+            const float rv = lds_read_f32(lds_addr(res) + (uint32_t)(b * T.nrows + lrow) * 4u);
+            if (lane == 0) lds_write_f32(lds_addr(outs + b * n_out_tile + lrow), rv + sum);
           } else if (EPI == MPK_EPI_SILU) {
             if (rr == 0) {
               gate[b] = sum * inv[b];
             } else if (lane == 0) {
-              gst(D.y + (int64_t)b * D.n_out + (vrow >> 1), silu(gate[b]) * (sum * inv[b]));
+              lds_write_f32(lds_addr(outs + b * n_out_tile + (lrow >> 1)), silu(gate[b]) * (sum * inv[b]));
             }
           } else {  // ARGMAX
             const float logit = sum * inv[b];
@@ -512,100 +599,157 @@ DEV bool gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I,
       }
     }
   }
-  if (EPI != MPK_EPI_ARGMAX) return true;
-
-  // ---- LM head: tile argmax, then the last tile picks the token ----
-  float* bv = reinterpret_cast<float*>(smem + LDS_BEST);
-  int* bi = reinterpret_cast<int*>(smem + LDS_BEST + MPK_NW * 8 * 4);
-  volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
-  if (!sched && lane == 0) {
+  if (EPI == MPK_EPI_ARGMAX) {
+    // tile argmax over the waves (lowest row among equal maxima)
+    float* bv = reinterpret_cast<float*>(smem + LDS_BEST);
+    int* bi = reinterpret_cast<int*>(smem + LDS_BEST + MPK_NW * 8 * 4);
+    if (!sched && lane == 0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) bv[wave * 8 + b] = best_v[b], bi[wave * 8 + b] = best_i[b];
-  }
-  __syncthreads();
-  float* part = D.part;  // [ntiles][NB] (value, index)
-  if (tid < NB) {
-    float v = -INFINITY;
-    int ix = 0x7fffffff;
-    for (int w = 0; w < MPK_NW; ++w) {
-      const float vv = bv[w * 8 + tid];
-      const int ii = bi[w * 8 + tid];
-      if (vv > v || (vv == v && ii < ix)) v = vv, ix = ii;
+      for (int b = 0; b < NB; ++b) bv[wave * 8 + b] = best_v[b], bi[wave * 8 + b] = best_i[b];
     }
-    gst(part + ((int64_t)T.tile * NB + tid) * 2, v);
-    gst(part + ((int64_t)T.tile * NB + tid) * 2 + 1, __int_as_float(ix));
-  }
-  __syncthreads();
-  if (sched && lane == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(D.tickets, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    ctl[1] = (old % (uint32_t)D.ntiles) == (uint32_t)D.ntiles - 1;
-  }
-  __syncthreads();
-  const bool last = ctl[1] != 0;
-  if (last && tid < NB) {
-    float v = -INFINITY;
-    int ix = 0x7fffffff;
-    for (int t = 0; t < D.ntiles; ++t) {
-      const float vv = gld(part + ((int64_t)t * NB + tid) * 2);
-      const int ii = __float_as_int(gld(part + ((int64_t)t * NB + tid) * 2 + 1));
-      if (vv > v || (vv == v && ii < ix)) v = vv, ix = ii;
+    __syncthreads();
+    if (tid < NB) {
+      float v = -INFINITY;
+      int ix = 0x7fffffff;
+      for (int w = 0; w < MPK_NW; ++w) {
+        const float vv = bv[w * 8 + tid];
+        const int ii = bi[w * 8 + tid];
+        if (vv > v || (vv == v && ii < ix)) v = vv, ix = ii;
+      }
+      outs[2 * tid] = v;
+      outs[2 * tid + 1] = __int_as_float(ix);
     }
-    const int p = gldi(P.step + tid);
-    if (p + 1 >= gldi(P.prompt_len + tid)) *(gi32*)(void*)(P.tokens + (int64_t)tid * P.tokens_width + p + 1) = ix;
-    *(gi32*)(void*)(P.step + tid) = p + 1;
   }
-  return last;
+}
+
+// Scheduler wavefront: publish a GEMV / LM-head task's staged outputs.
+template <int NB>
+DEV void publish_gemv(const mpk_kparams& P, ctask& T, cop& D, const char* smem, int lane) {
+  const float* outs = reinterpret_cast<const float*>(smem + LDS_OUT);
+  if (D.epi == MPK_EPI_ARGMAX) {
+    if (lane < 2 * NB) st_dev(D.part + (int64_t)T.tile * NB * 2 + lane, outs[lane]);
+    return;
+  }
+  const int n_out_tile = D.pairs ? T.nrows / 2 : T.nrows;
+  const int out0 = D.pairs ? T.row0 / 2 : T.row0;
+  for (int i = lane; i < NB * n_out_tile; i += 64) {
+    const int b = i / n_out_tile, j = i - b * n_out_tile;
+    st_dev(D.y + (int64_t)b * D.n_out + out0 + j, outs[i]);
+  }
 }
 
 // ---------------------------------------------------------------------------
+// Argmax task: reduce the LM-head tiles' (max, index) pairs, write the token
+// when the prompt is consumed, advance step (scheduler wavefront only).
+// ---------------------------------------------------------------------------
+template <int NB>
+DEV void argmax_publish(const mpk_kparams& P, cop& D, int lane) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float v = -INFINITY;
+    int ix = 0x7fffffff;
+    for (int t = lane; t < D.N1; t += 64) {  // N1: LM-head tiles
+      const float vv = ld_dev(D.part + ((int64_t)t * NB + b) * 2);
+      const int ii = __float_as_int(ld_dev(D.part + ((int64_t)t * NB + b) * 2 + 1));
+      if (vv > v || (vv == v && ii < ix)) v = vv, ix = ii;
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(v, off);
+      const int oi = __shfl_xor(ix, off);
+      if (ov > v || (ov == v && oi < ix)) v = ov, ix = oi;
+    }
+    if (lane == 0) {
+      const int p = ld_devi(P.step + b);
+      if (p + 1 >= ld_devi(P.prompt_len + b)) st_devi(P.tokens + (int64_t)b * P.tokens_width + p + 1, ix);
+      st_devi(P.step + b, p + 1);
+    }
+  }
+}
+// ---------------------------------------------------------------------------
 // Attention task (request r, kv head j, split c of nsplit): per-head RMSNorm
 // of q and k, RoPE at the request's position p, K/V of p into the caches
-// (written by the split that owns p), scores over this split's positions,
-// softmax partials (max, sum, weighted V) and, in the last arriving split of
-// (r, j), the merge into the attention output of the group's query heads.
+// (by the split that owns p), an online softmax over this split's positions
+// kept per lane group in registers, one merge across the wavefronts, and, in
+// the last arriving split of (r, j), the merge of the splits into the
+// attention output of the group's query heads.
 // ---------------------------------------------------------------------------
 #define ATT_MAXG 4
+#define ATT_ROUNDS 2  // position rounds per wavefront whose K/V rows are loaded together
 
-DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem,
-                   int tid, bool sched) {
+struct SoftState {
+  float m[ATT_MAXG], l[ATT_MAXG], acc[ATT_MAXG][8];
+};
+
+DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, bool sched) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = T.row0, j = T.nrows, c = T.split, NS = D.nsplit;
   const int d = D.d, G = D.nq / D.nkv, half = d >> 1, LP = d >> 3, PPR = 64 / LP;
-  const int p = gldi(P.step + r);
+  const int p = cur_pos(smem, r);
   const int n = p + 1;
-  const int lo = (int)(((int64_t)c * n) / NS), hi = (int)(((int64_t)(c + 1) * n) / NS);
+  // splits in use this iteration: about 128 positions each, at most nsplit
+  const int na = min(NS, (n + 127) / 128);
+  const bool active = c < na;
+  const int lo = active ? (int)(((int64_t)c * n) / na) : n, hi = active ? (int)(((int64_t)(c + 1) * n) / na) : n;
   float* qs = reinterpret_cast<float*>(smem + LDS_X);  // [G][d]
   float* kv = qs + ATT_MAXG * 128;                      // k [d], v [d] (bf16-rounded)
-  float* sc = kv + 256;                                 // [G][SUB]
-  float* redm = sc + ATT_MAXG * MPK_ATTN_SUB;           // [NW][G]
-  float* reds = redm + MPK_NW * ATT_MAXG;               // [NW][G]
-  float* accr = reds + MPK_NW * ATT_MAXG;               // [NW][G][d]
+  float* wm = kv + 256;                                 // [NW][G]
+  float* wl = wm + MPK_NW * ATT_MAXG;                   // [NW][G]
+  float* wacc = wl + MPK_NW * ATT_MAXG;                 // [NW][G][128]
   volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
+  float* outs = reinterpret_cast<float*>(smem + LDS_OUT);               // partial, then o
+  uint32_t* kvrow = reinterpret_cast<uint32_t*>(smem + LDS_OUT) + 640;  // bf16 K row, then V row
   const int qkv_w = (D.nq + 2 * D.nkv) * d;
   const float* qkv = D.x + (int64_t)r * qkv_w;
   uint16_t* kc = D.kc + ((int64_t)(r * D.nkv + j) * D.S) * d;
   uint16_t* vc = D.vc + ((int64_t)(r * D.nkv + j) * D.S) * d;
-  const bool owner = (c == NS - 1);
+  const bool owner = active && c == na - 1;
+  if (!active) return false;  // uniform over the workgroup: no barrier has been passed
+  const int dim0 = (lane % LP) * 8;
+  const int pg = lane / LP;
+  const float scale = 1.0f / sqrtf((float)d);
 
-  // ---- q / k / v of the group ----
+  SoftState st;
+#pragma unroll
+  for (int h = 0; h < ATT_MAXG; ++h) {
+    st.m[h] = -INFINITY, st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
+  }
+  // K/V rows of this wave's first rounds: issued before anything else (the
+  // cache rows below p do not depend on this iteration)
+  u32x4 kr[ATT_ROUNDS], vr[ATT_ROUNDS];
+  auto load_rounds = [&](int base) {
+#pragma unroll
+    for (int q = 0; q < ATT_ROUNDS; ++q) {
+      const int t = base + (wave + MPK_NW * q) * PPR + pg;
+      const int tc = t < hi && t != p ? t : lo;  // in-bounds row for idle lanes
+      kr[q] = gldv<u32x4>(kc + (int64_t)tc * d + dim0);
+      vr[q] = gldv<u32x4>(vc + (int64_t)tc * d + dim0);
+    }
+  };
+  if (!sched && lo < hi) load_rounds(lo);
+
+  // ---- q / k / v of the group: RMSNorm + RoPE (waves 0..G+1) ----
   if (!sched) {
     for (int hh = wave; hh < G + 2; hh += MPK_NW) {
       const float* src = hh < G ? qkv + (int64_t)(j * G + hh) * d
                                 : (hh == G ? qkv + (int64_t)D.nq * d + j * d
                                            : qkv + (int64_t)(D.nq + D.nkv) * d + j * d);
-      const float a = lane < half ? gld(src + lane) : 0.f;
-      const float b = lane < half ? gld(src + lane + half) : 0.f;
+      const float a = lane < half ? ld_dev(src + lane) : 0.f;
+      const float b = lane < half ? ld_dev(src + lane + half) : 0.f;
       if (hh <= G) {
+        const float cs = lane < half ? gld(P.rope_cos + (int64_t)p * half + lane) : 0.f;
+        const float sn = lane < half ? gld(P.rope_sin + (int64_t)p * half + lane) : 0.f;
+        const uint16_t* gsrc = hh < G ? D.qn : D.kn;
+        const float ga = lane < half ? bf16f(gld16(gsrc + lane)) : 0.f;
+        const float gb = lane < half ? bf16f(gld16(gsrc + lane + half)) : 0.f;
         const float ss = wave_sum(a * a + b * b);
         const float inv = 1.0f / sqrtf(ss / (float)d + P.rms_eps);
         if (lane < half) {
-          const uint16_t* g = hh < G ? D.qn : D.kn;
-          const float na = bf16f(g[lane]) * (a * inv);
-          const float nb = bf16f(g[lane + half]) * (b * inv);
-          const float cs = gld(P.rope_cos + (int64_t)p * half + lane);
-          const float sn = gld(P.rope_sin + (int64_t)p * half + lane);
-          const float ra = na * cs - nb * sn;
-          const float rb = nb * cs + na * sn;
+          const float ya = ga * (a * inv);
+          const float yb = gb * (b * inv);
+          const float ra = ya * cs - yb * sn;
+          const float rb = yb * cs + ya * sn;
           if (hh < G) {
             qs[hh * d + lane] = ra;
             qs[hh * d + lane + half] = rb;
@@ -613,241 +757,260 @@ DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem,
             const uint16_t ka = f2bf(ra), kb = f2bf(rb);
             kv[lane] = bf16f(ka);
             kv[lane + half] = bf16f(kb);
-            if (owner) {
-              gst16(kc + (int64_t)p * d + lane, ka);
-              gst16(kc + (int64_t)p * d + lane + half, kb);
-            }
+            reinterpret_cast<uint16_t*>(kvrow)[lane] = ka;
+            reinterpret_cast<uint16_t*>(kvrow)[lane + half] = kb;
           }
         }
       } else if (lane < half) {
         const uint16_t va = f2bf(a), vb = f2bf(b);
         kv[d + lane] = bf16f(va);
         kv[d + lane + half] = bf16f(vb);
-        if (owner) {
-          gst16(vc + (int64_t)p * d + lane, va);
-          gst16(vc + (int64_t)p * d + lane + half, vb);
-        }
+        reinterpret_cast<uint16_t*>(kvrow)[d + lane] = va;
+        reinterpret_cast<uint16_t*>(kvrow)[d + lane + half] = vb;
       }
     }
   }
   __syncthreads();
 
-  const float scale = 1.0f / sqrtf((float)d);
-  float m_run[ATT_MAXG], l_run[ATT_MAXG];
-  float acc[ATT_MAXG][8];
+  // ---- scores and online softmax over this wave's positions ----
+  if (!sched) {
+    float qv[ATT_MAXG][8];
 #pragma unroll
-  for (int h = 0; h < ATT_MAXG; ++h) {
-    m_run[h] = -INFINITY, l_run[h] = 0.f;
+    for (int h = 0; h < ATT_MAXG; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  }
-  const int dim0 = (lane % LP) * 8;
-  const int pg = lane / LP;
-  for (int base = lo; base < hi; base += MPK_ATTN_SUB) {
-    const int cnt = min(MPK_ATTN_SUB, hi - base);
-    // scores
-    if (!sched) {
-      for (int i0 = wave * PPR; i0 < cnt; i0 += MPK_NW * PPR) {
-        const int t = i0 + pg;
-        const bool valid = t < cnt;
-        const int tau = base + t;
-        float kf[8];
-        if (valid && tau != p) {
-          const u32x4 w = gldv<u32x4>(kc + (int64_t)tau * d + dim0);
-          kf[0] = bf16lo(w.x), kf[1] = bf16hi(w.x), kf[2] = bf16lo(w.y), kf[3] = bf16hi(w.y);
-          kf[4] = bf16lo(w.z), kf[5] = bf16hi(w.z), kf[6] = bf16lo(w.w), kf[7] = bf16hi(w.w);
+      for (int e = 0; e < 8; ++e) qv[h][e] = h < G ? qs[h * d + dim0 + e] : 0.f;
+    const int step = MPK_NW * PPR * ATT_ROUNDS;
+    for (int base = lo; base < hi; base += step) {
+      if (base != lo) load_rounds(base);
+#pragma unroll
+      for (int q = 0; q < ATT_ROUNDS; ++q) {
+        const int t = base + (wave + MPK_NW * q) * PPR + pg;
+        const bool valid = t < hi;
+        float kf[8], vf[8];
+        if (t == p) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kf[e] = kv[dim0 + e], vf[e] = kv[d + dim0 + e];
         } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kf[e] = valid ? kv[dim0 + e] : 0.f;
+          unpack8(kr[q], kf);
+          unpack8(vr[q], vf);
         }
 #pragma unroll
         for (int h = 0; h < ATT_MAXG; ++h) {
           if (h < G) {
             float part = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) part = fmaf(qs[h * d + dim0 + e], kf[e], part);
+            for (int e = 0; e < 8; ++e) part = fmaf(qv[h][e], kf[e], part);
             for (int off = 1; off < LP; off <<= 1) part += __shfl_xor(part, off);
-            if (valid && (lane % LP) == 0) sc[h * MPK_ATTN_SUB + t] = part * scale;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    // max per head
-    if (!sched) {
+            if (valid) {
+              const float sc = part * scale;
+              const float M = fmaxf(st.m[h], sc);
+              const float co = st.m[h] == -INFINITY ? 0.f : expf(st.m[h] - M);
+              const float cn = expf(sc - M);
+              st.l[h] = st.l[h] * co + cn;
 #pragma unroll
-      for (int h = 0; h < ATT_MAXG; ++h) {
-        if (h < G) {
-          float mx = -INFINITY;
-          for (int t = tid; t < cnt; t += MPK_NW * 64) mx = fmaxf(mx, sc[h * MPK_ATTN_SUB + t]);
-          mx = wave_max(mx);
-          if (lane == 0) redm[wave * ATT_MAXG + h] = mx;
-        }
-      }
-    }
-    __syncthreads();
-    float m_new[ATT_MAXG], alpha[ATT_MAXG];
-#pragma unroll
-    for (int h = 0; h < ATT_MAXG; ++h) {
-      float mx = m_run[h];
-      if (h < G)
-        for (int w = 0; w < MPK_NW; ++w) mx = fmaxf(mx, redm[w * ATT_MAXG + h]);
-      m_new[h] = mx;
-      alpha[h] = expf(m_run[h] - mx);  // m_run = -inf -> 0
-    }
-    if (!sched) {
-#pragma unroll
-      for (int h = 0; h < ATT_MAXG; ++h) {
-        if (h < G) {
-          float sm = 0.f;
-          for (int t = tid; t < cnt; t += MPK_NW * 64) {
-            const float e = expf(sc[h * MPK_ATTN_SUB + t] - m_new[h]);
-            sc[h * MPK_ATTN_SUB + t] = e;
-            sm += e;
-          }
-          sm = wave_sum(sm);
-          if (lane == 0) reds[wave * ATT_MAXG + h] = sm;
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < ATT_MAXG; ++h) {
-      float sm = 0.f;
-      if (h < G)
-        for (int w = 0; w < MPK_NW; ++w) sm += reds[w * ATT_MAXG + h];
-      l_run[h] = l_run[h] * alpha[h] + sm;
-      m_run[h] = m_new[h];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-    }
-    // weighted V
-    if (!sched) {
-      for (int i0 = wave * PPR; i0 < cnt; i0 += MPK_NW * PPR) {
-        const int t = i0 + pg;
-        if (t < cnt) {
-          const int tau = base + t;
-          float vf[8];
-          if (tau != p) {
-            const u32x4 w = gldv<u32x4>(vc + (int64_t)tau * d + dim0);
-            vf[0] = bf16lo(w.x), vf[1] = bf16hi(w.x), vf[2] = bf16lo(w.y), vf[3] = bf16hi(w.y);
-            vf[4] = bf16lo(w.z), vf[5] = bf16hi(w.z), vf[6] = bf16lo(w.w), vf[7] = bf16hi(w.w);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vf[e] = kv[d + dim0 + e];
-          }
-#pragma unroll
-          for (int h = 0; h < ATT_MAXG; ++h) {
-            if (h < G) {
-              const float wgt = sc[h * MPK_ATTN_SUB + t];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wgt, vf[e], acc[h][e]);
+              for (int e = 0; e < 8; ++e) st.acc[h][e] = st.acc[h][e] * co + cn * vf[e];
+              st.m[h] = M;
             }
           }
         }
       }
     }
-    __syncthreads();  // sc is rewritten by the next pass
-  }
-  // ---- reduce acc over position groups and waves; write the split partial ----
-  if (!sched) {
+    // merge the lane groups of the wave (positions), one head at a time
 #pragma unroll
     for (int h = 0; h < ATT_MAXG; ++h) {
       if (h < G) {
+        for (int off = LP; off < 64; off <<= 1) {
+          const float om = __shfl_xor(st.m[h], off);
+          const float ol = __shfl_xor(st.l[h], off);
+          const float M = fmaxf(st.m[h], om);
+          const float ca = st.m[h] == -INFINITY ? 0.f : expf(st.m[h] - M);
+          const float cb = om == -INFINITY ? 0.f : expf(om - M);
+          st.l[h] = st.l[h] * ca + ol * cb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float v = acc[h][e];
-          for (int off = LP; off < 64; off <<= 1) v += __shfl_xor(v, off);
-          if (lane < LP) accr[(wave * ATT_MAXG + h) * 128 + dim0 + e] = v;
+          for (int e = 0; e < 8; ++e) st.acc[h][e] = st.acc[h][e] * ca + __shfl_xor(st.acc[h][e], off) * cb;
+          st.m[h] = M;
         }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < ATT_MAXG; ++h) {
+      if (h < G) {
+        if (lane == 0) {
+          wm[wave * ATT_MAXG + h] = st.m[h];
+          wl[wave * ATT_MAXG + h] = st.l[h];
+        }
+        if (lane < LP)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wacc[(wave * ATT_MAXG + h) * 128 + dim0 + e] = st.acc[h][e];
       }
     }
   }
   __syncthreads();
+  // ---- merge the wavefronts: the split's partial (m, l, acc) per head ----
   const int stride = d + 2;
-  float* part = D.part + ((int64_t)((r * D.nkv + j) * NS + c) * G) * stride;
-  for (int idx = tid; idx < G * d; idx += MPK_THREADS) {
+  for (int idx = tid; idx < G * d && !sched; idx += MPK_NW * 64) {
     const int h = idx / d, i = idx - h * d;
-    float v = 0.f;
-    for (int w = 0; w < MPK_NW; ++w) v += accr[(w * ATT_MAXG + h) * 128 + i];
-    gst(part + h * stride + 2 + i, v);
-    if (i == 0) {
-      gst(part + h * stride, m_run[h]);
-      gst(part + h * stride + 1, l_run[h]);
+    float M = -INFINITY;
+    for (int w = 0; w < MPK_NW; ++w) M = fmaxf(M, wm[w * ATT_MAXG + h]);
+    float L = 0.f, A = 0.f;
+    for (int w = 0; w < MPK_NW; ++w) {
+      const float mw = wm[w * ATT_MAXG + h];
+      const float cw = mw == -INFINITY ? 0.f : expf(mw - M);
+      L = fmaf(wl[w * ATT_MAXG + h], cw, L);
+      A = fmaf(wacc[(w * ATT_MAXG + h) * 128 + i], cw, A);
+    }
+    if (na == 1) {
+      outs[idx] = A / L;  // the whole context in one split: this is o
+    } else {
+      outs[h * stride + 2 + i] = A;
+      if (i == 0) {
+        outs[h * stride] = M;
+        outs[h * stride + 1] = L;
+      }
     }
   }
   __syncthreads();
-  if (sched && lane == 0) {
-    uint32_t old = __hip_atomic_fetch_add(D.tickets + (r * D.nkv + j), 1u, __ATOMIC_ACQ_REL,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-    ctl[1] = (old % (uint32_t)NS) == (uint32_t)NS - 1;
+  if (na == 1) {
+    // publish the K/V row here (the scheduler wavefront publishes o after the task)
+    if (sched) {
+      uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * d);
+      uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * d);
+      for (int i = lane; i < d / 2; i += 64) {
+        st_devu(kdst + i, kvrow[i]);
+        st_devu(vdst + i, kvrow[d / 2 + i]);
+      }
+    }
+    return true;
+  }
+  // scheduler wavefront: publish the split's partial (and the new K/V row
+  // from the split that owns the position), then take a ticket of the group
+  if (sched) {
+    float* part = D.part + ((int64_t)((r * D.nkv + j) * NS + c) * G) * stride;
+    // (na == 1 returned earlier; here the partial goes to the group's merge)
+    for (int i = lane; i < G * stride; i += 64) st_dev(part + i, outs[i]);
+    if (owner) {
+      uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * d);
+      uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * d);
+      for (int i = lane; i < d / 2; i += 64) {
+        st_devu(kdst + i, kvrow[i]);
+        st_devu(vdst + i, kvrow[d / 2 + i]);
+      }
+    }
+    vm_drain();
+    if (lane == 0) {
+      uint32_t* tk = D.tickets + (r * D.nkv + j);
+      const uint32_t old = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last_arr = old + 1 == (uint32_t)na;
+      // The last arriver resets the counter for the next iteration: every
+      // split of this group has counted, and the next iteration's splits
+      // start only after this group's output flag.
+      if (last_arr) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ctl[1] = last_arr;
+    }
   }
   __syncthreads();
   const bool last = ctl[1] != 0;
   if (last) {
+    // merge the group's splits: o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M)
     const float* pbase = D.part + ((int64_t)((r * D.nkv + j) * NS) * G) * stride;
-    for (int idx = tid; idx < G * d; idx += MPK_THREADS) {
+    // G * d <= 512 = worker threads: one output element per worker thread
+    float o_val = 0.f;
+    const int idx = tid;
+    const bool mine = !sched && idx < G * d;
+    if (mine) {
       const int h = idx / d, i = idx - h * d;
       float M = -INFINITY;
-      for (int cc = 0; cc < NS; ++cc) M = fmaxf(M, gld(pbase + ((int64_t)cc * G + h) * stride));
+      for (int cc = 0; cc < na; ++cc) M = fmaxf(M, ld_dev(pbase + ((int64_t)cc * G + h) * stride));
       float L = 0.f, O = 0.f;
-      for (int cc = 0; cc < NS; ++cc) {
+      for (int cc = 0; cc < na; ++cc) {
         const float* pp = pbase + ((int64_t)cc * G + h) * stride;
-        const float lc = gld(pp + 1);
+        const float lc = ld_dev(pp + 1);
         if (lc > 0.f) {
-          const float wgt = expf(gld(pp) - M);
+          const float wgt = expf(ld_dev(pp) - M);
           L = fmaf(lc, wgt, L);
-          O = fmaf(gld(pp + 2 + i), wgt, O);
+          O = fmaf(ld_dev(pp + 2 + i), wgt, O);
         }
       }
-      gst(D.y + (int64_t)r * D.nq * d + (int64_t)(j * G + h) * d + i, O / L);
+      o_val = O / L;
     }
+    __syncthreads();  // the partial area of LDS_OUT is reused for o
+    if (mine) outs[idx] = o_val;
   }
   return last;
 }
 
 // ---------------------------------------------------------------------------
-// dispatch of one task body
+// dispatch of one task body; returns true when the task stamps its flag
 // ---------------------------------------------------------------------------
 template <int NB>
-DEV bool run_task(const mpk_kparams& P, ctask& T, Issuer& I, RingState& RS,
-                  cqent* Q, int qlen, int s, char* smem, int tid, bool sched) {
+DEV bool run_task(const mpk_kparams& P, ctask& T, Issuer& I, RingState& RS, cqent* Q, int qlen, int s,
+                  char* smem, int tid, bool sched) {
   cop& D = ops_of(P)[T.op];
   if (T.kind == MPK_TK_ATTN) return attn_task(P, T, D, smem, tid, sched);
-  return gemv_task<NB>(P, T, D, I, RS, Q, qlen, s, smem, tid, sched);
+  if (T.kind == MPK_TK_ARGMAX) return true;  // done by the scheduler wavefront in publish()
+  gemv_task<NB>(P, T, D, I, RS, Q, qlen, s, smem, tid, sched);
+  return true;
 }
 
-// Spin until every dependency of T for iteration s is satisfied.  Returns
-// false (after recording a status) on watchdog timeout or a stop request.
-DEV bool wait_deps(const mpk_kparams& P, ctask& T, int s, int task_id) {
+// Scheduler wavefront, after the task's end barrier: publish its outputs,
+// wait for the stores, stamp the flag.
+template <int NB>
+DEV void publish(const mpk_kparams& P, ctask& T, bool sig, int s, const char* smem, int lane) {
+  cop& D = ops_of(P)[T.op];
+  if (T.kind == MPK_TK_ATTN) {
+    if (sig) {
+      const int G = D.nq / D.nkv;
+      const float* outs = reinterpret_cast<const float*>(smem + LDS_OUT);
+      float* o = D.y + (int64_t)T.row0 * D.nq * D.d + (int64_t)T.nrows * G * D.d;
+      for (int i = lane; i < G * D.d; i += 64) st_dev(o + i, outs[i]);
+    }
+  } else if (T.kind == MPK_TK_ARGMAX) {
+    argmax_publish<NB>(P, D, lane);
+  } else {
+    publish_gemv<NB>(P, T, D, smem, lane);
+  }
+  vm_drain();
+  if (sig && lane == 0) st_devu(P.flags + T.out_flag, (uint32_t)(s + 1));
+}
+
+// Scheduler wavefront: spin until every producer flag of every dependency of
+// T carries the stamp of iteration s (or s - 1 for previous-iteration
+// dependencies).  Returns false (after recording a status) on watchdog
+// timeout or a stop request; false is uniform across the wavefront.
+DEV bool wait_deps(const mpk_kparams& P, ctask& T, int s, int task_id, int lane) {
   const uint64_t t0 = clock_now();
+  int spins = 0;
   for (int k = 0; k < T.n_deps; ++k) {
-    const uint32_t target = (uint32_t)T.dep_cnt[k] * (uint32_t)(s + 1 - T.dep_prev[k]);
-    uint32_t* ev = P.events + T.dep_ev[k];
-    int spins = 0;
-    while (__hip_atomic_load(ev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if ((++spins & 31) == 0) {
-        const int code = __hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int abort_req =
-            __hip_atomic_load(&P.status->abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        int mine = 0;
-        if (abort_req) mine = MPK_ERR_ABORTED;
-        else if (clock_now() - t0 > P.timeout_ticks) mine = MPK_ERR_DEVICE_TIMEOUT;
-        if (mine) {
-          int expected = 0;
-          if (__hip_atomic_compare_exchange_strong(&P.status->code, &expected, mine, __ATOMIC_RELAXED,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-            __hip_atomic_store(&P.status->iteration, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&P.status->task, task_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = (uint32_t)(s + 1 - T.dep_prev[k]);
+    const uint32_t* f = P.flags + T.dep_base[k];
+    const int n = T.dep_n[k];
+    for (;;) {
+      bool ok = true;
+      for (int i = lane; i < n; i += 64) ok &= ld_devu(f + i) >= target;
+      if (__ballot(!ok) == 0) break;
+      if ((++spins & 15) == 0) {
+        int mine = 0, code = 0;
+        if (lane == 0) {
+          code = __hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int abort_req =
+              __hip_atomic_load(&P.status->abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          if (abort_req) mine = MPK_ERR_ABORTED;
+          else if (clock_now() - t0 > P.timeout_ticks) mine = MPK_ERR_DEVICE_TIMEOUT;
+          if (mine) {
+            int expected = 0;
+            if (__hip_atomic_compare_exchange_strong(&P.status->code, &expected, mine, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+              __hip_atomic_store(&P.status->iteration, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(&P.status->task, task_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
-          return false;
         }
-        if (code) return false;
+        if (__builtin_amdgcn_readfirstlane(mine | code)) return false;
       }
       __builtin_amdgcn_s_sleep(1);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  asm volatile("" ::: "memory");  // the task's device-scope loads stay after the poll
   return true;
 }
 
@@ -873,17 +1036,21 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
     for (int k = 0; k < qlen; ++k) {
       const int task_id = Q[k].task;
       ctask& T = tasks_of(P)[task_id];
-      if (sched && lane == 0) {
-        const bool ok = wait_deps(P, T, s, task_id);
-        ctl[0] = ok ? 0 : 1;
-        if (ok && P.trace) {
-          mpk_trace_record& Rr = P.trace[(int64_t)s * P.n_tasks + task_id];
-          Rr.task = task_id;
-          Rr.iteration = s;
-          Rr.start_ticket = __hip_atomic_fetch_add(P.ticket_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          Rr.t_start = clock_now();
-          Rr.hw_id = hwreg_hw_id();
-          Rr.xcc_id = hwreg_xcc_id();
+      if (sched) {
+        if (k == 0) set_positions(P, smem, s, lane);
+        const bool ok = wait_deps(P, T, s, task_id, lane);
+        if (lane == 0) {
+          ctl[0] = ok ? 0 : 1;
+          if (ok && P.trace) {
+            mpk_trace_record& Rr = P.trace[(int64_t)s * P.n_tasks + task_id];
+            Rr.task = task_id;
+            Rr.iteration = s;
+            Rr.start_ticket = P.trace_tickets ? __hip_atomic_fetch_add(P.ticket_ctr, 1u, __ATOMIC_RELAXED,
+                                                                       __HIP_MEMORY_SCOPE_AGENT) : 0u;
+            Rr.t_start = clock_now();
+            Rr.hw_id = hwreg_hw_id();
+            Rr.xcc_id = hwreg_xcc_id();
+          }
         }
       }
       __syncthreads();
@@ -898,13 +1065,14 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
       asm volatile("" : "+v"(tid_o));
       const bool sig = run_task<NB>(P, T, I, RS, Q, qlen, s, smem, tid_o, sched);
       __syncthreads();
-      if (sched && lane == 0) {
-        if (P.trace) {
+      if (sched) {
+        if (P.trace && lane == 0) {
           mpk_trace_record& Rr = P.trace[(int64_t)s * P.n_tasks + task_id];
-          Rr.end_ticket = __hip_atomic_fetch_add(P.ticket_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          Rr.end_ticket = P.trace_tickets ? __hip_atomic_fetch_add(P.ticket_ctr, 1u, __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT) : 0u;
           Rr.t_end = clock_now();
         }
-        if (sig) __hip_atomic_fetch_add(P.events + T.out_ev, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        publish<NB>(P, T, sig, s, smem, lane);
       }
     }
   }
@@ -930,8 +1098,13 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_op_kernel(mpk_kparams P, i
   if (!sched) {
     issuer_seek(I, P1, q1, 1, 0, 0, wave);
     ring_fill<Lay<NB>::R>(I, RS, smem + Lay<NB>::RING + wave * Lay<NB>::R * 1024, P1, q1, 1, wave, lane);
+  } else {
+    set_positions(P, smem, s, lane);
   }
-  run_task<NB>(P, T, I, RS, q1, 1, s, smem, tid, sched);
+  __syncthreads();
+  const bool sig = run_task<NB>(P, T, I, RS, q1, 1, s, smem, tid, sched);
+  __syncthreads();
+  if (sched) publish<NB>(P, T, sig, s, smem, lane);
   vm_wait<0>();
 }
 
@@ -1056,14 +1229,12 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   const mpk_model_cfg& M = g->model;
   const int B = x->B;
 
-  // counters: events, then per-op tickets
+  // counters: completion flags, then attention merge tickets, then the trace ticket
   std::vector<mpk_dev_op> dops = g->dops;
-  int64_t ncnt = (int64_t)g->ev_count.size();
+  int64_t ncnt = (int64_t)g->n_flags;
   std::vector<int64_t> tick_off(dops.size(), -1);
-  for (size_t i = 0; i < dops.size(); ++i) {
+  for (size_t i = 0; i < dops.size(); ++i)
     if (dops[i].kind == MPK_TK_ATTN) tick_off[i] = ncnt, ncnt += (int64_t)B * dops[i].nkv;
-    if (dops[i].kind == MPK_TK_LMHEAD) tick_off[i] = ncnt, ncnt += 1;
-  }
   const int64_t ticket_ctr_off = ncnt++;
   x->n_counters = ncnt;
   if ((rc = dalloc(x.get(), &x->d_counters, (size_t)ncnt * 4))) return rc;
@@ -1072,8 +1243,8 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
 
   for (size_t i = 0; i < dops.size(); ++i) {
     mpk_dev_op& D = dops[i];
+    if (!D.kind || D.kind == MPK_TK_ARGMAX) continue;
     const mpk_op& o = g->ops[i];
-    if (!D.kind) continue;
     if (D.kind == MPK_TK_ATTN) {
       D.x = (const float*)P(o.in[0]);
       D.qn = (const uint16_t*)P(o.in[1]);
@@ -1109,8 +1280,13 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
       D.W0 = (const uint16_t*)P(o.in[2]);
       D.logits = o.out[0] >= 0 ? (float*)P(o.out[0]) : nullptr;
       if ((rc = dalloc(x.get(), &D.part, (size_t)D.ntiles * B * 2 * 4))) return rc;
-      D.tickets = x->d_counters + tick_off[i];
     }
+  }
+  if (g->argmax_op >= 0) {
+    // the argmax task reads the LM head's per-tile (max, index) pairs
+    const int lm = g->argmax_op - 1;
+    dops[g->argmax_op].part = dops[lm].part;
+    dops[g->argmax_op].N1 = dops[lm].ntiles;
   }
   if ((rc = dalloc(x.get(), &x->d_ops, dops.size() * sizeof(mpk_dev_op)))) return rc;
   HIPCHK(hipMemcpy(x->d_ops, dops.data(), dops.size() * sizeof(mpk_dev_op), hipMemcpyHostToDevice));
@@ -1147,7 +1323,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   K.queues = x->d_queues;
   K.single_q = x->d_single;
   K.qlen = x->d_qlen;
-  K.events = x->d_events;
+  K.flags = x->d_events;
   K.tokens = (int32_t*)P(g->meta.tokens);
   K.step = (int32_t*)P(g->meta.step);
   K.prompt_len = (const int32_t*)P(g->meta.prompt_len);
@@ -1211,7 +1387,14 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
     }
     HIPCHK(hipMemsetAsync(x->d_trace, 0xff, (size_t)need * sizeof(mpk_trace_record), st));
     x->kp.trace = x->d_trace;
+    x->kp.trace_tickets = x->g->launch.trace == 1;
   }
+  // positions at launch: request r is at step[r] + s in iteration s (the
+  // LM-head argmax advances step by one per iteration, on the device)
+  for (int r = 0; r < x->B; ++r) x->kp.pos0[r] = step[r];
+  // positions at launch: request r is at step[r] + s in iteration s (the
+  // LM-head argmax advances step by one per iteration, on the device)
+  for (int r = 0; r < x->B; ++r) x->kp.pos0[r] = step[r];
   x->kp.n_iter = n_iter;
   x->last_iters = n_iter;
   int64_t nz = x->n_counters;
@@ -1241,7 +1424,7 @@ extern "C" int mpk_run_steps_per_op(mpk_exec_t x, int32_t n_iter, void* stream) 
   x->kp.trace = nullptr;
   const mpk_graph_s* g = x->g;
   for (int s = 0; s < n_iter; ++s)
-    for (size_t i = 0; i < g->ops.size(); ++i) {
+    for (size_t i = 0; i < g->dops.size(); ++i) {
       if (!g->op_ntasks[i]) continue;
       int first = g->op_first_task[i];
       void* args[] = {&x->kp, &first, &s};
@@ -1295,8 +1478,8 @@ extern "C" int mpk_get_tensor_ptr(mpk_exec_t x, int32_t id, void** p) {
 
 extern "C" void mpk_destroy_exec(mpk_exec_t x) {
   if (!x) return;
-  hipSetDevice(x->device);
-  for (void* p : x->owned) hipFree(p);
-  if (x->side) hipStreamDestroy(x->side);
+  (void)hipSetDevice(x->device);
+  for (void* p : x->owned) (void)hipFree(p);
+  if (x->side) (void)hipStreamDestroy(x->side);
   delete x;
 }

@@ -66,10 +66,14 @@ def test_full_model_tiles_fill_every_cu():
         for t in tasks:
             per_op.setdefault(t.op, []).append(t)
         kinds = [o.kind for o in spec.ops]
-        # every operator with work has exactly one tile / task per CU
+        argmax_op = len(spec.ops)
+        assert info.num_ops == len(spec.ops) + 1 and info.sink_op == argmax_op
+        # every GEMV-type operator has exactly one tile per CU
         for i, k in enumerate(kinds):
             if k == mpk.MPK_OP_EMBED:
                 assert i not in per_op
+                continue
+            if k == mpk.MPK_OP_ATTENTION:
                 continue
             assert len(per_op[i]) == 256, (i, k, len(per_op[i]))
             assert sorted(t.worker for t in per_op[i]) == list(range(256))
@@ -83,19 +87,20 @@ def test_full_model_tiles_fill_every_cu():
             if k == mpk.MPK_OP_LMHEAD_ARGMAX:
                 assert {t.nrows for t in per_op[i]} == {593, 594}
                 assert sum(t.nrows for t in per_op[i]) == 151936
-        # 36 layers x 5 operators + LM head, in operator order on every queue
-        assert all(len(q) == 36 * 5 + 1 for q in queues)
+        # attention: 8 kv heads x ceil(551 / 128) = 5 splits at batch 1
+        attn = per_op[2]
+        assert sorted((t.nrows, t.split) for t in attn) == [(j, c) for j in range(8) for c in range(5)]
+        # one argmax task, on worker 0, last in its queue
+        assert len(per_op[argmax_op]) == 1 and per_op[argmax_op][0].worker == 0
+        assert tasks[queues[0][-1]].op == argmax_op
+        # operator order on every queue; 4 GEMV operators x 36 layers + LM head on each
         for q in queues:
             ops = [tasks[t].op for t in q]
             assert ops == sorted(ops)
-        assert info.sink_op == len(spec.ops) - 1
-        # attention: 8 kv heads x 32 splits at batch 1
-        attn = [t for t in tasks if kinds[t.op] == mpk.MPK_OP_ATTENTION and t.op == 2]
-        assert sorted((t.nrows, t.split) for t in attn) == [(j, c) for j in range(8) for c in range(32)]
-        # event counts: tiles (GEMV), merges per (request, kv head) (attention), 1 (LM head)
+            assert sum(kinds[o] != mpk.MPK_OP_ATTENTION for o in ops if o < argmax_op) == 36 * 4 + 1
+        # events: one flag per tile (GEMV, LM head), per (request, kv head) merge, 1 for argmax
         for e, (c, op) in enumerate(zip(ev_cnt, ev_op)):
-            k = kinds[op]
-            want = {mpk.MPK_OP_ATTENTION: 8, mpk.MPK_OP_LMHEAD_ARGMAX: 1}.get(k, 256)
+            want = 1 if op == argmax_op else {mpk.MPK_OP_ATTENTION: 8}.get(kinds[op], 256)
             assert c == want
     finally:
         mpk.mpk_destroy_graph(g)
@@ -113,12 +118,11 @@ def test_dependencies_follow_the_decoder_chain():
         assert all(len(v) == 1 for v in deps.values())
         deps = {k: next(iter(v)) for k, v in deps.items()}
         sink = info.sink_op
-        # op 0 is the (task-less) embedding; layer 0 QKV waits for the previous iteration's LM head
+        assert sink == len(kinds)  # the argmax task after the LM head
+        # op 0 is the (task-less) embedding; layer 0 QKV waits for the previous iteration's argmax
         assert deps[1] == ((sink, 1),)
-        for i in range(1, len(kinds) - 1):
-            if i > 1:
-                assert deps[i] == ((i - 1, 0),), (i, deps[i])
-        assert deps[sink] == ((sink - 1, 0),)
+        for i in range(2, len(kinds) + 1):
+            assert deps[i] == ((i - 1, 0),), (i, deps[i])
     finally:
         mpk.mpk_destroy_graph(g)
 
@@ -138,7 +142,7 @@ def test_simulated_protocol_respects_every_edge_under_jitter():
         for i, t in enumerate(tasks):
             by_op.setdefault(t.op, []).append(i)
         # edges derived from the decoder's operator order, not from the builder tables
-        chain = [i for i, k in enumerate(kinds) if k != mpk.MPK_OP_EMBED]
+        chain = [i for i, k in enumerate(kinds) if k != mpk.MPK_OP_EMBED] + [len(kinds)]
         for s in range(n_iter):
             for a, b in zip(chain, chain[1:]):
                 end_a = max(tr[s, i]["end_ticket"] for i in by_op[a])

@@ -147,7 +147,7 @@ def test_trace_orders_every_dependency(torch_dev):
         by_op.setdefault(t.op, []).append(i)
     # required edges from the decoder's operator sequence: embed -> [QKV -> attention -> o_proj ->
     # gate/up -> down] x L -> LM head -> next iteration
-    chain = [i for i, k in enumerate(kinds) if k != mpk.MPK_OP_EMBED]
+    chain = [i for i, k in enumerate(kinds) if k != mpk.MPK_OP_EMBED] + [len(kinds)]  # + argmax task
     for s in range(n):
         for a, b in zip(chain, chain[1:]):
             assert tr[s]["end_ticket"][by_op[a]].max() < tr[s]["start_ticket"][by_op[b]].min()
