@@ -39,27 +39,30 @@ typedef struct {
   /* attention */
   int32_t nq, nkv, d, nsplit, S;
   int32_t pad0;
-  const float* x;
+  const float* x;         /* plain input (a graph input tensor), or NULL */
+  const uint64_t* xll;    /* stamped input words (output of another operator), or NULL */
   const uint16_t* gain;
   const uint16_t* W0;
   const uint16_t* W1;
   const uint16_t* W2;
-  const float* resid;
-  float* y;
+  const float* resid;     /* plain residual input, or NULL */
+  const uint64_t* rll;    /* stamped residual words, or NULL */
+  float* y;               /* plain output (tensor attached by the caller), or NULL */
+  uint64_t* yll;          /* stamped output words */
   const uint16_t* E; /* embedding rows for x_embed / res_embed */
   const uint16_t* qn;
   const uint16_t* kn;
   uint16_t* kc;
   uint16_t* vc;
-  float* part;       /* attention split partials; LM head per-tile (value, index) */
-  uint32_t* tickets; /* attention: [B * nkv]; LM head: [1] */
+  uint64_t* pll;     /* stamped attention split partials [B][nkv][nsplit][G][d + 2];
+                        LM head: per tile and request (value, row) */
   float* logits;     /* LM head: optional [iters][B][V] */
   int64_t logits_iters;
 } mpk_dev_op;
 
-/* One task (a tile of an operator).  Completion is published as an
- * iteration stamp (iteration + 1) in the task's flag; a dependency on an
- * operator is satisfied when all of that operator's flags reach the stamp. */
+/* One task (a tile of an operator).  The dependency fields describe the
+ * operator-level graph (introspection and the host simulation); on the
+ * device a task waits for the stamped words it reads. */
 typedef struct {
   int32_t kind;
   int32_t op;
@@ -97,7 +100,7 @@ typedef struct {
   const mpk_dev_qentry* queues; /* [num_workers][qstride] */
   const mpk_dev_qentry* single_q; /* [n_tasks]: {task, -1} (one-launch-per-operator path) */
   const int32_t* qlen;          /* [num_workers] */
-  uint32_t* flags;               /* [n_flags] iteration stamps */
+  uint64_t* tok_ll;              /* [B] stamped next token, written by the argmax task */
   int32_t* tokens;
   int32_t* step;
   const int32_t* prompt_len;
@@ -117,6 +120,7 @@ typedef struct {
   float rms_eps;
   int32_t vocab;
   int32_t pos0[MPK_MAX_BATCH];  /* step[r] at launch: position of request r in iteration s is pos0[r] + s */
+  uint32_t iter_base;           /* stamp of iteration s is iter_base + s + 1 */
 } mpk_kparams;
 
 #endif

@@ -9,23 +9,24 @@
 //
 // One cooperative launch keeps one workgroup resident on every CU for the
 // whole decode loop (P1 "How MPK Works"; P4 "工作机制").  A workgroup is eight
-// worker wavefronts plus one scheduler wavefront.  The scheduler wavefront
-// walks the CU's static task queue: for each task it spins (agent-scope
-// relaxed loads, then one acquire fence) until every producer event has
-// reached count * (iteration + 1), releases the workers through a workgroup
-// barrier, and after the task signals the task's event with an agent-scope
-// release add.
+// worker wavefronts plus one scheduler wavefront and walks the CU's static
+// task queue.  Tasks hand values to each other as stamped 64-bit words
+// (payload + iteration stamp, see st_ll): a task waits for exactly the words
+// it reads, and a producer publishes each output word as soon as it is
+// computed - there is no per-task completion flag, fence or store drain on
+// the path between two tasks.
 //
 // Weights stream through a per-wavefront ring in LDS, filled by direct
 // global->LDS 16-byte loads (global_load_lds_dwordx4).  The ring's producer
 // side walks the CU's queue ahead of the consumer and crosses task
-// boundaries: while a task's dependencies are still pending, the first
+// boundaries: while a task's inputs are still being produced, the first
 // weight units of that task (and of the next ones) are already in flight.
 // This is the "load the next layer while computing this one" pipelining of
 // P3 "Why MPK?", done per CU with the queue known at compile time.
 //
-// The iteration's last operator picks the argmax token, writes it into
-// tokens, advances step (P1 "How MPK Works") and releases the next iteration.
+// The iteration's last task picks the argmax token, writes it into tokens,
+// advances step (P1 "How MPK Works") and publishes the token word the next
+// iteration's embedding reads wait for.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -179,13 +180,12 @@ DEV void vm_wait() {
 }
 
 // Device-scope ("sc1") accesses.  Every value one task hands to another task
-// on another CU (activations, attention partials, K/V rows, tokens, step,
-// completion flags) is written with device-scope stores and read with
-// device-scope loads: these go to the point of coherence shared by all XCDs,
-// so no L2 write-back or invalidate is needed to pass data between CUs.  A
-// producer stamps its flag only after s_waitcnt vmcnt(0) has seen all its
-// device-scope stores complete; a consumer issues its device-scope loads only
-// after it has seen every producer flag.
+// on another CU (stamped words, K/V rows, tokens, step) is written with
+// device-scope stores and read with device-scope loads: these go to the point
+// of coherence shared by all XCDs, so no L2 write-back or invalidate is needed
+// to pass data between CUs.  Data that is not itself stamped (a K/V row) is
+// stored and its stores waited for (s_waitcnt vmcnt(0)) before the stamped
+// word that orders its readers is published.
 DEV float ld_dev(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 DEV int ld_devi(const int32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 DEV uint32_t ld_devu(const uint32_t* p) {
@@ -202,8 +202,9 @@ DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // LDS layout (bytes)
-//   [0, 2048)                 control words, reductions, 1/rms, tile argmax
-//   [LDS_OUT, +4096)          task outputs staged for the scheduler wavefront
+//   [0, 2048)                 control words, reductions, 1/rms, tile argmax,
+//                             positions and tokens of the iteration
+//   [LDS_OUT, +4096)          attention: split partial / output, new K/V row
 //   [LDS_X, +XS)              staged activations x (or attention scratch)
 //   [RES, +2048)              staged residual rows of the tile
 //   [RING, +NW*R*1024)        weight rings, R units of 1 KB per wavefront
@@ -215,7 +216,8 @@ DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 #define LDS_RED 256                      // [16][8] floats: per-wave partials
 #define LDS_INV (LDS_RED + 16 * 8 * 4)   // [8] floats
 #define LDS_BEST (LDS_INV + 64)          // [8 waves][8] (float) + [8][8] (int)
-#define LDS_POS (LDS_BEST + 512)         // [8] int: step[r] of the current iteration
+#define LDS_POS (LDS_BEST + 512)         // [8] int: position of request r in the current iteration
+#define LDS_TOK (LDS_POS + 32)           // [8] int: token of request r in the current iteration
 #define LDS_OUT 2048
 #define LDS_OUT_FLOATS 1024
 #define LDS_X (LDS_OUT + LDS_OUT_FLOATS * 4)
@@ -238,9 +240,11 @@ DEV void lds_write_f32(uint32_t a, float v) {
 
 DEV int xperm(int k) { return (k & ~511) + ((k & 4) << 6) + (((k & 511) >> 3) << 2) + (k & 3); }
 
-// Position of request b in the current iteration (read once per iteration
-// by the scheduler wavefront into LDS_POS).
-DEV int cur_pos(const char* smem, int b) { return __builtin_amdgcn_readfirstlane(reinterpret_cast<const volatile int*>(smem + LDS_POS)[b]); }
+// Position of request b in the current iteration (written into LDS_POS by the
+// scheduler wavefront at the start of each iteration).
+DEV int cur_pos(const char* smem, int b) {
+  return __builtin_amdgcn_readfirstlane(reinterpret_cast<const volatile int*>(smem + LDS_POS)[b]);
+}
 
 // Scheduler wavefront: positions of iteration s into LDS_POS (uniform
 // indices into the kernel-argument array).
@@ -249,11 +253,158 @@ DEV void set_positions(const mpk_kparams& P, char* smem, int s, int lane) {
     for (int b = 0; b < P.B; ++b) reinterpret_cast<volatile int*>(smem + LDS_POS)[b] = P.pos0[b] + s;
 }
 
-// Token id consumed by request b in this iteration.
-DEV int cur_token(const mpk_kparams& P, const char* smem, int b) {
-  const int p = cur_pos(smem, b);
-  const int t = ld_devi(P.tokens + (int64_t)b * P.tokens_width + p);
-  return t < 0 ? 0 : (t >= P.vocab ? P.vocab - 1 : t);  // ids are checked on the host; stay in bounds
+// Per-lane forms: the position of request b (b may differ between lanes), and
+// the token id it consumes in this iteration (resolved into LDS_TOK by
+// resolve_tokens before a task reads embedding rows).
+DEV int cur_pos_v(const char* smem, int b) { return reinterpret_cast<const volatile int*>(smem + LDS_POS)[b]; }
+DEV int cur_token_v(const char* smem, int b) { return reinterpret_cast<const volatile int*>(smem + LDS_TOK)[b]; }
+
+// ---------------------------------------------------------------------------
+// Stamped words.  Every value one task hands to another (an activation
+// element, an attention split's partial, an LM-head tile's maximum, the next
+// token) travels as one 64-bit word: the 32-bit payload in the low half and
+// the stamp of the iteration that wrote it in the high half.  A 64-bit
+// device-scope store is single-copy atomic, so a reader that sees the
+// expected stamp also sees the payload: consumers spin on exactly the words
+// they read, and producers publish with plain device-scope stores - no
+// completion flag, no store drain, no fence between them.
+// The stamp of iteration s is iter_base + s + 1; iter_base grows by the
+// iteration count of every launch, so words left by an earlier launch (or an
+// aborted one) never carry a current stamp.  Buffers start zeroed (stamp 0).
+// ---------------------------------------------------------------------------
+DEV uint32_t stamp_of(const mpk_kparams& P, int s) { return P.iter_base + (uint32_t)s + 1u; }
+DEV void st_ll(uint64_t* p, float v, uint32_t st) {
+  __hip_atomic_store(p, ((uint64_t)st << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV void st_lli(uint64_t* p, int v, uint32_t st) {
+  __hip_atomic_store(p, ((uint64_t)st << 32) | (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV uint64_t ld_ll(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV bool ll_ok(uint64_t w, uint32_t st) { return (uint32_t)(w >> 32) == st; }
+DEV float ll_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// Workgroup-wide wait.  Every thread of the workgroup calls wait_round once
+// per round with `pending` = this thread still misses words; the result is
+// uniform: 0 = nobody waits any more, 1 = poll again, -1 = stop (watchdog
+// expired, stop requested by the host, or an error recorded by another
+// workgroup).  Thread 0 runs the watchdog; the first workgroup to fail
+// records the status.
+struct Waiter {
+  uint64_t t0;
+  int rounds;
+};
+
+DEV Waiter waiter_start() { return Waiter{clock_now(), 0}; }
+
+DEV int wait_round(const mpk_kparams& P, Waiter& Wt, bool pending, int s, int task_id, char* smem, int tid) {
+  volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
+  const int wave = tid >> 6;
+  ++Wt.rounds;
+  // (not on the first round: a wait satisfied at first look costs no status reads)
+  if (tid == 0 && (Wt.rounds & 7) == 2) {
+    int mine = 0;
+    const int code = __hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int abort_req = __hip_atomic_load(&P.status->abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (abort_req) mine = MPK_ERR_ABORTED;
+    else if (clock_now() - Wt.t0 > P.timeout_ticks) mine = MPK_ERR_DEVICE_TIMEOUT;
+    if (mine) {
+      int expected = 0;
+      if (__hip_atomic_compare_exchange_strong(&P.status->code, &expected, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+        __hip_atomic_store(&P.status->iteration, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&P.status->task, task_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (mine || code) ctl[0] = 1;
+  }
+  // per-wave "still waiting" bits, double-buffered by round parity so a
+  // wavefront entering the next round never overwrites a slot still read
+  volatile int* slot = ctl + 8 + (Wt.rounds & 1) * 16;
+  const bool any_wave = __ballot(pending) != 0;
+  if ((tid & 63) == 0) slot[wave] = any_wave ? 1 : 0;
+  __syncthreads();
+  int any = 0;
+  for (int w = 0; w <= MPK_NW; ++w) any |= slot[w];
+  if (ctl[0]) return -1;
+  if (!any) return 0;
+  __builtin_amdgcn_s_sleep(1);
+  return 1;
+}
+
+// Trace hook: the task's inputs are all present.  With tickets on, the
+// ticket is taken (and returned) before any output of the task is stored.
+DEV void mark_ready(const mpk_kparams& P, int s, int task_id, int tid) {
+  if (!P.trace) return;
+  if (tid == MPK_NW * 64) {
+    mpk_trace_record& Rr = P.trace[(int64_t)s * P.n_tasks + task_id];
+    Rr.t_ready = clock_now();
+    if (P.trace_tickets)
+      Rr.start_ticket = __hip_atomic_fetch_add(P.ticket_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (P.trace_tickets) __syncthreads();
+}
+
+// Tokens of this iteration into LDS_TOK.  In the first iteration of a launch
+// the token at the request's position is in `tokens` (prompt, or written by
+// the previous launch); later iterations take the previous iteration's
+// argmax task word (which also carries teacher-forced prompt tokens).
+DEV int resolve_tokens(const mpk_kparams& P, char* smem, int tid, int s, int task_id, Waiter& Wt) {
+  volatile int* tok = reinterpret_cast<volatile int*>(smem + LDS_TOK);
+  bool need = false;
+  if (tid < P.B) {
+    if (s == 0) {
+      tok[tid] = ld_devi(P.tokens + (int64_t)tid * P.tokens_width + cur_pos_v(smem, tid));
+    } else {
+      need = true;
+    }
+  }
+  const uint32_t want = stamp_of(P, s - 1);
+  for (;;) {
+    if (need) {
+      const uint64_t w = ld_ll(P.tok_ll + tid);
+      if (ll_ok(w, want)) tok[tid] = (int)(uint32_t)w, need = false;
+    }
+    const int rc = wait_round(P, Wt, need, s, task_id, smem, tid);
+    if (rc <= 0) {
+      if (rc == 0 && tid < P.B) {
+        const int t = tok[tid];
+        tok[tid] = t < 0 ? 0 : (t >= P.vocab ? P.vocab - 1 : t);  // ids are checked on the host; stay in bounds
+      }
+      __syncthreads();
+      return rc;
+    }
+  }
+}
+
+// Collective gather of n stamped words src[0, n) into LDS dst[0, n) (their
+// 32-bit payloads).  CH words per thread are in flight per round.
+template <int CH>
+DEV int gather_ll(const mpk_kparams& P, const uint64_t* src, int n, uint32_t* dst, uint32_t st, Waiter& Wt, int s,
+                  int task_id, char* smem, int tid) {
+  for (int base = 0; base < n; base += CH * MPK_THREADS) {
+    uint32_t need = 0;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (base + tid + j * MPK_THREADS < n) need |= 1u << j;
+    for (;;) {
+      uint64_t v[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        if ((need >> j) & 1u) v[j] = ld_ll(src + base + tid + j * MPK_THREADS);
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        if (((need >> j) & 1u) && ll_ok(v[j], st)) {
+          dst[base + tid + j * MPK_THREADS] = (uint32_t)v[j];
+          need &= ~(1u << j);
+        }
+      const int rc = wait_round(P, Wt, need != 0, s, task_id, smem, tid);
+      if (rc < 0) return rc;
+      if (rc == 0) break;
+    }
+  }
+  return 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -423,11 +574,13 @@ DEV void ring_fill(Issuer& I, RingState& S, char* ring_wave, const mpk_kparams& 
   for (int i = 0; i < R; ++i) ring_top_up<R>(I, S, ring_wave, P, Q, qlen, wave, lane);
 }
 
-// Stage x (times the RMSNorm gain when the operator normalises) into LDS,
-// compute 1 / rms per request, and stage the tile's residual rows.  All
-// waves take part in the barriers.
+// Stage the GEMV input into LDS: x (gathered from its producers' stamped
+// words, an embedding row, or a plain input tensor), times the RMSNorm gain
+// when the operator normalises, 1 / rms per request, and the tile's residual
+// rows.  Every thread of the workgroup takes part.  Returns -1 on stop.
+#define XCH 8  // stamped x words per thread per gather pass
 template <int NB>
-DEV void stage_x(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, bool sched) {
+DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, int s, int task_id) {
   float* xs = reinterpret_cast<float*>(smem + LDS_X);
   float* res = reinterpret_cast<float*>(smem + Lay<NB>::RES);
   float* red = reinterpret_cast<float*>(smem + LDS_RED);
@@ -435,52 +588,106 @@ DEV void stage_x(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, bo
   const int K = D.K;
   const int Kpad = ((K + 511) / 512) * 512;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t st = stamp_of(P, s);
+  Waiter Wt = waiter_start();
+  if (D.x_embed || D.res_embed) {
+    const int rc = resolve_tokens(P, smem, tid, s, task_id, Wt);
+    if (rc) return rc;
+  }
+  // residual element of this thread: request rb, row rrow of the tile
+  const int nres = D.epi == MPK_EPI_RESID ? NB * T.nrows : 0;
+  bool need_r = false;
+  float rv = 0.f;
+  int rb = 0, rrow = 0;
+  if (tid < nres) {
+    rb = tid / T.nrows;
+    rrow = T.row0 + tid - rb * T.nrows;
+    if (D.res_embed) rv = bf16f(gld16(D.E + (int64_t)cur_token_v(smem, rb) * D.n_out + rrow));
+    else if (D.rll) need_r = true;
+    else rv = gld(D.resid + (int64_t)rb * D.n_out + rrow);
+  }
   float ss[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) ss[b] = 0.f;
-  if (!sched) {
+  // x element e = b * K + k; thread tid takes e = base + tid + 512 j.  Raw
+  // values land in LDS as they arrive; the RMS sums and the gain are applied
+  // afterwards in a fixed order (deterministic).
+  const int NE = NB * K;
+  const bool worker = tid < MPK_NW * 64;
+  for (int base = 0; base < NE; base += XCH * MPK_NW * 64) {
+    uint32_t need = 0;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const uint16_t* erow = nullptr;
-      if (D.x_embed) erow = D.E + (int64_t)cur_token(P, smem, b) * K;
-      for (int k = tid * 4; k < Kpad; k += MPK_NW * 64 * 4) {
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        if (k < K) {
-          if (D.x_embed) {
-            const u32x2 e = gldv<u32x2>(erow + k);
-            v[0] = bf16lo(e.x), v[1] = bf16hi(e.x), v[2] = bf16lo(e.y), v[3] = bf16hi(e.y);
-          } else {
-            const float* xp = D.x + (int64_t)b * K + k;
-            v[0] = ld_dev(xp), v[1] = ld_dev(xp + 1), v[2] = ld_dev(xp + 2), v[3] = ld_dev(xp + 3);
-          }
-          if (D.has_norm) {
-            const u32x2 gg = gldv<u32x2>(D.gain + k);
-            const float g[4] = {bf16lo(gg.x), bf16hi(gg.x), bf16lo(gg.y), bf16hi(gg.y)};
+    for (int j = 0; j < XCH; ++j)
+      if (worker && base + tid + j * MPK_NW * 64 < NE) need |= 1u << j;
+    if (D.xll) {
+      for (;;) {
+        uint64_t v[XCH];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              ss[b] = fmaf(v[e], v[e], ss[b]);
-              v[e] = v[e] * g[e];
-            }
+        for (int j = 0; j < XCH; ++j)
+          if ((need >> j) & 1u) v[j] = ld_ll(D.xll + base + tid + j * MPK_NW * 64);
+        uint64_t wr = 0;
+        if (need_r) wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
+        // (request, column) of element j, stepped from j = 0 without divisions
+        int eb = (base + tid) / K, ek = base + tid - eb * K;
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+          if (((need >> j) & 1u) && ll_ok(v[j], st)) {
+            xs[eb * Kpad + xperm(ek)] = ll_f(v[j]);
+            need &= ~(1u << j);
           }
+          ek += MPK_NW * 64;
+          while (ek >= K) ek -= K, ++eb;
         }
-        *reinterpret_cast<float4*>(xs + b * Kpad + xperm(k)) = float4{v[0], v[1], v[2], v[3]};
+        if (need_r && ll_ok(wr, st)) rv = ll_f(wr), need_r = false;
+        const int rc = wait_round(P, Wt, need != 0 || need_r, s, task_id, smem, tid);
+        if (rc < 0) return rc;
+        if (rc == 0) break;
       }
-      if (D.epi == MPK_EPI_RESID) {
-        for (int i = tid; i < T.nrows; i += MPK_NW * 64) {
-          const int row = T.row0 + i;
-          float r;
-          if (D.res_embed) r = bf16f(gld16(D.E + (int64_t)cur_token(P, smem, b) * D.n_out + row));
-          else r = ld_dev(D.resid + (int64_t)b * D.n_out + row);
-          res[b * T.nrows + i] = r;
+    } else {
+#pragma unroll
+      for (int j = 0; j < XCH; ++j) {
+        if ((need >> j) & 1u) {
+          const int e = base + tid + j * MPK_NW * 64;
+          const int b = e / K, k = e - b * K;
+          xs[b * Kpad + xperm(k)] =
+              D.x_embed ? bf16f(gld16(D.E + (int64_t)cur_token_v(smem, b) * K + k)) : gld(D.x + e);
         }
       }
     }
-    if (D.has_norm) {
+  }
+  // RMS sums and gain, each thread over its own elements in a fixed order
+  if (D.has_norm) {
+    for (int e = worker ? tid : NE; e < NE; e += MPK_NW * 64) {
+      const int b = e / K, k = e - b * K;
+      float* px = xs + b * Kpad + xperm(k);
+      const float x = *px;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float t = wave_sum(ss[b]);
-        if ((tid & 63) == 0) red[wave * 8 + b] = t;
+      for (int bb = 0; bb < NB; ++bb) ss[bb] = fmaf(bb == b ? x : 0.f, x, ss[bb]);
+      *px = x * bf16f(gld16(D.gain + k));
+    }
+  }
+  // a residual not gathered with x (x did not come from stamped words)
+  if (D.rll && !D.xll) {
+    for (;;) {
+      if (need_r) {
+        const uint64_t wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
+        if (ll_ok(wr, st)) rv = ll_f(wr), need_r = false;
       }
+      const int rc = wait_round(P, Wt, need_r, s, task_id, smem, tid);
+      if (rc < 0) return rc;
+      if (rc == 0) break;
+    }
+  }
+  // zero padding columns of x (K not a multiple of 512)
+  for (int i = K + (worker ? tid : Kpad); i < Kpad; i += MPK_NW * 64)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xs[b * Kpad + xperm(i)] = 0.f;
+  if (tid < nres) res[tid] = rv;
+  if (D.has_norm && worker) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float t = wave_sum(ss[b]);
+      if ((tid & 63) == 0) red[wave * 8 + b] = t;
     }
   }
   __syncthreads();
@@ -494,6 +701,7 @@ DEV void stage_x(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, bo
     }
   }
   __syncthreads();
+  return 0;
 }
 
 DEV float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -503,31 +711,39 @@ DEV void unpack8(const u32x4 w, float (&f)[8]) {
   f[4] = bf16lo(w.z), f[5] = bf16hi(w.z), f[6] = bf16lo(w.w), f[7] = bf16hi(w.w);
 }
 
+// Publish one output element: its stamped word for consumer tasks, and the
+// plain value when the tensor is attached by the caller.
+DEV void put_out(cop& D, int64_t i, float v, uint32_t st) {
+  st_ll(D.yll + i, v, st);
+  if (D.y) gst(D.y + i, v);
+}
+
 // ---------------------------------------------------------------------------
 // GEMV-type task: rmsnorm_linear (EPI_STORE), linear + residual (EPI_RESID),
 // rmsnorm + gate/up + SiLU-mul (EPI_SILU), final norm + LM head + tile argmax
-// (EPI_ARGMAX).  Row results are staged in LDS (LDS_OUT); the scheduler
-// wavefront publishes them after the task.
+// (EPI_ARGMAX).  Lane 0 of the wavefront that finishes a row publishes the
+// row's output word at once.  Returns -1 on stop.
 // ---------------------------------------------------------------------------
 template <int NB>
-DEV void gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I, RingState& RS, cqent* Q, int qlen,
-                   int s, char* smem, int tid, bool sched) {
+DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I, RingState& RS, cqent* Q, int qlen, int s,
+                  int task_id, char* smem, int tid, bool sched) {
   constexpr int R = Lay<NB>::R;
-  stage_x<NB>(P, D, T, smem, tid, sched);
-  if (sched && P.trace && (tid & 63) == 0)
-    P.trace[(int64_t)s * P.n_tasks + (&T - tasks_of(P))].t_ready = clock_now();
+  {
+    const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id);
+    if (rc) return rc;
+  }
+  mark_ready(P, s, task_id, tid);
+  const uint32_t st = stamp_of(P, s);
   const int EPI = D.epi;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const float* xs = reinterpret_cast<const float*>(smem + LDS_X);
   const float* res = reinterpret_cast<const float*>(smem + Lay<NB>::RES);
-  float* outs = reinterpret_cast<float*>(smem + LDS_OUT);
   const float* inv_lds = reinterpret_cast<const float*>(smem + LDS_INV);
   float inv[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) inv[b] = inv_lds[b];
   char* ring_wave = smem + Lay<NB>::RING + wave * R * 1024;
   const int Kpad = ((D.K + 511) / 512) * 512;
-  const int n_out_tile = D.pairs ? T.nrows / 2 : T.nrows;
   float best_v[NB];
   int best_i[NB];
 #pragma unroll
@@ -575,15 +791,15 @@ DEV void gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I, RingState&
           acc[b] = 0.f;
           // LDS traffic inside the weight stream stays in asm (see lds_read_u32x4)
           if (EPI == MPK_EPI_STORE) {
-            if (lane == 0) lds_write_f32(lds_addr(outs + b * n_out_tile + lrow), sum * inv[b]);
+            if (lane == 0) put_out(D, (int64_t)b * D.n_out + vrow, sum * inv[b], st);
           } else if (EPI == MPK_EPI_RESID) {
             const float rv = lds_read_f32(lds_addr(res) + (uint32_t)(b * T.nrows + lrow) * 4u);
-            if (lane == 0) lds_write_f32(lds_addr(outs + b * n_out_tile + lrow), rv + sum);
+            if (lane == 0) put_out(D, (int64_t)b * D.n_out + vrow, rv + sum, st);
           } else if (EPI == MPK_EPI_SILU) {
             if (rr == 0) {
               gate[b] = sum * inv[b];
             } else if (lane == 0) {
-              lds_write_f32(lds_addr(outs + b * n_out_tile + (lrow >> 1)), silu(gate[b]) * (sum * inv[b]));
+              put_out(D, (int64_t)b * D.n_out + (vrow >> 1), silu(gate[b]) * (sum * inv[b]), st);
             }
           } else {  // ARGMAX
             const float logit = sum * inv[b];
@@ -600,7 +816,8 @@ DEV void gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I, RingState&
     }
   }
   if (EPI == MPK_EPI_ARGMAX) {
-    // tile argmax over the waves (lowest row among equal maxima)
+    // tile argmax over the waves (lowest row among equal maxima), published
+    // as two stamped words (value, row) per request
     float* bv = reinterpret_cast<float*>(smem + LDS_BEST);
     int* bi = reinterpret_cast<int*>(smem + LDS_BEST + MPK_NW * 8 * 4);
     if (!sched && lane == 0) {
@@ -616,62 +833,71 @@ DEV void gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I, RingState&
         const int ii = bi[w * 8 + tid];
         if (vv > v || (vv == v && ii < ix)) v = vv, ix = ii;
       }
-      outs[2 * tid] = v;
-      outs[2 * tid + 1] = __int_as_float(ix);
+      uint64_t* pw = D.pll + ((int64_t)T.tile * NB + tid) * 2;
+      st_ll(pw, v, st);
+      st_lli(pw + 1, ix, st);
     }
   }
+  return 0;
 }
 
-// Scheduler wavefront: publish a GEMV / LM-head task's staged outputs.
+// Argmax task: the LM head's per-tile maxima -> next token per request.
+// Writes tokens[r][p + 1] when generating (the prompt's own token otherwise
+// stays), advances step, and publishes the token word that the next
+// iteration's embedding reads wait for.
 template <int NB>
-DEV void publish_gemv(const mpk_kparams& P, ctask& T, cop& D, const char* smem, int lane) {
-  const float* outs = reinterpret_cast<const float*>(smem + LDS_OUT);
-  if (D.epi == MPK_EPI_ARGMAX) {
-    if (lane < 2 * NB) st_dev(D.part + (int64_t)T.tile * NB * 2 + lane, outs[lane]);
-    return;
+DEV int argmax_task(const mpk_kparams& P, cop& D, char* smem, int tid, int s, int task_id) {
+  const uint32_t st = stamp_of(P, s);
+  uint32_t* raw = reinterpret_cast<uint32_t*>(smem + LDS_X);  // [N1 * NB][2]
+  const int nw = D.N1 * NB * 2;                                // N1: LM-head tiles
+  Waiter Wt = waiter_start();
+  {
+    const int rc = gather_ll<4>(P, D.pll, nw, raw, st, Wt, s, task_id, smem, tid);
+    if (rc) return rc;
   }
-  const int n_out_tile = D.pairs ? T.nrows / 2 : T.nrows;
-  const int out0 = D.pairs ? T.row0 / 2 : T.row0;
-  for (int i = lane; i < NB * n_out_tile; i += 64) {
-    const int b = i / n_out_tile, j = i - b * n_out_tile;
-    st_dev(D.y + (int64_t)b * D.n_out + out0 + j, outs[i]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Argmax task: reduce the LM-head tiles' (max, index) pairs, write the token
-// when the prompt is consumed, advance step (scheduler wavefront only).
-// ---------------------------------------------------------------------------
-template <int NB>
-DEV void argmax_publish(const mpk_kparams& P, cop& D, int lane) {
+  mark_ready(P, s, task_id, tid);
+  const int wave = tid >> 6, lane = tid & 63;
+  if (wave == 0) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float v = -INFINITY;
-    int ix = 0x7fffffff;
-    for (int t = lane; t < D.N1; t += 64) {  // N1: LM-head tiles
-      const float vv = ld_dev(D.part + ((int64_t)t * NB + b) * 2);
-      const int ii = __float_as_int(ld_dev(D.part + ((int64_t)t * NB + b) * 2 + 1));
-      if (vv > v || (vv == v && ii < ix)) v = vv, ix = ii;
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(v, off);
-      const int oi = __shfl_xor(ix, off);
-      if (ov > v || (ov == v && oi < ix)) v = ov, ix = oi;
-    }
-    if (lane == 0) {
-      const int p = ld_devi(P.step + b);
-      if (p + 1 >= ld_devi(P.prompt_len + b)) st_devi(P.tokens + (int64_t)b * P.tokens_width + p + 1, ix);
-      st_devi(P.step + b, p + 1);
+    for (int b = 0; b < NB; ++b) {
+      float v = -INFINITY;
+      int ix = 0x7fffffff;
+      for (int t = lane; t < D.N1; t += 64) {
+        const float vv = __uint_as_float(raw[(t * NB + b) * 2]);
+        const int ii = (int)raw[(t * NB + b) * 2 + 1];
+        if (vv > v || (vv == v && ii < ix)) v = vv, ix = ii;
+      }
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(v, off);
+        const int oi = __shfl_xor(ix, off);
+        if (ov > v || (ov == v && oi < ix)) v = ov, ix = oi;
+      }
+      if (lane == 0) {
+        const int p = cur_pos(smem, b);
+        int next = ix;
+        if (p + 1 >= ld_devi(P.prompt_len + b)) {
+          st_devi(P.tokens + (int64_t)b * P.tokens_width + p + 1, ix);
+        } else {
+          next = ld_devi(P.tokens + (int64_t)b * P.tokens_width + p + 1);  // teacher-forced prompt token
+        }
+        st_devi(P.step + b, p + 1);
+        st_lli(P.tok_ll + b, next, st);
+      }
     }
   }
+  return 0;
 }
+
 // ---------------------------------------------------------------------------
 // Attention task (request r, kv head j, split c of nsplit): per-head RMSNorm
 // of q and k, RoPE at the request's position p, K/V of p into the caches
 // (by the split that owns p), an online softmax over this split's positions
-// kept per lane group in registers, one merge across the wavefronts, and, in
-// the last arriving split of (r, j), the merge of the splits into the
-// attention output of the group's query heads.
+// kept per lane group in registers, and one merge across the wavefronts.
+// The context [0, p] is cut into na = min(nsplit, ceil((p + 1) / 128))
+// splits; splits c >= na have nothing to do this iteration.  With one split
+// the task writes the attention output of the group's query heads; with
+// several, splits publish stamped partials (m, l, acc) and the split that
+// owns p merges them into the output.  Returns -1 on stop.
 // ---------------------------------------------------------------------------
 #define ATT_MAXG 4
 #define ATT_ROUNDS 2  // position rounds per wavefront whose K/V rows are loaded together
@@ -680,40 +906,38 @@ struct SoftState {
   float m[ATT_MAXG], l[ATT_MAXG], acc[ATT_MAXG][8];
 };
 
-DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, bool sched) {
+DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, bool sched, int s, int task_id) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = T.row0, j = T.nrows, c = T.split, NS = D.nsplit;
   const int d = D.d, G = D.nq / D.nkv, half = d >> 1, LP = d >> 3, PPR = 64 / LP;
   const int p = cur_pos(smem, r);
   const int n = p + 1;
-  // splits in use this iteration: about 128 positions each, at most nsplit
   const int na = min(NS, (n + 127) / 128);
-  const bool active = c < na;
-  const int lo = active ? (int)(((int64_t)c * n) / na) : n, hi = active ? (int)(((int64_t)(c + 1) * n) / na) : n;
+  if (c >= na) return 0;  // uniform over the workgroup: nothing to do this iteration
+  const int lo = (int)(((int64_t)c * n) / na), hi = (int)(((int64_t)(c + 1) * n) / na);
+  const bool owner = c == na - 1;  // the split holding position p
+  const uint32_t st = stamp_of(P, s);
   float* qs = reinterpret_cast<float*>(smem + LDS_X);  // [G][d]
   float* kv = qs + ATT_MAXG * 128;                      // k [d], v [d] (bf16-rounded)
   float* wm = kv + 256;                                 // [NW][G]
   float* wl = wm + MPK_NW * ATT_MAXG;                   // [NW][G]
   float* wacc = wl + MPK_NW * ATT_MAXG;                 // [NW][G][128]
-  volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
+  uint32_t* gath = reinterpret_cast<uint32_t*>(wacc + MPK_NW * ATT_MAXG * 128);  // gathered partials
   float* outs = reinterpret_cast<float*>(smem + LDS_OUT);               // partial, then o
   uint32_t* kvrow = reinterpret_cast<uint32_t*>(smem + LDS_OUT) + 640;  // bf16 K row, then V row
   const int qkv_w = (D.nq + 2 * D.nkv) * d;
-  const float* qkv = D.x + (int64_t)r * qkv_w;
   uint16_t* kc = D.kc + ((int64_t)(r * D.nkv + j) * D.S) * d;
   uint16_t* vc = D.vc + ((int64_t)(r * D.nkv + j) * D.S) * d;
-  const bool owner = active && c == na - 1;
-  if (!active) return false;  // uniform over the workgroup: no barrier has been passed
   const int dim0 = (lane % LP) * 8;
   const int pg = lane / LP;
   const float scale = 1.0f / sqrtf((float)d);
 
-  SoftState st;
+  SoftState sm;
 #pragma unroll
   for (int h = 0; h < ATT_MAXG; ++h) {
-    st.m[h] = -INFINITY, st.l[h] = 0.f;
+    sm.m[h] = -INFINITY, sm.l[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
+    for (int e = 0; e < 8; ++e) sm.acc[h][e] = 0.f;
   }
   // K/V rows of this wave's first rounds: issued before anything else (the
   // cache rows below p do not depend on this iteration)
@@ -729,48 +953,77 @@ DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, 
   };
   if (!sched && lo < hi) load_rounds(lo);
 
-  // ---- q / k / v of the group: RMSNorm + RoPE (waves 0..G+1) ----
-  if (!sched) {
-    for (int hh = wave; hh < G + 2; hh += MPK_NW) {
-      const float* src = hh < G ? qkv + (int64_t)(j * G + hh) * d
-                                : (hh == G ? qkv + (int64_t)D.nq * d + j * d
-                                           : qkv + (int64_t)(D.nq + D.nkv) * d + j * d);
-      const float a = lane < half ? ld_dev(src + lane) : 0.f;
-      const float b = lane < half ? ld_dev(src + lane + half) : 0.f;
-      if (hh <= G) {
-        const float cs = lane < half ? gld(P.rope_cos + (int64_t)p * half + lane) : 0.f;
-        const float sn = lane < half ? gld(P.rope_sin + (int64_t)p * half + lane) : 0.f;
-        const uint16_t* gsrc = hh < G ? D.qn : D.kn;
-        const float ga = lane < half ? bf16f(gld16(gsrc + lane)) : 0.f;
-        const float gb = lane < half ? bf16f(gld16(gsrc + lane + half)) : 0.f;
-        const float ss = wave_sum(a * a + b * b);
-        const float inv = 1.0f / sqrtf(ss / (float)d + P.rms_eps);
-        if (lane < half) {
-          const float ya = ga * (a * inv);
-          const float yb = gb * (b * inv);
-          const float ra = ya * cs - yb * sn;
-          const float rb = yb * cs + ya * sn;
-          if (hh < G) {
-            qs[hh * d + lane] = ra;
-            qs[hh * d + lane + half] = rb;
-          } else {
-            const uint16_t ka = f2bf(ra), kb = f2bf(rb);
-            kv[lane] = bf16f(ka);
-            kv[lane + half] = bf16f(kb);
-            reinterpret_cast<uint16_t*>(kvrow)[lane] = ka;
-            reinterpret_cast<uint16_t*>(kvrow)[lane + half] = kb;
-          }
-        }
-      } else if (lane < half) {
-        const uint16_t va = f2bf(a), vb = f2bf(b);
-        kv[d + lane] = bf16f(va);
-        kv[d + lane + half] = bf16f(vb);
-        reinterpret_cast<uint16_t*>(kvrow)[d + lane] = va;
-        reinterpret_cast<uint16_t*>(kvrow)[d + lane + half] = vb;
+  // ---- q / k / v words of the group: wave hh < G + 2 takes one head vector ----
+  Waiter Wt = waiter_start();
+  const int hh = wave;
+  const bool mine = !sched && hh < G + 2 && lane < half;
+  const uint64_t* src = D.xll + (int64_t)r * qkv_w +
+                        (hh < G ? (j * G + hh) * d : (hh == G ? D.nq * d + j * d : (D.nq + D.nkv) * d + j * d));
+  uint64_t wa = 0, wb = 0;
+  {
+    bool need = mine;
+    for (;;) {
+      if (need) {
+        wa = ld_ll(src + lane);
+        wb = ld_ll(src + lane + half);
+        need = !(ll_ok(wa, st) && ll_ok(wb, st));
       }
+      const int rc = wait_round(P, Wt, need, s, task_id, smem, tid);
+      if (rc < 0) return rc;
+      if (rc == 0) break;
+    }
+  }
+  mark_ready(P, s, task_id, tid);
+
+  // ---- RMSNorm + RoPE (waves 0..G+1) ----
+  if (!sched && hh < G + 2) {
+    const float a = lane < half ? ll_f(wa) : 0.f;
+    const float b = lane < half ? ll_f(wb) : 0.f;
+    if (hh <= G) {
+      const float cs = lane < half ? gld(P.rope_cos + (int64_t)p * half + lane) : 0.f;
+      const float sn = lane < half ? gld(P.rope_sin + (int64_t)p * half + lane) : 0.f;
+      const uint16_t* gsrc = hh < G ? D.qn : D.kn;
+      const float ga = lane < half ? bf16f(gld16(gsrc + lane)) : 0.f;
+      const float gb = lane < half ? bf16f(gld16(gsrc + lane + half)) : 0.f;
+      const float ss = wave_sum(a * a + b * b);
+      const float inv = 1.0f / sqrtf(ss / (float)d + P.rms_eps);
+      if (lane < half) {
+        const float ya = ga * (a * inv);
+        const float yb = gb * (b * inv);
+        const float ra = ya * cs - yb * sn;
+        const float rb = yb * cs + ya * sn;
+        if (hh < G) {
+          qs[hh * d + lane] = ra;
+          qs[hh * d + lane + half] = rb;
+        } else {
+          const uint16_t ka = f2bf(ra), kb = f2bf(rb);
+          kv[lane] = bf16f(ka);
+          kv[lane + half] = bf16f(kb);
+          reinterpret_cast<uint16_t*>(kvrow)[lane] = ka;
+          reinterpret_cast<uint16_t*>(kvrow)[lane + half] = kb;
+        }
+      }
+    } else if (lane < half) {
+      const uint16_t va = f2bf(a), vb = f2bf(b);
+      kv[d + lane] = bf16f(va);
+      kv[d + lane + half] = bf16f(vb);
+      reinterpret_cast<uint16_t*>(kvrow)[d + lane] = va;
+      reinterpret_cast<uint16_t*>(kvrow)[d + lane + half] = vb;
     }
   }
   __syncthreads();
+  // the owner's scheduler wavefront writes K/V of p into the caches while the
+  // workers score; its stores complete before the output is published (next
+  // iteration's readers are ordered after that output)
+  if (sched && owner) {
+    uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * d);
+    uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * d);
+    for (int i = lane; i < d / 2; i += 64) {
+      st_devu(kdst + i, kvrow[i]);
+      st_devu(vdst + i, kvrow[d / 2 + i]);
+    }
+    vm_drain();
+  }
 
   // ---- scores and online softmax over this wave's positions ----
   if (!sched) {
@@ -803,13 +1056,13 @@ DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, 
             for (int off = 1; off < LP; off <<= 1) part += __shfl_xor(part, off);
             if (valid) {
               const float sc = part * scale;
-              const float M = fmaxf(st.m[h], sc);
-              const float co = st.m[h] == -INFINITY ? 0.f : expf(st.m[h] - M);
+              const float M = fmaxf(sm.m[h], sc);
+              const float co = sm.m[h] == -INFINITY ? 0.f : expf(sm.m[h] - M);
               const float cn = expf(sc - M);
-              st.l[h] = st.l[h] * co + cn;
+              sm.l[h] = sm.l[h] * co + cn;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) st.acc[h][e] = st.acc[h][e] * co + cn * vf[e];
-              st.m[h] = M;
+              for (int e = 0; e < 8; ++e) sm.acc[h][e] = sm.acc[h][e] * co + cn * vf[e];
+              sm.m[h] = M;
             }
           }
         }
@@ -820,15 +1073,15 @@ DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, 
     for (int h = 0; h < ATT_MAXG; ++h) {
       if (h < G) {
         for (int off = LP; off < 64; off <<= 1) {
-          const float om = __shfl_xor(st.m[h], off);
-          const float ol = __shfl_xor(st.l[h], off);
-          const float M = fmaxf(st.m[h], om);
-          const float ca = st.m[h] == -INFINITY ? 0.f : expf(st.m[h] - M);
+          const float om = __shfl_xor(sm.m[h], off);
+          const float ol = __shfl_xor(sm.l[h], off);
+          const float M = fmaxf(sm.m[h], om);
+          const float ca = sm.m[h] == -INFINITY ? 0.f : expf(sm.m[h] - M);
           const float cb = om == -INFINITY ? 0.f : expf(om - M);
-          st.l[h] = st.l[h] * ca + ol * cb;
+          sm.l[h] = sm.l[h] * ca + ol * cb;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) st.acc[h][e] = st.acc[h][e] * ca + __shfl_xor(st.acc[h][e], off) * cb;
-          st.m[h] = M;
+          for (int e = 0; e < 8; ++e) sm.acc[h][e] = sm.acc[h][e] * ca + __shfl_xor(sm.acc[h][e], off) * cb;
+          sm.m[h] = M;
         }
       }
     }
@@ -836,18 +1089,19 @@ DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, 
     for (int h = 0; h < ATT_MAXG; ++h) {
       if (h < G) {
         if (lane == 0) {
-          wm[wave * ATT_MAXG + h] = st.m[h];
-          wl[wave * ATT_MAXG + h] = st.l[h];
+          wm[wave * ATT_MAXG + h] = sm.m[h];
+          wl[wave * ATT_MAXG + h] = sm.l[h];
         }
         if (lane < LP)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) wacc[(wave * ATT_MAXG + h) * 128 + dim0 + e] = st.acc[h][e];
+          for (int e = 0; e < 8; ++e) wacc[(wave * ATT_MAXG + h) * 128 + dim0 + e] = sm.acc[h][e];
       }
     }
   }
   __syncthreads();
-  // ---- merge the wavefronts: the split's partial (m, l, acc) per head ----
+  // ---- merge the wavefronts: this split's (m, l, acc) per head ----
   const int stride = d + 2;
+  const int64_t o_base = (int64_t)r * D.nq * d + (int64_t)j * G * d;
   for (int idx = tid; idx < G * d && !sched; idx += MPK_NW * 64) {
     const int h = idx / d, i = idx - h * d;
     float M = -INFINITY;
@@ -860,7 +1114,7 @@ DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, 
       A = fmaf(wacc[(w * ATT_MAXG + h) * 128 + i], cw, A);
     }
     if (na == 1) {
-      outs[idx] = A / L;  // the whole context in one split: this is o
+      put_out(D, o_base + idx, A / L, st);  // the whole context in one split
     } else {
       outs[h * stride + 2 + i] = A;
       if (i == 0) {
@@ -869,149 +1123,59 @@ DEV bool attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, 
       }
     }
   }
+  if (na == 1) return 0;
   __syncthreads();
-  if (na == 1) {
-    // publish the K/V row here (the scheduler wavefront publishes o after the task)
-    if (sched) {
-      uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * d);
-      uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * d);
-      for (int i = lane; i < d / 2; i += 64) {
-        st_devu(kdst + i, kvrow[i]);
-        st_devu(vdst + i, kvrow[d / 2 + i]);
-      }
-    }
-    return true;
+  uint64_t* pgrp = D.pll + (int64_t)((r * D.nkv + j) * NS) * G * stride;
+  if (!owner) {
+    // publish this split's partial for the owner
+    for (int i = tid; i < G * stride; i += MPK_THREADS) st_ll(pgrp + (int64_t)c * G * stride + i, outs[i], st);
+    return 0;
   }
-  // scheduler wavefront: publish the split's partial (and the new K/V row
-  // from the split that owns the position), then take a ticket of the group
-  if (sched) {
-    float* part = D.part + ((int64_t)((r * D.nkv + j) * NS + c) * G) * stride;
-    // (na == 1 returned earlier; here the partial goes to the group's merge)
-    for (int i = lane; i < G * stride; i += 64) st_dev(part + i, outs[i]);
-    if (owner) {
-      uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * d);
-      uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * d);
-      for (int i = lane; i < d / 2; i += 64) {
-        st_devu(kdst + i, kvrow[i]);
-        st_devu(vdst + i, kvrow[d / 2 + i]);
-      }
-    }
-    vm_drain();
-    if (lane == 0) {
-      uint32_t* tk = D.tickets + (r * D.nkv + j);
-      const uint32_t old = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last_arr = old + 1 == (uint32_t)na;
-      // The last arriver resets the counter for the next iteration: every
-      // split of this group has counted, and the next iteration's splits
-      // start only after this group's output flag.
-      if (last_arr) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ctl[1] = last_arr;
-    }
-  }
-  __syncthreads();
-  const bool last = ctl[1] != 0;
-  if (last) {
-    // merge the group's splits: o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M)
-    const float* pbase = D.part + ((int64_t)((r * D.nkv + j) * NS) * G) * stride;
-    // G * d <= 512 = worker threads: one output element per worker thread
-    float o_val = 0.f;
-    const int idx = tid;
-    const bool mine = !sched && idx < G * d;
-    if (mine) {
-      const int h = idx / d, i = idx - h * d;
-      float M = -INFINITY;
-      for (int cc = 0; cc < na; ++cc) M = fmaxf(M, ld_dev(pbase + ((int64_t)cc * G + h) * stride));
-      float L = 0.f, O = 0.f;
-      for (int cc = 0; cc < na; ++cc) {
-        const float* pp = pbase + ((int64_t)cc * G + h) * stride;
-        const float lc = ld_dev(pp + 1);
+  // owner: merge the other splits' partials (gathered in chunks) into its own,
+  // in split order: o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M)
+  const int idx = tid;
+  const bool mine_o = !sched && idx < G * d;
+  const int h = mine_o ? idx / d : 0, i = mine_o ? idx - h * d : 0;
+  float M = mine_o ? outs[h * stride] : 0.f;
+  float L = mine_o ? outs[h * stride + 1] : 0.f;
+  float O = mine_o ? outs[h * stride + 2 + i] : 0.f;
+  const int chunk = (Lay<1>::XS - (int)((char*)gath - (smem + LDS_X))) / 4 / (G * stride);
+  for (int c0 = 0; c0 < na - 1; c0 += chunk) {
+    const int nc = min(chunk, na - 1 - c0);
+    const int rc =
+        gather_ll<16>(P, pgrp + (int64_t)c0 * G * stride, nc * G * stride, gath, st, Wt, s, task_id, smem, tid);
+    if (rc) return rc;
+    if (mine_o) {
+      for (int cc = 0; cc < nc; ++cc) {
+        const float mc = __uint_as_float(gath[(cc * G + h) * stride]);
+        const float lc = __uint_as_float(gath[(cc * G + h) * stride + 1]);
+        const float ac = __uint_as_float(gath[(cc * G + h) * stride + 2 + i]);
         if (lc > 0.f) {
-          const float wgt = expf(ld_dev(pp) - M);
-          L = fmaf(lc, wgt, L);
-          O = fmaf(ld_dev(pp + 2 + i), wgt, O);
+          const float Mn = fmaxf(M, mc);
+          const float ca = M == -INFINITY ? 0.f : expf(M - Mn);
+          const float cb = expf(mc - Mn);
+          L = L * ca + lc * cb;
+          O = O * ca + ac * cb;
+          M = Mn;
         }
       }
-      o_val = O / L;
     }
-    __syncthreads();  // the partial area of LDS_OUT is reused for o
-    if (mine) outs[idx] = o_val;
+    __syncthreads();  // the gather area is reused by the next chunk
   }
-  return last;
+  if (mine_o) put_out(D, o_base + idx, O / L, st);
+  return 0;
 }
 
 // ---------------------------------------------------------------------------
-// dispatch of one task body; returns true when the task stamps its flag
+// dispatch of one task body; returns -1 when the run must stop
 // ---------------------------------------------------------------------------
 template <int NB>
-DEV bool run_task(const mpk_kparams& P, ctask& T, Issuer& I, RingState& RS, cqent* Q, int qlen, int s,
-                  char* smem, int tid, bool sched) {
+DEV int run_task(const mpk_kparams& P, ctask& T, int task_id, Issuer& I, RingState& RS, cqent* Q, int qlen, int s,
+                 char* smem, int tid, bool sched) {
   cop& D = ops_of(P)[T.op];
-  if (T.kind == MPK_TK_ATTN) return attn_task(P, T, D, smem, tid, sched);
-  if (T.kind == MPK_TK_ARGMAX) return true;  // done by the scheduler wavefront in publish()
-  gemv_task<NB>(P, T, D, I, RS, Q, qlen, s, smem, tid, sched);
-  return true;
-}
-
-// Scheduler wavefront, after the task's end barrier: publish its outputs,
-// wait for the stores, stamp the flag.
-template <int NB>
-DEV void publish(const mpk_kparams& P, ctask& T, bool sig, int s, const char* smem, int lane) {
-  cop& D = ops_of(P)[T.op];
-  if (T.kind == MPK_TK_ATTN) {
-    if (sig) {
-      const int G = D.nq / D.nkv;
-      const float* outs = reinterpret_cast<const float*>(smem + LDS_OUT);
-      float* o = D.y + (int64_t)T.row0 * D.nq * D.d + (int64_t)T.nrows * G * D.d;
-      for (int i = lane; i < G * D.d; i += 64) st_dev(o + i, outs[i]);
-    }
-  } else if (T.kind == MPK_TK_ARGMAX) {
-    argmax_publish<NB>(P, D, lane);
-  } else {
-    publish_gemv<NB>(P, T, D, smem, lane);
-  }
-  vm_drain();
-  if (sig && lane == 0) st_devu(P.flags + T.out_flag, (uint32_t)(s + 1));
-}
-
-// Scheduler wavefront: spin until every producer flag of every dependency of
-// T carries the stamp of iteration s (or s - 1 for previous-iteration
-// dependencies).  Returns false (after recording a status) on watchdog
-// timeout or a stop request; false is uniform across the wavefront.
-DEV bool wait_deps(const mpk_kparams& P, ctask& T, int s, int task_id, int lane) {
-  const uint64_t t0 = clock_now();
-  int spins = 0;
-  for (int k = 0; k < T.n_deps; ++k) {
-    const uint32_t target = (uint32_t)(s + 1 - T.dep_prev[k]);
-    const uint32_t* f = P.flags + T.dep_base[k];
-    const int n = T.dep_n[k];
-    for (;;) {
-      bool ok = true;
-      for (int i = lane; i < n; i += 64) ok &= ld_devu(f + i) >= target;
-      if (__ballot(!ok) == 0) break;
-      if ((++spins & 15) == 0) {
-        int mine = 0, code = 0;
-        if (lane == 0) {
-          code = __hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const int abort_req =
-              __hip_atomic_load(&P.status->abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-          if (abort_req) mine = MPK_ERR_ABORTED;
-          else if (clock_now() - t0 > P.timeout_ticks) mine = MPK_ERR_DEVICE_TIMEOUT;
-          if (mine) {
-            int expected = 0;
-            if (__hip_atomic_compare_exchange_strong(&P.status->code, &expected, mine, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-              __hip_atomic_store(&P.status->iteration, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              __hip_atomic_store(&P.status->task, task_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-          }
-        }
-        if (__builtin_amdgcn_readfirstlane(mine | code)) return false;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  asm volatile("" ::: "memory");  // the task's device-scope loads stay after the poll
-  return true;
+  if (T.kind == MPK_TK_ATTN) return attn_task(P, T, D, smem, tid, sched, s, task_id);
+  if (T.kind == MPK_TK_ARGMAX) return argmax_task<NB>(P, D, smem, tid, s, task_id);
+  return gemv_task<NB>(P, T, D, I, RS, Q, qlen, s, task_id, smem, tid, sched);
 }
 
 // ---------------------------------------------------------------------------
@@ -1025,6 +1189,7 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
   cqent* Q = (cqent*)(const void*)P.queues + (int64_t)blockIdx.x * P.qstride;
   const int qlen = ((const CAS int32_t*)(const void*)P.qlen)[blockIdx.x];
   volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
+  if (tid == 0) ctl[0] = 0;
   Issuer I;
   RingState RS{0, 0};
   I.live = 0;
@@ -1036,43 +1201,34 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
     for (int k = 0; k < qlen; ++k) {
       const int task_id = Q[k].task;
       ctask& T = tasks_of(P)[task_id];
-      if (sched) {
-        if (k == 0) set_positions(P, smem, s, lane);
-        const bool ok = wait_deps(P, T, s, task_id, lane);
-        if (lane == 0) {
-          ctl[0] = ok ? 0 : 1;
-          if (ok && P.trace) {
-            mpk_trace_record& Rr = P.trace[(int64_t)s * P.n_tasks + task_id];
-            Rr.task = task_id;
-            Rr.iteration = s;
-            Rr.start_ticket = P.trace_tickets ? __hip_atomic_fetch_add(P.ticket_ctr, 1u, __ATOMIC_RELAXED,
-                                                                       __HIP_MEMORY_SCOPE_AGENT) : 0u;
-            Rr.t_start = clock_now();
-            Rr.hw_id = hwreg_hw_id();
-            Rr.xcc_id = hwreg_xcc_id();
-          }
-        }
+      if (k == 0) {
+        if (sched) set_positions(P, smem, s, lane);
+        __syncthreads();
       }
-      __syncthreads();
-      if (ctl[0]) {
-        vm_wait<0>();  // leave no LDS-bound load in flight
-        return;
+      if (sched && lane == 0 && P.trace) {
+        mpk_trace_record& Rr = P.trace[(int64_t)s * P.n_tasks + task_id];
+        Rr.task = task_id;
+        Rr.iteration = s;
+        Rr.t_start = clock_now();
+        Rr.hw_id = hwreg_hw_id();
+        Rr.xcc_id = hwreg_xcc_id();
       }
       // An opaque copy of the thread id per task keeps the compiler from
       // hoisting per-lane address arithmetic of every body out of the task
       // loop (it would stay live, and spill, across all bodies).
       int tid_o = tid;
       asm volatile("" : "+v"(tid_o));
-      const bool sig = run_task<NB>(P, T, I, RS, Q, qlen, s, smem, tid_o, sched);
+      const int rc = run_task<NB>(P, T, task_id, I, RS, Q, qlen, s, smem, tid_o, sched);
+      if (rc < 0) {
+        vm_wait<0>();  // leave no LDS-bound load in flight
+        return;
+      }
       __syncthreads();
-      if (sched) {
-        if (P.trace && lane == 0) {
-          mpk_trace_record& Rr = P.trace[(int64_t)s * P.n_tasks + task_id];
-          Rr.end_ticket = P.trace_tickets ? __hip_atomic_fetch_add(P.ticket_ctr, 1u, __ATOMIC_RELAXED,
-                                                                   __HIP_MEMORY_SCOPE_AGENT) : 0u;
-          Rr.t_end = clock_now();
-        }
-        publish<NB>(P, T, sig, s, smem, lane);
+      if (sched && lane == 0 && P.trace) {
+        mpk_trace_record& Rr = P.trace[(int64_t)s * P.n_tasks + task_id];
+        Rr.end_ticket = P.trace_tickets ? __hip_atomic_fetch_add(P.ticket_ctr, 1u, __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        Rr.t_end = clock_now();
       }
     }
   }
@@ -1090,6 +1246,8 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_op_kernel(mpk_kparams P, i
   ctask& T = tasks_of(P)[task_id];
   // a one-entry queue holding this task, for the ring's producer side
   cqent* q1 = (cqent*)(const void*)P.single_q + task_id;
+  volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
+  if (tid == 0) ctl[0] = 0;
   Issuer I;
   RingState RS{0, 0};
   I.live = 0;
@@ -1102,9 +1260,7 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_op_kernel(mpk_kparams P, i
     set_positions(P, smem, s, lane);
   }
   __syncthreads();
-  const bool sig = run_task<NB>(P, T, I, RS, q1, 1, s, smem, tid, sched);
-  __syncthreads();
-  if (sched) publish<NB>(P, T, sig, s, smem, lane);
+  run_task<NB>(P, T, task_id, I, RS, q1, 1, s, smem, tid, sched);
   vm_wait<0>();
 }
 
@@ -1127,10 +1283,10 @@ struct mpk_exec_s {
   mpk_dev_qentry* d_queues = nullptr;
   mpk_dev_qentry* d_single = nullptr;
   int32_t* d_qlen = nullptr;
-  uint32_t* d_counters = nullptr;  // events | attention tickets | LM tickets | trace ticket
-  int64_t n_counters = 0;
-  uint32_t* d_events = nullptr;
-  uint32_t* d_ticket_ctr = nullptr;
+  uint32_t* d_ticket_ctr = nullptr;  // trace ticket counter
+  uint64_t* d_tok_ll = nullptr;      // [B] stamped next token
+  std::vector<uint64_t*> ll_ptr;     // per tensor: stamped words of an operator output, or NULL
+  uint32_t iter_base = 0;            // stamps used so far (see stamp_of)
   float* d_rope = nullptr;
   mpk_dev_status* d_status = nullptr;
   mpk_trace_record* d_trace = nullptr;
@@ -1217,75 +1373,90 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   // tensors
   const int NTEN = (int)g->tensors.size();
   x->tensor_ptr.assign(NTEN, nullptr);
+  // Operator outputs in f32 are handed between tasks as stamped words (one
+  // 64-bit word per element); an attached output is also written plainly.
+  x->ll_ptr.assign(NTEN, nullptr);
   for (int i = 0; i < NTEN; ++i) {
     const mpk_tensor& t = g->tensors[i];
+    const bool produced = g->producer[i] >= 0 && g->embed_src[i] < 0;
+    if (produced && t.dtype == MPK_F32) {
+      const int64_t n = tensor_bytes(t) / 4;
+      if ((rc = dalloc(x.get(), &x->ll_ptr[i], (size_t)n * 8))) return rc;
+    }
     if (t.dev_ptr) {
       x->tensor_ptr[i] = t.dev_ptr;
+    } else if (x->ll_ptr[i]) {
+      x->tensor_ptr[i] = x->ll_ptr[i];
     } else if (g->embed_src[i] < 0) {
       if ((rc = dalloc(x.get(), &x->tensor_ptr[i], (size_t)tensor_bytes(t)))) return rc;
     }
   }
   auto P = [&](int id) -> void* { return id >= 0 ? x->tensor_ptr[id] : nullptr; };
+  // plain pointer of an attached tensor (NULL for library-owned stamped ones)
+  auto PA = [&](int id) -> void* { return id >= 0 && g->tensors[id].dev_ptr ? x->tensor_ptr[id] : nullptr; };
+  auto PL = [&](int id) -> uint64_t* { return id >= 0 ? x->ll_ptr[id] : nullptr; };
   const mpk_model_cfg& M = g->model;
   const int B = x->B;
 
-  // counters: completion flags, then attention merge tickets, then the trace ticket
   std::vector<mpk_dev_op> dops = g->dops;
-  int64_t ncnt = (int64_t)g->n_flags;
-  std::vector<int64_t> tick_off(dops.size(), -1);
-  for (size_t i = 0; i < dops.size(); ++i)
-    if (dops[i].kind == MPK_TK_ATTN) tick_off[i] = ncnt, ncnt += (int64_t)B * dops[i].nkv;
-  const int64_t ticket_ctr_off = ncnt++;
-  x->n_counters = ncnt;
-  if ((rc = dalloc(x.get(), &x->d_counters, (size_t)ncnt * 4))) return rc;
-  x->d_events = x->d_counters;
-  x->d_ticket_ctr = x->d_counters + ticket_ctr_off;
+  if ((rc = dalloc(x.get(), &x->d_ticket_ctr, 4))) return rc;
+  if ((rc = dalloc(x.get(), &x->d_tok_ll, (size_t)B * 8))) return rc;
 
   for (size_t i = 0; i < dops.size(); ++i) {
     mpk_dev_op& D = dops[i];
     if (!D.kind || D.kind == MPK_TK_ARGMAX) continue;
     const mpk_op& o = g->ops[i];
     if (D.kind == MPK_TK_ATTN) {
-      D.x = (const float*)P(o.in[0]);
+      D.xll = PL(o.in[0]);
+      if (!D.xll) return mpk_fail(MPK_ERR_GRAPH, "attention input must be the output of an operator");
       D.qn = (const uint16_t*)P(o.in[1]);
       D.kn = (const uint16_t*)P(o.in[2]);
       D.kc = (uint16_t*)P(o.in[3]);
       D.vc = (uint16_t*)P(o.in[4]);
-      D.y = (float*)P(o.out[0]);
+      D.y = (float*)PA(o.out[0]);
+      D.yll = PL(o.out[0]);
       const int G = D.nq / D.nkv;
       if (G > ATT_MAXG) return mpk_fail(MPK_ERR_SHAPE, "more than 4 query heads per kv head");
-      if ((rc = dalloc(x.get(), &D.part, (size_t)B * D.nkv * D.nsplit * G * (D.d + 2) * 4))) return rc;
-      D.tickets = x->d_counters + tick_off[i];
+      if (D.d > 128) return mpk_fail(MPK_ERR_SHAPE, "head_dim above 128");
+      if ((rc = dalloc(x.get(), &D.pll, (size_t)B * D.nkv * D.nsplit * G * (D.d + 2) * 8))) return rc;
       continue;
     }
     const int e_in = o.in[0];
-    D.x = D.x_embed ? nullptr : (const float*)P(e_in);
+    D.xll = D.x_embed ? nullptr : PL(e_in);
+    D.x = D.x_embed || D.xll ? nullptr : (const float*)P(e_in);
     if (D.x_embed) D.E = (const uint16_t*)P(g->embed_src[e_in]);
     D.gain = D.has_norm ? (const uint16_t*)P(o.in[1]) : nullptr;
     if (o.kind == MPK_OP_RMSNORM_LINEAR) {
       D.W0 = (const uint16_t*)P(o.in[2]);
       D.W1 = (const uint16_t*)P(o.in[3]);
       D.W2 = (const uint16_t*)P(o.in[4]);
-      D.y = (float*)P(o.out[0]);
+      D.y = (float*)PA(o.out[0]);
+      D.yll = PL(o.out[0]);
     } else if (o.kind == MPK_OP_LINEAR_RESIDUAL) {
       D.W0 = (const uint16_t*)P(o.in[1]);
-      if (D.res_embed) D.E = (const uint16_t*)P(g->embed_src[o.in[2]]);
-      else D.resid = (const float*)P(o.in[2]);
-      D.y = (float*)P(o.out[0]);
+      if (D.res_embed) {
+        D.E = (const uint16_t*)P(g->embed_src[o.in[2]]);
+      } else {
+        D.rll = PL(o.in[2]);
+        D.resid = D.rll ? nullptr : (const float*)P(o.in[2]);
+      }
+      D.y = (float*)PA(o.out[0]);
+      D.yll = PL(o.out[0]);
     } else if (o.kind == MPK_OP_RMSNORM_GATEUP) {
       D.W0 = (const uint16_t*)P(o.in[2]);
       D.W1 = (const uint16_t*)P(o.in[3]);
-      D.y = (float*)P(o.out[0]);
+      D.y = (float*)PA(o.out[0]);
+      D.yll = PL(o.out[0]);
     } else {  // LM head
       D.W0 = (const uint16_t*)P(o.in[2]);
       D.logits = o.out[0] >= 0 ? (float*)P(o.out[0]) : nullptr;
-      if ((rc = dalloc(x.get(), &D.part, (size_t)D.ntiles * B * 2 * 4))) return rc;
+      if ((rc = dalloc(x.get(), &D.pll, (size_t)D.ntiles * B * 2 * 8))) return rc;
     }
   }
   if (g->argmax_op >= 0) {
     // the argmax task reads the LM head's per-tile (max, index) pairs
     const int lm = g->argmax_op - 1;
-    dops[g->argmax_op].part = dops[lm].part;
+    dops[g->argmax_op].pll = dops[lm].pll;
     dops[g->argmax_op].N1 = dops[lm].ntiles;
   }
   if ((rc = dalloc(x.get(), &x->d_ops, dops.size() * sizeof(mpk_dev_op)))) return rc;
@@ -1323,7 +1494,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   K.queues = x->d_queues;
   K.single_q = x->d_single;
   K.qlen = x->d_qlen;
-  K.flags = x->d_events;
+  K.tok_ll = x->d_tok_ll;
   K.tokens = (int32_t*)P(g->meta.tokens);
   K.step = (int32_t*)P(g->meta.step);
   K.prompt_len = (const int32_t*)P(g->meta.prompt_len);
@@ -1397,8 +1568,12 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
   for (int r = 0; r < x->B; ++r) x->kp.pos0[r] = step[r];
   x->kp.n_iter = n_iter;
   x->last_iters = n_iter;
-  int64_t nz = x->n_counters;
-  hipLaunchKernelGGL(mpk_zero_u32, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, x->d_counters, nz);
+  // stamps of this run: iter_base + 1 .. iter_base + n_iter (never reused)
+  if ((uint64_t)x->iter_base + (uint64_t)n_iter >= 0xffffffffull)
+    return mpk_fail(MPK_ERR_STATE, "iteration stamps exhausted (2^32 iterations per executable)");
+  x->kp.iter_base = x->iter_base;
+  x->iter_base += (uint32_t)n_iter;
+  hipLaunchKernelGGL(mpk_zero_u32, dim3(1), dim3(64), 0, st, x->d_ticket_ctr, (int64_t)1);
   // clear code / iteration / task; a stop request (abort_req) stays until cleared
   hipLaunchKernelGGL(mpk_zero_u32, dim3(1), dim3(64), 0, st, (uint32_t*)x->d_status, (int64_t)3);
   HIPCHK(hipGetLastError());

@@ -145,14 +145,40 @@ def test_trace_orders_every_dependency(torch_dev):
     by_op = {}
     for i, t in enumerate(tasks):
         by_op.setdefault(t.op, []).append(i)
-    # required edges from the decoder's operator sequence: embed -> [QKV -> attention -> o_proj ->
-    # gate/up -> down] x L -> LM head -> next iteration
+    # A task's start ticket is taken once every word it reads is present and
+    # before it stores any output, so for every data dependency the
+    # producer's ticket is below the consumer's.  Decoder edges: [QKV ->
+    # attention -> o_proj -> gate/up -> down] x L -> LM head -> argmax ->
+    # next iteration's first QKV (its embedding read waits for the token).
+    NONE = 0xFFFFFFFF
     chain = [i for i, k in enumerate(kinds) if k != mpk.MPK_OP_EMBED] + [len(kinds)]  # + argmax task
+    sh = w.shape
+    d, G = sh.head_dim, sh.n_q // sh.n_kv
+
+    def group_rows(j):
+        """virtual QKV rows an attention task of kv head j reads"""
+        rows = set(range(j * G * d, (j + 1) * G * d))
+        rows |= set(range(sh.n_q * d + j * d, sh.n_q * d + (j + 1) * d))
+        rows |= set(range((sh.n_q + sh.n_kv) * d + j * d, (sh.n_q + sh.n_kv) * d + (j + 1) * d))
+        return rows
+
     for s in range(n):
+        st = tr[s]["start_ticket"]
         for a, b in zip(chain, chain[1:]):
-            assert tr[s]["end_ticket"][by_op[a]].max() < tr[s]["start_ticket"][by_op[b]].min()
+            pa = [t for t in by_op[a] if st[t] != NONE]
+            pb = [t for t in by_op[b] if st[t] != NONE]
+            assert pa and pb
+            if a < len(kinds) and kinds[a] == mpk.MPK_OP_RMSNORM_LINEAR and \
+                    b < len(kinds) and kinds[b] == mpk.MPK_OP_ATTENTION:
+                for t in pb:
+                    rows = group_rows(tasks[t].nrows)
+                    prod = [q for q in pa if rows & set(range(tasks[q].row0, tasks[q].row0 + tasks[q].nrows))]
+                    assert prod and max(st[q] for q in prod) < st[t]
+            else:
+                assert max(st[t] for t in pa) < min(st[t] for t in pb), (s, a, b)
         if s:
-            assert tr[s - 1]["end_ticket"][by_op[chain[-1]]].max() < tr[s]["start_ticket"][by_op[chain[0]]].min()
+            prev = tr[s - 1]["start_ticket"][by_op[chain[-1]]].max()
+            assert prev < tr[s]["start_ticket"][by_op[chain[0]]].min()
     # one workgroup per CU: scheduler wavefronts report distinct (XCC, SE, SH, CU)
     ids = set()
     for t in range(NT):
