@@ -153,6 +153,8 @@ DEV uint32_t hwreg_xcc_id() {
 // slots and would otherwise wait for every ring load in flight before any
 // LDS read it sees.
 DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lptr_t)(void*)p; }
+// LDS pointer from an LDS byte address (no generic-pointer conversion)
+DEV lptr_t lds_ptr(uint32_t a) { return (lptr_t)(uintptr_t)a; }
 
 DEV u32x4 lds_read_u32x4(uint32_t a) {
   u32x4 v;
@@ -178,6 +180,12 @@ template <int N>
 DEV void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// s_waitcnt vmcnt(0) that the compiler's wait insertion sees (the asm form
+// above is opaque to it): afterwards it knows nothing is in flight, so its
+// own waits on a register ring stay exact instead of falling back to full
+// drains when stores or atomics of earlier code might still be pending.
+DEV void vm_drain_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt 0, expcnt 7, lgkmcnt 15
+
 
 // Device-scope ("sc1") accesses.  Every value one task hands to another task
 // on another CU (stamped words, K/V rows, tokens, step) is written with
@@ -207,7 +215,8 @@ DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 //   [LDS_OUT, +4096)          attention: split partial / output, new K/V row
 //   [LDS_X, +XS)              staged activations x (or attention scratch)
 //   [RES, +2048)              staged residual rows of the tile
-//   [RING, +NW*R*1024)        weight rings, R units of 1 KB per wavefront
+//   [RING, +NW*8*1024)        per wavefront, 8 slots of 1 KB: the first weight
+//                             units of its next stream task (NB = 1 only)
 // x is staged permuted so each 16-byte LDS read is lane-contiguous:
 //   column k -> unit u = k / 512, lane l = (k % 512) / 8, half h = (k % 8) / 4
 //   offset (floats) = u * 512 + h * 256 + l * 4 + (k % 4)
@@ -227,9 +236,9 @@ template <int NB>
 struct Lay {
   static constexpr int XS = 49152 * NB;             // staged x bytes
   static constexpr int RES = LDS_X + XS;            // residual rows
-  static constexpr int RING = RES + LDS_RES_BYTES;  // weight rings
-  static constexpr int R = NB == 1 ? 12 : 6;        // ring units per wavefront
-  static constexpr int TOTAL = RING + MPK_NW * R * 1024;
+  static constexpr int RING = RES + LDS_RES_BYTES;  // LDS slots of the next task's first units
+  static constexpr bool PF = NB == 1;               // cross-task LDS prefetch (room for it at NB = 1)
+  static constexpr int TOTAL = RING + (PF ? MPK_NW * 8 * 1024 : 0);
 };
 static_assert(Lay<1>::TOTAL <= 160 * 1024, "LDS budget");
 static_assert(Lay<2>::TOTAL <= 160 * 1024, "LDS budget");
@@ -413,8 +422,15 @@ DEV int gather_ll(const mpk_kparams& P, const uint64_t* src, int n, uint32_t* ds
 //   wavefronts in assignment units of `a` rows (a = 2 for gate/up pairs):
 //   wave w takes units w, w + 8, w + 16, ...  A row is read as ceil(K/512)
 //   units of 512 bf16 (1 KB, 16 bytes per lane); a wavefront's sequence is
-//   its rows in order, each row's units in order.
+//   its rows in order, each row's units in order, padded with repeat reads
+//   to a whole number of groups of 8 units (at least one group).
+//   Units 0..7 of a task arrive in the wavefront's LDS slots by global->LDS
+//   DMA, issued while the previous stream task of the queue ends; units 8..
+//   arrive in registers, eight in flight, each issued as the unit eight
+//   places earlier is consumed.
 // ---------------------------------------------------------------------------
+#define MPK_RING 8  // units in flight per wavefront (LDS slots = register slots)
+
 DEV int units_per_row(cop& D) { return (D.K + 511) >> 9; }
 
 DEV int wave_units(cop& D, ctask& T, int wave) {
@@ -424,154 +440,110 @@ DEV int wave_units(cop& D, ctask& T, int wave) {
   return mine * a * units_per_row(D);
 }
 
-// Producer side of a wavefront's ring: the next unit to load, walking stream
-// tasks in queue order across iterations.  Everything the producer needs is
-// copied out of the descriptors into wave-uniform scalars when it moves to a
-// task, so issuing a unit performs no memory read.
-struct Issuer {
+DEV int padded_units(int n) { return n <= MPK_RING ? MPK_RING : ((n + MPK_RING - 1) / MPK_RING) * MPK_RING; }
+
+// Walks one task's units for one wavefront.  Everything is copied out of the
+// descriptors into wave-uniform scalars, so stepping performs no memory read.
+struct Cursor {
   const uint16_t* W0;
   const uint16_t* W1;
   const uint16_t* W2;
   const uint16_t* row;  // current row (lane offset not included)
-  int N0, N1, K, pairs, row0;
-  int s, k;             // iteration and queue position of the task
-  int j, n;             // unit index within the wave's sequence, count
-  int kk, rr, u;        // assignment unit, row within unit, unit within row
-  int upr, a;
-  int live;
+  int N0, N1, K, pairs, row0, a, upr;
+  int kk, rr, u;  // assignment unit, row within it, unit within row
+  int i, n;       // next unit index, real units
 };
 
-DEV void issuer_row(Issuer& I, int wave) {
+DEV void cursor_row(Cursor& C, int wave) {
   // Select among loaded pointer values (not among field addresses: a
-  // variable-index field access would keep the issuer in scratch memory).
-  const uint16_t* w0 = unip(I.W0);
-  const uint16_t* w1 = unip(I.W1);
-  const uint16_t* w2 = unip(I.W2);
-  int vrow = I.row0 + (wave + MPK_NW * I.kk) * I.a + I.rr;
+  // variable-index field access would keep the cursor in scratch memory).
+  const uint16_t* w0 = unip(C.W0);
+  const uint16_t* w1 = unip(C.W1);
+  const uint16_t* w2 = unip(C.W2);
+  const int vrow = C.row0 + (wave + MPK_NW * C.kk) * C.a + C.rr;
   const uint16_t* base;
   int r;
-  if (I.pairs) {
+  if (C.pairs) {
     base = (vrow & 1) ? w1 : w0;
     r = vrow >> 1;
-  } else if (vrow < I.N0) {
+  } else if (vrow < C.N0) {
     base = w0;
     r = vrow;
-  } else if (vrow - I.N0 < I.N1) {
+  } else if (vrow - C.N0 < C.N1) {
     base = w1;
-    r = vrow - I.N0;
+    r = vrow - C.N0;
   } else {
     base = w2;
-    r = vrow - I.N0 - I.N1;
+    r = vrow - C.N0 - C.N1;
   }
-  I.row = unip(base + (int64_t)r * I.K);
+  C.row = unip(base + (int64_t)r * C.K);
 }
 
-// Point the issuer at the first stream task at or after queue position k of
-// iteration s that gives this wave at least one unit.
-DEV void issuer_seek(Issuer& I, const mpk_kparams& P, cqent* Q, int qlen, int s, int k, int wave) {
-  int found = 0;
-  s = uni(s);
-  k = uni(k);
-  qlen = uni(qlen);
-  for (int guard = 0; guard < 2 * qlen + 2 && !found; ++guard) {
-    k = uni(k);
-    if (k >= qlen) {
-      k = uni(k - qlen);
-      s = uni(s + 1);
+DEV void cursor_init(Cursor& C, cop& D, ctask& T, int wave) {
+  C.W0 = unip(D.W0), C.W1 = unip(D.W1), C.W2 = unip(D.W2);
+  C.N0 = uni(D.N0), C.N1 = uni(D.N1), C.K = uni(D.K), C.pairs = uni(D.pairs);
+  C.row0 = uni(T.row0);
+  C.a = C.pairs ? 2 : 1;
+  C.upr = uni(units_per_row(D));
+  C.kk = 0, C.rr = 0, C.u = 0, C.i = 0;
+  C.n = uni(wave_units(D, T, wave));
+  if (C.n > 0) cursor_row(C, wave);
+  else C.row = unip(C.W0);  // padding only: re-read the first unit of W0
+}
+
+// Global address of the cursor's current unit for this lane (padding units
+// re-read the last real unit; lanes past the end of a row re-read its start).
+DEV gptr_t cursor_addr(const Cursor& C, int lane) {
+  const int kleft = C.K - C.u * 512;
+  const int col = lane * 8 < kleft ? C.u * 512 + lane * 8 : 0;
+  return (gptr_t)(const void*)(C.row + col);
+}
+
+DEV void cursor_step(Cursor& C, int wave) {
+  C.i = uni(C.i + 1);
+  if (C.i >= C.n) return;  // padding: stay on the last real unit
+  C.u = uni(C.u + 1);
+  if (C.u == C.upr) {
+    C.u = 0;
+    C.rr = uni(C.rr + 1);
+    if (C.rr == C.a) {
+      C.rr = 0;
+      C.kk = uni(C.kk + 1);
     }
-    if (s >= P.n_iter || k < 0) break;
+    cursor_row(C, wave);
+  }
+}
+
+// The first stream task (GEMV / LM head) at queue position k or later of
+// iteration s, wrapping into the next iteration; false when there is none
+// before the end of the run.
+DEV bool next_stream_task(const mpk_kparams& P, cqent* Q, int qlen, int s, int k, int& s_out, int& task_out) {
+  for (int guard = 0; guard < 2 && qlen > 0; ++guard) {
+    if (k >= qlen) k -= qlen, s += 1;
+    if (s >= P.n_iter) return false;
     const int tix = uni(Q[k].task);
-    ctask& T = tasks_of(P)[tix];
-    const int kind = uni(T.kind);
+    const int kind = uni(tasks_of(P)[tix].kind);
     if (kind == MPK_TK_GEMV || kind == MPK_TK_LMHEAD) {
-      cop& D = ops_of(P)[uni(T.op)];
-      const int n = uni(wave_units(D, T, wave));
-      if (n > 0) {
-        I.W0 = unip(D.W0), I.W1 = unip(D.W1), I.W2 = unip(D.W2);
-        I.N0 = uni(D.N0), I.N1 = uni(D.N1), I.K = uni(D.K), I.pairs = uni(D.pairs);
-        I.row0 = uni(T.row0);
-        I.s = s, I.k = k, I.j = 0, I.n = n;
-        I.kk = 0, I.rr = 0, I.u = 0, I.upr = uni(units_per_row(D)), I.a = I.pairs ? 2 : 1;
-        found = 1;
-        break;
-      }
+      s_out = s, task_out = tix;
+      return true;
     }
-    const int nx = uni(Q[k].next_stream);  // > k; >= qlen means the next iteration
-    if (nx < 0) break;
-    k = nx;
+    k = uni(Q[k].next_stream);  // > k; >= qlen means the next iteration
+    if (k < 0) return false;
   }
-  I.live = found;
-  if (found) issuer_row(I, wave);
+  return false;
 }
 
-// Issue the issuer's next unit into LDS slot `slot` and advance.
-DEV void issue_unit(Issuer& I, char* ring_wave, int slot, const mpk_kparams& P, cqent* Q, int qlen,
-                    int wave, int lane) {
-  const int kleft = I.K - I.u * 512;
-  const int col = lane * 8 < kleft ? I.u * 512 + lane * 8 : 0;  // lanes past the row re-read its start
-  __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(I.row + col),
-                                   (lptr_t)(void*)(ring_wave + slot * 1024), 16, 0, 0);
-  I.j = uni(I.j + 1);
-  I.u = uni(I.u + 1);
-  if (I.u == I.upr) {
-    I.u = 0;
-    I.rr = uni(I.rr + 1);
-    if (I.rr == I.a) {
-      I.rr = 0;
-      I.kk = uni(I.kk + 1);
-    }
-    if (I.j < I.n) issuer_row(I, wave);
+// DMA units 0..7 of a stream task into this wavefront's LDS slots (LDS byte
+// address of slot 0).
+DEV void prefetch_task_lds(const mpk_kparams& P, int task, uint32_t slots, int wave, int lane) {
+  ctask& T = tasks_of(P)[task];
+  Cursor C;
+  cursor_init(C, ops_of(P)[uni(T.op)], T, wave);
+#pragma unroll
+  for (int j = 0; j < MPK_RING; ++j) {
+    __builtin_amdgcn_global_load_lds(cursor_addr(C, lane), lds_ptr(slots + j * 1024), 16, 0, 0);
+    cursor_step(C, wave);
   }
-  if (I.j == I.n) issuer_seek(I, P, Q, qlen, I.s, I.k + 1, wave);
-}
-
-// Per-wavefront ring state (uniform).
-struct RingState {
-  int head;      // slot of the oldest unit in flight
-  int inflight;  // units issued, not yet consumed
-};
-
-template <int R>
-DEV void wait_head(int inflight) {
-  // the head unit has (inflight - 1) loads issued after it
-  if (inflight >= R) {
-    vm_wait<R - 1>();
-  } else {
-    switch (inflight) {
-      case 12: vm_wait<11>(); break;
-      case 11: vm_wait<10>(); break;
-      case 10: vm_wait<9>(); break;
-      case 9: vm_wait<8>(); break;
-      case 8: vm_wait<7>(); break;
-      case 7: vm_wait<6>(); break;
-      case 6: vm_wait<5>(); break;
-      case 5: vm_wait<4>(); break;
-      case 4: vm_wait<3>(); break;
-      case 3: vm_wait<2>(); break;
-      case 2: vm_wait<1>(); break;
-      default: vm_wait<0>(); break;
-    }
-  }
-}
-
-// Issue one unit into the free slot after the ring's last unit, if the
-// producer has one; called once per consumed unit (steady state) and in a
-// loop at start-up.
-template <int R>
-DEV void ring_top_up(Issuer& I, RingState& S, char* ring_wave, const mpk_kparams& P, cqent* Q, int qlen,
-                     int wave, int lane) {
-  if (I.live && S.inflight < R) {
-    int slot = S.head + S.inflight;
-    if (slot >= R) slot -= R;
-    issue_unit(I, ring_wave, uni(slot), P, Q, qlen, wave, lane);
-    S.inflight = uni(S.inflight + 1);
-  }
-}
-
-template <int R>
-DEV void ring_fill(Issuer& I, RingState& S, char* ring_wave, const mpk_kparams& P, cqent* Q, int qlen,
-                   int wave, int lane) {
-  for (int i = 0; i < R; ++i) ring_top_up<R>(I, S, ring_wave, P, Q, qlen, wave, lane);
 }
 
 // Stage the GEMV input into LDS: x (gathered from its producers' stamped
@@ -722,107 +694,278 @@ DEV void put_out(cop& D, int64_t i, float v, uint32_t st) {
 // GEMV-type task: rmsnorm_linear (EPI_STORE), linear + residual (EPI_RESID),
 // rmsnorm + gate/up + SiLU-mul (EPI_SILU), final norm + LM head + tile argmax
 // (EPI_ARGMAX).  Lane 0 of the wavefront that finishes a row publishes the
-// row's output word at once.  Returns -1 on stop.
+// row's output word at once.  With LDS_PF the task's first eight units per
+// wavefront are already in LDS and the task's tail DMAs the next stream
+// task's first eight; otherwise all units go through registers.  Returns -1
+// on stop.
 // ---------------------------------------------------------------------------
+// LDS address of a logit of the LM-head tile: after the staged x of the NB
+// requests.
+DEV uint32_t lds_logits(uint32_t lb, int nb, cop& D, ctask& T, int b, int lrow) {
+  const int Kpad = ((D.K + 511) / 512) * 512;
+  return lb + LDS_X + (uint32_t)(nb * Kpad + b * T.nrows + lrow) * 4u;
+}
+
 template <int NB>
-DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I, RingState& RS, cqent* Q, int qlen, int s,
-                  int task_id, char* smem, int tid, bool sched) {
-  constexpr int R = Lay<NB>::R;
+struct GemvState {
+  float acc[NB], gate[NB], best_v[NB];
+  int best_i[NB];
+  int u, rr, kk;
+};
+
+template <int NB>
+DEV void unit_fma(const u32x4 w, uint32_t xaddr, int Kpad, float (&acc)[NB]) {
+  const float wf[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
+                       bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    f32x4 x0, x1;
+    lds_read_2f4(xaddr + (uint32_t)(b * Kpad) * 4u, x0, x1);
+    float sacc = acc[b];
+    sacc = fmaf(wf[0], x0.x, sacc);
+    sacc = fmaf(wf[1], x0.y, sacc);
+    sacc = fmaf(wf[2], x0.z, sacc);
+    sacc = fmaf(wf[3], x0.w, sacc);
+    sacc = fmaf(wf[4], x1.x, sacc);
+    sacc = fmaf(wf[5], x1.y, sacc);
+    sacc = fmaf(wf[6], x1.z, sacc);
+    sacc = fmaf(wf[7], x1.w, sacc);
+    acc[b] = sacc;
+  }
+  // The unit is consumed here, before the next load into its register is
+  // issued: without this the compiler sinks the FMAs below the refills and
+  // must then wait for every load in flight to copy the old values out.
+#pragma unroll
+  for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(acc[b])::"memory");
+}
+
+// A row of the tile is complete: reduce and apply the epilogue into LDS
+// (outputs, or logits and the running maximum for the LM head).  Nothing is
+// stored to memory inside the weight stream: a store pending among the
+// stream's loads would make every wait on them a full drain.
+template <int NB>
+DEV void row_done(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, const float (&inv)[NB], int a, int wave,
+                  int lane) {
+  const int EPI = D.epi;
+  const int lrow = (wave + MPK_NW * G.kk) * a + G.rr;  // row within the tile
+  const int vrow = T.row0 + lrow;
+  const uint32_t ob = lb + LDS_OUT;
+  const int n_out_tile = D.pairs ? T.nrows / 2 : T.nrows;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float sum = wave_sum(G.acc[b]);
+    G.acc[b] = 0.f;
+    // LDS traffic inside the weight stream stays in asm (see lds_read_u32x4)
+    if (EPI == MPK_EPI_STORE) {
+      if (lane == 0) lds_write_f32(ob + (uint32_t)(b * n_out_tile + lrow) * 4u, sum * inv[b]);
+    } else if (EPI == MPK_EPI_RESID) {
+      const float rv = lds_read_f32(lb + Lay<NB>::RES + (uint32_t)(b * T.nrows + lrow) * 4u);
+      if (lane == 0) lds_write_f32(ob + (uint32_t)(b * n_out_tile + lrow) * 4u, rv + sum);
+    } else if (EPI == MPK_EPI_SILU) {
+      if (G.rr == 0) {
+        G.gate[b] = sum * inv[b];
+      } else if (lane == 0) {
+        lds_write_f32(ob + (uint32_t)(b * n_out_tile + (lrow >> 1)) * 4u, silu(G.gate[b]) * (sum * inv[b]));
+      }
+    } else {  // ARGMAX
+      const float logit = sum * inv[b];
+      if (D.logits && lane == 0) lds_write_f32(lds_logits(lb, NB, D, T, b, lrow), logit);
+      if (logit > G.best_v[b]) G.best_v[b] = logit, G.best_i[b] = vrow;
+    }
+  }
+  if (++G.rr == a) {
+    G.rr = 0;
+    ++G.kk;
+  }
+}
+
+// Publish this wavefront's rows of the tile from LDS (stamped output words,
+// the plain output when attached, LM-head logits when requested).
+template <int NB>
+DEV void publish_rows(const mpk_kparams& P, cop& D, ctask& T, uint32_t lb, int s, uint32_t st, int wave, int lane) {
+  const int a = D.pairs ? 2 : 1;
+  const int au = T.nrows / a;
+  const int mine = au > wave ? (au - wave + MPK_NW - 1) / MPK_NW : 0;  // assignment units of this wave
+  const int nr = mine * a;                                            // rows of this wave
+  const uint32_t ob = lb + LDS_OUT;
+  const int n_out_tile = D.pairs ? T.nrows / 2 : T.nrows;
+  for (int i = lane; i < NB * nr; i += 64) {
+    const int b = i / nr, q = i - b * nr;
+    const int kk = q / a, rr = q - kk * a;
+    const int lrow = (wave + MPK_NW * kk) * a + rr;
+    const int vrow = T.row0 + lrow;
+    if (D.epi == MPK_EPI_ARGMAX) {
+      if (D.logits && s < D.logits_iters)
+        gst(D.logits + ((int64_t)s * P.B + b) * D.N0 + vrow, lds_read_f32(lds_logits(lb, NB, D, T, b, lrow)));
+    } else if (D.epi != MPK_EPI_SILU || rr == 1) {
+      const int ol = D.pairs ? lrow >> 1 : lrow;
+      const int orow = D.pairs ? vrow >> 1 : vrow;
+      put_out(D, (int64_t)b * D.n_out + orow, lds_read_f32(ob + (uint32_t)(b * n_out_tile + ol) * 4u), st);
+    }
+  }
+}
+
+// Generic consumer step (rows of any length): one unit, then the row's
+// epilogue when the unit ends a row.  Padding units are skipped.
+template <int NB>
+DEV void gemv_consume(ctask& T, cop& D, GemvState<NB>& G, const u32x4 w, int unit, int n, uint32_t lb,
+                      const float (&inv)[NB], int Kpad, int upr, int a, int wave, int lane) {
+  if (unit >= n) return;  // padding unit (uniform)
+  unit_fma<NB>(w, lb + LDS_X + (uint32_t)(G.u * 512 + lane * 4) * 4u, Kpad, G.acc);
+  if (++G.u == upr) {
+    G.u = 0;
+    row_done<NB>(D, T, G, lb, inv, a, wave, lane);
+  }
+}
+
+DEV u32x4 load_unit(const Cursor& C, int lane) {
+  return __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1)))*)cursor_addr(C, lane));
+}
+
+template <int NB, bool LDS_PF>
+DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, int k, int s, int task_id, char* smem,
+                  int tid, bool sched, bool cross) {
   {
     const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id);
     if (rc) return rc;
   }
   mark_ready(P, s, task_id, tid);
   const uint32_t st = stamp_of(P, s);
-  const int EPI = D.epi;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const float* xs = reinterpret_cast<const float*>(smem + LDS_X);
-  const float* res = reinterpret_cast<const float*>(smem + Lay<NB>::RES);
+  const uint32_t lb = lds_addr(smem);  // LDS byte address of the workgroup's area
   const float* inv_lds = reinterpret_cast<const float*>(smem + LDS_INV);
   float inv[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) inv[b] = inv_lds[b];
-  char* ring_wave = smem + Lay<NB>::RING + wave * R * 1024;
   const int Kpad = ((D.K + 511) / 512) * 512;
-  float best_v[NB];
-  int best_i[NB];
+  GemvState<NB> G;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) best_v[b] = -INFINITY, best_i[b] = 0x7fffffff;
+  for (int b = 0; b < NB; ++b) G.acc[b] = 0.f, G.gate[b] = 0.f, G.best_v[b] = -INFINITY, G.best_i[b] = 0x7fffffff;
+  G.u = 0, G.rr = 0, G.kk = 0;
   if (!sched) {
-    const int n = wave_units(D, T, wave);
     const int a = D.pairs ? 2 : 1;
-    const int upr = units_per_row(D);
-    int kk = 0, rr = 0, u = 0;
-    float acc[NB], gate[NB];
+    const int upr = uni(units_per_row(D));
+    Cursor I;  // issue side: runs MPK_RING units ahead of consumption
+    cursor_init(I, D, T, wave);
+    const int n = I.n, npad = uni(padded_units(n));
+    const uint32_t slots = lb + Lay<NB>::RING + wave * MPK_RING * 1024;
+    vm_drain_known();
+    u32x4 b[MPK_RING];
+    if (upr % MPK_RING == 0) {
+      // rows are whole groups of eight units (K a multiple of 4096): the
+      // epilogue runs between groups only, which keeps the register ring's
+      // waits exact inside the unrolled group
+      const uint32_t xl = lb + LDS_X + lane * 16;
+      const int ng = npad / MPK_RING;
+      int g = 0;
+      if (LDS_PF) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = 0.f, gate[b] = 0.f;
-    for (int i = 0; i < n; ++i) {
-      wait_head<R>(RS.inflight);
-      const u32x4 w = lds_read_u32x4(lds_addr(ring_wave) + RS.head * 1024 + lane * 16);
-      const float wf[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
-                           bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
-      const int base = u * 512 + lane * 4;
+        for (int j = 0; j < MPK_RING; ++j) cursor_step(I, wave);
+        const uint32_t xg = xl + G.u * 2048;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        f32x4 x0, x1;
-        lds_read_2f4(lds_addr(xs) + (uint32_t)(b * Kpad + base) * 4u, x0, x1);
-        float sacc = acc[b];
-        sacc = fmaf(wf[0], x0.x, sacc);
-        sacc = fmaf(wf[1], x0.y, sacc);
-        sacc = fmaf(wf[2], x0.z, sacc);
-        sacc = fmaf(wf[3], x0.w, sacc);
-        sacc = fmaf(wf[4], x1.x, sacc);
-        sacc = fmaf(wf[5], x1.y, sacc);
-        sacc = fmaf(wf[6], x1.z, sacc);
-        sacc = fmaf(wf[7], x1.w, sacc);
-        acc[b] = sacc;
-      }
-      // the slot just read is refilled with the next unit of the stream
-      RS.head = uni(RS.head + 1 == R ? 0 : RS.head + 1);
-      RS.inflight = uni(RS.inflight - 1);
-      ring_top_up<R>(I, RS, ring_wave, P, Q, qlen, wave, lane);
-      if (++u == upr) {
-        u = 0;
-        const int lrow = (wave + MPK_NW * kk) * a + rr;  // row within the tile
-        const int vrow = T.row0 + lrow;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float sum = wave_sum(acc[b]);
-          acc[b] = 0.f;
-          // LDS traffic inside the weight stream stays in asm (see lds_read_u32x4)
-          if (EPI == MPK_EPI_STORE) {
-            if (lane == 0) put_out(D, (int64_t)b * D.n_out + vrow, sum * inv[b], st);
-          } else if (EPI == MPK_EPI_RESID) {
-            const float rv = lds_read_f32(lds_addr(res) + (uint32_t)(b * T.nrows + lrow) * 4u);
-            if (lane == 0) put_out(D, (int64_t)b * D.n_out + vrow, rv + sum, st);
-          } else if (EPI == MPK_EPI_SILU) {
-            if (rr == 0) {
-              gate[b] = sum * inv[b];
-            } else if (lane == 0) {
-              put_out(D, (int64_t)b * D.n_out + (vrow >> 1), silu(gate[b]) * (sum * inv[b]), st);
-            }
-          } else {  // ARGMAX
-            const float logit = sum * inv[b];
-            if (D.logits && s < D.logits_iters && lane == 0)
-              gst(D.logits + ((int64_t)s * P.B + b) * D.N0 + vrow, logit);
-            if (logit > best_v[b]) best_v[b] = logit, best_i[b] = vrow;
+        for (int j = 0; j < MPK_RING; ++j) {
+          // slot j's DMA has (7 - j) DMA loads and j register loads younger
+          // than it; loads complete in order
+          vm_wait<MPK_RING - 1>();
+          const u32x4 w = lds_read_u32x4(slots + j * 1024 + lane * 16);
+          unit_fma<NB>(w, xg + j * 2048, Kpad, G.acc);
+          // refilled even when the task has no register groups (its padding
+          // units): a conditional refill leaves the compiler unsure which
+          // loads are in flight and every later wait becomes a full drain
+          b[j] = load_unit(I, lane);
+          cursor_step(I, wave);
+        }
+        if (n > 0) {
+          G.u += MPK_RING;
+          if (G.u == upr) {
+            G.u = 0;
+            row_done<NB>(D, T, G, lb, inv, a, wave, lane);
           }
         }
-        if (++rr == a) {
-          rr = 0;
-          ++kk;
+        g = 1;
+      } else {
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j) {
+          b[j] = load_unit(I, lane);
+          cursor_step(I, wave);
         }
       }
+      // steady state: consume b[j], refill it with the unit eight places on
+      for (; g < ng - 1; ++g) {
+        const uint32_t xg = xl + G.u * 2048;
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j) {
+          unit_fma<NB>(b[j], xg + j * 2048, Kpad, G.acc);
+          b[j] = load_unit(I, lane);
+          cursor_step(I, wave);
+        }
+        G.u += MPK_RING;
+        if (G.u == upr) {
+          G.u = 0;
+          row_done<NB>(D, T, G, lb, inv, a, wave, lane);
+        }
+      }
+      // last group (unless group 0 was it)
+      if (g == ng - 1) {
+        const uint32_t xg = xl + G.u * 2048;
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j) unit_fma<NB>(b[j], xg + j * 2048, Kpad, G.acc);
+        if (n > 0) {
+          G.u += MPK_RING;
+          if (G.u == upr) {
+            G.u = 0;
+            row_done<NB>(D, T, G, lb, inv, a, wave, lane);
+          }
+        }
+      }
+    } else {
+      // generic rows (short K): per-unit bookkeeping, padding skipped
+      int g0 = 0;
+      if (LDS_PF) {
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j) cursor_step(I, wave);
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j) {
+          vm_wait<MPK_RING - 1>();
+          const u32x4 w = lds_read_u32x4(slots + j * 1024 + lane * 16);
+          gemv_consume<NB>(T, D, G, w, j, n, lb, inv, Kpad, upr, a, wave, lane);
+          b[j] = load_unit(I, lane);
+          cursor_step(I, wave);
+        }
+        g0 = 1;
+      } else {
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j) {
+          b[j] = load_unit(I, lane);
+          cursor_step(I, wave);
+        }
+      }
+      const int ng = npad / MPK_RING;
+      for (int g = g0; g < ng - 1; ++g) {
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j) {
+          gemv_consume<NB>(T, D, G, b[j], g * MPK_RING + j, n, lb, inv, Kpad, upr, a, wave, lane);
+          b[j] = load_unit(I, lane);
+          cursor_step(I, wave);
+        }
+      }
+      if (ng - 1 >= g0) {
+        const int g = ng - 1;
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j)
+          gemv_consume<NB>(T, D, G, b[j], g * MPK_RING + j, n, lb, inv, Kpad, upr, a, wave, lane);
+      }
     }
+    publish_rows<NB>(P, D, T, lb, s, st, wave, lane);
   }
-  if (EPI == MPK_EPI_ARGMAX) {
+  if (D.epi == MPK_EPI_ARGMAX) {
     // tile argmax over the waves (lowest row among equal maxima), published
     // as two stamped words (value, row) per request
     float* bv = reinterpret_cast<float*>(smem + LDS_BEST);
     int* bi = reinterpret_cast<int*>(smem + LDS_BEST + MPK_NW * 8 * 4);
     if (!sched && lane == 0) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) bv[wave * 8 + b] = best_v[b], bi[wave * 8 + b] = best_i[b];
+      for (int b = 0; b < NB; ++b) bv[wave * 8 + b] = G.best_v[b], bi[wave * 8 + b] = G.best_i[b];
     }
     __syncthreads();
     if (tid < NB) {
@@ -837,6 +980,13 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, Issuer& I, RingState& 
       st_ll(pw, v, st);
       st_lli(pw + 1, ix, st);
     }
+  }
+  // outputs are out: the first units of the next stream task in the queue go
+  // to this wavefront's LDS slots while the task's consumers gather
+  if (LDS_PF && cross && !sched) {
+    int s2 = 0, t2 = 0;
+    if (next_stream_task(P, Q, qlen, s, k + 1, s2, t2))
+      prefetch_task_lds(P, t2, lb + Lay<NB>::RING + wave * MPK_RING * 1024, wave, lane);
   }
   return 0;
 }
@@ -1170,12 +1320,13 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 // dispatch of one task body; returns -1 when the run must stop
 // ---------------------------------------------------------------------------
 template <int NB>
-DEV int run_task(const mpk_kparams& P, ctask& T, int task_id, Issuer& I, RingState& RS, cqent* Q, int qlen, int s,
-                 char* smem, int tid, bool sched) {
+DEV int run_task(const mpk_kparams& P, ctask& T, int task_id, cqent* Q, int qlen, int k, int s, char* smem, int tid,
+                 bool sched, bool cross) {
   cop& D = ops_of(P)[T.op];
   if (T.kind == MPK_TK_ATTN) return attn_task(P, T, D, smem, tid, sched, s, task_id);
   if (T.kind == MPK_TK_ARGMAX) return argmax_task<NB>(P, D, smem, tid, s, task_id);
-  return gemv_task<NB>(P, T, D, I, RS, Q, qlen, s, task_id, smem, tid, sched);
+  if (cross) return gemv_task<NB, Lay<NB>::PF>(P, T, D, Q, qlen, k, s, task_id, smem, tid, sched, true);
+  return gemv_task<NB, false>(P, T, D, Q, qlen, k, s, task_id, smem, tid, sched, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -1190,12 +1341,10 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
   const int qlen = ((const CAS int32_t*)(const void*)P.qlen)[blockIdx.x];
   volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
   if (tid == 0) ctl[0] = 0;
-  Issuer I;
-  RingState RS{0, 0};
-  I.live = 0;
-  if (!sched && qlen > 0) {
-    issuer_seek(I, P, Q, qlen, 0, 0, wave);
-    ring_fill<Lay<NB>::R>(I, RS, smem + Lay<NB>::RING + wave * Lay<NB>::R * 1024, P, Q, qlen, wave, lane);
+  if (Lay<NB>::PF && !sched) {
+    int s0 = 0, t0 = 0;
+    if (next_stream_task(P, Q, qlen, 0, 0, s0, t0))
+      prefetch_task_lds(P, t0, lds_addr(smem) + Lay<NB>::RING + wave * MPK_RING * 1024, wave, lane);
   }
   for (int s = 0; s < P.n_iter; ++s) {
     for (int k = 0; k < qlen; ++k) {
@@ -1218,7 +1367,7 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
       // loop (it would stay live, and spill, across all bodies).
       int tid_o = tid;
       asm volatile("" : "+v"(tid_o));
-      const int rc = run_task<NB>(P, T, task_id, I, RS, Q, qlen, s, smem, tid_o, sched);
+      const int rc = run_task<NB>(P, T, task_id, Q, qlen, k, s, smem, tid_o, sched, true);
       if (rc < 0) {
         vm_wait<0>();  // leave no LDS-bound load in flight
         return;
@@ -1248,19 +1397,9 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_op_kernel(mpk_kparams P, i
   cqent* q1 = (cqent*)(const void*)P.single_q + task_id;
   volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
   if (tid == 0) ctl[0] = 0;
-  Issuer I;
-  RingState RS{0, 0};
-  I.live = 0;
-  mpk_kparams P1 = P;
-  P1.n_iter = 1;
-  if (!sched) {
-    issuer_seek(I, P1, q1, 1, 0, 0, wave);
-    ring_fill<Lay<NB>::R>(I, RS, smem + Lay<NB>::RING + wave * Lay<NB>::R * 1024, P1, q1, 1, wave, lane);
-  } else {
-    set_positions(P, smem, s, lane);
-  }
+  if (sched) set_positions(P, smem, s, lane);
   __syncthreads();
-  run_task<NB>(P, T, task_id, I, RS, q1, 1, s, smem, tid, sched);
+  run_task<NB>(P, T, task_id, q1, 1, 0, s, smem, tid, sched, false);
   vm_wait<0>();
 }
 
