@@ -7,7 +7,8 @@ tied 151936-row embedding / LM head, seeded N(0, 0.02) bf16 weights, a
 39-token prompt, 512 generated tokens).  A step is one decode iteration:
 every layer, the LM head, the argmax and the step/tokens advance for the one
 request.  The warm-up steps ingest the prompt (untimed); the timed steps are
-the generating ones (defaults: 38 warm-up, 512 timed).
+the generating ones (defaults: 38 warm-up, 512 timed, in launches of 64
+iterations).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -23,6 +24,24 @@ if ROOT not in sys.path:
 
 METRIC = "ms/token decode latency at batch 1 (Qwen3-8B shape) + % of HBM roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+# HBM bytes per 64-iteration launch of the persistent kernel from rocprofv3
+# FETCH_SIZE + WRITE_SIZE, each scaled by a plain 1 GiB copy's readings
+# (profiles/mpk_persistent_qwen3_8b_b1_hbm_counters.md).  Reported only while
+# the kernel source is the one the counters were taken on.
+TRAFFIC = {"gb_per_launch": 976.4, "iters_per_launch": 64, "runtime_sha256_16": "9b447bd54f6811d2"}
+
+
+def measured_traffic(iters_per_launch: int):
+    import hashlib
+
+    src = os.path.join(ROOT, "persistent_task_runtime_amd", "csrc", "runtime.hip")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if sha != TRAFFIC["runtime_sha256_16"] or iters_per_launch != TRAFFIC["iters_per_launch"]:
+        return None
+    return TRAFFIC["gb_per_launch"]
 
 
 def log(*a):
@@ -42,15 +61,35 @@ def iteration_bytes(sh, p: int) -> int:
     return sh.streamed_weight_bytes() + kv_bytes_per_position(sh) * (p + 1) + 2 * sh.hidden
 
 
+def copy_calibration(n_bytes: int = 1 << 30) -> None:
+    """A plain device copy of n_bytes (torch's copy kernel): run under
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it gives the counters' bytes for a
+    known amount of traffic, the factor that scales the megakernel's counters."""
+    import torch
+
+    src = torch.empty(n_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copied %d bytes 3 times" % n_bytes)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
-    ap.add_argument("--warmup", type=int, default=38)
+    ap.add_argument("--steps", type=int, default=512, help="timed decode iterations")
+    ap.add_argument("--warmup", type=int, default=38,
+                    help="untimed iterations before the timed ones (the prompt)")
+    ap.add_argument("--launch-iters", type=int, default=64,
+                    help="iterations per persistent launch in the timed region")
     ap.add_argument("--per-op-steps", type=int, default=64)
     ap.add_argument("--cpu-iters", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-op", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -67,7 +106,9 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     sh = synth.QWEN3_8B
     P = 39
-    K, W = args.steps, args.warmup
+    K, W, L = args.steps, args.warmup, args.launch_iters
+    if K % L:
+        sys.exit("--steps must be a multiple of --launch-iters")
     total = W + K
     width = max(P + 512 + 1, total + 2)
     w = synth.Workload("qwen3_8b", sh, 1, n_iter=total, tokens_width=width,
@@ -78,31 +119,42 @@ def main():
     model = runner.DeviceModel(sh, weights=weights)
     torch.cuda.synchronize()
     log("uploaded %.2f GB in %.1f s" % (model.bytes() / 1e9, time.time() - t0))
+    if args.copy_calibration:
+        copy_calibration()
 
     stream = torch.cuda.current_stream()
     sess = runner.Session(w, model, max_seq=width)
     if W:
-        sess.run(W)
+        # the prompt goes through the one-launch-per-operator path: the same
+        # task bodies, bitwise the same state, and no persistent launch of
+        # another length in the profile of the timed one
+        sess.run(W, per_op=True)
         torch.cuda.synchronize()
         sess.check_status()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_launch = K // L
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launch)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    sess.run(K)
-    e1.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        sess.run(L)
+        b.record(stream)
     torch.cuda.synchronize()
     sess.check_status()
-    ms = e0.elapsed_time(e1)
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = ev[0][0].elapsed_time(ev[-1][1])
     ms_tok = ms / K
     step_now = int(sess.step.cpu()[0])
     assert step_now == total, (step_now, total)
     toks = sess.tokens.cpu().numpy()[0]
     assert (toks[: total + 1] >= 0).all()
     alg_bytes = sum(iteration_bytes(sh, W + i) for i in range(K))
-    achieved = alg_bytes / (ms / 1e3) / 1e9
+    # roofline of the dominant kernel: algorithmic bytes per launch / mean launch duration
+    launch_avg = sum(launch_ms) / n_launch
+    achieved = (alg_bytes / n_launch) / (launch_avg / 1e3) / 1e9
     bound_ms = alg_bytes / K / (HBM_PEAK_GBS * 1e9) * 1e3
-    log("persistent: %.4f ms/token, %.1f GB/s algorithmic (%.1f%% of %.0f GB/s)"
-        % (ms_tok, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
+    log("persistent: %.4f ms/token over %d launches of %d iterations (mean launch %.3f ms), "
+        "%.1f GB/s algorithmic (%.1f%% of %.0f GB/s)"
+        % (ms_tok, n_launch, L, launch_avg, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
     sess.close()
 
     per_op = None
@@ -111,6 +163,7 @@ def main():
         s2 = runner.Session(w, model, max_seq=width)
         s2.run(W, per_op=True)
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         s2.run(Kp, per_op=True)
         e1.record(stream)
@@ -152,9 +205,13 @@ def main():
         "config": {"workload": "qwen3_8b_batch1_prompt39_greedy", "layers": sh.layers,
                    "hidden": sh.hidden, "q_heads": sh.n_q, "kv_heads": sh.n_kv, "head_dim": sh.head_dim,
                    "ffn": sh.ffn, "vocab": sh.vocab, "tied_lm_head": True, "batch": 1,
-                   "prompt_tokens": P, "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16"},
+                   "prompt_tokens": P, "generated_tokens": K, "iterations_per_launch": L,
+                   "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(L)},
+        "kernel": "mpk_persistent<1>",
+        "traffic_unit": "GB per launch",
+        "launch_ms": round(launch_avg, 4),
         "bound_ms_per_token": round(bound_ms, 5),
         "frac_of_bound": round(bound_ms / ms_tok, 4),
         "per_op_ms_per_token": round(per_op, 5) if per_op else None,
