@@ -40,10 +40,10 @@ void mpk_clear_error() { g_err.clear(); }
 extern "C" const char* mpk_last_error(void) { return g_err.c_str(); }
 
 int mpk_attn_splits(int num_workers, int batch, int nkv, int max_seq) {
-  // Enough splits that one split holds at most ~128 positions at full
-  // length, but no more tasks than workers.
+  // Enough splits that one split holds at most MPK_ATTN_SPLIT positions at
+  // full length, but no more tasks than workers.
   int ns = num_workers / std::max(1, batch * nkv);
-  int by_len = (max_seq + 127) / 128;
+  int by_len = (max_seq + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT;
   ns = std::min(ns, by_len);
   return std::max(1, ns);
 }

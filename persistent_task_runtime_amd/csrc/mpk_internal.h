@@ -15,7 +15,7 @@
 #define MPK_SEG 4096                    /* columns of one weight block */
 #define MPK_BU 8                        /* 16-byte-per-lane units per block */
 #define MPK_MAX_DEPS 3
-#define MPK_ATTN_SUB 512                /* positions scored per pass of an attention task */
+#define MPK_ATTN_SPLIT 64              /* positions per attention split (at full use) */
 #define MPK_LDS_BYTES (96 * 1024)       /* dynamic LDS per workgroup (forces one per CU) */
 #define MPK_MAX_BATCH 8
 

@@ -29,6 +29,7 @@
 // iteration's embedding reads wait for.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <memory>
@@ -184,6 +185,10 @@ DEV void vm_wait() {
 // above is opaque to it): afterwards it knows nothing is in flight, so its
 // own waits on a register ring stay exact instead of falling back to full
 // drains when stores or atomics of earlier code might still be pending.
+// Also the fence between loads of different kinds (plain, nontemporal,
+// device-scope): the hardware returns loads in order only within a kind, so
+// a wait on an older load of one kind must not rely on younger loads of
+// another kind having completed after it.
 DEV void vm_drain_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt 0, expcnt 7, lgkmcnt 15
 
 
@@ -277,9 +282,11 @@ DEV int cur_token_v(const char* smem, int b) { return reinterpret_cast<const vol
 // expected stamp also sees the payload: consumers spin on exactly the words
 // they read, and producers publish with plain device-scope stores - no
 // completion flag, no store drain, no fence between them.
-// The stamp of iteration s is iter_base + s + 1; iter_base grows by the
-// iteration count of every launch, so words left by an earlier launch (or an
-// aborted one) never carry a current stamp.  Buffers start zeroed (stamp 0).
+// The stamp of iteration s is iter_base + s + 1, with iter_base taken from a
+// process-wide counter that grows by the iteration count of every launch, so
+// words left by an earlier launch (an aborted one, or another executable
+// whose memory was reused) never carry a current stamp.  Buffers are zeroed
+// (stamp 0) before an executable is returned.
 // ---------------------------------------------------------------------------
 DEV uint32_t stamp_of(const mpk_kparams& P, int s) { return P.iter_base + (uint32_t)s + 1u; }
 DEV void st_ll(uint64_t* p, float v, uint32_t st) {
@@ -627,6 +634,9 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       }
     }
   }
+  // the residual element may have been a plain load issued before the
+  // device-scope polls: see vm_drain_known
+  vm_drain_known();
   // RMS sums and gain, each thread over its own elements in a fixed order
   if (D.has_norm) {
     for (int e = worker ? tid : NE; e < NE; e += MPK_NW * 64) {
@@ -1043,7 +1053,7 @@ DEV int argmax_task(const mpk_kparams& P, cop& D, char* smem, int tid, int s, in
 // of q and k, RoPE at the request's position p, K/V of p into the caches
 // (by the split that owns p), an online softmax over this split's positions
 // kept per lane group in registers, and one merge across the wavefronts.
-// The context [0, p] is cut into na = min(nsplit, ceil((p + 1) / 128))
+// The context [0, p] is cut into na = min(nsplit, ceil((p + 1) / 64))
 // splits; splits c >= na have nothing to do this iteration.  With one split
 // the task writes the attention output of the group's query heads; with
 // several, splits publish stamped partials (m, l, acc) and the split that
@@ -1062,7 +1072,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   const int d = D.d, G = D.nq / D.nkv, half = d >> 1, LP = d >> 3, PPR = 64 / LP;
   const int p = cur_pos(smem, r);
   const int n = p + 1;
-  const int na = min(NS, (n + 127) / 128);
+  const int na = min(NS, (n + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT);
   if (c >= na) return 0;  // uniform over the workgroup: nothing to do this iteration
   const int lo = (int)(((int64_t)c * n) / na), hi = (int)(((int64_t)(c + 1) * n) / na);
   const bool owner = c == na - 1;  // the split holding position p
@@ -1104,8 +1114,18 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   if (!sched && lo < hi) load_rounds(lo);
 
   // ---- q / k / v words of the group: wave hh < G + 2 takes one head vector ----
-  Waiter Wt = waiter_start();
   const int hh = wave;
+  // RoPE factors and norm gains do not depend on this iteration's words:
+  // loaded before the wait
+  float cs = 0.f, sn = 0.f, ga = 0.f, gb = 0.f;
+  if (!sched && hh <= G && lane < half) {
+    cs = gld(P.rope_cos + (int64_t)p * half + lane);
+    sn = gld(P.rope_sin + (int64_t)p * half + lane);
+    const uint16_t* gsrc = hh < G ? D.qn : D.kn;
+    ga = bf16f(gld16(gsrc + lane));
+    gb = bf16f(gld16(gsrc + lane + half));
+  }
+  Waiter Wt = waiter_start();
   const bool mine = !sched && hh < G + 2 && lane < half;
   const uint64_t* src = D.xll + (int64_t)r * qkv_w +
                         (hh < G ? (j * G + hh) * d : (hh == G ? D.nq * d + j * d : (D.nq + D.nkv) * d + j * d));
@@ -1123,6 +1143,12 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       if (rc == 0) break;
     }
   }
+  // The K/V rows, RoPE factors and gains above were loaded before the
+  // device-scope polls.  Loads of different kinds need not return in issue
+  // order, so the compiler's count-based waits (which assume they do) could
+  // pass while an older plain load is still in flight: wait for all of them
+  // here, where it costs nothing (they were issued first).
+  vm_drain_known();
   mark_ready(P, s, task_id, tid);
 
   // ---- RMSNorm + RoPE (waves 0..G+1) ----
@@ -1130,11 +1156,6 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     const float a = lane < half ? ll_f(wa) : 0.f;
     const float b = lane < half ? ll_f(wb) : 0.f;
     if (hh <= G) {
-      const float cs = lane < half ? gld(P.rope_cos + (int64_t)p * half + lane) : 0.f;
-      const float sn = lane < half ? gld(P.rope_sin + (int64_t)p * half + lane) : 0.f;
-      const uint16_t* gsrc = hh < G ? D.qn : D.kn;
-      const float ga = lane < half ? bf16f(gld16(gsrc + lane)) : 0.f;
-      const float gb = lane < half ? bf16f(gld16(gsrc + lane + half)) : 0.f;
       const float ss = wave_sum(a * a + b * b);
       const float inv = 1.0f / sqrtf(ss / (float)d + P.rms_eps);
       if (lane < half) {
@@ -1425,7 +1446,6 @@ struct mpk_exec_s {
   uint32_t* d_ticket_ctr = nullptr;  // trace ticket counter
   uint64_t* d_tok_ll = nullptr;      // [B] stamped next token
   std::vector<uint64_t*> ll_ptr;     // per tensor: stamped words of an operator output, or NULL
-  uint32_t iter_base = 0;            // stamps used so far (see stamp_of)
   float* d_rope = nullptr;
   mpk_dev_status* d_status = nullptr;
   mpk_trace_record* d_trace = nullptr;
@@ -1651,9 +1671,17 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   K.rope_half = half;
   K.rms_eps = M.rms_eps;
   K.vocab = M.vocab;
+  // The zero fills above (hipMemset) are ordered on the null stream only;
+  // a run on another stream must never see a buffer before it is zeroed (a
+  // reused allocation could still hold words stamped by an earlier
+  // executable).
+  HIPCHK(hipDeviceSynchronize());
   *out = x.release();
   return MPK_OK;
 }
+
+// Iteration stamps handed out so far in this process (see prepare_run).
+static std::atomic<uint64_t> g_stamps{0};
 
 static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
   if (!x) return mpk_fail(MPK_ERR_INVALID_ARG, "NULL exec");
@@ -1707,11 +1735,13 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
   for (int r = 0; r < x->B; ++r) x->kp.pos0[r] = step[r];
   x->kp.n_iter = n_iter;
   x->last_iters = n_iter;
-  // stamps of this run: iter_base + 1 .. iter_base + n_iter (never reused)
-  if ((uint64_t)x->iter_base + (uint64_t)n_iter >= 0xffffffffull)
-    return mpk_fail(MPK_ERR_STATE, "iteration stamps exhausted (2^32 iterations per executable)");
-  x->kp.iter_base = x->iter_base;
-  x->iter_base += (uint32_t)n_iter;
+  // stamps of this run: base + 1 .. base + n_iter, taken from a counter
+  // shared by every executable of the process, so no two runs (of this or
+  // any other executable) ever use the same stamp
+  const uint64_t base = g_stamps.fetch_add((uint64_t)n_iter);
+  if (base + (uint64_t)n_iter >= 0xffffffffull)
+    return mpk_fail(MPK_ERR_STATE, "iteration stamps exhausted (2^32 iterations per process)");
+  x->kp.iter_base = (uint32_t)base;
   hipLaunchKernelGGL(mpk_zero_u32, dim3(1), dim3(64), 0, st, x->d_ticket_ctr, (int64_t)1);
   // clear code / iteration / task; a stop request (abort_req) stays until cleared
   hipLaunchKernelGGL(mpk_zero_u32, dim3(1), dim3(64), 0, st, (uint32_t*)x->d_status, (int64_t)3);

@@ -87,9 +87,9 @@ def test_full_model_tiles_fill_every_cu():
             if k == mpk.MPK_OP_LMHEAD_ARGMAX:
                 assert {t.nrows for t in per_op[i]} == {593, 594}
                 assert sum(t.nrows for t in per_op[i]) == 151936
-        # attention: 8 kv heads x ceil(551 / 128) = 5 splits at batch 1
+        # attention: 8 kv heads x ceil(551 / 64) = 9 splits at batch 1
         attn = per_op[2]
-        assert sorted((t.nrows, t.split) for t in attn) == [(j, c) for j in range(8) for c in range(5)]
+        assert sorted((t.nrows, t.split) for t in attn) == [(j, c) for j in range(8) for c in range(9)]
         # one argmax task, on worker 0, last in its queue
         assert len(per_op[argmax_op]) == 1 and per_op[argmax_op][0].worker == 0
         assert tasks[queues[0][-1]].op == argmax_op

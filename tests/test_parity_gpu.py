@@ -277,10 +277,13 @@ def test_one_layer_matches_oracle(torch_dev):
     log("h max-abs err %.3g (|h| max %.3g)" % (err, np.max(np.abs(h_or))))
     assert err <= LOGIT_TOL
     # the new K/V row: equal, or one bf16 step apart where the fp32 values straddle a rounding boundary
-    for got, want in ((k_gpu, st.kcache[0, 0]), (v_gpu, st.vcache[0, 0])):
+    for nm, got, want in (("K", k_gpu, st.kcache[0, 0]), ("V", v_gpu, st.vcache[0, 0])):
         a = synth.bf16_bits_to_f32(got[:, 512]).astype(np.float64)
         b = synth.bf16_bits_to_f32(want[:, 512]).astype(np.float64)
-        assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(b), 1e-30))
+        bad = np.abs(a - b) > 2.0 ** -7 * np.maximum(np.abs(b), 1e-30)
+        where = [(j, int(i), a[j, i], b[j, i]) for j, i in zip(*np.nonzero(bad))][:8]
+        assert not bad.any(), "%s row 512: %d elements off, first (head, dim, gpu, oracle): %s" % (
+            nm, int(bad.sum()), where)
         assert np.array_equal(got[:, :512], want[:, :512]), "pre-filled positions untouched"
     sess.close()
 
