@@ -185,10 +185,10 @@ DEV void vm_wait() {
 // above is opaque to it): afterwards it knows nothing is in flight, so its
 // own waits on a register ring stay exact instead of falling back to full
 // drains when stores or atomics of earlier code might still be pending.
-// Also the fence between loads of different kinds (plain, nontemporal,
-// device-scope): the hardware returns loads in order only within a kind, so
-// a wait on an older load of one kind must not rely on younger loads of
-// another kind having completed after it.
+// Also used as a precaution between loads of different kinds (plain,
+// nontemporal, device-scope): the compiler's count-based waits assume that
+// all of a wavefront's loads return in issue order; the code does not rely
+// on that across kinds where the fence costs nothing.
 DEV void vm_drain_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt 0, expcnt 7, lgkmcnt 15
 
 
@@ -835,56 +835,64 @@ DEV u32x4 load_unit(const Cursor& C, int lane) {
 template <int NB, bool LDS_PF>
 DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, int k, int s, int task_id, char* smem,
                   int tid, bool sched, bool cross) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // The stream's first register group (units 8..15 after the eight LDS
+  // units, or 0..7 without them) is issued before the inputs are awaited:
+  // these weights do not depend on them, and the wait is what they hide.
+  Cursor I;  // issue side: runs MPK_RING units ahead of consumption
+  u32x4 b[MPK_RING];
+  int n = 0, npad = MPK_RING;
+  if (!sched) {
+    cursor_init(I, D, T, wave);
+    n = I.n;
+    npad = uni(padded_units(n));
+    if (LDS_PF) {
+#pragma unroll
+      for (int j = 0; j < MPK_RING; ++j) cursor_step(I, wave);
+    }
+#pragma unroll
+    for (int j = 0; j < MPK_RING; ++j) {
+      b[j] = load_unit(I, lane);
+      cursor_step(I, wave);
+    }
+  }
   {
     const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id);
     if (rc) return rc;
   }
   mark_ready(P, s, task_id, tid);
   const uint32_t st = stamp_of(P, s);
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const uint32_t lb = lds_addr(smem);  // LDS byte address of the workgroup's area
   const float* inv_lds = reinterpret_cast<const float*>(smem + LDS_INV);
   float inv[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) inv[b] = inv_lds[b];
+  for (int bb = 0; bb < NB; ++bb) inv[bb] = inv_lds[bb];
   const int Kpad = ((D.K + 511) / 512) * 512;
   GemvState<NB> G;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) G.acc[b] = 0.f, G.gate[b] = 0.f, G.best_v[b] = -INFINITY, G.best_i[b] = 0x7fffffff;
+  for (int bb = 0; bb < NB; ++bb)
+    G.acc[bb] = 0.f, G.gate[bb] = 0.f, G.best_v[bb] = -INFINITY, G.best_i[bb] = 0x7fffffff;
   G.u = 0, G.rr = 0, G.kk = 0;
   if (!sched) {
     const int a = D.pairs ? 2 : 1;
     const int upr = uni(units_per_row(D));
-    Cursor I;  // issue side: runs MPK_RING units ahead of consumption
-    cursor_init(I, D, T, wave);
-    const int n = I.n, npad = uni(padded_units(n));
     const uint32_t slots = lb + Lay<NB>::RING + wave * MPK_RING * 1024;
+    // everything issued so far (LDS DMA of units 0..7, the register group,
+    // the staging's loads) is complete here; the compiler knows it too
     vm_drain_known();
-    u32x4 b[MPK_RING];
+    // register groups: group g holds units 8g .. 8g + 7
+    const int ng = npad / MPK_RING;
+    const int g0 = LDS_PF ? 1 : 0;
     if (upr % MPK_RING == 0) {
       // rows are whole groups of eight units (K a multiple of 4096): the
       // epilogue runs between groups only, which keeps the register ring's
       // waits exact inside the unrolled group
       const uint32_t xl = lb + LDS_X + lane * 16;
-      const int ng = npad / MPK_RING;
-      int g = 0;
       if (LDS_PF) {
-#pragma unroll
-        for (int j = 0; j < MPK_RING; ++j) cursor_step(I, wave);
         const uint32_t xg = xl + G.u * 2048;
 #pragma unroll
-        for (int j = 0; j < MPK_RING; ++j) {
-          // slot j's DMA has (7 - j) DMA loads and j register loads younger
-          // than it; loads complete in order
-          vm_wait<MPK_RING - 1>();
-          const u32x4 w = lds_read_u32x4(slots + j * 1024 + lane * 16);
-          unit_fma<NB>(w, xg + j * 2048, Kpad, G.acc);
-          // refilled even when the task has no register groups (its padding
-          // units): a conditional refill leaves the compiler unsure which
-          // loads are in flight and every later wait becomes a full drain
-          b[j] = load_unit(I, lane);
-          cursor_step(I, wave);
-        }
+        for (int j = 0; j < MPK_RING; ++j)
+          unit_fma<NB>(lds_read_u32x4(slots + j * 1024 + lane * 16), xg + j * 2048, Kpad, G.acc);
         if (n > 0) {
           G.u += MPK_RING;
           if (G.u == upr) {
@@ -892,16 +900,9 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, in
             row_done<NB>(D, T, G, lb, inv, a, wave, lane);
           }
         }
-        g = 1;
-      } else {
-#pragma unroll
-        for (int j = 0; j < MPK_RING; ++j) {
-          b[j] = load_unit(I, lane);
-          cursor_step(I, wave);
-        }
       }
       // steady state: consume b[j], refill it with the unit eight places on
-      for (; g < ng - 1; ++g) {
+      for (int g = g0; g < ng - 1; ++g) {
         const uint32_t xg = xl + G.u * 2048;
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
@@ -915,8 +916,8 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, in
           row_done<NB>(D, T, G, lb, inv, a, wave, lane);
         }
       }
-      // last group (unless group 0 was it)
-      if (g == ng - 1) {
+      // last group (when it is a register group)
+      if (ng - 1 >= g0) {
         const uint32_t xg = xl + G.u * 2048;
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) unit_fma<NB>(b[j], xg + j * 2048, Kpad, G.acc);
@@ -930,27 +931,12 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, in
       }
     } else {
       // generic rows (short K): per-unit bookkeeping, padding skipped
-      int g0 = 0;
       if (LDS_PF) {
 #pragma unroll
-        for (int j = 0; j < MPK_RING; ++j) cursor_step(I, wave);
-#pragma unroll
-        for (int j = 0; j < MPK_RING; ++j) {
-          vm_wait<MPK_RING - 1>();
-          const u32x4 w = lds_read_u32x4(slots + j * 1024 + lane * 16);
-          gemv_consume<NB>(T, D, G, w, j, n, lb, inv, Kpad, upr, a, wave, lane);
-          b[j] = load_unit(I, lane);
-          cursor_step(I, wave);
-        }
-        g0 = 1;
-      } else {
-#pragma unroll
-        for (int j = 0; j < MPK_RING; ++j) {
-          b[j] = load_unit(I, lane);
-          cursor_step(I, wave);
-        }
+        for (int j = 0; j < MPK_RING; ++j)
+          gemv_consume<NB>(T, D, G, lds_read_u32x4(slots + j * 1024 + lane * 16), j, n, lb, inv, Kpad, upr, a,
+                           wave, lane);
       }
-      const int ng = npad / MPK_RING;
       for (int g = g0; g < ng - 1; ++g) {
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
@@ -1143,11 +1129,9 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       if (rc == 0) break;
     }
   }
-  // The K/V rows, RoPE factors and gains above were loaded before the
-  // device-scope polls.  Loads of different kinds need not return in issue
-  // order, so the compiler's count-based waits (which assume they do) could
-  // pass while an older plain load is still in flight: wait for all of them
-  // here, where it costs nothing (they were issued first).
+  // The K/V rows, RoPE factors and gains above are plain loads issued
+  // before the device-scope polls: complete them here (see vm_drain_known;
+  // they were issued first, so this costs nothing).
   vm_drain_known();
   mark_ready(P, s, task_id, tid);
 
