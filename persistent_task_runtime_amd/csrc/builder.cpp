@@ -458,21 +458,12 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
     g->qlen[w] = (int)q[w].size();
     g->max_queue = std::max(g->max_queue, g->qlen[w]);
   }
-  g->queues.assign((size_t)W * g->max_queue, mpk_dev_qentry{-1, -1});
+  g->queues.assign((size_t)W * g->max_queue, mpk_dev_qentry{-1});
   g->queue_ids.assign((size_t)W * g->max_queue, -1);
   for (int w = 0; w < W; ++w) {
     const int n = g->qlen[w];
     for (int k = 0; k < n; ++k) {
-      int nx = -1;
-      for (int j = 1; j <= n; ++j) {
-        int kk = k + j;
-        const mpk_dev_task& T = g->tasks[q[w][kk % n]];
-        if (T.kind == MPK_TK_GEMV || T.kind == MPK_TK_LMHEAD) {
-          nx = kk;
-          break;
-        }
-      }
-      g->queues[(size_t)w * g->max_queue + k] = mpk_dev_qentry{q[w][k], nx};
+      g->queues[(size_t)w * g->max_queue + k] = mpk_dev_qentry{q[w][k]};
       g->queue_ids[(size_t)w * g->max_queue + k] = q[w][k];
     }
   }

@@ -79,12 +79,9 @@ typedef struct {
   int32_t pad[1];
 } mpk_dev_task;
 
-/* Per queue entry: task id and the queue position of the next task that
- * streams weights (to prefetch), or -1. Positions >= queue length wrap into
- * the next iteration. */
+/* Per queue entry: the task id. */
 typedef struct {
   int32_t task;
-  int32_t next_stream;
 } mpk_dev_qentry;
 
 typedef struct {
@@ -98,7 +95,6 @@ typedef struct {
   const mpk_dev_task* tasks;
   const mpk_dev_op* ops;
   const mpk_dev_qentry* queues; /* [num_workers][qstride] */
-  const mpk_dev_qentry* single_q; /* [n_tasks]: {task, -1} (one-launch-per-operator path) */
   const int32_t* qlen;          /* [num_workers] */
   uint64_t* tok_ll;              /* [B] stamped next token, written by the argmax task */
   int32_t* tokens;

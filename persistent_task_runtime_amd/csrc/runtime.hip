@@ -16,13 +16,12 @@
 // computed - there is no per-task completion flag, fence or store drain on
 // the path between two tasks.
 //
-// Weights stream through a per-wavefront ring in LDS, filled by direct
-// global->LDS 16-byte loads (global_load_lds_dwordx4).  The ring's producer
-// side walks the CU's queue ahead of the consumer and crosses task
-// boundaries: while a task's inputs are still being produced, the first
-// weight units of that task (and of the next ones) are already in flight.
-// This is the "load the next layer while computing this one" pipelining of
-// P3 "Why MPK?", done per CU with the queue known at compile time.
+// Weights stream through an eight-deep register ring per wavefront
+// (16-byte nontemporal loads).  A task issues its first eight units before
+// it waits for its inputs, so the weights of the next operator are already
+// in flight while the current one's outputs are still being produced: the
+// "load the next layer while computing this one" overlap of P3 "Why MPK?",
+// done per CU with the queue known at compile time.
 //
 // The iteration's last task picks the argmax token, writes it into tokens,
 // advances step (P1 "How MPK Works") and publishes the token word the next
@@ -145,23 +144,11 @@ DEV uint32_t hwreg_xcc_id() {
   return v;
 }
 
-// Wait until at most N vector-memory operations of this wavefront are in
-// flight.  The compiler does not model the LDS writes of global_load_lds, so
-// the ring's consumer waits explicitly; the memory clobber keeps the LDS read
-// of the slot after the wait.
-// LDS reads inside the weight stream are written in asm, each block waiting
-// for its own reads: the compiler cannot tell LDS reads from the DMA'd ring
-// slots and would otherwise wait for every ring load in flight before any
-// LDS read it sees.
+// LDS traffic inside the weight stream is written in asm, each block waiting
+// for its own reads (with a memory clobber): it pins each unit's x reads and
+// FMAs between the ring's refills, which keeps the compiler from reordering
+// the stream into a shape whose waits drain the whole ring.
 DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lptr_t)(void*)p; }
-// LDS pointer from an LDS byte address (no generic-pointer conversion)
-DEV lptr_t lds_ptr(uint32_t a) { return (lptr_t)(uintptr_t)a; }
-
-DEV u32x4 lds_read_u32x4(uint32_t a) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-  return v;
-}
 
 // Two float4 at byte address a and a + 1024.
 DEV void lds_read_2f4(uint32_t a, f32x4& x0, f32x4& x1) {
@@ -177,6 +164,8 @@ DEV float lds_read_f32(uint32_t a) {
   return v;
 }
 
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (opaque to the compiler's own wait insertion).
 template <int N>
 DEV void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -220,8 +209,6 @@ DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 //   [LDS_OUT, +4096)          attention: split partial / output, new K/V row
 //   [LDS_X, +XS)              staged activations x (or attention scratch)
 //   [RES, +2048)              staged residual rows of the tile
-//   [RING, +NW*8*1024)        per wavefront, 8 slots of 1 KB: the first weight
-//                             units of its next stream task (NB = 1 only)
 // x is staged permuted so each 16-byte LDS read is lane-contiguous:
 //   column k -> unit u = k / 512, lane l = (k % 512) / 8, half h = (k % 8) / 4
 //   offset (floats) = u * 512 + h * 256 + l * 4 + (k % 4)
@@ -241,9 +228,7 @@ template <int NB>
 struct Lay {
   static constexpr int XS = 49152 * NB;             // staged x bytes
   static constexpr int RES = LDS_X + XS;            // residual rows
-  static constexpr int RING = RES + LDS_RES_BYTES;  // LDS slots of the next task's first units
-  static constexpr bool PF = NB == 1;               // cross-task LDS prefetch (room for it at NB = 1)
-  static constexpr int TOTAL = RING + (PF ? MPK_NW * 8 * 1024 : 0);
+  static constexpr int TOTAL = RES + LDS_RES_BYTES;
 };
 static_assert(Lay<1>::TOTAL <= 160 * 1024, "LDS budget");
 static_assert(Lay<2>::TOTAL <= 160 * 1024, "LDS budget");
@@ -431,12 +416,12 @@ DEV int gather_ll(const mpk_kparams& P, const uint64_t* src, int n, uint32_t* ds
 //   units of 512 bf16 (1 KB, 16 bytes per lane); a wavefront's sequence is
 //   its rows in order, each row's units in order, padded with repeat reads
 //   to a whole number of groups of 8 units (at least one group).
-//   Units 0..7 of a task arrive in the wavefront's LDS slots by global->LDS
-//   DMA, issued while the previous stream task of the queue ends; units 8..
-//   arrive in registers, eight in flight, each issued as the unit eight
-//   places earlier is consumed.
+//   Units travel in an eight-deep register ring per wavefront: eight
+//   16-byte loads in flight, each refilled as the unit eight places earlier
+//   is consumed.  A task's first eight are issued before its inputs are
+//   awaited.
 // ---------------------------------------------------------------------------
-#define MPK_RING 8  // units in flight per wavefront (LDS slots = register slots)
+#define MPK_RING 8  // units in flight per wavefront
 
 DEV int units_per_row(cop& D) { return (D.K + 511) >> 9; }
 
@@ -518,38 +503,6 @@ DEV void cursor_step(Cursor& C, int wave) {
       C.kk = uni(C.kk + 1);
     }
     cursor_row(C, wave);
-  }
-}
-
-// The first stream task (GEMV / LM head) at queue position k or later of
-// iteration s, wrapping into the next iteration; false when there is none
-// before the end of the run.
-DEV bool next_stream_task(const mpk_kparams& P, cqent* Q, int qlen, int s, int k, int& s_out, int& task_out) {
-  for (int guard = 0; guard < 2 && qlen > 0; ++guard) {
-    if (k >= qlen) k -= qlen, s += 1;
-    if (s >= P.n_iter) return false;
-    const int tix = uni(Q[k].task);
-    const int kind = uni(tasks_of(P)[tix].kind);
-    if (kind == MPK_TK_GEMV || kind == MPK_TK_LMHEAD) {
-      s_out = s, task_out = tix;
-      return true;
-    }
-    k = uni(Q[k].next_stream);  // > k; >= qlen means the next iteration
-    if (k < 0) return false;
-  }
-  return false;
-}
-
-// DMA units 0..7 of a stream task into this wavefront's LDS slots (LDS byte
-// address of slot 0).
-DEV void prefetch_task_lds(const mpk_kparams& P, int task, uint32_t slots, int wave, int lane) {
-  ctask& T = tasks_of(P)[task];
-  Cursor C;
-  cursor_init(C, ops_of(P)[uni(T.op)], T, wave);
-#pragma unroll
-  for (int j = 0; j < MPK_RING; ++j) {
-    __builtin_amdgcn_global_load_lds(cursor_addr(C, lane), lds_ptr(slots + j * 1024), 16, 0, 0);
-    cursor_step(C, wave);
   }
 }
 
@@ -703,11 +656,8 @@ DEV void put_out(cop& D, int64_t i, float v, uint32_t st) {
 // ---------------------------------------------------------------------------
 // GEMV-type task: rmsnorm_linear (EPI_STORE), linear + residual (EPI_RESID),
 // rmsnorm + gate/up + SiLU-mul (EPI_SILU), final norm + LM head + tile argmax
-// (EPI_ARGMAX).  Lane 0 of the wavefront that finishes a row publishes the
-// row's output word at once.  With LDS_PF the task's first eight units per
-// wavefront are already in LDS and the task's tail DMAs the next stream
-// task's first eight; otherwise all units go through registers.  Returns -1
-// on stop.
+// (EPI_ARGMAX).  Each wavefront publishes its rows' output words after its
+// stream (see row_done).  Returns -1 on stop.
 // ---------------------------------------------------------------------------
 // LDS address of a logit of the LM-head tile: after the staged x of the NB
 // requests.
@@ -765,7 +715,7 @@ DEV void row_done(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, const float (
   for (int b = 0; b < NB; ++b) {
     const float sum = wave_sum(G.acc[b]);
     G.acc[b] = 0.f;
-    // LDS traffic inside the weight stream stays in asm (see lds_read_u32x4)
+    // LDS traffic inside the weight stream stays in asm (see lds_addr)
     if (EPI == MPK_EPI_STORE) {
       if (lane == 0) lds_write_f32(ob + (uint32_t)(b * n_out_tile + lrow) * 4u, sum * inv[b]);
     } else if (EPI == MPK_EPI_RESID) {
@@ -832,13 +782,12 @@ DEV u32x4 load_unit(const Cursor& C, int lane) {
   return __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1)))*)cursor_addr(C, lane));
 }
 
-template <int NB, bool LDS_PF>
-DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, int k, int s, int task_id, char* smem,
-                  int tid, bool sched, bool cross) {
+template <int NB>
+DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, char* smem, int tid, bool sched) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  // The stream's first register group (units 8..15 after the eight LDS
-  // units, or 0..7 without them) is issued before the inputs are awaited:
-  // these weights do not depend on them, and the wait is what they hide.
+  // The ring's first group (units 0..7) is issued before the inputs are
+  // awaited: these weights do not depend on them, and the wait is what
+  // they hide.
   Cursor I;  // issue side: runs MPK_RING units ahead of consumption
   u32x4 b[MPK_RING];
   int n = 0, npad = MPK_RING;
@@ -846,10 +795,6 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, in
     cursor_init(I, D, T, wave);
     n = I.n;
     npad = uni(padded_units(n));
-    if (LDS_PF) {
-#pragma unroll
-      for (int j = 0; j < MPK_RING; ++j) cursor_step(I, wave);
-    }
 #pragma unroll
     for (int j = 0; j < MPK_RING; ++j) {
       b[j] = load_unit(I, lane);
@@ -876,33 +821,18 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, in
   if (!sched) {
     const int a = D.pairs ? 2 : 1;
     const int upr = uni(units_per_row(D));
-    const uint32_t slots = lb + Lay<NB>::RING + wave * MPK_RING * 1024;
-    // everything issued so far (LDS DMA of units 0..7, the register group,
-    // the staging's loads) is complete here; the compiler knows it too
+    // everything issued so far (the first group, the staging's loads) is
+    // complete here, and the compiler knows it: its waits on the ring stay
+    // exact
     vm_drain_known();
-    // register groups: group g holds units 8g .. 8g + 7
-    const int ng = npad / MPK_RING;
-    const int g0 = LDS_PF ? 1 : 0;
+    const int ng = npad / MPK_RING;  // group g holds units 8g .. 8g + 7
     if (upr % MPK_RING == 0) {
       // rows are whole groups of eight units (K a multiple of 4096): the
       // epilogue runs between groups only, which keeps the register ring's
       // waits exact inside the unrolled group
       const uint32_t xl = lb + LDS_X + lane * 16;
-      if (LDS_PF) {
-        const uint32_t xg = xl + G.u * 2048;
-#pragma unroll
-        for (int j = 0; j < MPK_RING; ++j)
-          unit_fma<NB>(lds_read_u32x4(slots + j * 1024 + lane * 16), xg + j * 2048, Kpad, G.acc);
-        if (n > 0) {
-          G.u += MPK_RING;
-          if (G.u == upr) {
-            G.u = 0;
-            row_done<NB>(D, T, G, lb, inv, a, wave, lane);
-          }
-        }
-      }
       // steady state: consume b[j], refill it with the unit eight places on
-      for (int g = g0; g < ng - 1; ++g) {
+      for (int g = 0; g < ng - 1; ++g) {
         const uint32_t xg = xl + G.u * 2048;
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
@@ -916,28 +846,20 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, in
           row_done<NB>(D, T, G, lb, inv, a, wave, lane);
         }
       }
-      // last group (when it is a register group)
-      if (ng - 1 >= g0) {
-        const uint32_t xg = xl + G.u * 2048;
+      // last group
+      const uint32_t xg = xl + G.u * 2048;
 #pragma unroll
-        for (int j = 0; j < MPK_RING; ++j) unit_fma<NB>(b[j], xg + j * 2048, Kpad, G.acc);
-        if (n > 0) {
-          G.u += MPK_RING;
-          if (G.u == upr) {
-            G.u = 0;
-            row_done<NB>(D, T, G, lb, inv, a, wave, lane);
-          }
+      for (int j = 0; j < MPK_RING; ++j) unit_fma<NB>(b[j], xg + j * 2048, Kpad, G.acc);
+      if (n > 0) {
+        G.u += MPK_RING;
+        if (G.u == upr) {
+          G.u = 0;
+          row_done<NB>(D, T, G, lb, inv, a, wave, lane);
         }
       }
     } else {
       // generic rows (short K): per-unit bookkeeping, padding skipped
-      if (LDS_PF) {
-#pragma unroll
-        for (int j = 0; j < MPK_RING; ++j)
-          gemv_consume<NB>(T, D, G, lds_read_u32x4(slots + j * 1024 + lane * 16), j, n, lb, inv, Kpad, upr, a,
-                           wave, lane);
-      }
-      for (int g = g0; g < ng - 1; ++g) {
+      for (int g = 0; g < ng - 1; ++g) {
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
           gemv_consume<NB>(T, D, G, b[j], g * MPK_RING + j, n, lb, inv, Kpad, upr, a, wave, lane);
@@ -945,12 +867,10 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, in
           cursor_step(I, wave);
         }
       }
-      if (ng - 1 >= g0) {
-        const int g = ng - 1;
+      const int g = ng - 1;
 #pragma unroll
-        for (int j = 0; j < MPK_RING; ++j)
-          gemv_consume<NB>(T, D, G, b[j], g * MPK_RING + j, n, lb, inv, Kpad, upr, a, wave, lane);
-      }
+      for (int j = 0; j < MPK_RING; ++j)
+        gemv_consume<NB>(T, D, G, b[j], g * MPK_RING + j, n, lb, inv, Kpad, upr, a, wave, lane);
     }
     publish_rows<NB>(P, D, T, lb, s, st, wave, lane);
   }
@@ -976,13 +896,6 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, cqent* Q, int qlen, in
       st_ll(pw, v, st);
       st_lli(pw + 1, ix, st);
     }
-  }
-  // outputs are out: the first units of the next stream task in the queue go
-  // to this wavefront's LDS slots while the task's consumers gather
-  if (LDS_PF && cross && !sched) {
-    int s2 = 0, t2 = 0;
-    if (next_stream_task(P, Q, qlen, s, k + 1, s2, t2))
-      prefetch_task_lds(P, t2, lb + Lay<NB>::RING + wave * MPK_RING * 1024, wave, lane);
   }
   return 0;
 }
@@ -1325,13 +1238,11 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 // dispatch of one task body; returns -1 when the run must stop
 // ---------------------------------------------------------------------------
 template <int NB>
-DEV int run_task(const mpk_kparams& P, ctask& T, int task_id, cqent* Q, int qlen, int k, int s, char* smem, int tid,
-                 bool sched, bool cross) {
+DEV int run_task(const mpk_kparams& P, ctask& T, int task_id, int s, char* smem, int tid, bool sched) {
   cop& D = ops_of(P)[T.op];
   if (T.kind == MPK_TK_ATTN) return attn_task(P, T, D, smem, tid, sched, s, task_id);
   if (T.kind == MPK_TK_ARGMAX) return argmax_task<NB>(P, D, smem, tid, s, task_id);
-  if (cross) return gemv_task<NB, Lay<NB>::PF>(P, T, D, Q, qlen, k, s, task_id, smem, tid, sched, true);
-  return gemv_task<NB, false>(P, T, D, Q, qlen, k, s, task_id, smem, tid, sched, false);
+  return gemv_task<NB>(P, T, D, s, task_id, smem, tid, sched);
 }
 
 // ---------------------------------------------------------------------------
@@ -1346,11 +1257,6 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
   const int qlen = ((const CAS int32_t*)(const void*)P.qlen)[blockIdx.x];
   volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
   if (tid == 0) ctl[0] = 0;
-  if (Lay<NB>::PF && !sched) {
-    int s0 = 0, t0 = 0;
-    if (next_stream_task(P, Q, qlen, 0, 0, s0, t0))
-      prefetch_task_lds(P, t0, lds_addr(smem) + Lay<NB>::RING + wave * MPK_RING * 1024, wave, lane);
-  }
   for (int s = 0; s < P.n_iter; ++s) {
     for (int k = 0; k < qlen; ++k) {
       const int task_id = Q[k].task;
@@ -1372,9 +1278,9 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
       // loop (it would stay live, and spill, across all bodies).
       int tid_o = tid;
       asm volatile("" : "+v"(tid_o));
-      const int rc = run_task<NB>(P, T, task_id, Q, qlen, k, s, smem, tid_o, sched, true);
+      const int rc = run_task<NB>(P, T, task_id, s, smem, tid_o, sched);
       if (rc < 0) {
-        vm_wait<0>();  // leave no LDS-bound load in flight
+        vm_wait<0>();  // leave no load in flight
         return;
       }
       __syncthreads();
@@ -1398,13 +1304,11 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_op_kernel(mpk_kparams P, i
   const bool sched = wave == MPK_NW;
   const int task_id = first_task + blockIdx.x;
   ctask& T = tasks_of(P)[task_id];
-  // a one-entry queue holding this task, for the ring's producer side
-  cqent* q1 = (cqent*)(const void*)P.single_q + task_id;
   volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
   if (tid == 0) ctl[0] = 0;
   if (sched) set_positions(P, smem, s, lane);
   __syncthreads();
-  run_task<NB>(P, T, task_id, q1, 1, 0, s, smem, tid, sched, false);
+  run_task<NB>(P, T, task_id, s, smem, tid, sched);
   vm_wait<0>();
 }
 
@@ -1425,7 +1329,6 @@ struct mpk_exec_s {
   mpk_dev_task* d_tasks = nullptr;
   mpk_dev_op* d_ops = nullptr;
   mpk_dev_qentry* d_queues = nullptr;
-  mpk_dev_qentry* d_single = nullptr;
   int32_t* d_qlen = nullptr;
   uint32_t* d_ticket_ctr = nullptr;  // trace ticket counter
   uint64_t* d_tok_ll = nullptr;      // [B] stamped next token
@@ -1608,12 +1511,6 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   HIPCHK(hipMemcpy(x->d_tasks, g->tasks.data(), g->tasks.size() * sizeof(mpk_dev_task), hipMemcpyHostToDevice));
   if ((rc = dalloc(x.get(), &x->d_queues, g->queues.size() * sizeof(mpk_dev_qentry)))) return rc;
   HIPCHK(hipMemcpy(x->d_queues, g->queues.data(), g->queues.size() * sizeof(mpk_dev_qentry), hipMemcpyHostToDevice));
-  {
-    std::vector<mpk_dev_qentry> single(g->tasks.size());
-    for (size_t i = 0; i < single.size(); ++i) single[i] = mpk_dev_qentry{(int32_t)i, -1};
-    if ((rc = dalloc(x.get(), &x->d_single, single.size() * sizeof(mpk_dev_qentry)))) return rc;
-    HIPCHK(hipMemcpy(x->d_single, single.data(), single.size() * sizeof(mpk_dev_qentry), hipMemcpyHostToDevice));
-  }
   if ((rc = dalloc(x.get(), &x->d_qlen, g->qlen.size() * 4))) return rc;
   HIPCHK(hipMemcpy(x->d_qlen, g->qlen.data(), g->qlen.size() * 4, hipMemcpyHostToDevice));
   if ((rc = dalloc(x.get(), &x->d_status, sizeof(mpk_dev_status)))) return rc;
@@ -1635,7 +1532,6 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   K.tasks = x->d_tasks;
   K.ops = x->d_ops;
   K.queues = x->d_queues;
-  K.single_q = x->d_single;
   K.qlen = x->d_qlen;
   K.tok_ll = x->d_tok_ll;
   K.tokens = (int32_t*)P(g->meta.tokens);
