@@ -228,10 +228,12 @@ template <int NB>
 struct Lay {
   static constexpr int XS = 49152 * NB;             // staged x bytes
   static constexpr int RES = LDS_X + XS;            // residual rows
-  static constexpr int TOTAL = RES + LDS_RES_BYTES;
+  // attention uses [LDS_X, TOTAL) as scratch (position-group partials and
+  // the gathered split partials); one workgroup per CU, so the whole LDS
+  static constexpr int TOTAL = 156 * 1024;
 };
-static_assert(Lay<1>::TOTAL <= 160 * 1024, "LDS budget");
-static_assert(Lay<2>::TOTAL <= 160 * 1024, "LDS budget");
+static_assert(Lay<1>::RES + LDS_RES_BYTES <= Lay<1>::TOTAL, "LDS budget");
+static_assert(Lay<2>::RES + LDS_RES_BYTES <= Lay<2>::TOTAL, "LDS budget");
 
 DEV void lds_write_f32(uint32_t a, float v) {
   asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(v) : "memory");
@@ -526,6 +528,15 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
     const int rc = resolve_tokens(P, smem, tid, s, task_id, Wt);
     if (rc) return rc;
   }
+  // RMSNorm gains of this thread's columns (k = tid + 512 j), loaded before
+  // the inputs are awaited when K fits one gather pass
+  const bool gains_early = K <= XCH * MPK_NW * 64;
+  float gk[XCH];
+#pragma unroll
+  for (int j = 0; j < XCH; ++j) {
+    const int k = tid + j * MPK_NW * 64;
+    gk[j] = D.has_norm && gains_early && tid < MPK_NW * 64 && k < K ? bf16f(gld16(D.gain + k)) : 0.f;
+  }
   // residual element of this thread: request rb, row rrow of the tile
   const int nres = D.epi == MPK_EPI_RESID ? NB * T.nrows : 0;
   bool need_r = false;
@@ -590,8 +601,21 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
   // the residual element may have been a plain load issued before the
   // device-scope polls: see vm_drain_known
   vm_drain_known();
-  // RMS sums and gain, each thread over its own elements in a fixed order
-  if (D.has_norm) {
+  // RMS sums and gain, each thread over its own columns in a fixed order
+  if (D.has_norm && gains_early) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < XCH; ++j) {
+        const int k = tid + j * MPK_NW * 64;
+        if (worker && k < K) {
+          float* px = xs + b * Kpad + xperm(k);
+          const float x = *px;
+          ss[b] = fmaf(x, x, ss[b]);
+          *px = x * gk[j];
+        }
+      }
+  } else if (D.has_norm) {
     for (int e = worker ? tid : NE; e < NE; e += MPK_NW * 64) {
       const int b = e / K, k = e - b * K;
       float* px = xs + b * Kpad + xperm(k);
@@ -959,7 +983,19 @@ DEV int argmax_task(const mpk_kparams& P, cop& D, char* smem, int tid, int s, in
 // owns p merges them into the output.  Returns -1 on stop.
 // ---------------------------------------------------------------------------
 #define ATT_MAXG 4
-#define ATT_ROUNDS 2  // position rounds per wavefront whose K/V rows are loaded together
+#define ATT_ROUNDS 2    // position rounds per wavefront whose K/V rows are loaded together
+#define ATT_GROUPS 64   // position groups per workgroup at most (NW waves x 64 / LP, d >= 64)
+
+// Sum over the LP lanes of a position group (lanes [g*LP, (g+1)*LP)), every
+// lane of the group receiving the same value (quad swaps, then half-row and
+// row mirrors: DPP, no LDS round trip).
+DEV float group_sum(float v, int LP) {
+  v += dpp<0xB1>(v);                  // quad_perm [1,0,3,2]
+  if (LP >= 4) v += dpp<0x4E>(v);     // quad_perm [2,3,0,1]
+  if (LP >= 8) v += dpp<0x141>(v);    // row_half_mirror
+  if (LP >= 16) v += dpp<0x140>(v);   // row_mirror
+  return v;
+}
 
 struct SoftState {
   float m[ATT_MAXG], l[ATT_MAXG], acc[ATT_MAXG][8];
@@ -976,12 +1012,15 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   const int lo = (int)(((int64_t)c * n) / na), hi = (int)(((int64_t)(c + 1) * n) / na);
   const bool owner = c == na - 1;  // the split holding position p
   const uint32_t st = stamp_of(P, s);
+  // position groups: lanes [g*LP, (g+1)*LP) of a wavefront take one position
+  // (LP lanes x 8 dims); NG = NW * PPR groups per workgroup
+  const int NG = MPK_NW * PPR;
   float* qs = reinterpret_cast<float*>(smem + LDS_X);  // [G][d]
   float* kv = qs + ATT_MAXG * 128;                      // k [d], v [d] (bf16-rounded)
-  float* wm = kv + 256;                                 // [NW][G]
-  float* wl = wm + MPK_NW * ATT_MAXG;                   // [NW][G]
-  float* wacc = wl + MPK_NW * ATT_MAXG;                 // [NW][G][128]
-  uint32_t* gath = reinterpret_cast<uint32_t*>(wacc + MPK_NW * ATT_MAXG * 128);  // gathered partials
+  float* wm = kv + 256;                                 // [NG][G] group maxima
+  float* wl = wm + ATT_GROUPS * ATT_MAXG;               // [NG][G] group sums
+  float* wacc = wl + ATT_GROUPS * ATT_MAXG;             // [NG][G][d] group accumulators
+  uint32_t* gath = reinterpret_cast<uint32_t*>(wacc + ATT_GROUPS * ATT_MAXG * 64);  // gathered partials
   float* outs = reinterpret_cast<float*>(smem + LDS_OUT);               // partial, then o
   uint32_t* kvrow = reinterpret_cast<uint32_t*>(smem + LDS_OUT) + 640;  // bf16 K row, then V row
   const int qkv_w = (D.nq + 2 * D.nkv) * d;
@@ -1121,7 +1160,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
             float part = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) part = fmaf(qv[h][e], kf[e], part);
-            for (int off = 1; off < LP; off <<= 1) part += __shfl_xor(part, off);
+            part = group_sum(part, LP);
             if (valid) {
               const float sc = part * scale;
               const float M = fmaxf(sm.m[h], sc);
@@ -1136,33 +1175,19 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
         }
       }
     }
-    // merge the lane groups of the wave (positions), one head at a time
+    // each position group's (m, l, acc) to LDS: merged across groups and
+    // wavefronts below in one pass
+    const int grp = wave * PPR + pg;
 #pragma unroll
     for (int h = 0; h < ATT_MAXG; ++h) {
       if (h < G) {
-        for (int off = LP; off < 64; off <<= 1) {
-          const float om = __shfl_xor(sm.m[h], off);
-          const float ol = __shfl_xor(sm.l[h], off);
-          const float M = fmaxf(sm.m[h], om);
-          const float ca = sm.m[h] == -INFINITY ? 0.f : expf(sm.m[h] - M);
-          const float cb = om == -INFINITY ? 0.f : expf(om - M);
-          sm.l[h] = sm.l[h] * ca + ol * cb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sm.acc[h][e] = sm.acc[h][e] * ca + __shfl_xor(sm.acc[h][e], off) * cb;
-          sm.m[h] = M;
+        if ((lane % LP) == 0) {
+          wm[grp * ATT_MAXG + h] = sm.m[h];
+          wl[grp * ATT_MAXG + h] = sm.l[h];
         }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < ATT_MAXG; ++h) {
-      if (h < G) {
-        if (lane == 0) {
-          wm[wave * ATT_MAXG + h] = sm.m[h];
-          wl[wave * ATT_MAXG + h] = sm.l[h];
-        }
-        if (lane < LP)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) wacc[(wave * ATT_MAXG + h) * 128 + dim0 + e] = sm.acc[h][e];
+        float* dst = wacc + (grp * ATT_MAXG + h) * d + dim0;
+        *reinterpret_cast<float4*>(dst) = float4{sm.acc[h][0], sm.acc[h][1], sm.acc[h][2], sm.acc[h][3]};
+        *reinterpret_cast<float4*>(dst + 4) = float4{sm.acc[h][4], sm.acc[h][5], sm.acc[h][6], sm.acc[h][7]};
       }
     }
   }
@@ -1173,13 +1198,13 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   for (int idx = tid; idx < G * d && !sched; idx += MPK_NW * 64) {
     const int h = idx / d, i = idx - h * d;
     float M = -INFINITY;
-    for (int w = 0; w < MPK_NW; ++w) M = fmaxf(M, wm[w * ATT_MAXG + h]);
+    for (int g = 0; g < NG; ++g) M = fmaxf(M, wm[g * ATT_MAXG + h]);
     float L = 0.f, A = 0.f;
-    for (int w = 0; w < MPK_NW; ++w) {
-      const float mw = wm[w * ATT_MAXG + h];
-      const float cw = mw == -INFINITY ? 0.f : expf(mw - M);
-      L = fmaf(wl[w * ATT_MAXG + h], cw, L);
-      A = fmaf(wacc[(w * ATT_MAXG + h) * 128 + i], cw, A);
+    for (int g = 0; g < NG; ++g) {
+      const float mg = wm[g * ATT_MAXG + h];
+      const float cg = mg == -INFINITY ? 0.f : expf(mg - M);
+      L = fmaf(wl[g * ATT_MAXG + h], cg, L);
+      A = fmaf(wacc[(g * ATT_MAXG + h) * d + i], cg, A);
     }
     if (na == 1) {
       put_out(D, o_base + idx, A / L, st);  // the whole context in one split
@@ -1207,7 +1232,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   float M = mine_o ? outs[h * stride] : 0.f;
   float L = mine_o ? outs[h * stride + 1] : 0.f;
   float O = mine_o ? outs[h * stride + 2 + i] : 0.f;
-  const int chunk = (Lay<1>::XS - (int)((char*)gath - (smem + LDS_X))) / 4 / (G * stride);
+  const int chunk = (Lay<1>::TOTAL - (int)((char*)gath - smem)) / 4 / (G * stride);
   for (int c0 = 0; c0 < na - 1; c0 += chunk) {
     const int nc = min(chunk, na - 1 - c0);
     const int rc =
