@@ -1028,7 +1028,9 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   uint16_t* vc = D.vc + ((int64_t)(r * D.nkv + j) * D.S) * d;
   const int dim0 = (lane % LP) * 8;
   const int pg = lane / LP;
-  const float scale = 1.0f / sqrtf((float)d);
+  // scores are kept in base-2 units, s * log2(e) / sqrt(d): every
+  // exponential below is one exp2
+  const float scale = 1.4426950408889634f / sqrtf((float)d);
 
   SoftState sm;
 #pragma unroll
@@ -1142,35 +1144,50 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     const int step = MPK_NW * PPR * ATT_ROUNDS;
     for (int base = lo; base < hi; base += step) {
       if (base != lo) load_rounds(base);
+      // this round's ATT_ROUNDS positions per lane group are folded into the
+      // running (m, l, acc) together: one rescale per head per base step
+      float kf[ATT_ROUNDS][8], vf[ATT_ROUNDS][8];
+      bool valid[ATT_ROUNDS];
 #pragma unroll
       for (int q = 0; q < ATT_ROUNDS; ++q) {
         const int t = base + (wave + MPK_NW * q) * PPR + pg;
-        const bool valid = t < hi;
-        float kf[8], vf[8];
+        valid[q] = t < hi;
         if (t == p) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kf[e] = kv[dim0 + e], vf[e] = kv[d + dim0 + e];
+          for (int e = 0; e < 8; ++e) kf[q][e] = kv[dim0 + e], vf[q][e] = kv[d + dim0 + e];
         } else {
-          unpack8(kr[q], kf);
-          unpack8(vr[q], vf);
+          unpack8(kr[q], kf[q]);
+          unpack8(vr[q], vf[q]);
         }
+      }
 #pragma unroll
-        for (int h = 0; h < ATT_MAXG; ++h) {
-          if (h < G) {
+      for (int h = 0; h < ATT_MAXG; ++h) {
+        if (h < G) {
+          float sc[ATT_ROUNDS];
+          float M = sm.m[h];
+#pragma unroll
+          for (int q = 0; q < ATT_ROUNDS; ++q) {
             float part = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) part = fmaf(qv[h][e], kf[e], part);
-            part = group_sum(part, LP);
-            if (valid) {
-              const float sc = part * scale;
-              const float M = fmaxf(sm.m[h], sc);
-              const float co = sm.m[h] == -INFINITY ? 0.f : expf(sm.m[h] - M);
-              const float cn = expf(sc - M);
-              sm.l[h] = sm.l[h] * co + cn;
+            for (int e = 0; e < 8; ++e) part = fmaf(qv[h][e], kf[q][e], part);
+            part = group_sum(part, LP);  // all lanes of a group share valid[q]
+            sc[q] = valid[q] ? part * scale : -INFINITY;
+            M = fmaxf(M, sc[q]);
+          }
+          if (M != -INFINITY) {
+            const float co = sm.m[h] == -INFINITY ? 0.f : exp2f(sm.m[h] - M);
+            float L = sm.l[h] * co;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) sm.acc[h][e] = sm.acc[h][e] * co + cn * vf[e];
-              sm.m[h] = M;
+            for (int e = 0; e < 8; ++e) sm.acc[h][e] *= co;
+#pragma unroll
+            for (int q = 0; q < ATT_ROUNDS; ++q) {
+              const float w = sc[q] == -INFINITY ? 0.f : exp2f(sc[q] - M);
+              L += w;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) sm.acc[h][e] = fmaf(w, vf[q][e], sm.acc[h][e]);
             }
+            sm.l[h] = L;
+            sm.m[h] = M;
           }
         }
       }
@@ -1192,20 +1209,40 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     }
   }
   __syncthreads();
-  // ---- merge the wavefronts: this split's (m, l, acc) per head ----
+  // ---- merge the position groups: this split's (m, l, acc) per head ----
+  // wave h (< G) turns the groups' maxima into per-group weights once
+  float* hML = reinterpret_cast<float*>(smem + LDS_RED);  // [G][2]: M, L per head
+  if (!sched && wave < G) {
+    const int h = wave;
+    float mg = -INFINITY, lg = 0.f;
+    float M = -INFINITY;
+    for (int g0 = 0; g0 < NG; g0 += 64) {
+      const int g = g0 + lane;
+      M = fmaxf(M, g < NG ? wm[g * ATT_MAXG + h] : -INFINITY);
+    }
+    M = wave_max(M);
+    float L = 0.f;
+    for (int g0 = 0; g0 < NG; g0 += 64) {
+      const int g = g0 + lane;
+      if (g < NG) {
+        mg = wm[g * ATT_MAXG + h];
+        lg = wl[g * ATT_MAXG + h];
+      }
+      const float cg = g < NG && mg != -INFINITY ? exp2f(mg - M) : 0.f;
+      L += lg * cg;
+      if (g < NG) wm[g * ATT_MAXG + h] = cg;  // the group's weight replaces its maximum
+    }
+    L = wave_sum(L);
+    if (lane == 0) hML[2 * h] = M, hML[2 * h + 1] = L;
+  }
+  __syncthreads();
   const int stride = d + 2;
   const int64_t o_base = (int64_t)r * D.nq * d + (int64_t)j * G * d;
   for (int idx = tid; idx < G * d && !sched; idx += MPK_NW * 64) {
     const int h = idx / d, i = idx - h * d;
-    float M = -INFINITY;
-    for (int g = 0; g < NG; ++g) M = fmaxf(M, wm[g * ATT_MAXG + h]);
-    float L = 0.f, A = 0.f;
-    for (int g = 0; g < NG; ++g) {
-      const float mg = wm[g * ATT_MAXG + h];
-      const float cg = mg == -INFINITY ? 0.f : expf(mg - M);
-      L = fmaf(wl[g * ATT_MAXG + h], cg, L);
-      A = fmaf(wacc[(g * ATT_MAXG + h) * d + i], cg, A);
-    }
+    float A = 0.f;
+    for (int g = 0; g < NG; ++g) A = fmaf(wacc[(g * ATT_MAXG + h) * d + i], wm[g * ATT_MAXG + h], A);
+    const float M = hML[2 * h], L = hML[2 * h + 1];
     if (na == 1) {
       put_out(D, o_base + idx, A / L, st);  // the whole context in one split
     } else {
@@ -1245,8 +1282,8 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
         const float ac = __uint_as_float(gath[(cc * G + h) * stride + 2 + i]);
         if (lc > 0.f) {
           const float Mn = fmaxf(M, mc);
-          const float ca = M == -INFINITY ? 0.f : expf(M - Mn);
-          const float cb = expf(mc - Mn);
+          const float ca = M == -INFINITY ? 0.f : exp2f(M - Mn);
+          const float cb = exp2f(mc - Mn);
           L = L * ca + lc * cb;
           O = O * ca + ac * cb;
           M = Mn;
