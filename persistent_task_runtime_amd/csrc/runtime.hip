@@ -144,11 +144,20 @@ DEV uint32_t hwreg_xcc_id() {
   return v;
 }
 
+// LDS pointer from an LDS byte address (no generic-pointer conversion)
+DEV lptr_t lds_ptr(uint32_t a) { return (lptr_t)(uintptr_t)a; }
+
 // LDS traffic inside the weight stream is written in asm, each block waiting
 // for its own reads (with a memory clobber): it pins each unit's x reads and
 // FMAs between the ring's refills, which keeps the compiler from reordering
 // the stream into a shape whose waits drain the whole ring.
 DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lptr_t)(void*)p; }
+
+DEV u32x4 lds_read_u32x4(uint32_t a) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
 
 // Two float4 at byte address a and a + 1024.
 DEV void lds_read_2f4(uint32_t a, f32x4& x0, f32x4& x1) {
@@ -552,12 +561,58 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
   float ss[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) ss[b] = 0.f;
-  // x element e = b * K + k; thread tid takes e = base + tid + 512 j.  Raw
-  // values land in LDS as they arrive; the RMS sums and the gain are applied
-  // afterwards in a fixed order (deterministic).
+  // x element e = b * K + k.  Raw values land in LDS as they arrive; the
+  // RMS sums and the gain are applied afterwards in a fixed order
+  // (deterministic).
   const int NE = NB * K;
   const bool worker = tid < MPK_NW * 64;
-  for (int base = 0; base < NE; base += XCH * MPK_NW * 64) {
+  // Stamped x words that fit the free LDS beyond the residual rows come by
+  // global->LDS DMA, 1 KB chunks (128 words) per wavefront instruction:
+  // every chunk of x is in flight at once and no register holds the words.
+  // A chunk with a stale word is fetched again in the next round.
+  const int land = Lay<NB>::RES + LDS_RES_BYTES;
+  const int nchunk = (NE + 127) >> 7;
+  const bool dma = D.xll && land + nchunk * 1024 <= Lay<NB>::TOTAL && nchunk <= 32 * MPK_NW;
+  if (dma) {
+    const int lane = tid & 63;
+    const uint32_t lb = lds_addr(smem);
+    uint32_t need = 0;  // chunks c = wave + 8 i of this wavefront, bit i
+    if (worker)
+      for (int i = 0; wave + MPK_NW * i < nchunk; ++i) need |= 1u << i;
+    need = __builtin_amdgcn_readfirstlane(need);
+    for (;;) {
+      for (uint32_t m = need; m; m &= m - 1) {
+        const int c = wave + MPK_NW * __builtin_ctz(m);
+        const int e = c * 128 + lane * 2;
+        const uint64_t* src = D.xll + (e < NE ? e : 0);  // lanes past the end re-read word 0
+        __builtin_amdgcn_global_load_lds((gptr_t)(const void*)src, lds_ptr(lb + land + c * 1024), 16, 0,
+                                         16 /* sc1: device scope */);
+      }
+      uint64_t wr = 0;
+      if (need_r) wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
+      vm_drain_known();
+      for (uint32_t m = need; m; m &= m - 1) {
+        const int c = wave + MPK_NW * __builtin_ctz(m);
+        const int e = c * 128 + lane * 2;
+        const u32x4 w = lds_read_u32x4(lb + land + c * 1024 + lane * 16);
+        const bool ok = e >= NE || ((w.y == st) && (w.w == st));
+        if (__ballot(!ok) == 0) {
+          need &= ~(1u << __builtin_ctz(m));
+          if (e < NE) {
+            const int b = e / K, k = e - b * K;  // K is even: e, e + 1 share b
+            *reinterpret_cast<float2*>(xs + b * Kpad + xperm(k)) = float2{__uint_as_float(w.x), __uint_as_float(w.z)};
+          }
+        }
+      }
+      need = __builtin_amdgcn_readfirstlane(need);
+      if (need_r && ll_ok(wr, st)) rv = ll_f(wr), need_r = false;
+      const int rc = wait_round(P, Wt, need != 0 || need_r, s, task_id, smem, tid);
+      if (rc < 0) return rc;
+      if (rc == 0) break;
+    }
+  }
+  // otherwise, per thread: e = base + tid + 512 j
+  for (int base = 0; base < (dma ? 0 : NE); base += XCH * MPK_NW * 64) {
     uint32_t need = 0;
 #pragma unroll
     for (int j = 0; j < XCH; ++j)
