@@ -90,6 +90,7 @@ DEV void gst16(uint16_t* p, uint16_t v) { *(gu16*)(void*)p = v; }
 DEV float gld(const float* p) { return *(const gfloat*)(const void*)p; }
 DEV int gldi(const int32_t* p) { return *(const gi32*)(const void*)p; }
 DEV uint16_t gld16(const uint16_t* p) { return *(const gu16*)(const void*)p; }
+DEV uint32_t gld32(const uint32_t* p) { return *(const __attribute__((address_space(1))) uint32_t*)(const void*)p; }
 template <typename T>
 DEV T gldv(const void* p) { return *(const T __attribute__((address_space(1)))*)p; }
 
@@ -158,6 +159,8 @@ DEV u32x4 lds_read_u32x4(uint32_t a) {
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
   return v;
 }
+DEV void lds_write_u32x4(uint32_t a, u32x4 v) { asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory"); }
+DEV void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Two float4 at byte address a and a + 1024.
 DEV void lds_read_2f4(uint32_t a, f32x4& x0, f32x4& x1) {
@@ -188,6 +191,13 @@ DEV void vm_wait() {
 // all of a wavefront's loads return in issue order; the code does not rely
 // on that across kinds where the fence costs nothing.
 DEV void vm_drain_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt 0, expcnt 7, lgkmcnt 15
+// The same with N vector-memory operations left in flight (the N issued
+// last: loads complete in issue order).
+template <int N>
+DEV void vm_wait_known() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 
 // Device-scope ("sc1") accesses.  Every value one task hands to another task
@@ -224,7 +234,7 @@ DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // ---------------------------------------------------------------------------
 #define LDS_CTL 0
 #define LDS_RED 256                      // [16][8] floats: per-wave partials
-#define LDS_INV (LDS_RED + 16 * 8 * 4)   // [8] floats
+#define LDS_INV (LDS_RED + 16 * 8 * 4)   // [8] floats (spare)
 #define LDS_BEST (LDS_INV + 64)          // [8 waves][8] (float) + [8][8] (int)
 #define LDS_POS (LDS_BEST + 512)         // [8] int: position of request r in the current iteration
 #define LDS_TOK (LDS_POS + 32)           // [8] int: token of request r in the current iteration
@@ -519,35 +529,48 @@ DEV void cursor_step(Cursor& C, int wave) {
 
 // Stage the GEMV input into LDS: x (gathered from its producers' stamped
 // words, an embedding row, or a plain input tensor), times the RMSNorm gain
-// when the operator normalises, 1 / rms per request, and the tile's residual
-// rows.  Every thread of the workgroup takes part.  Returns -1 on stop.
-#define XCH 8  // stamped x words per thread per gather pass
-template <int NB>
-DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, int s, int task_id) {
+// when the operator normalises, and the tile's residual rows; inv receives
+// 1 / rms per request (1 without a norm) in every thread.  Every thread of
+// the workgroup takes part.  issue_ring() issues the calling wavefront's
+// first weight loads: it is called once, as early as the input wait allows.
+// Returns -1 on stop.
+#define XCH 8    // stamped x words per thread per gather pass (register path)
+#define XGMAX 4  // chunks per wavefront whose gains and values stay in registers (DMA path)
+template <int NB, class Ring>
+DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, int s, int task_id,
+                     float (&inv)[NB], Ring&& issue_ring) {
   float* xs = reinterpret_cast<float*>(smem + LDS_X);
   float* res = reinterpret_cast<float*>(smem + Lay<NB>::RES);
   float* red = reinterpret_cast<float*>(smem + LDS_RED);
-  float* inv = reinterpret_cast<float*>(smem + LDS_INV);
   const int K = D.K;
   const int Kpad = ((K + 511) / 512) * 512;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const bool worker = tid < MPK_NW * 64;
   const uint32_t st = stamp_of(P, s);
   Waiter Wt = waiter_start();
   if (D.x_embed || D.res_embed) {
     const int rc = resolve_tokens(P, smem, tid, s, task_id, Wt);
     if (rc) return rc;
   }
-  // RMSNorm gains of this thread's columns (k = tid + 512 j), loaded before
-  // the inputs are awaited when K fits one gather pass
-  const bool gains_early = K <= XCH * MPK_NW * 64;
-  float gk[XCH];
-#pragma unroll
-  for (int j = 0; j < XCH; ++j) {
-    const int k = tid + j * MPK_NW * 64;
-    gk[j] = D.has_norm && gains_early && tid < MPK_NW * 64 && k < K ? bf16f(gld16(D.gain + k)) : 0.f;
-  }
-  // residual element of this thread: request rb, row rrow of the tile
+  const int NE = NB * K;
+  // Stamped x words that fit the free LDS beyond the residual rows come by
+  // global->LDS DMA, 1 KB chunks (128 words, 2 per lane) per wavefront
+  // instruction: wavefront w owns chunks w + 8 i, all in flight at once, and
+  // a chunk with a stale word is fetched again in the next round.  The first
+  // round is issued ahead of the weight loads, so it is not queued behind
+  // them.  Each wavefront applies the gain to its chunks as they arrive and
+  // publishes its RMS partial sums once all of them are in; the sums run in
+  // a fixed order whatever the arrival order (deterministic).
+  const int land = Lay<NB>::RES + LDS_RES_BYTES;
+  const int nchunk = (NE + 127) >> 7;
   const int nres = D.epi == MPK_EPI_RESID ? NB * T.nrows : 0;
+  const bool dma = D.xll && (K & 127) == 0 && land + nchunk * 1024 <= Lay<NB>::TOTAL && nchunk <= 32 * MPK_NW &&
+                   (!D.has_norm || nchunk <= XGMAX * MPK_NW);
+  // zero padding columns of x (K not a multiple of 512); no gather writes them
+  for (int i = K + (worker ? tid : Kpad); i < Kpad; i += MPK_NW * 64)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xs[b * Kpad + xperm(i)] = 0.f;
+  // residual element of this thread: request rb, row rrow of the tile
   bool need_r = false;
   float rv = 0.f;
   int rb = 0, rrow = 0;
@@ -558,163 +581,215 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
     else if (D.rll) need_r = true;
     else rv = gld(D.resid + (int64_t)rb * D.n_out + rrow);
   }
-  float ss[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) ss[b] = 0.f;
-  // x element e = b * K + k.  Raw values land in LDS as they arrive; the
-  // RMS sums and the gain are applied afterwards in a fixed order
-  // (deterministic).
-  const int NE = NB * K;
-  const bool worker = tid < MPK_NW * 64;
-  // Stamped x words that fit the free LDS beyond the residual rows come by
-  // global->LDS DMA, 1 KB chunks (128 words) per wavefront instruction:
-  // every chunk of x is in flight at once and no register holds the words.
-  // A chunk with a stale word is fetched again in the next round.
-  const int land = Lay<NB>::RES + LDS_RES_BYTES;
-  const int nchunk = (NE + 127) >> 7;
-  const bool dma = D.xll && land + nchunk * 1024 <= Lay<NB>::TOTAL && nchunk <= 32 * MPK_NW;
   if (dma) {
-    const int lane = tid & 63;
     const uint32_t lb = lds_addr(smem);
     uint32_t need = 0;  // chunks c = wave + 8 i of this wavefront, bit i
     if (worker)
       for (int i = 0; wave + MPK_NW * i < nchunk; ++i) need |= 1u << i;
     need = __builtin_amdgcn_readfirstlane(need);
+    const uint32_t mine = need;
+    // gains of this lane's two columns in chunks i < XGMAX (packed bf16 pair)
+    uint32_t gp[XGMAX];
+    float2 xv[XGMAX];
+#pragma unroll
+    for (int i = 0; i < XGMAX; ++i) {
+      const int c = wave + MPK_NW * i;
+      const int k = (c * 128) % K + lane * 2;
+      gp[i] = D.has_norm && ((mine >> i) & 1u) ? gld32(reinterpret_cast<const uint32_t*>(D.gain + k)) : 0u;
+      xv[i] = float2{0.f, 0.f};
+    }
+    bool first = true, published = false;
     for (;;) {
+      if (first) {
+        // stale landing data must not pass the stamp check before the first
+        // round's DMA has landed: clear the landing stamps first
+        for (uint32_t m = need; m; m &= m - 1)
+          lds_write_u32x4(lb + land + (wave + MPK_NW * __builtin_ctz(m)) * 1024 + lane * 16, u32x4{0u, 0u, 0u, 0u});
+        lds_wait();
+      }
       for (uint32_t m = need; m; m &= m - 1) {
         const int c = wave + MPK_NW * __builtin_ctz(m);
-        const int e = c * 128 + lane * 2;
-        const uint64_t* src = D.xll + (e < NE ? e : 0);  // lanes past the end re-read word 0
-        __builtin_amdgcn_global_load_lds((gptr_t)(const void*)src, lds_ptr(lb + land + c * 1024), 16, 0,
-                                         16 /* sc1: device scope */);
+        __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.xll + c * 128 + lane * 2), lds_ptr(lb + land + c * 1024),
+                                         16, 0, 16 /* sc1: device scope */);
       }
       uint64_t wr = 0;
       if (need_r) wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
-      vm_drain_known();
+      if (first) {
+        // the weights go out behind this round's words; wait for the words
+        // only (loads complete in issue order)
+        issue_ring();
+        if (worker) vm_wait_known<MPK_RING>();
+      } else if (worker) {
+        vm_drain_known();
+      }
       for (uint32_t m = need; m; m &= m - 1) {
-        const int c = wave + MPK_NW * __builtin_ctz(m);
-        const int e = c * 128 + lane * 2;
+        const int i = __builtin_ctz(m), c = wave + MPK_NW * i;
         const u32x4 w = lds_read_u32x4(lb + land + c * 1024 + lane * 16);
-        const bool ok = e >= NE || ((w.y == st) && (w.w == st));
-        if (__ballot(!ok) == 0) {
-          need &= ~(1u << __builtin_ctz(m));
-          if (e < NE) {
-            const int b = e / K, k = e - b * K;  // K is even: e, e + 1 share b
-            *reinterpret_cast<float2*>(xs + b * Kpad + xperm(k)) = float2{__uint_as_float(w.x), __uint_as_float(w.z)};
+        if (__ballot(w.y != st || w.w != st) == 0) {
+          need &= ~(1u << i);
+          const int e = c * 128 + lane * 2;
+          const int b = e / K, k = e - b * K;
+          float2 x{__uint_as_float(w.x), __uint_as_float(w.z)};
+          if (D.has_norm) {
+            // i < XGMAX here (checked with dma)
+#pragma unroll
+            for (int j = 0; j < XGMAX; ++j)
+              if (j == i) xv[j] = x, x = float2{x.x * bf16lo(gp[j]), x.y * bf16hi(gp[j])};
           }
+          *reinterpret_cast<float2*>(xs + b * Kpad + xperm(k)) = x;
         }
       }
       need = __builtin_amdgcn_readfirstlane(need);
-      if (need_r && ll_ok(wr, st)) rv = ll_f(wr), need_r = false;
+      if (D.has_norm && worker && need == 0 && !published) {
+        published = true;
+        // this wavefront's chunks are all in: its RMS partials, in chunk order
+        float ss[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+#pragma unroll
+        for (int i = 0; i < XGMAX; ++i) {
+          if ((mine >> i) & 1u) {
+            const int b = (wave + MPK_NW * i) * 128 / K;
+            const float q = fmaf(xv[i].x, xv[i].x, xv[i].y * xv[i].y);
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) ss[bb] += bb == b ? q : 0.f;
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float t = wave_sum(ss[b]);
+          if (lane == 0) red[wave * 8 + b] = t;
+        }
+      }
+      if (need_r && ll_ok(wr, st)) res[tid] = ll_f(wr), need_r = false;
+      if (first && tid < nres && !D.rll) res[tid] = rv;
+      first = false;
       const int rc = wait_round(P, Wt, need != 0 || need_r, s, task_id, smem, tid);
       if (rc < 0) return rc;
       if (rc == 0) break;
     }
-  }
-  // otherwise, per thread: e = base + tid + 512 j
-  for (int base = 0; base < (dma ? 0 : NE); base += XCH * MPK_NW * 64) {
-    uint32_t need = 0;
+  } else {
+    issue_ring();
+    // RMSNorm gains of this thread's columns (k = tid + 512 j), loaded before
+    // the inputs are awaited when K fits one gather pass
+    const bool gains_early = K <= XCH * MPK_NW * 64;
+    float gk[XCH];
 #pragma unroll
-    for (int j = 0; j < XCH; ++j)
-      if (worker && base + tid + j * MPK_NW * 64 < NE) need |= 1u << j;
-    if (D.xll) {
-      for (;;) {
-        uint64_t v[XCH];
+    for (int j = 0; j < XCH; ++j) {
+      const int k = tid + j * MPK_NW * 64;
+      gk[j] = D.has_norm && gains_early && worker && k < K ? bf16f(gld16(D.gain + k)) : 0.f;
+    }
+    float ss[NB];
 #pragma unroll
-        for (int j = 0; j < XCH; ++j)
-          if ((need >> j) & 1u) v[j] = ld_ll(D.xll + base + tid + j * MPK_NW * 64);
-        uint64_t wr = 0;
-        if (need_r) wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
-        // (request, column) of element j, stepped from j = 0 without divisions
-        int eb = (base + tid) / K, ek = base + tid - eb * K;
+    for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+    // x element e = b * K + k, per thread e = base + tid + 512 j.  Raw values
+    // land in LDS as they arrive; the RMS sums and the gain are applied
+    // afterwards in a fixed order (deterministic).
+    for (int base = 0; base < NE; base += XCH * MPK_NW * 64) {
+      uint32_t need = 0;
+#pragma unroll
+      for (int j = 0; j < XCH; ++j)
+        if (worker && base + tid + j * MPK_NW * 64 < NE) need |= 1u << j;
+      if (D.xll) {
+        for (;;) {
+          uint64_t v[XCH];
+#pragma unroll
+          for (int j = 0; j < XCH; ++j)
+            if ((need >> j) & 1u) v[j] = ld_ll(D.xll + base + tid + j * MPK_NW * 64);
+          uint64_t wr = 0;
+          if (need_r) wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
+          // (request, column) of element j, stepped from j = 0 without divisions
+          int eb = (base + tid) / K, ek = base + tid - eb * K;
+#pragma unroll
+          for (int j = 0; j < XCH; ++j) {
+            if (((need >> j) & 1u) && ll_ok(v[j], st)) {
+              xs[eb * Kpad + xperm(ek)] = ll_f(v[j]);
+              need &= ~(1u << j);
+            }
+            ek += MPK_NW * 64;
+            while (ek >= K) ek -= K, ++eb;
+          }
+          if (need_r && ll_ok(wr, st)) rv = ll_f(wr), need_r = false;
+          const int rc = wait_round(P, Wt, need != 0 || need_r, s, task_id, smem, tid);
+          if (rc < 0) return rc;
+          if (rc == 0) break;
+        }
+      } else {
 #pragma unroll
         for (int j = 0; j < XCH; ++j) {
-          if (((need >> j) & 1u) && ll_ok(v[j], st)) {
-            xs[eb * Kpad + xperm(ek)] = ll_f(v[j]);
-            need &= ~(1u << j);
+          if ((need >> j) & 1u) {
+            const int e = base + tid + j * MPK_NW * 64;
+            const int b = e / K, k = e - b * K;
+            xs[b * Kpad + xperm(k)] =
+                D.x_embed ? bf16f(gld16(D.E + (int64_t)cur_token_v(smem, b) * K + k)) : gld(D.x + e);
           }
-          ek += MPK_NW * 64;
-          while (ek >= K) ek -= K, ++eb;
         }
-        if (need_r && ll_ok(wr, st)) rv = ll_f(wr), need_r = false;
-        const int rc = wait_round(P, Wt, need != 0 || need_r, s, task_id, smem, tid);
+      }
+    }
+    // the residual element may have been a plain load issued before the
+    // device-scope polls: see vm_drain_known
+    vm_drain_known();
+    // RMS sums and gain, each thread over its own columns in a fixed order
+    if (D.has_norm && gains_early) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float xr[XCH];
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+          const int k = tid + j * MPK_NW * 64;
+          xr[j] = worker && k < K ? xs[b * Kpad + xperm(k)] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+          const int k = tid + j * MPK_NW * 64;
+          ss[b] = fmaf(xr[j], xr[j], ss[b]);
+          if (worker && k < K) xs[b * Kpad + xperm(k)] = xr[j] * gk[j];
+        }
+      }
+    } else if (D.has_norm) {
+      for (int e = worker ? tid : NE; e < NE; e += MPK_NW * 64) {
+        const int b = e / K, k = e - b * K;
+        float* px = xs + b * Kpad + xperm(k);
+        const float x = *px;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) ss[bb] = fmaf(bb == b ? x : 0.f, x, ss[bb]);
+        *px = x * bf16f(gld16(D.gain + k));
+      }
+    }
+    // a residual not gathered with x (x did not come from stamped words)
+    if (D.rll && !D.xll) {
+      for (;;) {
+        if (need_r) {
+          const uint64_t wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
+          if (ll_ok(wr, st)) rv = ll_f(wr), need_r = false;
+        }
+        const int rc = wait_round(P, Wt, need_r, s, task_id, smem, tid);
         if (rc < 0) return rc;
         if (rc == 0) break;
       }
-    } else {
+    }
+    if (tid < nres) res[tid] = rv;
+    if (D.has_norm && worker) {
 #pragma unroll
-      for (int j = 0; j < XCH; ++j) {
-        if ((need >> j) & 1u) {
-          const int e = base + tid + j * MPK_NW * 64;
-          const int b = e / K, k = e - b * K;
-          xs[b * Kpad + xperm(k)] =
-              D.x_embed ? bf16f(gld16(D.E + (int64_t)cur_token_v(smem, b) * K + k)) : gld(D.x + e);
-        }
+      for (int b = 0; b < NB; ++b) {
+        const float t = wave_sum(ss[b]);
+        if (lane == 0) red[wave * 8 + b] = t;
       }
     }
+    __syncthreads();
   }
-  // the residual element may have been a plain load issued before the
-  // device-scope polls: see vm_drain_known
-  vm_drain_known();
-  // RMS sums and gain, each thread over its own columns in a fixed order
-  if (D.has_norm && gains_early) {
+  // every wavefront's partials are in (the last barrier above, or the final
+  // wait round): each thread forms 1 / rms itself, in the same order
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int j = 0; j < XCH; ++j) {
-        const int k = tid + j * MPK_NW * 64;
-        if (worker && k < K) {
-          float* px = xs + b * Kpad + xperm(k);
-          const float x = *px;
-          ss[b] = fmaf(x, x, ss[b]);
-          *px = x * gk[j];
-        }
-      }
-  } else if (D.has_norm) {
-    for (int e = worker ? tid : NE; e < NE; e += MPK_NW * 64) {
-      const int b = e / K, k = e - b * K;
-      float* px = xs + b * Kpad + xperm(k);
-      const float x = *px;
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) ss[bb] = fmaf(bb == b ? x : 0.f, x, ss[bb]);
-      *px = x * bf16f(gld16(D.gain + k));
-    }
-  }
-  // a residual not gathered with x (x did not come from stamped words)
-  if (D.rll && !D.xll) {
-    for (;;) {
-      if (need_r) {
-        const uint64_t wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
-        if (ll_ok(wr, st)) rv = ll_f(wr), need_r = false;
-      }
-      const int rc = wait_round(P, Wt, need_r, s, task_id, smem, tid);
-      if (rc < 0) return rc;
-      if (rc == 0) break;
-    }
-  }
-  // zero padding columns of x (K not a multiple of 512)
-  for (int i = K + (worker ? tid : Kpad); i < Kpad; i += MPK_NW * 64)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) xs[b * Kpad + xperm(i)] = 0.f;
-  if (tid < nres) res[tid] = rv;
-  if (D.has_norm && worker) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float t = wave_sum(ss[b]);
-      if ((tid & 63) == 0) red[wave * 8 + b] = t;
-    }
-  }
-  __syncthreads();
-  if (tid < NB) {
+  for (int b = 0; b < NB; ++b) {
     if (D.has_norm) {
       float t = 0.f;
-      for (int w = 0; w < MPK_NW; ++w) t += red[w * 8 + tid];
-      inv[tid] = 1.0f / sqrtf(t / (float)K + P.rms_eps);
+      for (int w = 0; w < MPK_NW; ++w) t += red[w * 8 + b];
+      inv[b] = 1.0f / sqrtf(t / (float)K + P.rms_eps);
     } else {
-      inv[tid] = 1.0f;
+      inv[b] = 1.0f;
     }
   }
-  __syncthreads();
   return 0;
 }
 
@@ -874,23 +949,23 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
     cursor_init(I, D, T, wave);
     n = I.n;
     npad = uni(padded_units(n));
-#pragma unroll
-    for (int j = 0; j < MPK_RING; ++j) {
-      b[j] = load_unit(I, lane);
-      cursor_step(I, wave);
-    }
   }
+  float inv[NB];
   {
-    const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id);
+    const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id, inv, [&]() {
+      if (!sched) {
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j) {
+          b[j] = load_unit(I, lane);
+          cursor_step(I, wave);
+        }
+      }
+    });
     if (rc) return rc;
   }
   mark_ready(P, s, task_id, tid);
   const uint32_t st = stamp_of(P, s);
   const uint32_t lb = lds_addr(smem);  // LDS byte address of the workgroup's area
-  const float* inv_lds = reinterpret_cast<const float*>(smem + LDS_INV);
-  float inv[NB];
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) inv[bb] = inv_lds[bb];
   const int Kpad = ((D.K + 511) / 512) * 512;
   GemvState<NB> G;
 #pragma unroll
