@@ -463,7 +463,7 @@ struct Cursor {
   const uint16_t* W2;
   const uint16_t* row;  // current row (lane offset not included)
   int N0, N1, K, pairs, row0, a, upr;
-  int kk, rr, u;  // assignment unit, row within it, unit within row
+  int au, rr, u;  // assignment unit (a rows) of the tile, row within it, unit within row
   int i, n;       // next unit index, real units
 };
 
@@ -473,7 +473,7 @@ DEV void cursor_row(Cursor& C, int wave) {
   const uint16_t* w0 = unip(C.W0);
   const uint16_t* w1 = unip(C.W1);
   const uint16_t* w2 = unip(C.W2);
-  const int vrow = C.row0 + (wave + MPK_NW * C.kk) * C.a + C.rr;
+  const int vrow = C.row0 + C.au * C.a + C.rr;
   const uint16_t* base;
   int r;
   if (C.pairs) {
@@ -498,7 +498,7 @@ DEV void cursor_init(Cursor& C, cop& D, ctask& T, int wave) {
   C.row0 = uni(T.row0);
   C.a = C.pairs ? 2 : 1;
   C.upr = uni(units_per_row(D));
-  C.kk = 0, C.rr = 0, C.u = 0, C.i = 0;
+  C.au = wave, C.rr = 0, C.u = 0, C.i = 0;
   C.n = uni(wave_units(D, T, wave));
   if (C.n > 0) cursor_row(C, wave);
   else C.row = unip(C.W0);  // padding only: re-read the first unit of W0
@@ -512,6 +512,14 @@ DEV gptr_t cursor_addr(const Cursor& C, int lane) {
   return (gptr_t)(const void*)(C.row + col);
 }
 
+// Point the cursor at unit u of row rr of assignment unit au; the caller
+// bounds the walk from there (no padding).
+DEV void cursor_goto(Cursor& C, int au, int rr, int u, int wave) {
+  C.au = au, C.rr = rr, C.u = u;
+  C.i = 0, C.n = 1 << 30;
+  cursor_row(C, wave);
+}
+
 DEV void cursor_step(Cursor& C, int wave) {
   C.i = uni(C.i + 1);
   if (C.i >= C.n) return;  // padding: stay on the last real unit
@@ -521,7 +529,7 @@ DEV void cursor_step(Cursor& C, int wave) {
     C.rr = uni(C.rr + 1);
     if (C.rr == C.a) {
       C.rr = 0;
-      C.kk = uni(C.kk + 1);
+      C.au = uni(C.au + MPK_NW);
     }
     cursor_row(C, wave);
   }
@@ -824,7 +832,7 @@ template <int NB>
 struct GemvState {
   float acc[NB], gate[NB], best_v[NB];
   int best_i[NB];
-  int u, rr, kk;
+  int u, rr, kk;  // unit within the row, row within the assignment unit, static assignment count
 };
 
 template <int NB>
@@ -858,10 +866,10 @@ DEV void unit_fma(const u32x4 w, uint32_t xaddr, int Kpad, float (&acc)[NB]) {
 // stored to memory inside the weight stream: a store pending among the
 // stream's loads would make every wait on them a full drain.
 template <int NB>
-DEV void row_done(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, const float (&inv)[NB], int a, int wave,
+DEV void row_done(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, const float (&inv)[NB], int a, int au,
                   int lane) {
   const int EPI = D.epi;
-  const int lrow = (wave + MPK_NW * G.kk) * a + G.rr;  // row within the tile
+  const int lrow = au * a + G.rr;  // row within the tile
   const int vrow = T.row0 + lrow;
   const uint32_t ob = lb + LDS_OUT;
   const int n_out_tile = D.pairs ? T.nrows / 2 : T.nrows;
@@ -893,29 +901,26 @@ DEV void row_done(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, const float (
   }
 }
 
-// Publish this wavefront's rows of the tile from LDS (stamped output words,
-// the plain output when attached, LM-head logits when requested).
+// Publish the tile's outputs from LDS (stamped output words, the plain
+// output when attached, LM-head logits when requested), every thread of the
+// workgroup taking a share.  Called after a barrier that follows the
+// stream.
 template <int NB>
-DEV void publish_rows(const mpk_kparams& P, cop& D, ctask& T, uint32_t lb, int s, uint32_t st, int wave, int lane) {
-  const int a = D.pairs ? 2 : 1;
-  const int au = T.nrows / a;
-  const int mine = au > wave ? (au - wave + MPK_NW - 1) / MPK_NW : 0;  // assignment units of this wave
-  const int nr = mine * a;                                            // rows of this wave
+DEV void publish_tile(const mpk_kparams& P, cop& D, ctask& T, uint32_t lb, int s, uint32_t st, int tid) {
   const uint32_t ob = lb + LDS_OUT;
+  if (D.epi == MPK_EPI_ARGMAX) {
+    if (D.logits && s < D.logits_iters)
+      for (int i = tid; i < NB * T.nrows; i += MPK_THREADS) {
+        const int b = i / T.nrows, lrow = i - b * T.nrows;
+        gst(D.logits + ((int64_t)s * P.B + b) * D.N0 + T.row0 + lrow, lds_read_f32(lds_logits(lb, NB, D, T, b, lrow)));
+      }
+    return;
+  }
   const int n_out_tile = D.pairs ? T.nrows / 2 : T.nrows;
-  for (int i = lane; i < NB * nr; i += 64) {
-    const int b = i / nr, q = i - b * nr;
-    const int kk = q / a, rr = q - kk * a;
-    const int lrow = (wave + MPK_NW * kk) * a + rr;
-    const int vrow = T.row0 + lrow;
-    if (D.epi == MPK_EPI_ARGMAX) {
-      if (D.logits && s < D.logits_iters)
-        gst(D.logits + ((int64_t)s * P.B + b) * D.N0 + vrow, lds_read_f32(lds_logits(lb, NB, D, T, b, lrow)));
-    } else if (D.epi != MPK_EPI_SILU || rr == 1) {
-      const int ol = D.pairs ? lrow >> 1 : lrow;
-      const int orow = D.pairs ? vrow >> 1 : vrow;
-      put_out(D, (int64_t)b * D.n_out + orow, lds_read_f32(ob + (uint32_t)(b * n_out_tile + ol) * 4u), st);
-    }
+  const int orow0 = D.pairs ? T.row0 / 2 : T.row0;
+  for (int i = tid; i < NB * n_out_tile; i += MPK_THREADS) {
+    const int b = i / n_out_tile, ol = i - b * n_out_tile;
+    put_out(D, (int64_t)b * D.n_out + orow0 + ol, lds_read_f32(ob + (uint32_t)(b * n_out_tile + ol) * 4u), st);
   }
 }
 
@@ -928,7 +933,7 @@ DEV void gemv_consume(ctask& T, cop& D, GemvState<NB>& G, const u32x4 w, int uni
   unit_fma<NB>(w, lb + LDS_X + (uint32_t)(G.u * 512 + lane * 4) * 4u, Kpad, G.acc);
   if (++G.u == upr) {
     G.u = 0;
-    row_done<NB>(D, T, G, lb, inv, a, wave, lane);
+    row_done<NB>(D, T, G, lb, inv, a, wave + MPK_NW * G.kk, lane);
   }
 }
 
@@ -936,9 +941,23 @@ DEV u32x4 load_unit(const Cursor& C, int lane) {
   return __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1)))*)cursor_addr(C, lane));
 }
 
+// Next free assignment unit of the tile (workgroup counter in LDS, reset to
+// MPK_NW at task start: units 0 .. MPK_NW - 1 go to the wavefronts of the
+// same index).
+#define LDS_CLAIM (LDS_CTL + 40 * 4)
+DEV int claim_unit(char* smem, int lane) {
+  int v = 0;
+  if (lane == 0)
+    v = __hip_atomic_fetch_add(reinterpret_cast<int*>(smem + LDS_CLAIM), 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 template <int NB>
 DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, char* smem, int tid, bool sched) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // claims start after the staging's barriers
+  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_CLAIM) = MPK_NW;
   // The ring's first group (units 0..7) is issued before the inputs are
   // awaited: these weights do not depend on them, and the wait is what
   // they hide.
@@ -979,14 +998,30 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
     // complete here, and the compiler knows it: its waits on the ring stay
     // exact
     vm_drain_known();
-    const int ng = npad / MPK_RING;  // group g holds units 8g .. 8g + 7
     if (upr % MPK_RING == 0) {
-      // rows are whole groups of eight units (K a multiple of 4096): the
-      // epilogue runs between groups only, which keeps the register ring's
-      // waits exact inside the unrolled group
+      // Rows are whole groups of eight units (K a multiple of 4096 bf16 per
+      // group): the epilogue runs between groups only, which keeps the
+      // register ring's waits exact inside the unrolled group.  Assignment
+      // units (a rows) are handed out dynamically within the workgroup:
+      // wavefront w starts on unit w and claims the next free one from an
+      // LDS counter when its issue side finishes one, so wavefronts that
+      // stream slower take fewer rows and all end together.
+      const int nau = T.nrows / a;
+      const int gpa = a * upr / MPK_RING;  // groups per assignment unit
       const uint32_t xl = lb + LDS_X + lane * 16;
-      // steady state: consume b[j], refill it with the unit eight places on
-      for (int g = 0; g < ng - 1; ++g) {
+      int au_c = wave, gc = 0;  // the group in the ring: its assignment unit, group within it
+      for (;;) {
+        int au_n = au_c, gn = gc + 1;  // the group to issue next
+        if (gn == gpa) {
+          au_n = claim_unit(smem, lane);
+          gn = 0;
+        }
+        if (au_n >= nau || au_c >= nau) break;
+        {
+          const int q = gn * MPK_RING;  // first unit of the group within the assignment unit
+          const int rr = q / upr;
+          cursor_goto(I, au_n, rr, q - rr * upr, wave);
+        }
         const uint32_t xg = xl + G.u * 2048;
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
@@ -997,22 +1032,25 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
         G.u += MPK_RING;
         if (G.u == upr) {
           G.u = 0;
-          row_done<NB>(D, T, G, lb, inv, a, wave, lane);
+          row_done<NB>(D, T, G, lb, inv, a, au_c, lane);
         }
+        au_c = au_n, gc = gn;
       }
-      // last group
-      const uint32_t xg = xl + G.u * 2048;
+      // last group (none when this wavefront had no assignment unit)
+      if (au_c < nau) {
+        const uint32_t xg = xl + G.u * 2048;
 #pragma unroll
-      for (int j = 0; j < MPK_RING; ++j) unit_fma<NB>(b[j], xg + j * 2048, Kpad, G.acc);
-      if (n > 0) {
+        for (int j = 0; j < MPK_RING; ++j) unit_fma<NB>(b[j], xg + j * 2048, Kpad, G.acc);
         G.u += MPK_RING;
         if (G.u == upr) {
           G.u = 0;
-          row_done<NB>(D, T, G, lb, inv, a, wave, lane);
+          row_done<NB>(D, T, G, lb, inv, a, au_c, lane);
         }
       }
     } else {
-      // generic rows (short K): per-unit bookkeeping, padding skipped
+      // generic rows (short K): static assignment units, per-unit
+      // bookkeeping, padding skipped
+      const int ng = npad / MPK_RING;  // group g holds units 8g .. 8g + 7
       for (int g = 0; g < ng - 1; ++g) {
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
@@ -1026,8 +1064,9 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
       for (int j = 0; j < MPK_RING; ++j)
         gemv_consume<NB>(T, D, G, b[j], g * MPK_RING + j, n, lb, inv, Kpad, upr, a, wave, lane);
     }
-    publish_rows<NB>(P, D, T, lb, s, st, wave, lane);
   }
+  __syncthreads();  // every row of the tile is in LDS
+  publish_tile<NB>(P, D, T, lb, s, st, tid);
   if (D.epi == MPK_EPI_ARGMAX) {
     // tile argmax over the waves (lowest row among equal maxima), published
     // as two stamped words (value, row) per request
