@@ -162,10 +162,12 @@ DEV u32x4 lds_read_u32x4(uint32_t a) {
 DEV void lds_write_u32x4(uint32_t a, u32x4 v) { asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory"); }
 DEV void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Two float4 at byte address a and a + 1024.
+// Two float4 at byte address a and a + 1024.  The outputs are early-clobber:
+// the first read may land before the second has read its address operand, so
+// neither output may share a register with the address.
 DEV void lds_read_2f4(uint32_t a, f32x4& x0, f32x4& x1) {
   asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(x0), "=v"(x1)
+               : "=&v"(x0), "=&v"(x1)
                : "v"(a)
                : "memory");
 }
