@@ -12,6 +12,8 @@ pages give no weights, so weights are seeded random, see ``make_model``):
                   vocab 1024; 39 random prompt ids, 32 greedy tokens.
 * ``one_layer``   one Qwen3-8B-shaped layer, KV cache pre-filled to 512
                   positions with N(0,1) bf16, fp32 input h ~ N(0,1), one step.
+* ``wide1``       one Qwen3-8B-shaped layer with a 16384-id tied embedding /
+                  LM head; 4 random prompt ids, 5 greedy tokens.
 * ``qwen3_8b``    36 layers + tied 151936-row embedding / LM head, batch 1,
                   39 random prompt ids, 512 greedy tokens.
 * ``qwen3_8b_b8`` same model at batch 8, prompt lengths uniform in [16, 512],
@@ -201,6 +203,14 @@ def workload(name: str, seed: int = 0, gains: str = "ones", **over) -> Workload:
         w = Workload("one_layer", sh, 1, n_iter=1, tokens_width=514,
                      prompt_len=np.array([513], np.int32), step0=np.array([512], np.int32),
                      kv_prefill=512, seed=seed, gains=gains)
+    elif name == "wide1":
+        # Qwen3-8B layer and head widths, one layer, a 16384-id vocabulary: every
+        # streaming operator of the full model's kinds at its real width
+        P = 4
+        sh = ModelShape(1, 4096, 32, 8, 128, 12288, 16384)
+        w = Workload("wide1", sh, 1, n_iter=(P - 1) + 5, tokens_width=P + 5,
+                     prompt_len=np.array([P], np.int32), step0=np.zeros(1, np.int32),
+                     seed=seed, gains=gains)
     elif name == "qwen3_8b":
         P = 39
         w = Workload("qwen3_8b", QWEN3_8B, 1, n_iter=(P - 1) + 512, tokens_width=P + 512,

@@ -101,6 +101,34 @@ def test_megakernel_equals_per_op_bitwise(torch_dev):
     a["session"].close(), b["session"].close()
 
 
+def test_real_width_megakernel_equals_per_op_and_oracle(torch_dev):
+    """Real-width operators (a Qwen3-8B layer and a 16384-id head, every
+    streaming operator on the fast whole-group path): several persistent runs
+    and the one-launch-per-operator path give bit-identical activations,
+    logits and tokens, and the logits match the oracle.  Each row is computed
+    by one wavefront with fixed arithmetic, whichever wavefront takes it, so
+    any difference is a race (such a race showed as one wrong row in a few
+    runs out of 24)."""
+    from persistent_task_runtime_amd import runner
+
+    log("real-width: wide1")
+    w = synth.workload("wide1", gains="random")
+    weights = synth.make_model(w.shape, seed=w.seed, gains=w.gains)
+    model = runner.DeviceModel(w.shape, weights=weights)
+    ref = runner.run_workload(w, w.n_iter, want_logits=True, model=model, per_op=True)
+    for rep in range(6):
+        got = runner.run_workload(w, w.n_iter, want_logits=True, model=model)
+        assert np.array_equal(got["tokens"], ref["tokens"]), rep
+        bad = np.nonzero(got["logits"].view(np.uint32) != ref["logits"].view(np.uint32))
+        assert len(bad[0]) == 0, "run %d: %d logits differ, first (iter, req, id) %s" % (
+            rep, len(bad[0]), list(zip(*bad))[:4])
+        got["session"].close()
+    st, ol, oam, omg = oracle_decode(w, w.n_iter, weights)
+    c, k, worst = compare_greedy(w, w.n_iter, ref["logits"], ref["tokens"], ref["step"], st, ol, oam, omg)
+    log("compared %d steps, %d margin-checked, worst logit err %.3g" % (c, k, worst))
+    ref["session"].close()
+
+
 def test_run_to_run_deterministic_and_resumable(torch_dev):
     import torch
     from persistent_task_runtime_amd import runner
