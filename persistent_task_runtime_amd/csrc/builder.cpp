@@ -269,8 +269,22 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
         const int U = N / a;
         const int per_wave_units = (2 + a * nseg - 1) / (a * nseg);
         const int min_units = MPK_NW * per_wave_units;
-        int T = o.num_tiles > 0 ? o.num_tiles : std::max(1, std::min(W, U / min_units));
-        if (T > W || U / T < min_units)
+        // A GEMV reading an attention output waits for the whole attention
+        // phase, which occupies only the attention tasks' workers: its tiles
+        // go to the other workers, which stream ahead into LDS meanwhile
+        // (one row per wavefront beyond the register ring; rows of one
+        // 4096-column group, one request, so the LDS holds them).
+        {
+          const int xp = g->producer[o.in[0]];
+          if (xp >= 0 && g->dops[xp].kind == MPK_TK_ATTN && g->dops[xp].ntiles <= W / 2 && o.num_tiles <= 0 &&
+              !D.pairs && K == 4096 && B == 1 && U / (W - g->dops[xp].ntiles) >= 2 * MPK_NW) {
+            D.worker_base = g->dops[xp].ntiles;
+            D.lds_pre = 1;
+          }
+        }
+        const int Wt = W - D.worker_base;  // workers this operator's tiles may use
+        int T = o.num_tiles > 0 ? o.num_tiles : std::max(1, std::min(Wt, U / min_units));
+        if (T > Wt || U / T < min_units)
           return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": " + std::to_string(U) +
                                              " rows cannot give " + std::to_string(T) +
                                              " tiles of >= " + std::to_string(min_units) + " rows");
@@ -409,7 +423,10 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
       T.kind = D.kind;
       T.op = i;
       T.tile = t;
-      T.worker = (int)(((int64_t)t * W) / D.ntiles);
+      // attention tasks take workers 0, 1, ... (one each); other tiles spread
+      // evenly over their workers
+      T.worker = D.kind == MPK_TK_ATTN ? t
+                                       : D.worker_base + (int)(((int64_t)t * (W - D.worker_base)) / D.ntiles);
       T.split = -1;
       T.out_flag = g->ev_base[op_ev[i]] + t;
       if (D.kind == MPK_TK_ATTN) {

@@ -38,6 +38,12 @@ typedef struct {
   int32_t ntiles;    /* tasks of this operator */
   /* attention */
   int32_t nq, nkv, d, nsplit, S;
+  /* GEMV whose input is an attention output: its tiles run on workers
+   * [worker_base, W) (the attention tasks on [0, worker_base)), and while the
+   * attention runs each wavefront also prefetches one more row of its tile
+   * into LDS (lds_pre = 1) */
+  int32_t worker_base;
+  int32_t lds_pre;
   int32_t pad0;
   const float* x;         /* plain input (a graph input tensor), or NULL */
   const uint64_t* xll;    /* stamped input words (output of another operator), or NULL */

@@ -219,6 +219,15 @@ DEV void st_devi(int32_t* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED,
 DEV void st_devu(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16 bytes written earlier in the launch by another CU, possibly on another
+// XCD (the K/V rows of earlier positions): device-scope loads, since a plain
+// load may hit a line of this XCD's L2 that predates the write.
+DEV u32x4 ld_dev16(const void* p) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<void*>(p));
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
 // all vector-memory operations of this wavefront complete (the scheduler
 // wavefront issues no weight loads, so this waits only for its own stores)
 DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -240,6 +249,7 @@ DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 #define LDS_BEST (LDS_INV + 64)          // [8 waves][8] (float) + [8][8] (int)
 #define LDS_POS (LDS_BEST + 512)         // [8] int: position of request r in the current iteration
 #define LDS_TOK (LDS_POS + 32)           // [8] int: token of request r in the current iteration
+#define LDS_SYNCED (LDS_TOK + 32)        // int: a task of this iteration has received inputs of it
 #define LDS_OUT 2048
 #define LDS_OUT_FLOATS 1024
 #define LDS_X (LDS_OUT + LDS_OUT_FLOATS * 4)
@@ -542,13 +552,13 @@ DEV void cursor_step(Cursor& C, int wave) {
 // when the operator normalises, and the tile's residual rows; inv receives
 // 1 / rms per request (1 without a norm) in every thread.  Every thread of
 // the workgroup takes part.  issue_ring() issues the calling wavefront's
-// first weight loads: it is called once, as early as the input wait allows.
-// Returns -1 on stop.
+// first weight loads (8 vector-memory operations, 16 when ring16): it is
+// called once, as early as the input wait allows.  Returns -1 on stop.
 #define XCH 8    // stamped x words per thread per gather pass (register path)
 #define XGMAX 4  // chunks per wavefront whose gains and values stay in registers (DMA path)
 template <int NB, class Ring>
 DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, int s, int task_id,
-                     float (&inv)[NB], Ring&& issue_ring) {
+                     float (&inv)[NB], bool ring16, Ring&& issue_ring) {
   float* xs = reinterpret_cast<float*>(smem + LDS_X);
   float* res = reinterpret_cast<float*>(smem + Lay<NB>::RES);
   float* red = reinterpret_cast<float*>(smem + LDS_RED);
@@ -628,7 +638,8 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
         // the weights go out behind this round's words; wait for the words
         // only (loads complete in issue order)
         issue_ring();
-        if (worker) vm_wait_known<MPK_RING>();
+        if (worker && ring16) vm_wait_known<2 * MPK_RING>();  // ring group + an LDS row
+        else if (worker) vm_wait_known<MPK_RING>();
       } else if (worker) {
         vm_drain_known();
       }
@@ -800,6 +811,7 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       inv[b] = 1.0f;
     }
   }
+  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_SYNCED) = 1;
   return 0;
 }
 
@@ -955,11 +967,34 @@ DEV int claim_unit(char* smem, int lane) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// One row (one group of eight units) whose weights are in LDS at pf (1 KB
+// per unit, 16 bytes per lane), then its epilogue; same arithmetic as the
+// register path.
+template <int NB>
+DEV void lds_row(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, uint32_t pf, uint32_t xl, int Kpad,
+                 const float (&inv)[NB], int au, int lane) {
+#pragma unroll
+  for (int u = 0; u < MPK_RING; ++u) unit_fma<NB>(lds_read_u32x4(pf + u * 1024 + lane * 16), xl + u * 2048, Kpad, G.acc);
+  row_done<NB>(D, T, G, lb, inv, 1, au, lane);
+}
+
 template <int NB>
 DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, char* smem, int tid, bool sched) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const uint32_t lb = lds_addr(smem);  // LDS byte address of the workgroup's area
+  // LDS rows: with lds_pre, wavefront w also prefetches unit MPK_NW + w of the
+  // tile (one row of one 4096-column group) into LDS beside the input's
+  // landing zone while the inputs are awaited, and computes it after its
+  // first row.
+  const int land_end = Lay<NB>::RES + LDS_RES_BYTES + ((NB * D.K + 127) >> 7) * 1024;
+  const bool pre = D.lds_pre && NB == 1 && !D.pairs && D.K == MPK_RING * 512 &&
+                   land_end + MPK_NW * MPK_RING * 1024 <= Lay<NB>::TOTAL;
+  const int nau_all = D.pairs ? T.nrows / 2 : T.nrows;
+  const int npre = pre ? min(MPK_NW, max(0, nau_all - MPK_NW)) : 0;  // LDS rows of the tile
+  bool lds_pending = !sched && wave < npre;
+  const uint32_t pf = lb + land_end + wave * MPK_RING * 1024;  // this wavefront's LDS row
   // claims start after the staging's barriers
-  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_CLAIM) = MPK_NW;
+  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_CLAIM) = MPK_NW + npre;
   // The ring's first group (units 0..7) is issued before the inputs are
   // awaited: these weights do not depend on them, and the wait is what
   // they hide.
@@ -973,12 +1008,21 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
   }
   float inv[NB];
   {
-    const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id, inv, [&]() {
+    const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id, inv, lds_pending, [&]() {
       if (!sched) {
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
           b[j] = load_unit(I, lane);
           cursor_step(I, wave);
+        }
+        if (lds_pending) {
+          Cursor C2 = I;
+          cursor_goto(C2, MPK_NW + wave, 0, 0, wave);
+#pragma unroll
+          for (int u = 0; u < MPK_RING; ++u) {
+            C2.u = u;
+            __builtin_amdgcn_global_load_lds(cursor_addr(C2, lane), lds_ptr(pf + u * 1024), 16, 0, 0);
+          }
         }
       }
     });
@@ -986,7 +1030,6 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
   }
   mark_ready(P, s, task_id, tid);
   const uint32_t st = stamp_of(P, s);
-  const uint32_t lb = lds_addr(smem);  // LDS byte address of the workgroup's area
   const int Kpad = ((D.K + 511) / 512) * 512;
   GemvState<NB> G;
 #pragma unroll
@@ -1036,6 +1079,12 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
           G.u = 0;
           row_done<NB>(D, T, G, lb, inv, a, au_c, lane);
         }
+        if (lds_pending) {
+          // the first row is done and the next one's loads are in flight:
+          // compute the row waiting in LDS meanwhile
+          lds_row<NB>(D, T, G, lb, pf, xl, Kpad, inv, MPK_NW + wave, lane);
+          lds_pending = false;
+        }
         au_c = au_n, gc = gn;
       }
       // last group (none when this wavefront had no assignment unit)
@@ -1049,6 +1098,7 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
           row_done<NB>(D, T, G, lb, inv, a, au_c, lane);
         }
       }
+      if (lds_pending) lds_row<NB>(D, T, G, lb, pf, xl, Kpad, inv, MPK_NW + wave, lane);
     } else {
       // generic rows (short K): static assignment units, per-unit
       // bookkeeping, padding skipped
@@ -1210,19 +1260,24 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 #pragma unroll
     for (int e = 0; e < 8; ++e) sm.acc[h][e] = 0.f;
   }
-  // K/V rows of this wave's first rounds: issued before anything else (the
-  // cache rows below p do not depend on this iteration)
+  // K/V rows of this wave's first rounds.  The cache rows below p were
+  // written by earlier iterations, all ended once any input of this
+  // iteration has arrived.  If an earlier task of this iteration on this CU
+  // has already waited for one (LDS_SYNCED), the rows are loaded before
+  // this task's own wait; otherwise (nothing before it on this queue, or only
+  // tasks with nothing to do) after it.
   u32x4 kr[ATT_ROUNDS], vr[ATT_ROUNDS];
   auto load_rounds = [&](int base) {
 #pragma unroll
     for (int q = 0; q < ATT_ROUNDS; ++q) {
       const int t = base + (wave + MPK_NW * q) * PPR + pg;
       const int tc = t < hi && t != p ? t : lo;  // in-bounds row for idle lanes
-      kr[q] = gldv<u32x4>(kc + (int64_t)tc * d + dim0);
-      vr[q] = gldv<u32x4>(vc + (int64_t)tc * d + dim0);
+      kr[q] = ld_dev16(kc + (int64_t)tc * d + dim0);
+      vr[q] = ld_dev16(vc + (int64_t)tc * d + dim0);
     }
   };
-  if (!sched && lo < hi) load_rounds(lo);
+  const bool early = uni(*reinterpret_cast<volatile int*>(smem + LDS_SYNCED)) != 0;
+  if (!sched && lo < hi && early) load_rounds(lo);
 
   // ---- q / k / v words of the group: wave hh < G + 2 takes one head vector ----
   const int hh = wave;
@@ -1254,9 +1309,11 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       if (rc == 0) break;
     }
   }
-  // The K/V rows, RoPE factors and gains above are plain loads issued
-  // before the device-scope polls: complete them here (see vm_drain_known;
-  // they were issued first, so this costs nothing).
+  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_SYNCED) = 1;
+  if (!sched && lo < hi && !early) load_rounds(lo);
+  // The K/V rows, RoPE factors and gains above are loads issued before the
+  // device-scope polls: complete them here (see vm_drain_known; they were
+  // issued first, so this costs little).
   vm_drain_known();
   mark_ready(P, s, task_id, tid);
 
@@ -1496,6 +1553,7 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
       ctask& T = tasks_of(P)[task_id];
       if (k == 0) {
         if (sched) set_positions(P, smem, s, lane);
+        if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_SYNCED) = 0;
         __syncthreads();
       }
       if (sched && lane == 0 && P.trace) {
@@ -1539,6 +1597,8 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_op_kernel(mpk_kparams P, i
   ctask& T = tasks_of(P)[task_id];
   volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
   if (tid == 0) ctl[0] = 0;
+  // every earlier launch (every earlier iteration) has ended
+  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_SYNCED) = 1;
   if (sched) set_positions(P, smem, s, lane);
   __syncthreads();
   run_task<NB>(P, T, task_id, s, smem, tid, sched);

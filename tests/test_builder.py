@@ -68,22 +68,29 @@ def test_full_model_tiles_fill_every_cu():
         kinds = [o.kind for o in spec.ops]
         argmax_op = len(spec.ops)
         assert info.num_ops == len(spec.ops) + 1 and info.sink_op == argmax_op
-        # every GEMV-type operator has exactly one tile per CU
+        # every GEMV-type operator has exactly one tile per CU, except the
+        # o projection (the consumer of attention): its tiles take the 256 - 72
+        # workers without an attention task (72 = 8 kv heads x 9 splits), which
+        # prefetch ahead while the attention runs
         for i, k in enumerate(kinds):
             if k == mpk.MPK_OP_EMBED:
                 assert i not in per_op
                 continue
             if k == mpk.MPK_OP_ATTENTION:
+                assert sorted(t.worker for t in per_op[i]) == list(range(72))
                 continue
-            assert len(per_op[i]) == 256, (i, k, len(per_op[i]))
-            assert sorted(t.worker for t in per_op[i]) == list(range(256))
+            after_attn = i > 0 and kinds[i - 1] == mpk.MPK_OP_ATTENTION
+            want = list(range(72, 256)) if after_attn else list(range(256))
+            assert sorted(t.worker for t in per_op[i]) == want, (i, k)
         # row split of the named shapes (P1 "The API": blocks a multiple of the workers)
         rows = {mpk.MPK_OP_RMSNORM_LINEAR: 24, mpk.MPK_OP_RMSNORM_GATEUP: 96}
         for i, k in enumerate(kinds):
             if k in rows:
                 assert {t.nrows for t in per_op[i]} == {rows[k]}
             if k == mpk.MPK_OP_LINEAR_RESIDUAL:
-                assert {t.nrows for t in per_op[i]} == {16}
+                after_attn = kinds[i - 1] == mpk.MPK_OP_ATTENTION
+                assert {t.nrows for t in per_op[i]} == ({22, 23} if after_attn else {16})
+                assert sum(t.nrows for t in per_op[i]) == 4096
             if k == mpk.MPK_OP_LMHEAD_ARGMAX:
                 assert {t.nrows for t in per_op[i]} == {593, 594}
                 assert sum(t.nrows for t in per_op[i]) == 151936
@@ -93,14 +100,19 @@ def test_full_model_tiles_fill_every_cu():
         # one argmax task, on worker 0, last in its queue
         assert len(per_op[argmax_op]) == 1 and per_op[argmax_op][0].worker == 0
         assert tasks[queues[0][-1]].op == argmax_op
-        # operator order on every queue; 4 GEMV operators x 36 layers + LM head on each
-        for q in queues:
+        # operator order on every queue: per layer an attention task or an o
+        # tile (never both), and qkv, gate/up, down; the LM head on each
+        for w, q in enumerate(queues):
             ops = [tasks[t].op for t in q]
             assert ops == sorted(ops)
-            assert sum(kinds[o] != mpk.MPK_OP_ATTENTION for o in ops if o < argmax_op) == 36 * 4 + 1
+            n_attn = sum(kinds[o] == mpk.MPK_OP_ATTENTION for o in ops if o < argmax_op)
+            n_o = sum(o > 0 and kinds[o - 1] == mpk.MPK_OP_ATTENTION for o in ops if o < argmax_op)
+            assert (n_attn, n_o) == ((36, 0) if w < 72 else (0, 36)), w
+            assert sum(kinds[o] != mpk.MPK_OP_ATTENTION for o in ops if o < argmax_op) == 36 * 3 + n_o + 1
         # events: one flag per tile (GEMV, LM head), per (request, kv head) merge, 1 for argmax
         for e, (c, op) in enumerate(zip(ev_cnt, ev_op)):
-            want = 1 if op == argmax_op else {mpk.MPK_OP_ATTENTION: 8}.get(kinds[op], 256)
+            after_attn = op > 0 and op < argmax_op and kinds[op - 1] == mpk.MPK_OP_ATTENTION
+            want = 1 if op == argmax_op else {mpk.MPK_OP_ATTENTION: 8}.get(kinds[op], 184 if after_attn else 256)
             assert c == want
     finally:
         mpk.mpk_destroy_graph(g)
