@@ -154,6 +154,13 @@ DEV lptr_t lds_ptr(uint32_t a) { return (lptr_t)(uintptr_t)a; }
 // the stream into a shape whose waits drain the whole ring.
 DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lptr_t)(void*)p; }
 
+// Volatile LDS words (control flags, counters, wait slots) through an LDS
+// pointer: through a generic pointer a volatile access stays a FLAT access,
+// which also counts as a vector-memory operation, and the compiler follows
+// each with a full vmcnt drain (the weight ring included).
+typedef volatile __attribute__((address_space(3))) int lds_vi;
+DEV lds_vi* lvi(const void* smem, int off) { return (lds_vi*)lds_ptr(lds_addr(smem) + (uint32_t)off); }
+
 DEV u32x4 lds_read_u32x4(uint32_t a) {
   u32x4 v;
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
@@ -250,6 +257,11 @@ DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 #define LDS_POS (LDS_BEST + 512)         // [8] int: position of request r in the current iteration
 #define LDS_TOK (LDS_POS + 32)           // [8] int: token of request r in the current iteration
 #define LDS_SYNCED (LDS_TOK + 32)        // int: a task of this iteration has received inputs of it
+// control words: [0] stop flag, [8, 40) wait-round slots, [40] row claims,
+// [41] worker wavefronts done issuing weight loads, [42, 45) prefetched input
+// chunks (task, iteration, count)
+#define LDS_ISSUED (LDS_CTL + 41 * 4)
+#define LDS_PF (LDS_CTL + 42 * 4)
 #define LDS_OUT 2048
 #define LDS_OUT_FLOATS 1024
 #define LDS_X (LDS_OUT + LDS_OUT_FLOATS * 4)
@@ -269,27 +281,30 @@ static_assert(Lay<2>::RES + LDS_RES_BYTES <= Lay<2>::TOTAL, "LDS budget");
 DEV void lds_write_f32(uint32_t a, float v) {
   asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(v) : "memory");
 }
+DEV void lds_write_f32x2(uint32_t a, float2 v) {
+  asm volatile("ds_write_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(v) : "memory");
+}
 
 DEV int xperm(int k) { return (k & ~511) + ((k & 4) << 6) + (((k & 511) >> 3) << 2) + (k & 3); }
 
 // Position of request b in the current iteration (written into LDS_POS by the
 // scheduler wavefront at the start of each iteration).
 DEV int cur_pos(const char* smem, int b) {
-  return __builtin_amdgcn_readfirstlane(reinterpret_cast<const volatile int*>(smem + LDS_POS)[b]);
+  return __builtin_amdgcn_readfirstlane(lvi(smem, LDS_POS)[b]);
 }
 
 // Scheduler wavefront: positions of iteration s into LDS_POS (uniform
 // indices into the kernel-argument array).
 DEV void set_positions(const mpk_kparams& P, char* smem, int s, int lane) {
   if (lane == 0)
-    for (int b = 0; b < P.B; ++b) reinterpret_cast<volatile int*>(smem + LDS_POS)[b] = P.pos0[b] + s;
+    for (int b = 0; b < P.B; ++b) lvi(smem, LDS_POS)[b] = P.pos0[b] + s;
 }
 
 // Per-lane forms: the position of request b (b may differ between lanes), and
 // the token id it consumes in this iteration (resolved into LDS_TOK by
 // resolve_tokens before a task reads embedding rows).
-DEV int cur_pos_v(const char* smem, int b) { return reinterpret_cast<const volatile int*>(smem + LDS_POS)[b]; }
-DEV int cur_token_v(const char* smem, int b) { return reinterpret_cast<const volatile int*>(smem + LDS_TOK)[b]; }
+DEV int cur_pos_v(const char* smem, int b) { return lvi(smem, LDS_POS)[b]; }
+DEV int cur_token_v(const char* smem, int b) { return lvi(smem, LDS_TOK)[b]; }
 
 // ---------------------------------------------------------------------------
 // Stamped words.  Every value one task hands to another (an activation
@@ -325,6 +340,12 @@ DEV float ll_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
 // expired, stop requested by the host, or an error recorded by another
 // workgroup).  Thread 0 runs the watchdog; the first workgroup to fail
 // records the status.
+// Workgroup barrier over LDS data only: this wavefront's LDS operations are
+// complete first, its vector-memory loads need not be (the barrier that
+// __syncthreads compiles to also drains vmcnt, which would wait out a weight
+// ring just issued).
+DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 struct Waiter {
   uint64_t t0;
   int rounds;
@@ -333,7 +354,7 @@ struct Waiter {
 DEV Waiter waiter_start() { return Waiter{clock_now(), 0}; }
 
 DEV int wait_round(const mpk_kparams& P, Waiter& Wt, bool pending, int s, int task_id, char* smem, int tid) {
-  volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
+  lds_vi* ctl = lvi(smem, LDS_CTL);
   const int wave = tid >> 6;
   ++Wt.rounds;
   // (not on the first round: a wait satisfied at first look costs no status reads)
@@ -355,10 +376,10 @@ DEV int wait_round(const mpk_kparams& P, Waiter& Wt, bool pending, int s, int ta
   }
   // per-wave "still waiting" bits, double-buffered by round parity so a
   // wavefront entering the next round never overwrites a slot still read
-  volatile int* slot = ctl + 8 + (Wt.rounds & 1) * 16;
+  lds_vi* slot = ctl + 8 + (Wt.rounds & 1) * 16;
   const bool any_wave = __ballot(pending) != 0;
   if ((tid & 63) == 0) slot[wave] = any_wave ? 1 : 0;
-  __syncthreads();
+  lds_barrier();
   int any = 0;
   for (int w = 0; w <= MPK_NW; ++w) any |= slot[w];
   if (ctl[0]) return -1;
@@ -385,7 +406,7 @@ DEV void mark_ready(const mpk_kparams& P, int s, int task_id, int tid) {
 // the previous launch); later iterations take the previous iteration's
 // argmax task word (which also carries teacher-forced prompt tokens).
 DEV int resolve_tokens(const mpk_kparams& P, char* smem, int tid, int s, int task_id, Waiter& Wt) {
-  volatile int* tok = reinterpret_cast<volatile int*>(smem + LDS_TOK);
+  lds_vi* tok = lvi(smem, LDS_TOK);
   bool need = false;
   if (tid < P.B) {
     if (s == 0) {
@@ -556,6 +577,33 @@ DEV void cursor_step(Cursor& C, int wave) {
 // called once, as early as the input wait allows.  Returns -1 on stop.
 #define XCH 8    // stamped x words per thread per gather pass (register path)
 #define XGMAX 4  // chunks per wavefront whose gains and values stay in registers (DMA path)
+#define PF_MAX 56  // input chunks the scheduler wavefront prefetches (in flight at once)
+
+// DMA staging area beyond the residual rows: the landing zone (1 KB per
+// chunk of 128 stamped words), then with a norm the gains of each chunk's
+// columns (256 bytes per chunk).  Bytes from the landing zone's start:
+template <int NB>
+DEV int land_bytes(cop& D) {
+  const int nchunk = (NB * D.K + 127) >> 7;
+  return nchunk * 1024 + (D.has_norm ? nchunk * 256 : 0);
+}
+
+// Chunks in which the task's x arrives by global->LDS DMA, or 0 when it
+// takes the register path.
+template <int NB>
+DEV int dma_chunks(cop& D) {
+  const int land = Lay<NB>::RES + LDS_RES_BYTES;
+  const int nchunk = (NB * D.K + 127) >> 7;
+  const bool ok = D.xll && (D.K & 127) == 0 && land + land_bytes<NB>(D) <= Lay<NB>::TOTAL &&
+                  nchunk <= 32 * MPK_NW && (!D.has_norm || nchunk <= XGMAX * MPK_NW);
+  return ok ? nchunk : 0;
+}
+
+DEV uint32_t lds_read_u32(uint32_t a) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
 template <int NB, class Ring>
 DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, int s, int task_id,
                      float (&inv)[NB], bool ring16, Ring&& issue_ring) {
@@ -584,19 +632,30 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
   const int land = Lay<NB>::RES + LDS_RES_BYTES;
   const int nchunk = (NE + 127) >> 7;
   const int nres = D.epi == MPK_EPI_RESID ? NB * T.nrows : 0;
-  const bool dma = D.xll && (K & 127) == 0 && land + nchunk * 1024 <= Lay<NB>::TOTAL && nchunk <= 32 * MPK_NW &&
-                   (!D.has_norm || nchunk <= XGMAX * MPK_NW);
+  const bool dma = dma_chunks<NB>(D) > 0;
+  // chunks 0 .. nheld - 1 were fetched into the landing zone by the previous
+  // task's scheduler wavefront (complete, not yet checked)
+  int nheld = 0;
+  if (dma) {
+    lds_vi* pfr = lvi(smem, LDS_PF);
+    nheld = uni(pfr[0] == task_id && pfr[1] == s ? min(pfr[2], nchunk) : 0);
+  }
   // zero padding columns of x (K not a multiple of 512); no gather writes them
   for (int i = K + (worker ? tid : Kpad); i < Kpad; i += MPK_NW * 64)
 #pragma unroll
     for (int b = 0; b < NB; ++b) xs[b * Kpad + xperm(i)] = 0.f;
-  // residual element of this thread: request rb, row rrow of the tile
+  // Residual element rt of the tile (request rb, row rrow).  With the DMA
+  // path the scheduler wavefront's lanes take them: it streams no weights,
+  // so waiting for a residual word (its count of loads in flight unknown to
+  // the compiler: a full drain) waits behind no weight ring.
+  const bool rsched = dma && nres <= 64;
+  const int rt = rsched ? tid - MPK_NW * 64 : tid;
   bool need_r = false;
   float rv = 0.f;
   int rb = 0, rrow = 0;
-  if (tid < nres) {
-    rb = tid / T.nrows;
-    rrow = T.row0 + tid - rb * T.nrows;
+  if (rt >= 0 && rt < nres) {
+    rb = rt / T.nrows;
+    rrow = T.row0 + rt - rb * T.nrows;
     if (D.res_embed) rv = bf16f(gld16(D.E + (int64_t)cur_token_v(smem, rb) * D.n_out + rrow));
     else if (D.rll) need_r = true;
     else rv = gld(D.resid + (int64_t)rb * D.n_out + rrow);
@@ -608,15 +667,58 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       for (int i = 0; wave + MPK_NW * i < nchunk; ++i) need |= 1u << i;
     need = __builtin_amdgcn_readfirstlane(need);
     const uint32_t mine = need;
-    // gains of this lane's two columns in chunks i < XGMAX (packed bf16 pair)
+    // Gains of this lane's two columns in chunks i < XGMAX (packed bf16
+    // pair), by DMA into LDS after the landing zone: as loads into registers
+    // the compiler would wait for them with a full drain (the ring behind
+    // them has a path-dependent length).
+    const uint32_t gla = lb + land + nchunk * 1024;
     uint32_t gp[XGMAX];
     float2 xv[XGMAX];
 #pragma unroll
     for (int i = 0; i < XGMAX; ++i) {
       const int c = wave + MPK_NW * i;
-      const int k = (c * 128) % K + lane * 2;
-      gp[i] = D.has_norm && ((mine >> i) & 1u) ? gld32(reinterpret_cast<const uint32_t*>(D.gain + k)) : 0u;
+      const int k = (c * 128) % K;
+      if (D.has_norm && ((mine >> i) & 1u))
+        __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.gain + k + lane * 2), lds_ptr(gla + c * 256), 4, 0, 0);
+      gp[i] = 0u;
       xv[i] = float2{0.f, 0.f};
+    }
+    // Chunks of this wavefront in LDS (mask m): take each whose words are
+    // all current.  With a norm the raw values stay in registers and the
+    // gain is applied now, or (gain_now false: the gains may still be in
+    // flight) by gain_pending afterwards.
+    auto take = [&](uint32_t m, bool gain_now) {
+      for (; m; m &= m - 1) {
+        const int i = __builtin_ctz(m), c = wave + MPK_NW * i;
+        const u32x4 w = lds_read_u32x4(lb + land + c * 1024 + lane * 16);
+        if (__ballot(w.y != st || w.w != st) == 0) {
+          need &= ~(1u << i);
+          const int e = c * 128 + lane * 2;
+          const int b = e / K, k = e - b * K;
+          float2 x{__uint_as_float(w.x), __uint_as_float(w.z)};
+          if (D.has_norm) {
+            // i < XGMAX here (checked with dma)
+#pragma unroll
+            for (int j = 0; j < XGMAX; ++j)
+              if (j == i) {
+                xv[j] = x;
+                if (gain_now) x = float2{x.x * bf16lo(gp[j]), x.y * bf16hi(gp[j])};
+              }
+          }
+          // (LDS stores written in asm: after a global->LDS DMA the
+          // compiler puts a full vmcnt drain before its own LDS stores)
+          if (gain_now || !D.has_norm) lds_write_f32x2(lb + LDS_X + (uint32_t)(b * Kpad + xperm(k)) * 4u, x);
+        }
+      }
+      need = __builtin_amdgcn_readfirstlane(need);
+    };
+    // the prefetched chunks first: only those not current are fetched again
+    uint32_t gain_pending = 0;
+    if (worker && wave < nheld) {
+      const int nh = (nheld - wave + MPK_NW - 1) / MPK_NW;
+      const uint32_t before = need;
+      take(need & (nh >= 32 ? ~0u : (1u << nh) - 1u), false);
+      if (D.has_norm) gain_pending = before & ~need;
     }
     bool first = true, published = false;
     for (;;) {
@@ -640,27 +742,27 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
         issue_ring();
         if (worker && ring16) vm_wait_known<2 * MPK_RING>();  // ring group + an LDS row
         else if (worker) vm_wait_known<MPK_RING>();
+        // the gains are in LDS
+        if (D.has_norm) {
+#pragma unroll
+          for (int i = 0; i < XGMAX; ++i)
+            if ((mine >> i) & 1u) gp[i] = lds_read_u32(gla + (wave + MPK_NW * i) * 256 + lane * 4);
+        }
+        // the gains have arrived: apply them to the chunks taken from the prefetch
+        for (uint32_t m = gain_pending; m; m &= m - 1) {
+          const int i = __builtin_ctz(m), c = wave + MPK_NW * i;
+          const int e = c * 128 + lane * 2;
+          const int b = e / K, k = e - b * K;
+          float2 x{0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < XGMAX; ++j)
+            if (j == i) x = float2{xv[j].x * bf16lo(gp[j]), xv[j].y * bf16hi(gp[j])};
+          lds_write_f32x2(lb + LDS_X + (uint32_t)(b * Kpad + xperm(k)) * 4u, x);
+        }
       } else if (worker) {
         vm_drain_known();
       }
-      for (uint32_t m = need; m; m &= m - 1) {
-        const int i = __builtin_ctz(m), c = wave + MPK_NW * i;
-        const u32x4 w = lds_read_u32x4(lb + land + c * 1024 + lane * 16);
-        if (__ballot(w.y != st || w.w != st) == 0) {
-          need &= ~(1u << i);
-          const int e = c * 128 + lane * 2;
-          const int b = e / K, k = e - b * K;
-          float2 x{__uint_as_float(w.x), __uint_as_float(w.z)};
-          if (D.has_norm) {
-            // i < XGMAX here (checked with dma)
-#pragma unroll
-            for (int j = 0; j < XGMAX; ++j)
-              if (j == i) xv[j] = x, x = float2{x.x * bf16lo(gp[j]), x.y * bf16hi(gp[j])};
-          }
-          *reinterpret_cast<float2*>(xs + b * Kpad + xperm(k)) = x;
-        }
-      }
-      need = __builtin_amdgcn_readfirstlane(need);
+      take(need, true);
       if (D.has_norm && worker && need == 0 && !published) {
         published = true;
         // this wavefront's chunks are all in: its RMS partials, in chunk order
@@ -679,11 +781,11 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const float t = wave_sum(ss[b]);
-          if (lane == 0) red[wave * 8 + b] = t;
+          if (lane == 0) lds_write_f32(lb + LDS_RED + (uint32_t)(wave * 8 + b) * 4u, t);
         }
       }
-      if (need_r && ll_ok(wr, st)) res[tid] = ll_f(wr), need_r = false;
-      if (first && tid < nres && !D.rll) res[tid] = rv;
+      if (need_r && ll_ok(wr, st)) res[rt] = ll_f(wr), need_r = false;
+      if (first && rt >= 0 && rt < nres && !D.rll) res[rt] = rv;
       first = false;
       const int rc = wait_round(P, Wt, need != 0 || need_r, s, task_id, smem, tid);
       if (rc < 0) return rc;
@@ -789,7 +891,7 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
         if (rc == 0) break;
       }
     }
-    if (tid < nres) res[tid] = rv;
+    if (rt >= 0 && rt < nres) res[rt] = rv;
     if (D.has_norm && worker) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -805,13 +907,13 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
   for (int b = 0; b < NB; ++b) {
     if (D.has_norm) {
       float t = 0.f;
-      for (int w = 0; w < MPK_NW; ++w) t += red[w * 8 + b];
+      for (int w = 0; w < MPK_NW; ++w) t += lds_read_f32(lds_addr(smem) + LDS_RED + (uint32_t)(w * 8 + b) * 4u);
       inv[b] = 1.0f / sqrtf(t / (float)K + P.rms_eps);
     } else {
       inv[b] = 1.0f;
     }
   }
-  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_SYNCED) = 1;
+  if (tid == 0) *lvi(smem, LDS_SYNCED) = 1;
   return 0;
 }
 
@@ -955,6 +1057,13 @@ DEV u32x4 load_unit(const Cursor& C, int lane) {
   return __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1)))*)cursor_addr(C, lane));
 }
 
+// This lane's 16 bytes of unit u of the cursor's current row, unit u + j
+// at p[64 j] (rows of whole groups: no clamping, no row change)
+typedef const u32x4 __attribute__((address_space(1))) gu32x4;
+DEV const gu32x4* unit_ptr(const Cursor& C, int u, int lane) {
+  return (const gu32x4*)(const void*)(C.row + u * 512) + lane;
+}
+
 // Next free assignment unit of the tile (workgroup counter in LDS, reset to
 // MPK_NW at task start: units 0 .. MPK_NW - 1 go to the wavefronts of the
 // same index).
@@ -978,15 +1087,72 @@ DEV void lds_row(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, uint32_t pf, u
   row_done<NB>(D, T, G, lb, inv, 1, au, lane);
 }
 
+// A worker wavefront has issued its last weight loads of the task.
+DEV void mark_issued(char* smem, int lane) {
+  if (lane == 0)
+    __hip_atomic_fetch_add(reinterpret_cast<int*>(smem + LDS_ISSUED), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// The scheduler wavefront's part of a GEMV task whose queue holds another
+// task after it.  Once every worker wavefront has issued its last weight
+// loads, it fetches the next task's input chunks (global->LDS DMA into that
+// task's landing zone, up to PF_MAX of them) and waits for them: they land
+// at about the time the workers' last weights do, and the next task's
+// staging then fetches again only the chunks that were not yet current.
+// Only when the next task reads this operator's output: most of it (the
+// other tiles) may be complete by then; an input that a later operator
+// produces is not.  free_end: end of the LDS this task leaves free beyond
+// the landing zone.
 template <int NB>
-DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, char* smem, int tid, bool sched) {
+DEV void prefetch_next(const mpk_kparams& P, cop& D, char* smem, uint32_t lb, int lane, int s, int next,
+                       int free_end) {
+  ctask& Tn = *unip(tasks_of(P) + next);
+  if (Tn.kind == MPK_TK_ATTN || Tn.kind == MPK_TK_ARGMAX) return;
+  cop& Dn = *unip(ops_of(P) + Tn.op);
+  if (Dn.xll != D.yll) return;
+  const int land = Lay<NB>::RES + LDS_RES_BYTES;
+  const int nheld = uni(min(dma_chunks<NB>(Dn), min(PF_MAX, (free_end - land) >> 10)));
+  if (nheld <= 0) return;
+  lds_vi* issued = lvi(smem, LDS_ISSUED);
+  while (uni(*issued) < MPK_NW) __builtin_amdgcn_s_sleep(1);
+  // words of another tensor with this iteration's stamp may sit in the
+  // landing zone: clear the stamps before the DMA
+  for (int c = 0; c < nheld; ++c) lds_write_u32x4(lb + land + c * 1024 + lane * 16, u32x4{0u, 0u, 0u, 0u});
+  lds_wait();
+  for (int c = 0; c < nheld; ++c)
+    __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(Dn.xll + c * 128 + lane * 2), lds_ptr(lb + land + c * 1024),
+                                     16, 0, 16 /* sc1: device scope */);
+  vm_drain();
+  if (lane == 0) {
+    lds_vi* pfr = lvi(smem, LDS_PF);
+    pfr[0] = next, pfr[1] = s, pfr[2] = nheld;
+  }
+}
+
+// Pull the next task's descriptors into the scalar cache while this task
+// streams.  A task's first table reads form a chain (queue entry, task,
+// operator); each miss would wait out the memory system's latency under the
+// weight stream.
+DEV void warm_tables(const mpk_kparams& P, int next) {
+  const CAS uint32_t* t = (const CAS uint32_t*)(const CAS void*)unip(tasks_of(P) + next);
+  const int op = uni((int)t[offsetof(mpk_dev_task, op) / 4]);
+  const CAS uint32_t* d = (const CAS uint32_t*)(const CAS void*)unip(ops_of(P) + op);
+  uint32_t acc = t[sizeof(mpk_dev_task) / 4 - 1];
+  for (int i = 0; i < (int)(sizeof(mpk_dev_op) / 4); i += 16) acc ^= d[i];
+  acc ^= d[sizeof(mpk_dev_op) / 4 - 1];
+  asm volatile("" ::"s"(acc));
+}
+
+template <int NB>
+DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, char* smem, int tid, bool sched,
+                  int next) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const uint32_t lb = lds_addr(smem);  // LDS byte address of the workgroup's area
   // LDS rows: with lds_pre, wavefront w also prefetches unit MPK_NW + w of the
   // tile (one row of one 4096-column group) into LDS beside the input's
   // landing zone while the inputs are awaited, and computes it after its
   // first row.
-  const int land_end = Lay<NB>::RES + LDS_RES_BYTES + ((NB * D.K + 127) >> 7) * 1024;
+  const int land_end = Lay<NB>::RES + LDS_RES_BYTES + land_bytes<NB>(D);
   const bool pre = D.lds_pre && NB == 1 && !D.pairs && D.K == MPK_RING * 512 &&
                    land_end + MPK_NW * MPK_RING * 1024 <= Lay<NB>::TOTAL;
   const int nau_all = D.pairs ? T.nrows / 2 : T.nrows;
@@ -994,12 +1160,18 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
   bool lds_pending = !sched && wave < npre;
   const uint32_t pf = lb + land_end + wave * MPK_RING * 1024;  // this wavefront's LDS row
   // claims start after the staging's barriers
-  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_CLAIM) = MPK_NW + npre;
+  if (tid == 0) {
+    *lvi(smem, LDS_CLAIM) = MPK_NW + npre;
+    *lvi(smem, LDS_ISSUED) = 0;
+  }
   // The ring's first group (units 0..7) is issued before the inputs are
   // awaited: these weights do not depend on them, and the wait is what
   // they hide.
   Cursor I;  // issue side: runs MPK_RING units ahead of consumption
   u32x4 b[MPK_RING];
+  // rows are whole groups of eight full units (K a multiple of 4096): a
+  // group's units are consecutive in one row
+  const bool whole = D.K % (MPK_RING * 512) == 0;
   int n = 0, npad = MPK_RING;
   if (!sched) {
     cursor_init(I, D, T, wave);
@@ -1009,12 +1181,19 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
   float inv[NB];
   {
     const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id, inv, lds_pending, [&]() {
-      if (!sched) {
+      if (!sched && whole) {
+        // units 0..7 of the wavefront's first row (of W0 when it has none)
+        const gu32x4* wp = unit_ptr(I, 0, lane);
+#pragma unroll
+        for (int j = 0; j < MPK_RING; ++j) b[j] = __builtin_nontemporal_load(wp + j * 64);
+      } else if (!sched) {
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
           b[j] = load_unit(I, lane);
           cursor_step(I, wave);
         }
+      }
+      if (!sched) {
         if (lds_pending) {
           Cursor C2 = I;
           cursor_goto(C2, MPK_NW + wave, 0, 0, wave);
@@ -1043,7 +1222,7 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
     // complete here, and the compiler knows it: its waits on the ring stay
     // exact
     vm_drain_known();
-    if (upr % MPK_RING == 0) {
+    if (whole) {
       // Rows are whole groups of eight units (K a multiple of 4096 bf16 per
       // group): the epilogue runs between groups only, which keeps the
       // register ring's waits exact inside the unrolled group.  Assignment
@@ -1068,11 +1247,11 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
           cursor_goto(I, au_n, rr, q - rr * upr, wave);
         }
         const uint32_t xg = xl + G.u * 2048;
+        const gu32x4* wp = unit_ptr(I, I.u, lane);
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
           unit_fma<NB>(b[j], xg + j * 2048, Kpad, G.acc);
-          b[j] = load_unit(I, lane);
-          cursor_step(I, wave);
+          b[j] = __builtin_nontemporal_load(wp + j * 64);
         }
         G.u += MPK_RING;
         if (G.u == upr) {
@@ -1087,6 +1266,7 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
         }
         au_c = au_n, gc = gn;
       }
+      mark_issued(smem, lane);
       // last group (none when this wavefront had no assignment unit)
       if (au_c < nau) {
         const uint32_t xg = xl + G.u * 2048;
@@ -1111,11 +1291,17 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
           cursor_step(I, wave);
         }
       }
+      mark_issued(smem, lane);
       const int g = ng - 1;
 #pragma unroll
       for (int j = 0; j < MPK_RING; ++j)
         gemv_consume<NB>(T, D, G, b[j], g * MPK_RING + j, n, lb, inv, Kpad, upr, a, wave, lane);
     }
+  } else if (next >= 0) {
+    warm_tables(P, next);
+#ifdef MPK_PF_CHUNKS
+    prefetch_next<NB>(P, D, smem, lb, lane, s, next, npre > 0 ? land_end : Lay<NB>::TOTAL);
+#endif
   }
   __syncthreads();  // every row of the tile is in LDS
   publish_tile<NB>(P, D, T, lb, s, st, tid);
@@ -1276,7 +1462,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       vr[q] = ld_dev16(vc + (int64_t)tc * d + dim0);
     }
   };
-  const bool early = uni(*reinterpret_cast<volatile int*>(smem + LDS_SYNCED)) != 0;
+  const bool early = uni(*lvi(smem, LDS_SYNCED)) != 0;
   if (!sched && lo < hi && early) load_rounds(lo);
 
   // ---- q / k / v words of the group: wave hh < G + 2 takes one head vector ----
@@ -1309,7 +1495,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       if (rc == 0) break;
     }
   }
-  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_SYNCED) = 1;
+  if (tid == 0) *lvi(smem, LDS_SYNCED) = 1;
   if (!sched && lo < hi && !early) load_rounds(lo);
   // The K/V rows, RoPE factors and gains above are loads issued before the
   // device-scope polls: complete them here (see vm_drain_known; they were
@@ -1528,11 +1714,11 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 // dispatch of one task body; returns -1 when the run must stop
 // ---------------------------------------------------------------------------
 template <int NB>
-DEV int run_task(const mpk_kparams& P, ctask& T, int task_id, int s, char* smem, int tid, bool sched) {
+DEV int run_task(const mpk_kparams& P, ctask& T, int task_id, int s, char* smem, int tid, bool sched, int next) {
   cop& D = ops_of(P)[T.op];
   if (T.kind == MPK_TK_ATTN) return attn_task(P, T, D, smem, tid, sched, s, task_id);
   if (T.kind == MPK_TK_ARGMAX) return argmax_task<NB>(P, D, smem, tid, s, task_id);
-  return gemv_task<NB>(P, T, D, s, task_id, smem, tid, sched);
+  return gemv_task<NB>(P, T, D, s, task_id, smem, tid, sched, next);
 }
 
 // ---------------------------------------------------------------------------
@@ -1545,15 +1731,15 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
   const bool sched = wave == MPK_NW;
   cqent* Q = (cqent*)(const void*)P.queues + (int64_t)blockIdx.x * P.qstride;
   const int qlen = ((const CAS int32_t*)(const void*)P.qlen)[blockIdx.x];
-  volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
-  if (tid == 0) ctl[0] = 0;
+  lds_vi* ctl = lvi(smem, LDS_CTL);
+  if (tid == 0) ctl[0] = 0, ctl[42] = -1;  // no prefetched inputs
   for (int s = 0; s < P.n_iter; ++s) {
     for (int k = 0; k < qlen; ++k) {
       const int task_id = Q[k].task;
       ctask& T = tasks_of(P)[task_id];
       if (k == 0) {
         if (sched) set_positions(P, smem, s, lane);
-        if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_SYNCED) = 0;
+        if (tid == 0) *lvi(smem, LDS_SYNCED) = 0;
         __syncthreads();
       }
       if (sched && lane == 0 && P.trace) {
@@ -1569,7 +1755,7 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
       // loop (it would stay live, and spill, across all bodies).
       int tid_o = tid;
       asm volatile("" : "+v"(tid_o));
-      const int rc = run_task<NB>(P, T, task_id, s, smem, tid_o, sched);
+      const int rc = run_task<NB>(P, T, task_id, s, smem, tid_o, sched, k + 1 < qlen ? Q[k + 1].task : -1);
       if (rc < 0) {
         vm_wait<0>();  // leave no load in flight
         return;
@@ -1595,13 +1781,13 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_op_kernel(mpk_kparams P, i
   const bool sched = wave == MPK_NW;
   const int task_id = first_task + blockIdx.x;
   ctask& T = tasks_of(P)[task_id];
-  volatile int* ctl = reinterpret_cast<volatile int*>(smem + LDS_CTL);
-  if (tid == 0) ctl[0] = 0;
+  lds_vi* ctl = lvi(smem, LDS_CTL);
+  if (tid == 0) ctl[0] = 0, ctl[42] = -1;  // no prefetched inputs
   // every earlier launch (every earlier iteration) has ended
-  if (tid == 0) *reinterpret_cast<volatile int*>(smem + LDS_SYNCED) = 1;
+  if (tid == 0) *lvi(smem, LDS_SYNCED) = 1;
   if (sched) set_positions(P, smem, s, lane);
   __syncthreads();
-  run_task<NB>(P, T, task_id, s, smem, tid, sched);
+  run_task<NB>(P, T, task_id, s, smem, tid, sched, -1);
   vm_wait<0>();
 }
 
