@@ -257,11 +257,7 @@ DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 #define LDS_POS (LDS_BEST + 512)         // [8] int: position of request r in the current iteration
 #define LDS_TOK (LDS_POS + 32)           // [8] int: token of request r in the current iteration
 #define LDS_SYNCED (LDS_TOK + 32)        // int: a task of this iteration has received inputs of it
-// control words: [0] stop flag, [8, 40) wait-round slots, [40] row claims,
-// [41] worker wavefronts done issuing weight loads, [42, 45) prefetched input
-// chunks (task, iteration, count)
-#define LDS_ISSUED (LDS_CTL + 41 * 4)
-#define LDS_PF (LDS_CTL + 42 * 4)
+// control words: [0] stop flag, [8, 40) wait-round slots, [40] row claims
 #define LDS_OUT 2048
 #define LDS_OUT_FLOATS 1024
 #define LDS_X (LDS_OUT + LDS_OUT_FLOATS * 4)
@@ -334,24 +330,28 @@ DEV uint64_t ld_ll(const uint64_t* p) {
 DEV bool ll_ok(uint64_t w, uint32_t st) { return (uint32_t)(w >> 32) == st; }
 DEV float ll_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
-// Workgroup-wide wait.  Every thread of the workgroup calls wait_round once
-// per round with `pending` = this thread still misses words; the result is
-// uniform: 0 = nobody waits any more, 1 = poll again, -1 = stop (watchdog
-// expired, stop requested by the host, or an error recorded by another
-// workgroup).  Thread 0 runs the watchdog; the first workgroup to fail
-// records the status.
 // Workgroup barrier over LDS data only: this wavefront's LDS operations are
 // complete first, its vector-memory loads need not be (the barrier that
 // __syncthreads compiles to also drains vmcnt, which would wait out a weight
 // ring just issued).
 DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Workgroup-wide wait.  Every thread of the workgroup calls wait_round once
+// per round with `pending` = this thread still misses words; the result is
+// uniform: 0 = nobody waits any more, 1 = poll again, -1 = stop (watchdog
+// expired, stop requested by the host, or an error recorded by another
+// workgroup).  Thread 0 runs the watchdog; the first workgroup to fail
+// records the status.
+// The watchdog's clock starts when a wait first polls again (t0 = 0 until
+// then): a wait satisfied at first look reads no clock (s_memrealtime is a
+// scalar-memory operation, and every later lgkmcnt wait of the wavefront,
+// LDS waits included, would wait for it).
 struct Waiter {
   uint64_t t0;
   int rounds;
 };
 
-DEV Waiter waiter_start() { return Waiter{clock_now(), 0}; }
+DEV Waiter waiter_start() { return Waiter{0, 0}; }
 
 DEV int wait_round(const mpk_kparams& P, Waiter& Wt, bool pending, int s, int task_id, char* smem, int tid) {
   lds_vi* ctl = lvi(smem, LDS_CTL);
@@ -363,7 +363,7 @@ DEV int wait_round(const mpk_kparams& P, Waiter& Wt, bool pending, int s, int ta
     const int code = __hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int abort_req = __hip_atomic_load(&P.status->abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     if (abort_req) mine = MPK_ERR_ABORTED;
-    else if (clock_now() - Wt.t0 > P.timeout_ticks) mine = MPK_ERR_DEVICE_TIMEOUT;
+    else if (Wt.t0 != 0 && clock_now() - Wt.t0 > P.timeout_ticks) mine = MPK_ERR_DEVICE_TIMEOUT;
     if (mine) {
       int expected = 0;
       if (__hip_atomic_compare_exchange_strong(&P.status->code, &expected, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -384,6 +384,7 @@ DEV int wait_round(const mpk_kparams& P, Waiter& Wt, bool pending, int s, int ta
   for (int w = 0; w <= MPK_NW; ++w) any |= slot[w];
   if (ctl[0]) return -1;
   if (!any) return 0;
+  if (tid == 0 && Wt.t0 == 0) Wt.t0 = clock_now();
   __builtin_amdgcn_s_sleep(1);
   return 1;
 }
@@ -577,7 +578,6 @@ DEV void cursor_step(Cursor& C, int wave) {
 // called once, as early as the input wait allows.  Returns -1 on stop.
 #define XCH 8    // stamped x words per thread per gather pass (register path)
 #define XGMAX 4  // chunks per wavefront whose gains and values stay in registers (DMA path)
-#define PF_MAX 56  // input chunks the scheduler wavefront prefetches (in flight at once)
 
 // DMA staging area beyond the residual rows: the landing zone (1 KB per
 // chunk of 128 stamped words), then with a norm the gains of each chunk's
@@ -633,13 +633,6 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
   const int nchunk = (NE + 127) >> 7;
   const int nres = D.epi == MPK_EPI_RESID ? NB * T.nrows : 0;
   const bool dma = dma_chunks<NB>(D) > 0;
-  // chunks 0 .. nheld - 1 were fetched into the landing zone by the previous
-  // task's scheduler wavefront (complete, not yet checked)
-  int nheld = 0;
-  if (dma) {
-    lds_vi* pfr = lvi(smem, LDS_PF);
-    nheld = uni(pfr[0] == task_id && pfr[1] == s ? min(pfr[2], nchunk) : 0);
-  }
   // zero padding columns of x (K not a multiple of 512); no gather writes them
   for (int i = K + (worker ? tid : Kpad); i < Kpad; i += MPK_NW * 64)
 #pragma unroll
@@ -684,10 +677,9 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       xv[i] = float2{0.f, 0.f};
     }
     // Chunks of this wavefront in LDS (mask m): take each whose words are
-    // all current.  With a norm the raw values stay in registers and the
-    // gain is applied now, or (gain_now false: the gains may still be in
-    // flight) by gain_pending afterwards.
-    auto take = [&](uint32_t m, bool gain_now) {
+    // all current (with a norm the raw values also stay in registers for
+    // the RMS sums).
+    auto take = [&](uint32_t m) {
       for (; m; m &= m - 1) {
         const int i = __builtin_ctz(m), c = wave + MPK_NW * i;
         const u32x4 w = lds_read_u32x4(lb + land + c * 1024 + lane * 16);
@@ -700,26 +692,15 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
             // i < XGMAX here (checked with dma)
 #pragma unroll
             for (int j = 0; j < XGMAX; ++j)
-              if (j == i) {
-                xv[j] = x;
-                if (gain_now) x = float2{x.x * bf16lo(gp[j]), x.y * bf16hi(gp[j])};
-              }
+              if (j == i) xv[j] = x, x = float2{x.x * bf16lo(gp[j]), x.y * bf16hi(gp[j])};
           }
           // (LDS stores written in asm: after a global->LDS DMA the
           // compiler puts a full vmcnt drain before its own LDS stores)
-          if (gain_now || !D.has_norm) lds_write_f32x2(lb + LDS_X + (uint32_t)(b * Kpad + xperm(k)) * 4u, x);
+          lds_write_f32x2(lb + LDS_X + (uint32_t)(b * Kpad + xperm(k)) * 4u, x);
         }
       }
       need = __builtin_amdgcn_readfirstlane(need);
     };
-    // the prefetched chunks first: only those not current are fetched again
-    uint32_t gain_pending = 0;
-    if (worker && wave < nheld) {
-      const int nh = (nheld - wave + MPK_NW - 1) / MPK_NW;
-      const uint32_t before = need;
-      take(need & (nh >= 32 ? ~0u : (1u << nh) - 1u), false);
-      if (D.has_norm) gain_pending = before & ~need;
-    }
     bool first = true, published = false;
     for (;;) {
       if (first) {
@@ -748,21 +729,10 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
           for (int i = 0; i < XGMAX; ++i)
             if ((mine >> i) & 1u) gp[i] = lds_read_u32(gla + (wave + MPK_NW * i) * 256 + lane * 4);
         }
-        // the gains have arrived: apply them to the chunks taken from the prefetch
-        for (uint32_t m = gain_pending; m; m &= m - 1) {
-          const int i = __builtin_ctz(m), c = wave + MPK_NW * i;
-          const int e = c * 128 + lane * 2;
-          const int b = e / K, k = e - b * K;
-          float2 x{0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < XGMAX; ++j)
-            if (j == i) x = float2{xv[j].x * bf16lo(gp[j]), xv[j].y * bf16hi(gp[j])};
-          lds_write_f32x2(lb + LDS_X + (uint32_t)(b * Kpad + xperm(k)) * 4u, x);
-        }
       } else if (worker) {
         vm_drain_known();
       }
-      take(need, true);
+      take(need);
       if (D.has_norm && worker && need == 0 && !published) {
         published = true;
         // this wavefront's chunks are all in: its RMS partials, in chunk order
@@ -1087,48 +1057,6 @@ DEV void lds_row(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, uint32_t pf, u
   row_done<NB>(D, T, G, lb, inv, 1, au, lane);
 }
 
-// A worker wavefront has issued its last weight loads of the task.
-DEV void mark_issued(char* smem, int lane) {
-  if (lane == 0)
-    __hip_atomic_fetch_add(reinterpret_cast<int*>(smem + LDS_ISSUED), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// The scheduler wavefront's part of a GEMV task whose queue holds another
-// task after it.  Once every worker wavefront has issued its last weight
-// loads, it fetches the next task's input chunks (global->LDS DMA into that
-// task's landing zone, up to PF_MAX of them) and waits for them: they land
-// at about the time the workers' last weights do, and the next task's
-// staging then fetches again only the chunks that were not yet current.
-// Only when the next task reads this operator's output: most of it (the
-// other tiles) may be complete by then; an input that a later operator
-// produces is not.  free_end: end of the LDS this task leaves free beyond
-// the landing zone.
-template <int NB>
-DEV void prefetch_next(const mpk_kparams& P, cop& D, char* smem, uint32_t lb, int lane, int s, int next,
-                       int free_end) {
-  ctask& Tn = *unip(tasks_of(P) + next);
-  if (Tn.kind == MPK_TK_ATTN || Tn.kind == MPK_TK_ARGMAX) return;
-  cop& Dn = *unip(ops_of(P) + Tn.op);
-  if (Dn.xll != D.yll) return;
-  const int land = Lay<NB>::RES + LDS_RES_BYTES;
-  const int nheld = uni(min(dma_chunks<NB>(Dn), min(PF_MAX, (free_end - land) >> 10)));
-  if (nheld <= 0) return;
-  lds_vi* issued = lvi(smem, LDS_ISSUED);
-  while (uni(*issued) < MPK_NW) __builtin_amdgcn_s_sleep(1);
-  // words of another tensor with this iteration's stamp may sit in the
-  // landing zone: clear the stamps before the DMA
-  for (int c = 0; c < nheld; ++c) lds_write_u32x4(lb + land + c * 1024 + lane * 16, u32x4{0u, 0u, 0u, 0u});
-  lds_wait();
-  for (int c = 0; c < nheld; ++c)
-    __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(Dn.xll + c * 128 + lane * 2), lds_ptr(lb + land + c * 1024),
-                                     16, 0, 16 /* sc1: device scope */);
-  vm_drain();
-  if (lane == 0) {
-    lds_vi* pfr = lvi(smem, LDS_PF);
-    pfr[0] = next, pfr[1] = s, pfr[2] = nheld;
-  }
-}
-
 // Pull the next task's descriptors into the scalar cache while this task
 // streams.  A task's first table reads form a chain (queue entry, task,
 // operator); each miss would wait out the memory system's latency under the
@@ -1160,10 +1088,7 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
   bool lds_pending = !sched && wave < npre;
   const uint32_t pf = lb + land_end + wave * MPK_RING * 1024;  // this wavefront's LDS row
   // claims start after the staging's barriers
-  if (tid == 0) {
-    *lvi(smem, LDS_CLAIM) = MPK_NW + npre;
-    *lvi(smem, LDS_ISSUED) = 0;
-  }
+  if (tid == 0) *lvi(smem, LDS_CLAIM) = MPK_NW + npre;
   // The ring's first group (units 0..7) is issued before the inputs are
   // awaited: these weights do not depend on them, and the wait is what
   // they hide.
@@ -1266,7 +1191,6 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
         }
         au_c = au_n, gc = gn;
       }
-      mark_issued(smem, lane);
       // last group (none when this wavefront had no assignment unit)
       if (au_c < nau) {
         const uint32_t xg = xl + G.u * 2048;
@@ -1291,7 +1215,6 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
           cursor_step(I, wave);
         }
       }
-      mark_issued(smem, lane);
       const int g = ng - 1;
 #pragma unroll
       for (int j = 0; j < MPK_RING; ++j)
@@ -1299,9 +1222,6 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
     }
   } else if (next >= 0) {
     warm_tables(P, next);
-#ifdef MPK_PF_CHUNKS
-    prefetch_next<NB>(P, D, smem, lb, lane, s, next, npre > 0 ? land_end : Lay<NB>::TOTAL);
-#endif
   }
   __syncthreads();  // every row of the tile is in LDS
   publish_tile<NB>(P, D, T, lb, s, st, tid);
@@ -1732,7 +1652,7 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
   cqent* Q = (cqent*)(const void*)P.queues + (int64_t)blockIdx.x * P.qstride;
   const int qlen = ((const CAS int32_t*)(const void*)P.qlen)[blockIdx.x];
   lds_vi* ctl = lvi(smem, LDS_CTL);
-  if (tid == 0) ctl[0] = 0, ctl[42] = -1;  // no prefetched inputs
+  if (tid == 0) ctl[0] = 0;
   for (int s = 0; s < P.n_iter; ++s) {
     for (int k = 0; k < qlen; ++k) {
       const int task_id = Q[k].task;
@@ -1782,7 +1702,7 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_op_kernel(mpk_kparams P, i
   const int task_id = first_task + blockIdx.x;
   ctask& T = tasks_of(P)[task_id];
   lds_vi* ctl = lvi(smem, LDS_CTL);
-  if (tid == 0) ctl[0] = 0, ctl[42] = -1;  // no prefetched inputs
+  if (tid == 0) ctl[0] = 0;
   // every earlier launch (every earlier iteration) has ended
   if (tid == 0) *lvi(smem, LDS_SYNCED) = 1;
   if (sched) set_positions(P, smem, s, lane);
