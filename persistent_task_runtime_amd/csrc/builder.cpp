@@ -269,18 +269,18 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
         const int U = N / a;
         const int per_wave_units = (2 + a * nseg - 1) / (a * nseg);
         const int min_units = MPK_NW * per_wave_units;
+        // Rows of one 4096-column group, one request: while a tile's inputs
+        // are awaited, its wavefronts also stream assignment units into the
+        // LDS beyond the input's landing zone (as many as fit).
+        D.lds_pre = K == 4096 && B == 1 ? 1 : 0;
         // A GEMV reading an attention output waits for the whole attention
         // phase, which occupies only the attention tasks' workers: its tiles
-        // go to the other workers, which stream ahead into LDS meanwhile
-        // (one row per wavefront beyond the register ring; rows of one
-        // 4096-column group, one request, so the LDS holds them).
+        // go to the other workers, which stream ahead meanwhile.
         {
           const int xp = g->producer[o.in[0]];
           if (xp >= 0 && g->dops[xp].kind == MPK_TK_ATTN && g->dops[xp].ntiles <= W / 2 && o.num_tiles <= 0 &&
-              !D.pairs && K == 4096 && B == 1 && U / (W - g->dops[xp].ntiles) >= 2 * MPK_NW) {
+              !D.pairs && K == 4096 && B == 1 && U / (W - g->dops[xp].ntiles) >= 2 * MPK_NW)
             D.worker_base = g->dops[xp].ntiles;
-            D.lds_pre = 1;
-          }
         }
         const int Wt = W - D.worker_base;  // workers this operator's tiles may use
         int T = o.num_tiles > 0 ? o.num_tiles : std::max(1, std::min(Wt, U / min_units));

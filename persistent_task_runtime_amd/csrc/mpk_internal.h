@@ -38,10 +38,11 @@ typedef struct {
   int32_t ntiles;    /* tasks of this operator */
   /* attention */
   int32_t nq, nkv, d, nsplit, S;
-  /* GEMV whose input is an attention output: its tiles run on workers
-   * [worker_base, W) (the attention tasks on [0, worker_base)), and while the
-   * attention runs each wavefront also prefetches one more row of its tile
-   * into LDS (lds_pre = 1) */
+  /* worker_base: a GEMV whose input is an attention output runs its tiles on
+   * workers [worker_base, W) (the attention tasks on [0, worker_base)).
+   * lds_pre = 1: rows of one 4096-column group and one request, so while a
+   * tile's inputs are awaited its wavefronts also stream assignment units of
+   * the tile into LDS (as many as fit beyond the input's landing zone) */
   int32_t worker_base;
   int32_t lds_pre;
   int32_t pad0;

@@ -574,18 +574,27 @@ DEV void cursor_step(Cursor& C, int wave) {
 // when the operator normalises, and the tile's residual rows; inv receives
 // 1 / rms per request (1 without a norm) in every thread.  Every thread of
 // the workgroup takes part.  issue_ring() issues the calling wavefront's
-// first weight loads (8 vector-memory operations, 16 when ring16): it is
+// first weight loads (ring_ops vector-memory operations: 8, 16 or 24): it is
 // called once, as early as the input wait allows.  Returns -1 on stop.
 #define XCH 8    // stamped x words per thread per gather pass (register path)
 #define XGMAX 4  // chunks per wavefront whose gains and values stay in registers (DMA path)
 
-// DMA staging area beyond the residual rows: the landing zone (1 KB per
-// chunk of 128 stamped words), then with a norm the gains of each chunk's
-// columns (256 bytes per chunk).  Bytes from the landing zone's start:
+// DMA staging: the landing zone beyond the residual rows (1 KB per chunk of
+// 128 stamped words) and, with a norm, the gains of each chunk's columns
+// (256 bytes per chunk), which go into the staged-x area beyond x when they
+// fit there (they are read before x is complete) and after the landing zone
+// otherwise.
+template <int NB>
+DEV bool gains_in_xs(cop& D) {
+  const int Kpad = ((D.K + 511) / 512) * 512;
+  const int nchunk = (NB * D.K + 127) >> 7;
+  return LDS_X + NB * Kpad * 4 + nchunk * 256 <= Lay<NB>::RES;
+}
+// bytes the DMA staging occupies from the landing zone's start
 template <int NB>
 DEV int land_bytes(cop& D) {
   const int nchunk = (NB * D.K + 127) >> 7;
-  return nchunk * 1024 + (D.has_norm ? nchunk * 256 : 0);
+  return nchunk * 1024 + (D.has_norm && !gains_in_xs<NB>(D) ? nchunk * 256 : 0);
 }
 
 // Chunks in which the task's x arrives by global->LDS DMA, or 0 when it
@@ -606,7 +615,7 @@ DEV uint32_t lds_read_u32(uint32_t a) {
 }
 template <int NB, class Ring>
 DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, int s, int task_id,
-                     float (&inv)[NB], bool ring16, Ring&& issue_ring) {
+                     float (&inv)[NB], int ring_ops, Ring&& issue_ring) {
   float* xs = reinterpret_cast<float*>(smem + LDS_X);
   float* res = reinterpret_cast<float*>(smem + Lay<NB>::RES);
   float* red = reinterpret_cast<float*>(smem + LDS_RED);
@@ -664,7 +673,7 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
     // pair), by DMA into LDS after the landing zone: as loads into registers
     // the compiler would wait for them with a full drain (the ring behind
     // them has a path-dependent length).
-    const uint32_t gla = lb + land + nchunk * 1024;
+    const uint32_t gla = lb + (gains_in_xs<NB>(D) ? LDS_X + NB * Kpad * 4 : land + nchunk * 1024);
     uint32_t gp[XGMAX];
     float2 xv[XGMAX];
 #pragma unroll
@@ -721,7 +730,9 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
         // the weights go out behind this round's words; wait for the words
         // only (loads complete in issue order)
         issue_ring();
-        if (worker && ring16) vm_wait_known<2 * MPK_RING>();  // ring group + an LDS row
+        // (ring group, and the rows of an LDS assignment unit)
+        if (worker && ring_ops == 3 * MPK_RING) vm_wait_known<3 * MPK_RING>();
+        else if (worker && ring_ops == 2 * MPK_RING) vm_wait_known<2 * MPK_RING>();
         else if (worker) vm_wait_known<MPK_RING>();
         // the gains are in LDS
         if (D.has_norm) {
@@ -1046,15 +1057,19 @@ DEV int claim_unit(char* smem, int lane) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
-// One row (one group of eight units) whose weights are in LDS at pf (1 KB
-// per unit, 16 bytes per lane), then its epilogue; same arithmetic as the
-// register path.
+// One assignment unit (a rows of one group of eight units each) whose
+// weights are in LDS at pf (row rr at pf + 8 KB rr, 1 KB per unit, 16 bytes
+// per lane), with the epilogue of each row; same arithmetic as the register
+// path.  Called between assignment units (G.rr == 0).
 template <int NB>
-DEV void lds_row(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, uint32_t pf, uint32_t xl, int Kpad,
-                 const float (&inv)[NB], int au, int lane) {
+DEV void lds_au(cop& D, ctask& T, GemvState<NB>& G, uint32_t lb, uint32_t pf, uint32_t xl, int Kpad,
+                const float (&inv)[NB], int a, int au, int lane) {
+  for (int rr = 0; rr < a; ++rr) {
 #pragma unroll
-  for (int u = 0; u < MPK_RING; ++u) unit_fma<NB>(lds_read_u32x4(pf + u * 1024 + lane * 16), xl + u * 2048, Kpad, G.acc);
-  row_done<NB>(D, T, G, lb, inv, 1, au, lane);
+    for (int u = 0; u < MPK_RING; ++u)
+      unit_fma<NB>(lds_read_u32x4(pf + (rr * MPK_RING + u) * 1024 + lane * 16), xl + u * 2048, Kpad, G.acc);
+    row_done<NB>(D, T, G, lb, inv, a, au, lane);
+  }
 }
 
 // Pull the next task's descriptors into the scalar cache while this task
@@ -1076,17 +1091,20 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
                   int next) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const uint32_t lb = lds_addr(smem);  // LDS byte address of the workgroup's area
-  // LDS rows: with lds_pre, wavefront w also prefetches unit MPK_NW + w of the
-  // tile (one row of one 4096-column group) into LDS beside the input's
-  // landing zone while the inputs are awaited, and computes it after its
-  // first row.
+  // LDS assignment units: with lds_pre (rows of one 4096-column group, one
+  // request), wavefront w < npre also prefetches assignment unit MPK_NW + w
+  // of the tile (a rows of 8 KB) into the LDS beyond the input's landing
+  // zone while the inputs are awaited, and computes it after its first one:
+  // up to twice the weights in flight during the wait.
+  const int a_pre = D.pairs ? 2 : 1;
   const int land_end = Lay<NB>::RES + LDS_RES_BYTES + land_bytes<NB>(D);
-  const bool pre = D.lds_pre && NB == 1 && !D.pairs && D.K == MPK_RING * 512 &&
-                   land_end + MPK_NW * MPK_RING * 1024 <= Lay<NB>::TOTAL;
+  const int pre_cap = D.lds_pre && NB == 1 && D.K == MPK_RING * 512
+                          ? min(MPK_NW, max(0, Lay<NB>::TOTAL - land_end) / (a_pre * MPK_RING * 1024))
+                          : 0;
   const int nau_all = D.pairs ? T.nrows / 2 : T.nrows;
-  const int npre = pre ? min(MPK_NW, max(0, nau_all - MPK_NW)) : 0;  // LDS rows of the tile
+  const int npre = uni(min(pre_cap, max(0, nau_all - MPK_NW)));  // LDS assignment units of the tile
   bool lds_pending = !sched && wave < npre;
-  const uint32_t pf = lb + land_end + wave * MPK_RING * 1024;  // this wavefront's LDS row
+  const uint32_t pf = lb + land_end + wave * a_pre * MPK_RING * 1024;  // this wavefront's LDS unit
   // claims start after the staging's barriers
   if (tid == 0) *lvi(smem, LDS_CLAIM) = MPK_NW + npre;
   // The ring's first group (units 0..7) is issued before the inputs are
@@ -1105,7 +1123,8 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
   }
   float inv[NB];
   {
-    const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id, inv, lds_pending, [&]() {
+    const int ring_ops = MPK_RING + (lds_pending ? a_pre * MPK_RING : 0);
+    const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id, inv, ring_ops, [&]() {
       if (!sched && whole) {
         // units 0..7 of the wavefront's first row (of W0 when it has none)
         const gu32x4* wp = unit_ptr(I, 0, lane);
@@ -1121,11 +1140,13 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
       if (!sched) {
         if (lds_pending) {
           Cursor C2 = I;
-          cursor_goto(C2, MPK_NW + wave, 0, 0, wave);
+          for (int rr = 0; rr < a_pre; ++rr) {
+            cursor_goto(C2, MPK_NW + wave, rr, 0, wave);
+            const gu32x4* wp = unit_ptr(C2, 0, lane);
 #pragma unroll
-          for (int u = 0; u < MPK_RING; ++u) {
-            C2.u = u;
-            __builtin_amdgcn_global_load_lds(cursor_addr(C2, lane), lds_ptr(pf + u * 1024), 16, 0, 0);
+            for (int u = 0; u < MPK_RING; ++u)
+              __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(wp + u * 64),
+                                               lds_ptr(pf + (rr * MPK_RING + u) * 1024), 16, 0, 0);
           }
         }
       }
@@ -1183,10 +1204,10 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
           G.u = 0;
           row_done<NB>(D, T, G, lb, inv, a, au_c, lane);
         }
-        if (lds_pending) {
-          // the first row is done and the next one's loads are in flight:
-          // compute the row waiting in LDS meanwhile
-          lds_row<NB>(D, T, G, lb, pf, xl, Kpad, inv, MPK_NW + wave, lane);
+        if (lds_pending && G.rr == 0 && G.u == 0) {
+          // the first assignment unit is done and the next one's loads are
+          // in flight: compute the unit waiting in LDS meanwhile
+          lds_au<NB>(D, T, G, lb, pf, xl, Kpad, inv, a, MPK_NW + wave, lane);
           lds_pending = false;
         }
         au_c = au_n, gc = gn;
@@ -1202,7 +1223,7 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
           row_done<NB>(D, T, G, lb, inv, a, au_c, lane);
         }
       }
-      if (lds_pending) lds_row<NB>(D, T, G, lb, pf, xl, Kpad, inv, MPK_NW + wave, lane);
+      if (lds_pending) lds_au<NB>(D, T, G, lb, pf, xl, Kpad, inv, a, MPK_NW + wave, lane);
     } else {
       // generic rows (short K): static assignment units, per-unit
       // bookkeeping, padding skipped
