@@ -389,6 +389,34 @@ DEV int wait_round(const mpk_kparams& P, Waiter& Wt, bool pending, int s, int ta
   return 1;
 }
 
+// A wavefront's own watchdog for per-wavefront polling (the rules of
+// wait_round: a stop requested by the host, an error recorded by another
+// workgroup, or this wait past the timeout, whose clock starts at the first
+// repeated poll).  Called once per repeated poll; true = the workgroup stops
+// (its stop flag is set).
+DEV bool wave_watch(const mpk_kparams& P, Waiter& Wt, int s, int task_id, char* smem, int lane) {
+  lds_vi* ctl = lvi(smem, LDS_CTL);
+  ++Wt.rounds;
+  if (Wt.t0 == 0) {
+    Wt.t0 = clock_now();
+  } else if ((Wt.rounds & 7) == 0) {
+    const int code = __hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int abort_req = __hip_atomic_load(&P.status->abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int mine = abort_req ? MPK_ERR_ABORTED
+                               : (clock_now() - Wt.t0 > P.timeout_ticks ? MPK_ERR_DEVICE_TIMEOUT : 0);
+    if (mine && lane == 0) {
+      int expected = 0;
+      if (__hip_atomic_compare_exchange_strong(&P.status->code, &expected, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+        __hip_atomic_store(&P.status->iteration, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&P.status->task, task_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if ((mine || code) && lane == 0) ctl[0] = 1;
+  }
+  return ctl[0] != 0;
+}
+
 // Trace hook: the task's inputs are all present.  With tickets on, the
 // ticket is taken (and returned) before any output of the task is stored.
 DEV void mark_ready(const mpk_kparams& P, int s, int task_id, int tid) {
@@ -633,7 +661,9 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
   // Stamped x words that fit the free LDS beyond the residual rows come by
   // global->LDS DMA, 1 KB chunks (128 words, 2 per lane) per wavefront
   // instruction: wavefront w owns chunks w + 8 i, all in flight at once, and
-  // a chunk with a stale word is fetched again in the next round.  The first
+  // a chunk with a stale word is fetched again in the wavefront's next round.
+  // Each wavefront polls on its own (one barrier at the end): a round then
+  // lasts one chunk's round trip, not the slowest of the workgroup's.  The first
   // round is issued ahead of the weight loads, so it is not queued behind
   // them.  Each wavefront applies the gain to its chunks as they arrive and
   // publishes its RMS partial sums once all of them are in; the sums run in
@@ -768,10 +798,13 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       if (need_r && ll_ok(wr, st)) res[rt] = ll_f(wr), need_r = false;
       if (first && rt >= 0 && rt < nres && !D.rll) res[rt] = rv;
       first = false;
-      const int rc = wait_round(P, Wt, need != 0 || need_r, s, task_id, smem, tid);
-      if (rc < 0) return rc;
-      if (rc == 0) break;
+      if (need == 0 && __ballot(need_r) == 0) break;
+      if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+      __builtin_amdgcn_s_sleep(1);
     }
+    // every wavefront's inputs are in, or the workgroup stops
+    lds_barrier();
+    if (*lvi(smem, LDS_CTL)) return -1;
   } else {
     issue_ring();
     // RMSNorm gains of this thread's columns (k = tid + 512 j), loaded before
