@@ -463,11 +463,15 @@ DEV int resolve_tokens(const mpk_kparams& P, char* smem, int tid, int s, int tas
 }
 
 // Collective gather of n stamped words src[0, n) into LDS dst[0, n) (their
-// 32-bit payloads).  CH words per thread are in flight per round.
+// 32-bit payloads).  CH words per thread are in flight per round; each
+// wavefront polls its own words (wave_watch), the workgroup meets once at
+// the end.
 template <int CH>
 DEV int gather_ll(const mpk_kparams& P, const uint64_t* src, int n, uint32_t* dst, uint32_t st, Waiter& Wt, int s,
                   int task_id, char* smem, int tid) {
-  for (int base = 0; base < n; base += CH * MPK_THREADS) {
+  const int lane = tid & 63;
+  bool stop = false;
+  for (int base = 0; base < n && !stop; base += CH * MPK_THREADS) {
     uint32_t need = 0;
 #pragma unroll
     for (int j = 0; j < CH; ++j)
@@ -483,12 +487,16 @@ DEV int gather_ll(const mpk_kparams& P, const uint64_t* src, int n, uint32_t* ds
           dst[base + tid + j * MPK_THREADS] = (uint32_t)v[j];
           need &= ~(1u << j);
         }
-      const int rc = wait_round(P, Wt, need != 0, s, task_id, smem, tid);
-      if (rc < 0) return rc;
-      if (rc == 0) break;
+      if (__ballot(need != 0) == 0) break;
+      if (wave_watch(P, Wt, s, task_id, smem, lane)) {
+        stop = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
   }
-  return 0;
+  lds_barrier();
+  return *lvi(smem, LDS_CTL) ? -1 : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1457,6 +1465,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
                         (hh < G ? (j * G + hh) * d : (hh == G ? D.nq * d + j * d : (D.nq + D.nkv) * d + j * d));
   uint64_t wa = 0, wb = 0;
   {
+    // each wavefront polls its own head vector; the workgroup meets once
     bool need = mine;
     for (;;) {
       if (need) {
@@ -1464,10 +1473,12 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
         wb = ld_ll(src + lane + half);
         need = !(ll_ok(wa, st) && ll_ok(wb, st));
       }
-      const int rc = wait_round(P, Wt, need, s, task_id, smem, tid);
-      if (rc < 0) return rc;
-      if (rc == 0) break;
+      if (__ballot(need) == 0) break;
+      if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+      __builtin_amdgcn_s_sleep(1);
     }
+    lds_barrier();
+    if (*lvi(smem, LDS_CTL)) return -1;
   }
   if (tid == 0) *lvi(smem, LDS_SYNCED) = 1;
   if (!sched && lo < hi && !early) load_rounds(lo);
