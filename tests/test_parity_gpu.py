@@ -340,3 +340,30 @@ def test_full_model_sampled_steps(torch_dev):
     c, k, worst = compare_greedy(w, n, res["logits"], res["tokens"], res["step"], st, ol, oam, omg)
     log("compared %d, margin-checked %d, worst %.3g" % (c, k, worst))
     res["session"].close()
+
+
+@pytest.mark.timeout(900)
+def test_long_context_sampled_steps(torch_dev):
+    """The long-context configuration: the full model with each layer's K/V
+    cache pre-filled N(0,1) to 32768 positions, decoding at positions
+    32768.. (the attention splits then hold ~1024 positions each).  Two
+    iterations against the oracle: the first consumes the seeded token at
+    position 32768, the second the generated one."""
+    from persistent_task_runtime_amd import runner
+
+    log("long context: generating weights")
+    t0 = time.time()
+    n = 2
+    w = synth.workload("qwen3_8b_long", n_iter=n)
+    weights = synth.make_model(w.shape, seed=w.seed)
+    log("generated in %.1f s; uploading (K/V prefill per layer)" % (time.time() - t0))
+    model = runner.DeviceModel(w.shape, weights=weights)
+    res = runner.run_workload(w, n, want_logits=True, model=model)
+    res["session"].close()
+    log("gpu done; oracle")
+    t1 = time.time()
+    st, ol, oam, omg = oracle_decode(w, n, weights)
+    log("oracle %.1f s" % (time.time() - t1))
+    c, k, worst = compare_greedy(w, n, res["logits"], res["tokens"], res["step"], st, ol, oam, omg)
+    log("compared %d, margin-checked %d, worst %.3g" % (c, k, worst))
+    assert c == n
