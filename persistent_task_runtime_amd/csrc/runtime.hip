@@ -179,6 +179,15 @@ DEV void lds_read_2f4(uint32_t a, f32x4& x0, f32x4& x1) {
                : "memory");
 }
 
+// Two float4 at byte address a and a + 16 (early-clobber outputs, see
+// lds_read_2f4).
+DEV void lds_read_2f4_near(uint32_t a, f32x4& x0, f32x4& x1) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(x0), "=&v"(x1)
+               : "v"(a)
+               : "memory");
+}
+
 DEV float lds_read_f32(uint32_t a) {
   float v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
@@ -1434,16 +1443,17 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   // has already waited for one (LDS_SYNCED), the rows are loaded before
   // this task's own wait; otherwise (nothing before it on this queue, or only
   // tasks with nothing to do) after it.
-  u32x4 kr[ATT_ROUNDS], vr[ATT_ROUNDS];
-  auto load_rounds = [&](int base) {
+  u32x4 kr[ATT_ROUNDS], vr[ATT_ROUNDS], kr2[ATT_ROUNDS], vr2[ATT_ROUNDS];
+  auto load_into = [&](u32x4(&K)[ATT_ROUNDS], u32x4(&V)[ATT_ROUNDS], int base) {
 #pragma unroll
     for (int q = 0; q < ATT_ROUNDS; ++q) {
       const int t = base + (wave + MPK_NW * q) * PPR + pg;
       const int tc = t < hi && t != p ? t : lo;  // in-bounds row for idle lanes
-      kr[q] = ld_dev16(kc + (int64_t)tc * d + dim0);
-      vr[q] = ld_dev16(vc + (int64_t)tc * d + dim0);
+      K[q] = ld_dev16(kc + (int64_t)tc * d + dim0);
+      V[q] = ld_dev16(vc + (int64_t)tc * d + dim0);
     }
   };
+  auto load_rounds = [&](int base) { load_into(kr, vr, base); };
   const bool early = uni(*lvi(smem, LDS_SYNCED)) != 0;
   if (!sched && lo < hi && early) load_rounds(lo);
 
@@ -1535,14 +1545,12 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 
   // ---- scores and online softmax over this wave's positions ----
   if (!sched) {
-    float qv[ATT_MAXG][8];
-#pragma unroll
-    for (int h = 0; h < ATT_MAXG; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[h][e] = h < G ? qs[h * d + dim0 + e] : 0.f;
+    // q is read from LDS in each step (asm reads: not hoisted into 32 more
+    // live registers beside the two K/V register sets)
+    const uint32_t qa = lds_addr(qs) + (uint32_t)dim0 * 4u;
     const int step = MPK_NW * PPR * ATT_ROUNDS;
-    for (int base = lo; base < hi; base += step) {
-      if (base != lo) load_rounds(base);
+    // one base step: its positions folded into the running (m, l, acc)
+    auto fold = [&](u32x4(&K)[ATT_ROUNDS], u32x4(&V)[ATT_ROUNDS], int base) {
       // this round's ATT_ROUNDS positions per lane group are folded into the
       // running (m, l, acc) together: one rescale per head per base step
       float kf[ATT_ROUNDS][8], vf[ATT_ROUNDS][8];
@@ -1551,24 +1559,30 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       for (int q = 0; q < ATT_ROUNDS; ++q) {
         const int t = base + (wave + MPK_NW * q) * PPR + pg;
         valid[q] = t < hi;
-        if (t == p) {
+        // row p comes from LDS; an idle lane (its row is not this split's)
+        // takes it too, so no value outside the rows in [lo, p) reaches
+        // the sums, whatever the cache holds there
+        if (t == p || !valid[q]) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) kf[q][e] = kv[dim0 + e], vf[q][e] = kv[d + dim0 + e];
         } else {
-          unpack8(kr[q], kf[q]);
-          unpack8(vr[q], vf[q]);
+          unpack8(K[q], kf[q]);
+          unpack8(V[q], vf[q]);
         }
       }
 #pragma unroll
       for (int h = 0; h < ATT_MAXG; ++h) {
         if (h < G) {
+          f32x4 q0, q1;  // q of head h, dims dim0 .. dim0 + 7
+          lds_read_2f4_near(qa + (uint32_t)(h * d) * 4u, q0, q1);
+          const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
           float sc[ATT_ROUNDS];
           float M = sm.m[h];
 #pragma unroll
           for (int q = 0; q < ATT_ROUNDS; ++q) {
             float part = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) part = fmaf(qv[h][e], kf[q][e], part);
+            for (int e = 0; e < 8; ++e) part = fmaf(qv[e], kf[q][e], part);
             part = group_sum(part, LP);  // all lanes of a group share valid[q]
             sc[q] = valid[q] ? part * scale : -INFINITY;
             M = fmaxf(M, sc[q]);
@@ -1590,6 +1604,15 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
           }
         }
       }
+    };
+    // The next step's K/V rows are loaded while this step is folded (two
+    // register sets in turn).
+    for (int base = lo; base < hi; base += 2 * step) {
+      if (base + step < hi) load_into(kr2, vr2, base + step);
+      fold(kr, vr, base);
+      if (base + step >= hi) break;
+      if (base + 2 * step < hi) load_into(kr, vr, base + 2 * step);
+      fold(kr2, vr2, base + step);
     }
     // each position group's (m, l, acc) to LDS: merged across groups and
     // wavefronts below in one pass
