@@ -1559,15 +1559,17 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       for (int q = 0; q < ATT_ROUNDS; ++q) {
         const int t = base + (wave + MPK_NW * q) * PPR + pg;
         valid[q] = t < hi;
-        // row p comes from LDS; an idle lane (its row is not this split's)
-        // takes it too, so no value outside the rows in [lo, p) reaches
-        // the sums, whatever the cache holds there
+        // The loaded rows are unpacked on every lane (the wait for them is
+        // then in straight-line code, not in a branch that all lanes may
+        // skip, which would leave them outstanding into the next step's
+        // loads).  Row p comes from LDS; an idle lane (its row is not this
+        // split's) takes it too, so no value outside the rows in [lo, p)
+        // reaches the sums, whatever the cache holds there.
+        unpack8(K[q], kf[q]);
+        unpack8(V[q], vf[q]);
         if (t == p || !valid[q]) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) kf[q][e] = kv[dim0 + e], vf[q][e] = kv[d + dim0 + e];
-        } else {
-          unpack8(K[q], kf[q]);
-          unpack8(V[q], vf[q]);
         }
       }
 #pragma unroll
@@ -1606,13 +1608,23 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       }
     };
     // The next step's K/V rows are loaded while this step is folded (two
-    // register sets in turn).
-    for (int base = lo; base < hi; base += 2 * step) {
-      if (base + step < hi) load_into(kr2, vr2, base + step);
-      fold(kr, vr, base);
-      if (base + step >= hi) break;
-      if (base + 2 * step < hi) load_into(kr, vr, base + 2 * step);
-      fold(kr2, vr2, base + step);
+    // register sets in turn).  Inside the loop the loads are issued
+    // unconditionally (past the end every lane reads row lo, which is
+    // folded with weight 0): a load behind a branch makes the compiler's
+    // wait at the next fold count it as possibly absent, and that wait then
+    // also waits out the loads just issued for the step after.  A split of
+    // one step (every split up to 128 positions) folds it without loading
+    // a step past its end.
+    if (hi - lo <= step) {
+      fold(kr, vr, lo);
+    } else {
+      for (int base = lo; base < hi; base += 2 * step) {
+        load_into(kr2, vr2, base + step);
+        fold(kr, vr, base);
+        if (base + step >= hi) break;
+        load_into(kr, vr, base + 2 * step);
+        fold(kr2, vr2, base + step);
+      }
     }
     // each position group's (m, l, acc) to LDS: merged across groups and
     // wavefronts below in one pass
