@@ -1613,8 +1613,9 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     // folded with weight 0): a load behind a branch makes the compiler's
     // wait at the next fold count it as possibly absent, and that wait then
     // also waits out the loads just issued for the step after.  A split of
-    // one step (every split up to 128 positions) folds it without loading
-    // a step past its end.
+    // one step (8 x 64 / LP x ATT_ROUNDS positions: 64 at d = 128, the
+    // split size below which the context is not cut further) folds it
+    // without loading a step past its end.
     if (hi - lo <= step) {
       fold(kr, vr, lo);
     } else {
