@@ -16,6 +16,7 @@ import pytest
 import oracle
 import synth
 import persistent_task_runtime_amd as mpk
+from persistent_task_runtime_amd import timeline
 
 pytestmark = pytest.mark.gpu
 
@@ -218,6 +219,20 @@ def test_trace_orders_every_dependency(torch_dev):
     assert all(len(v) == 1 for v in per_worker.values())
     cus = [next(iter(v)) for v in per_worker.values()]
     assert len(set(cus)) == len(cus), "two workers shared a CU"
+    # the timeline export of the same records: one event per task on its
+    # worker's lane, lanes never overlapping, every boundary measured
+    doc = timeline.chrome_trace(tr.reshape(-1), tasks, timeline.op_labels(kinds))
+    ev = [e for e in doc["traceEvents"] if e.get("cat") == "task"]
+    assert len(ev) == n * NT
+    lanes = {}
+    for e in ev:
+        assert e["tid"] == tasks[e["args"]["task"]].worker
+        lanes.setdefault((e["pid"], e["tid"]), []).append((e["ts"], e["ts"] + e["dur"]))
+    for spans in lanes.values():
+        spans.sort()
+        assert all(a1 <= b0 + 1e-3 for (_, a1), (b0, _) in zip(spans, spans[1:]))
+    gaps = timeline.boundary_gaps(tr.reshape(-1), tasks, NT, chain)
+    assert np.isfinite(gaps["span_b"]).all() and (gaps["span_b"] > 0).all()
     sess.close()
 
 
