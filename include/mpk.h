@@ -198,9 +198,11 @@ int mpk_get_status(mpk_exec_t exec, int32_t* code, int32_t* iteration, int32_t* 
  * (flag == 0).  Uses an internal stream; waits for the flag write only. */
 int mpk_set_abort(mpk_exec_t exec, int32_t flag);
 
-/* Trace of the last run (launch cfg trace = 1): records of type
+/* Trace of the last run (launch cfg trace = 1 or 2): records of type
  * mpk_trace_record, one per (iteration, task), at index iteration * num_tasks
- * + task.  Tickets come from one device-wide atomic counter, so ticket order
+ * + task; every field of a record no task wrote is all ones (task = -1).
+ * Under trace = 2 no tickets are taken: start_ticket stays all ones and
+ * end_ticket is 0.  Tickets come from one device-wide atomic counter, so ticket order
  * is consistent with the order in which tasks became visible to each other. */
 typedef struct {
   int32_t task;          /* task id, -1 if the slot was never written */
@@ -211,7 +213,9 @@ typedef struct {
   uint64_t t_end;
   uint32_t hw_id;        /* HW_ID hardware register of the scheduler wave */
   uint32_t xcc_id;       /* XCC_ID hardware register */
-  uint64_t t_ready;      /* inputs staged, weight stream about to be consumed (GEMV tasks; else 0) */
+  uint64_t t_ready;      /* all inputs present (GEMV: staged, weight stream about to be consumed;
+                            attention and argmax: their words gathered); all ones when the
+                            task had nothing to do (an attention split beyond the context) */
 } mpk_trace_record;
 
 int mpk_read_trace(mpk_exec_t exec, void* host_buf, size_t bytes, size_t* written);

@@ -74,7 +74,7 @@ def task_events(records: np.ndarray, tasks, labels: Sequence[str],
                 "rows": [int(ti.row0), int(ti.row0) + int(ti.nrows)]}
         if ti.split >= 0:
             args["split"] = int(ti.split)
-        if int(r["start_ticket"]) or int(r["end_ticket"]):
+        if int(r["start_ticket"]) != 0xFFFFFFFF:  # taken under trace = 1 only
             args["tickets"] = [int(r["start_ticket"]), int(r["end_ticket"])]
         ev.append({"name": name, "cat": "task", "ph": "X", "pid": pid, "tid": int(ti.worker),
                    "ts": ts, "dur": dur, "args": args})
