@@ -188,6 +188,18 @@ DEV void lds_read_2f4_near(uint32_t a, f32x4& x0, f32x4& x1) {
                : "memory");
 }
 
+// K and V of two position rounds from an LDS ring slot: [K0][K1][V0][V1],
+// 1 KB each, this lane's 16 bytes at a (early-clobber outputs, see
+// lds_read_2f4).
+DEV void lds_read_kv2(uint32_t a, u32x4 (&K)[2], u32x4 (&V)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(K[0]), "=&v"(K[1]), "=&v"(V[0]), "=&v"(V[1])
+      : "v"(a)
+      : "memory");
+}
+
 DEV float lds_read_f32(uint32_t a) {
   float v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
@@ -1383,6 +1395,13 @@ DEV int argmax_task(const mpk_kparams& P, cop& D, char* smem, int tid, int s, in
 #define ATT_MAXG 4
 #define ATT_ROUNDS 2    // position rounds per wavefront whose K/V rows are loaded together
 #define ATT_GROUPS 64   // position groups per workgroup at most (NW waves x 64 / LP, d >= 64)
+#define ATT_RING 4      // steps of K/V rows in flight per wavefront (LDS ring, multi-step splits)
+#define ATT_SLOT (2 * ATT_ROUNDS * 1024)  // one ring slot: K and V of a step, 1 KB per round each
+static_assert(ATT_ROUNDS == 2, "lds_read_kv2 reads two rounds");
+// the ring overlays the group accumulators and what follows them
+static_assert(LDS_X + (ATT_MAXG * 128 + 256 + 2 * ATT_GROUPS * ATT_MAXG) * 4 + MPK_NW * ATT_RING * ATT_SLOT <=
+                  Lay<1>::TOTAL,
+              "attention K/V ring exceeds the LDS");
 
 // Sum over the LP lanes of a position group (lanes [g*LP, (g+1)*LP)), every
 // lane of the group receiving the same value (quad swaps, then half-row and
@@ -1403,6 +1422,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = T.row0, j = T.nrows, c = T.split, NS = D.nsplit;
   const int d = D.d, G = D.nq / D.nkv, half = d >> 1, LP = d >> 3, PPR = 64 / LP;
+  const int step = MPK_NW * PPR * ATT_ROUNDS;  // positions per step of all wavefronts
   const int p = cur_pos(smem, r);
   const int n = p + 1;
   const int na = min(NS, (n + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT);
@@ -1443,7 +1463,10 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   // has already waited for one (LDS_SYNCED), the rows are loaded before
   // this task's own wait; otherwise (nothing before it on this queue, or only
   // tasks with nothing to do) after it.
-  u32x4 kr[ATT_ROUNDS], vr[ATT_ROUNDS], kr2[ATT_ROUNDS], vr2[ATT_ROUNDS];
+  // (Splits of more than one step stream their rows through an LDS ring
+  // instead, below.)
+  const bool multi = hi - lo > step;
+  u32x4 kr[ATT_ROUNDS], vr[ATT_ROUNDS];
   auto load_into = [&](u32x4(&K)[ATT_ROUNDS], u32x4(&V)[ATT_ROUNDS], int base) {
 #pragma unroll
     for (int q = 0; q < ATT_ROUNDS; ++q) {
@@ -1455,7 +1478,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   };
   auto load_rounds = [&](int base) { load_into(kr, vr, base); };
   const bool early = uni(*lvi(smem, LDS_SYNCED)) != 0;
-  if (!sched && lo < hi && early) load_rounds(lo);
+  if (!sched && lo < hi && !multi && early) load_rounds(lo);
 
   // ---- q / k / v words of the group: wave hh < G + 2 takes one head vector ----
   const int hh = wave;
@@ -1491,7 +1514,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     if (*lvi(smem, LDS_CTL)) return -1;
   }
   if (tid == 0) *lvi(smem, LDS_SYNCED) = 1;
-  if (!sched && lo < hi && !early) load_rounds(lo);
+  if (!sched && lo < hi && !multi && !early) load_rounds(lo);
   // The K/V rows, RoPE factors and gains above are loads issued before the
   // device-scope polls: complete them here (see vm_drain_known; they were
   // issued first, so this costs little).
@@ -1548,7 +1571,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     // q is read from LDS in each step (asm reads: not hoisted into 32 more
     // live registers beside the two K/V register sets)
     const uint32_t qa = lds_addr(qs) + (uint32_t)dim0 * 4u;
-    const int step = MPK_NW * PPR * ATT_ROUNDS;
+    const uint32_t kva = lds_addr(kv) + (uint32_t)dim0 * 4u;
     // one base step: its positions folded into the running (m, l, acc)
     auto fold = [&](u32x4(&K)[ATT_ROUNDS], u32x4(&V)[ATT_ROUNDS], int base) {
       // this round's ATT_ROUNDS positions per lane group are folded into the
@@ -1568,8 +1591,15 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
         unpack8(K[q], kf[q]);
         unpack8(V[q], vf[q]);
         if (t == p || !valid[q]) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kf[q][e] = kv[dim0 + e], vf[q][e] = kv[d + dim0 + e];
+          // (asm reads: a compiler-visible LDS read here would wait for
+          // every K/V ring DMA in flight)
+          f32x4 k0, k1, v0, v1;
+          lds_read_2f4_near(kva, k0, k1);
+          lds_read_2f4_near(kva + (uint32_t)d * 4u, v0, v1);
+          kf[q][0] = k0.x, kf[q][1] = k0.y, kf[q][2] = k0.z, kf[q][3] = k0.w;
+          kf[q][4] = k1.x, kf[q][5] = k1.y, kf[q][6] = k1.z, kf[q][7] = k1.w;
+          vf[q][0] = v0.x, vf[q][1] = v0.y, vf[q][2] = v0.z, vf[q][3] = v0.w;
+          vf[q][4] = v1.x, vf[q][5] = v1.y, vf[q][6] = v1.z, vf[q][7] = v1.w;
         }
       }
 #pragma unroll
@@ -1607,26 +1637,48 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
         }
       }
     };
-    // The next step's K/V rows are loaded while this step is folded (two
-    // register sets in turn).  Inside the loop the loads are issued
-    // unconditionally (past the end every lane reads row lo, which is
-    // folded with weight 0): a load behind a branch makes the compiler's
-    // wait at the next fold count it as possibly absent, and that wait then
-    // also waits out the loads just issued for the step after.  A split of
-    // one step (8 x 64 / LP x ATT_ROUNDS positions: 64 at d = 128, the
-    // split size below which the context is not cut further) folds it
-    // without loading a step past its end.
-    if (hi - lo <= step) {
+    if (!multi) {
       fold(kr, vr, lo);
     } else {
-      for (int base = lo; base < hi; base += 2 * step) {
-        load_into(kr2, vr2, base + step);
-        fold(kr, vr, base);
-        if (base + step >= hi) break;
-        load_into(kr, vr, base + 2 * step);
-        fold(kr2, vr2, base + step);
+      // K/V rows through a ring of ATT_RING steps per wavefront in LDS,
+      // filled by global->LDS DMA: ATT_RING - 1 steps stay in flight while
+      // one is folded, and no registers are held by loads in flight.  The
+      // ring overlays the group accumulators (written below, after every
+      // wavefront has left this loop) and the gathered partials.  Past the
+      // end, steps re-read row lo (folded with weight 0).  Waits are exact
+      // counts: the loop issues no other vector-memory operation, and its
+      // LDS reads are asm, which the compiler does not hold for the DMAs.
+      const uint32_t ring = lds_addr(wacc) + (uint32_t)wave * (ATT_RING * ATT_SLOT);
+      auto dma_step = [&](int i) {
+        const int base = lo + i * step;
+        const uint32_t slot = ring + (uint32_t)(i & (ATT_RING - 1)) * ATT_SLOT;
+#pragma unroll
+        for (int q = 0; q < ATT_ROUNDS; ++q) {
+          const int t = base + (wave + MPK_NW * q) * PPR + pg;
+          const int tc = t < hi && t != p ? t : lo;  // in-bounds row for idle lanes
+          __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(kc + (int64_t)tc * d + dim0),
+                                           lds_ptr(slot + q * 1024), 16, 0, 16 /* sc1: device scope */);
+          __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(vc + (int64_t)tc * d + dim0),
+                                           lds_ptr(slot + (ATT_ROUNDS + q) * 1024), 16, 0, 16);
+        }
+      };
+      const int nst = (hi - lo + step - 1) / step;
+#pragma unroll
+      for (int i = 0; i < ATT_RING - 1; ++i) dma_step(i);
+      for (int i = 0; i < nst; ++i) {
+        dma_step(i + ATT_RING - 1);
+        vm_wait_known<(ATT_RING - 1) * 2 * ATT_ROUNDS>();  // step i has landed
+        u32x4 K[ATT_ROUNDS], V[ATT_ROUNDS];
+        lds_read_kv2(ring + (uint32_t)(i & (ATT_RING - 1)) * ATT_SLOT + (uint32_t)lane * 16u, K, V);
+        fold(K, V, lo + i * step);
       }
+      vm_drain_known();
     }
+  }
+  // every wavefront is done with the ring before the accumulators over it
+  // are written
+  if (multi) __syncthreads();
+  if (!sched) {
     // each position group's (m, l, acc) to LDS: merged across groups and
     // wavefronts below in one pass
     const int grp = wave * PPR + pg;

@@ -292,14 +292,19 @@ def test_watchdog_and_abort_end_the_run(torch_dev):
     s.close()
 
 
-def test_one_layer_matches_oracle(torch_dev):
-    """One Qwen3-8B-shaped layer, KV cache pre-filled N(0,1) to 512 positions,
-    input h ~ N(0,1), one decode step at position 512."""
+@pytest.mark.parametrize("ctx", [512, 10300])
+def test_one_layer_matches_oracle(torch_dev, ctx):
+    """One Qwen3-8B-shaped layer, KV cache pre-filled N(0,1) to ctx positions,
+    input h ~ N(0,1), one decode step at position ctx.  At 512 every
+    attention split is one step of 64 positions (register path); at 10300
+    the 32 splits hold 321-322 positions: six steps through the LDS ring of
+    four, the last one ragged (1-2 positions)."""
     import torch
     from persistent_task_runtime_amd import runner
 
-    log("one 8B layer")
-    w = synth.workload("one_layer")
+    log("one 8B layer, context %d" % ctx)
+    w = synth.workload("one_layer", tokens_width=ctx + 2, prompt_len=np.array([ctx + 1], np.int32),
+                       step0=np.array([ctx], np.int32), kv_prefill=ctx)
     sh = w.shape
     weights = synth.make_model(sh, seed=w.seed, with_embedding=False)
     x = synth.normal_f32(w.seed, "one_layer.h", (1, sh.hidden), 1.0)
@@ -314,20 +319,20 @@ def test_one_layer_matches_oracle(torch_dev):
     k_gpu = sess.kc[0].cpu().numpy().view(np.uint16)[0]
     v_gpu = sess.vc[0].cpu().numpy().view(np.uint16)[0]
     om = oracle.Model(sh, weights)
-    st = oracle.State(sh, np.zeros((1, 514), np.int32), w.step0, w.prompt_len, w.max_seq, K, V)
-    h_or = oracle.layer(om, 0, st, 0, 512, x[0])
+    st = oracle.State(sh, np.zeros((1, ctx + 2), np.int32), w.step0, w.prompt_len, w.max_seq, K, V)
+    h_or = oracle.layer(om, 0, st, 0, ctx, x[0])
     err = float(np.max(np.abs(h_gpu - h_or)))
     log("h max-abs err %.3g (|h| max %.3g)" % (err, np.max(np.abs(h_or))))
     assert err <= LOGIT_TOL
     # the new K/V row: equal, or one bf16 step apart where the fp32 values straddle a rounding boundary
     for nm, got, want in (("K", k_gpu, st.kcache[0, 0]), ("V", v_gpu, st.vcache[0, 0])):
-        a = synth.bf16_bits_to_f32(got[:, 512]).astype(np.float64)
-        b = synth.bf16_bits_to_f32(want[:, 512]).astype(np.float64)
+        a = synth.bf16_bits_to_f32(got[:, ctx]).astype(np.float64)
+        b = synth.bf16_bits_to_f32(want[:, ctx]).astype(np.float64)
         bad = np.abs(a - b) > 2.0 ** -7 * np.maximum(np.abs(b), 1e-30)
         where = [(j, int(i), a[j, i], b[j, i]) for j, i in zip(*np.nonzero(bad))][:8]
-        assert not bad.any(), "%s row 512: %d elements off, first (head, dim, gpu, oracle): %s" % (
-            nm, int(bad.sum()), where)
-        assert np.array_equal(got[:, :512], want[:, :512]), "pre-filled positions untouched"
+        assert not bad.any(), "%s row %d: %d elements off, first (head, dim, gpu, oracle): %s" % (
+            nm, ctx, int(bad.sum()), where)
+        assert np.array_equal(got[:, :ctx], want[:, :ctx]), "pre-filled positions untouched"
     sess.close()
 
 
