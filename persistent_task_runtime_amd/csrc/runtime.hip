@@ -1609,7 +1609,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
           lds_read_2f4_near(qa + (uint32_t)(h * d) * 4u, q0, q1);
           const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
           float sc[ATT_ROUNDS];
-          float M = sm.m[h];
+          float Mx = -INFINITY;
 #pragma unroll
           for (int q = 0; q < ATT_ROUNDS; ++q) {
             float part = 0.f;
@@ -1617,22 +1617,30 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
             for (int e = 0; e < 8; ++e) part = fmaf(qv[e], kf[q][e], part);
             part = group_sum(part, LP);  // all lanes of a group share valid[q]
             sc[q] = valid[q] ? part * scale : -INFINITY;
-            M = fmaxf(M, sc[q]);
+            Mx = fmaxf(Mx, sc[q]);
           }
-          if (M != -INFINITY) {
-            const float co = sm.m[h] == -INFINITY ? 0.f : exp2f(sm.m[h] - M);
-            float L = sm.l[h] * co;
+          // (m, l, acc) hold the sums relative to a reference m that moves
+          // only when a score exceeds it by more than 8 (base 2; always for
+          // the first score, m = -inf): weights stay below 2^8, and most
+          // steps skip the rescale.  Any reference gives the same softmax
+          // once l and acc share it, which the merges below rely on.
+          if (Mx > sm.m[h] + 8.f) {
+            const float co = sm.m[h] == -INFINITY ? 0.f : exp2f(sm.m[h] - Mx);
+            sm.l[h] *= co;
 #pragma unroll
             for (int e = 0; e < 8; ++e) sm.acc[h][e] *= co;
+            sm.m[h] = Mx;
+          }
+          if (Mx != -INFINITY) {
+            float L = sm.l[h];
 #pragma unroll
             for (int q = 0; q < ATT_ROUNDS; ++q) {
-              const float w = sc[q] == -INFINITY ? 0.f : exp2f(sc[q] - M);
+              const float w = sc[q] == -INFINITY ? 0.f : exp2f(sc[q] - sm.m[h]);
               L += w;
 #pragma unroll
               for (int e = 0; e < 8; ++e) sm.acc[h][e] = fmaf(w, vf[q][e], sm.acc[h][e]);
             }
             sm.l[h] = L;
-            sm.m[h] = M;
           }
         }
       }
@@ -1717,7 +1725,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       }
       const float cg = g < NG && mg != -INFINITY ? exp2f(mg - M) : 0.f;
       L += lg * cg;
-      if (g < NG) wm[g * ATT_MAXG + h] = cg;  // the group's weight replaces its maximum
+      if (g < NG) wm[g * ATT_MAXG + h] = cg;  // the group's weight replaces its reference m
     }
     L = wave_sum(L);
     if (lane == 0) hML[2 * h] = M, hML[2 * h + 1] = L;
