@@ -1624,8 +1624,10 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
           // the first score, m = -inf): weights stay below 2^8, and most
           // steps skip the rescale.  Any reference gives the same softmax
           // once l and acc share it, which the merges below rely on.
+          // (exponentials: the hardware's v_exp_f32, which maps -inf to 0;
+          // no weight here needs a denormal result)
           if (Mx > sm.m[h] + 8.f) {
-            const float co = sm.m[h] == -INFINITY ? 0.f : exp2f(sm.m[h] - Mx);
+            const float co = __builtin_amdgcn_exp2f(sm.m[h] - Mx);  // 0 for m = -inf
             sm.l[h] *= co;
 #pragma unroll
             for (int e = 0; e < 8; ++e) sm.acc[h][e] *= co;
@@ -1635,7 +1637,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
             float L = sm.l[h];
 #pragma unroll
             for (int q = 0; q < ATT_ROUNDS; ++q) {
-              const float w = sc[q] == -INFINITY ? 0.f : exp2f(sc[q] - sm.m[h]);
+              const float w = __builtin_amdgcn_exp2f(sc[q] - sm.m[h]);  // 0 for an idle position
               L += w;
 #pragma unroll
               for (int e = 0; e < 8; ++e) sm.acc[h][e] = fmaf(w, vf[q][e], sm.acc[h][e]);
