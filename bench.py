@@ -28,7 +28,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 # FETCH_SIZE + WRITE_SIZE, each scaled by a plain 1 GiB copy's readings
 # (profiles/mpk_persistent_qwen3_8b_b1_hbm_counters.md).  Reported only while
 # the kernel source is the one the counters were taken on.
-TRAFFIC = {"gb_per_launch": 977.3, "iters_per_launch": 64, "runtime_sha256_16": "19b8e6f9baf5123c"}
+TRAFFIC = {"gb_per_launch": 977.2, "iters_per_launch": 64, "runtime_sha256_16": "f7217c9c604b6ee6"}
 
 
 def measured_traffic(iters_per_launch: int):

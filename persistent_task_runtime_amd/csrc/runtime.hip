@@ -1447,7 +1447,8 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   const int dim0 = (lane % LP) * 8;
   const int pg = lane / LP;
   // scores are kept in base-2 units, s * log2(e) / sqrt(d): every
-  // exponential below is one exp2
+  // exponential below is one exp2.  The factor is applied to q once, when
+  // q is staged, rather than to every score.
   const float scale = 1.4426950408889634f / sqrtf((float)d);
 
   SoftState sm;
@@ -1534,8 +1535,8 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
         const float ra = ya * cs - yb * sn;
         const float rb = yb * cs + ya * sn;
         if (hh < G) {
-          qs[hh * d + lane] = ra;
-          qs[hh * d + lane + half] = rb;
+          qs[hh * d + lane] = ra * scale;
+          qs[hh * d + lane + half] = rb * scale;
         } else {
           const uint16_t ka = f2bf(ra), kb = f2bf(rb);
           kv[lane] = bf16f(ka);
@@ -1616,7 +1617,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 #pragma unroll
             for (int e = 0; e < 8; ++e) part = fmaf(qv[e], kf[q][e], part);
             part = group_sum(part, LP);  // all lanes of a group share valid[q]
-            sc[q] = valid[q] ? part * scale : -INFINITY;
+            sc[q] = valid[q] ? part : -INFINITY;
             Mx = fmaxf(Mx, sc[q]);
           }
           // (m, l, acc) hold the sums relative to a reference m that moves
