@@ -27,19 +27,35 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 # HBM bytes per 64-iteration launch of the persistent kernel from rocprofv3
 # FETCH_SIZE + WRITE_SIZE, each scaled by a plain 1 GiB copy's readings
 # (profiles/mpk_persistent_qwen3_8b_b1_hbm_counters.md).  Reported only while
-# the kernel source is the one the counters were taken on.
-TRAFFIC = {"gb_per_launch": 977.2, "iters_per_launch": 64, "runtime_sha256_16": "f7217c9c604b6ee6"}
+# the code the counters were taken on is unchanged: the digest covers the
+# device code, its tables and the graph builder, comments and layout
+# stripped.
+TRAFFIC = {"gb_per_launch": 977.2, "iters_per_launch": 64, "code_digest": "c82c63c50218e49a"}
+CODE_FILES = ("runtime.hip", "mpk_internal.h", "builder.cpp")
+
+
+def code_digest() -> str:
+    """sha256 (16 hex digits) of the C/HIP sources in CODE_FILES with
+    comments removed and whitespace collapsed (string literals are kept
+    as they are; none of these files has a comment marker inside one)."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for name in CODE_FILES:
+        src = open(os.path.join(ROOT, "persistent_task_runtime_amd", "csrc", name)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(name.encode() + b"\0" + " ".join(src.split()).encode() + b"\0")
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(iters_per_launch: int):
-    import hashlib
-
-    src = os.path.join(ROOT, "persistent_task_runtime_amd", "csrc", "runtime.hip")
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        dig = code_digest()
     except OSError:
         return None
-    if sha != TRAFFIC["runtime_sha256_16"] or iters_per_launch != TRAFFIC["iters_per_launch"]:
+    if dig != TRAFFIC["code_digest"] or iters_per_launch != TRAFFIC["iters_per_launch"]:
         return None
     return TRAFFIC["gb_per_launch"]
 

@@ -1570,7 +1570,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   // ---- scores and online softmax over this wave's positions ----
   if (!sched) {
     // q is read from LDS in each step (asm reads: not hoisted into 32 more
-    // live registers beside the two K/V register sets)
+    // live registers across the loop)
     const uint32_t qa = lds_addr(qs) + (uint32_t)dim0 * 4u;
     const uint32_t kva = lds_addr(kv) + (uint32_t)dim0 * 4u;
     // one base step: its positions folded into the running (m, l, acc)
