@@ -1395,9 +1395,10 @@ DEV int argmax_task(const mpk_kparams& P, cop& D, char* smem, int tid, int s, in
 #define ATT_MAXG 4
 #define ATT_ROUNDS 2    // position rounds per wavefront whose K/V rows are loaded together
 #define ATT_GROUPS 64   // position groups per workgroup at most (NW waves x 64 / LP, d >= 64)
-#define ATT_RING 4      // steps of K/V rows in flight per wavefront (LDS ring, multi-step splits)
+#define ATT_RING 2      // LDS ring slots (steps of K/V rows) per wavefront, multi-step splits
 #define ATT_SLOT (2 * ATT_ROUNDS * 1024)  // one ring slot: K and V of a step, 1 KB per round each
 static_assert(ATT_ROUNDS == 2, "lds_read_kv2 reads two rounds");
+static_assert((ATT_RING & (ATT_RING - 1)) == 0 && ATT_RING >= 2, "ring slots are indexed with i & (ATT_RING - 1)");
 // the ring overlays the group accumulators and what follows them
 static_assert(LDS_X + (ATT_MAXG * 128 + 256 + 2 * ATT_GROUPS * ATT_MAXG) * 4 + MPK_NW * ATT_RING * ATT_SLOT <=
                   Lay<1>::TOTAL,

@@ -297,8 +297,8 @@ def test_one_layer_matches_oracle(torch_dev, ctx):
     """One Qwen3-8B-shaped layer, KV cache pre-filled N(0,1) to ctx positions,
     input h ~ N(0,1), one decode step at position ctx.  At 512 every
     attention split is one step of 64 positions (register path); at 10300
-    the 32 splits hold 321-322 positions: six steps through the LDS ring of
-    four, the last one ragged (1-2 positions)."""
+    the 32 splits hold 321-322 positions: six steps through the two-slot
+    LDS ring (it wraps twice), the last one ragged (1-2 positions)."""
     import torch
     from persistent_task_runtime_amd import runner
 
