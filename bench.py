@@ -6,9 +6,17 @@ tied 151936-row embedding / LM head, seeded N(0, 0.02) bf16 weights, a
 39-token seeded prompt and greedy decoding (the pages' Figure 1 workload:
 39-token prompt, 512 generated tokens).  A step is one decode iteration:
 every layer, the LM head, the argmax and the step/tokens advance for the one
-request.  The warm-up steps ingest the prompt (untimed); the timed steps are
-the generating ones (defaults: 38 warm-up, 512 timed, in launches of 64
-iterations).
+request.
+
+Order of a run: --warmup persistent iterations on the same executable
+(untimed; step, tokens and the prompt are then restored), the 38 prompt
+iterations through the one-launch-per-operator path (untimed, whatever
+--warmup says: the prompt is input, not the measured work), then the timed
+generating iterations as persistent launches of --launch-iters iterations
+(the last launch takes the remainder).  The timed region covers the whole
+configured generation: max(--steps, 512) tokens, so the driver's short
+--steps still measures the 512-token workload; "steps" in the output is the
+number of iterations actually timed.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -60,8 +68,48 @@ def measured_traffic(iters_per_launch: int):
     return TRAFFIC["gb_per_launch"]
 
 
+GENERATED_TOKENS = 512  # the configured workload: 512 greedy tokens after a 39-token prompt
+PROMPT_TOKENS = 39
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def log_native_maps():
+    """Address ranges of the repository's native libraries and the HIP / HSA
+    runtimes in this process (stderr), to attribute any frame of a crash
+    report printed after the program's last line."""
+    spans = {}
+    try:
+        for line in open("/proc/self/maps"):
+            f = line.split()
+            if len(f) < 6:
+                continue
+            path = f[5]
+            if path.startswith(ROOT) or any(k in path for k in ("libamdhip64", "libhsa-runtime64", "libgomp")):
+                lo, hi = (int(x, 16) for x in f[0].split("-"))
+                a, b = spans.get(path, (lo, hi))
+                spans[path] = (min(a, lo), max(b, hi))
+    except OSError:
+        return
+    for path, (lo, hi) in sorted(spans.items(), key=lambda kv: kv[1]):
+        log("native map %#x-%#x %s" % (lo, hi, path))
+
+
+def plan_launches(n_iter: int, per_launch: int):
+    """Lengths of the persistent launches that cover n_iter iterations: as many
+    launches of per_launch as fit, then one with the remainder."""
+    if n_iter <= 0 or per_launch <= 0:
+        raise ValueError("iterations and iterations per launch must be positive")
+    full, rest = divmod(n_iter, per_launch)
+    return [per_launch] * full + ([rest] if rest else [])
+
+
+def timed_tokens(steps: int) -> int:
+    """Generated tokens in the timed region: the whole configured generation,
+    or more when --steps asks for more."""
+    return max(steps, GENERATED_TOKENS)
 
 
 def kv_bytes_per_position(sh) -> int:
@@ -92,16 +140,17 @@ def copy_calibration(n_bytes: int = 1 << 30) -> None:
     log("copied %d bytes 3 times" % n_bytes)
 
 
-def main():
+def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512, help="timed decode iterations")
-    ap.add_argument("--warmup", type=int, default=38,
-                    help="untimed iterations before the timed ones (the prompt)")
+    ap.add_argument("--steps", type=int, default=GENERATED_TOKENS,
+                    help="timed generated tokens (at least the configured 512 are timed)")
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed persistent iterations before the prompt is ingested")
     ap.add_argument("--launch-iters", type=int, default=64,
-                    help="iterations per persistent launch in the timed region")
+                    help="iterations per persistent launch in the timed region (last launch: remainder)")
     ap.add_argument("--per-op-steps", type=int, default=64)
-    ap.add_argument("--cpu-iters", type=int, default=6)
+    ap.add_argument("--cpu-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-op", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -109,7 +158,11 @@ def main():
     ap.add_argument("--workload", choices=("qwen3_8b", "long"), default="qwen3_8b",
                     help="long: the same model with each layer's K/V cache pre-filled N(0,1) to "
                          "32768 positions, 128 decode iterations from there (attention-heavy)")
-    args = ap.parse_args()
+    return ap.parse_args(argv)
+
+
+def main():
+    args = parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -126,12 +179,17 @@ def main():
     if args.workload == "long":
         return bench_long(args)
     sh = synth.QWEN3_8B
-    P = 39
-    K, W, L = args.steps, args.warmup, args.launch_iters
-    if K % L:
-        sys.exit("--steps must be a multiple of --launch-iters")
-    total = W + K
-    width = max(P + 512 + 1, total + 2)
+    P = PROMPT_TOKENS
+    K, W = timed_tokens(args.steps), args.warmup
+    launches = plan_launches(K, args.launch_iters)
+    # iterations at positions 0 .. P-2 consume prompt ids and write nothing;
+    # the iteration at P-1 consumes the last prompt id and yields the first
+    # generated token, so the timed iterations are positions P-1 .. P-2+K
+    n_prompt = P - 1
+    total = n_prompt + K
+    width = max(total + 2, W + 2)
+    if K != args.steps:
+        log("timing the configured %d generated tokens (--steps %d asks for fewer)" % (K, args.steps))
     w = synth.Workload("qwen3_8b", sh, 1, n_iter=total, tokens_width=width,
                        prompt_len=np.array([P], np.int32), step0=np.zeros(1, np.int32))
     t0 = time.time()
@@ -145,17 +203,32 @@ def main():
 
     stream = torch.cuda.current_stream()
     sess = runner.Session(w, model, max_seq=width)
-    if W:
+    toks0 = sess.tokens.clone()
+
+    def restart():
+        """step, tokens back to the prompt (the K/V rows are rewritten as the
+        positions are consumed again)"""
+        sess.step.zero_()
+        sess.tokens.copy_(toks0)
+
+    def ingest_prompt():
         # the prompt goes through the one-launch-per-operator path: the same
         # task bodies, bitwise the same state, and no persistent launch of
-        # another length in the profile of the timed one
-        sess.run(W, per_op=True)
+        # another length in the profile of the timed ones
+        sess.run(n_prompt, per_op=True)
         torch.cuda.synchronize()
         sess.check_status()
-    n_launch = K // L
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launch)]
+
+    if W:
+        sess.run(W)
+        torch.cuda.synchronize()
+        sess.check_status()
+        restart()
+        log("warm-up: %d persistent iterations" % W)
+    ingest_prompt()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
     torch.cuda.synchronize()
-    for a, b in ev:
+    for (a, b), L in zip(ev, launches):
         a.record(stream)
         sess.run(L)
         b.record(stream)
@@ -167,32 +240,38 @@ def main():
     step_now = int(sess.step.cpu()[0])
     assert step_now == total, (step_now, total)
     toks = sess.tokens.cpu().numpy()[0]
-    assert (toks[: total + 1] >= 0).all()
-    alg_bytes = sum(iteration_bytes(sh, W + i) for i in range(K))
-    # roofline of the dominant kernel: algorithmic bytes per launch / mean launch duration
-    launch_avg = sum(launch_ms) / n_launch
-    achieved = (alg_bytes / n_launch) / (launch_avg / 1e3) / 1e9
+    assert (toks[: total + 1] >= 0).all() and (toks[: total + 1] < sh.vocab).all()
+    # roofline of the dominant kernel: algorithmic bytes per launch / mean
+    # launch duration (HIP events on the launch stream)
+    pos = n_prompt
+    launch_bytes = []
+    for L in launches:
+        launch_bytes.append(sum(iteration_bytes(sh, pos + i) for i in range(L)))
+        pos += L
+    alg_bytes = sum(launch_bytes)
+    achieved = sum(b / (t / 1e3) for b, t in zip(launch_bytes, launch_ms)) / len(launches) / 1e9
+    launch_avg = sum(launch_ms) / len(launches)
     bound_ms = alg_bytes / K / (HBM_PEAK_GBS * 1e9) * 1e3
-    log("persistent: %.4f ms/token over %d launches of %d iterations (mean launch %.3f ms), "
+    log("persistent: %.4f ms/token over %d launches %s (mean launch %.3f ms), "
         "%.1f GB/s algorithmic (%.1f%% of %.0f GB/s)"
-        % (ms_tok, n_launch, L, launch_avg, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
-    sess.close()
+        % (ms_tok, len(launches), launches, launch_avg, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
 
     per_op = None
     if not args.no_per_op:
         Kp = min(args.per_op_steps, K)
-        s2 = runner.Session(w, model, max_seq=width)
-        s2.run(W, per_op=True)
-        torch.cuda.synchronize()
+        restart()
+        ingest_prompt()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        s2.run(Kp, per_op=True)
+        sess.run(Kp, per_op=True)
         e1.record(stream)
         torch.cuda.synchronize()
-        s2.check_status()
+        sess.check_status()
         per_op = e0.elapsed_time(e1) / Kp
         log("one launch per operator: %.4f ms/token over %d steps" % (per_op, Kp))
-        s2.close()
+    sess.close()
+    del sess, model
+    torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -226,10 +305,12 @@ def main():
         "config": {"workload": "qwen3_8b_batch1_prompt39_greedy", "layers": sh.layers,
                    "hidden": sh.hidden, "q_heads": sh.n_q, "kv_heads": sh.n_kv, "head_dim": sh.head_dim,
                    "ffn": sh.ffn, "vocab": sh.vocab, "tied_lm_head": True, "batch": 1,
-                   "prompt_tokens": P, "generated_tokens": K, "iterations_per_launch": L,
+                   "prompt_tokens": P, "generated_tokens": K, "iterations_per_launch": launches[0],
+                   "launches": len(launches),
                    "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(L)},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(launches[0]) if len(set(launches)) == 1 else None},
         "kernel": "mpk_persistent<1>",
         "traffic_unit": "GB per launch",
         "launch_ms": round(launch_avg, 4),
@@ -240,6 +321,7 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    log_native_maps()
 
 
 def bench_long(args):

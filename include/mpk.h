@@ -79,9 +79,11 @@ typedef struct {
  *     wavefront beside its eight worker wavefronts; num_workers must equal
  *     the CU count and num_schedulers must be 0 or num_workers.
  *   MPK_SCHED_DEDICATED: rule num_workers + num_schedulers / 4 == CU count,
- *     num_schedulers a multiple of 4 (four scheduler wavefronts on each
- *     scheduler CU).  Accepted by mpk_build_graph for the rule check only;
- *     mpk_compile rejects it with MPK_ERR_SPLIT (not implemented). */
+ *     num_schedulers a multiple of 4 (four scheduler wavefronts per
+ *     scheduler CU).  Operator tiles go to the num_workers worker CUs only;
+ *     the num_schedulers / 4 scheduler CUs hold no tile: the first of them
+ *     runs each iteration's argmax / step-advance task, the others idle.
+ *     The launch still covers every CU (the pages' split of the chip). */
 enum { MPK_SCHED_CORESIDENT = 0, MPK_SCHED_DEDICATED = 1 };
 
 typedef struct {
@@ -177,10 +179,20 @@ int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg* launch,
 int mpk_compile(mpk_graph_t graph, int32_t device, mpk_exec_t* out);
 
 /* Run `num_iterations` decode iterations as ONE persistent cooperative launch
- * on `stream` (preceded by one small kernel that clears the event counters).
- * Requires step[r] + num_iterations < tokens width and < max_seq for every r
- * (checked on the device values at the start of the run after a copy to the
- * host; returns MPK_ERR_SHAPE without launching otherwise). */
+ * on `stream`, preceded by one small kernel (mpk_begin_run) that clears the
+ * status word and checks the meta tensors on the device.  Asynchronous: the
+ * call makes no host-device round trip and returns once both kernels are
+ * queued (the first traced run of a length allocates its trace buffer).
+ * Returns MPK_ERR_SHAPE without launching when num_iterations alone exceeds
+ * the tokens width or max_seq, or a logits tensor holds fewer iterations.
+ * The device check (same rule as mpk_check_run): for every request r,
+ * 0 <= step[r], step[r] + num_iterations < tokens width, step[r] +
+ * num_iterations <= max_seq, and every token id the run reads from tokens
+ * (position step[r], and the prompt positions up to step[r] + num_iterations
+ * - 1 below prompt_len[r]) is in [0, vocab).  On failure no iteration runs:
+ * after synchronisation mpk_get_status reports MPK_ERR_SHAPE with
+ * iteration -1 and the request index as task, and tokens, step and the KV
+ * caches are unchanged. */
 int mpk_run_steps(mpk_exec_t exec, int32_t num_iterations, void* stream);
 
 /* The same task bodies launched one kernel per operator per iteration (the
@@ -190,8 +202,10 @@ int mpk_run_steps(mpk_exec_t exec, int32_t num_iterations, void* stream);
 int mpk_run_steps_per_op(mpk_exec_t exec, int32_t num_iterations, void* stream);
 
 /* After the stream of the last run is synchronised: device status code
- * (MPK_OK, MPK_ERR_DEVICE_TIMEOUT or MPK_ERR_ABORTED), the iteration and the
- * task id at which it was raised (-1 when OK).  Any pointer may be NULL. */
+ * (MPK_OK, MPK_ERR_DEVICE_TIMEOUT, MPK_ERR_ABORTED, or MPK_ERR_SHAPE from
+ * the start-of-run check), the iteration and the task id at which it was
+ * raised (-1 when OK; for MPK_ERR_SHAPE iteration -1 and the request index).
+ * Any pointer may be NULL.  Synchronous (one small device-to-host copy). */
 int mpk_get_status(mpk_exec_t exec, int32_t* code, int32_t* iteration, int32_t* task);
 
 /* Ask a running persistent launch to stop (flag != 0) or clear the request
@@ -228,33 +242,91 @@ typedef struct {
   int32_t worker;       /* worker (workgroup) whose queue holds the task */
   int32_t row0, nrows;  /* GEMV tiles: virtual rows; attention: request, kv head */
   int32_t split;        /* attention: KV split index; -1 otherwise */
-  int32_t dep_event[3]; /* -1 = none */
-  int32_t dep_count[3]; /* signals per iteration on that event */
-  int32_t dep_prev[3];  /* 1 = wait for the previous iteration's signals */
-  int32_t out_event;    /* event signalled when done (-1 = none) */
+  /* Operator-level data edges (introspection; the device waits on the
+   * stamped words each task body reads, not on these): an "event" is one
+   * operator's output words, published by `count` tasks per iteration. */
+  int32_t dep_event[3]; /* producing operator's event, -1 = none */
+  int32_t dep_count[3]; /* tasks that publish that operator's words */
+  int32_t dep_prev[3];  /* 1 = the previous iteration's words (the token word of the argmax task) */
+  int32_t out_event;    /* this operator's event */
 } mpk_task_info;
 
 typedef struct {
   int32_t num_tasks, num_events, num_workers, max_queue;
   int32_t num_ops;
   int32_t sink_op;
+  int32_t num_queues;          /* CUs of the launch grid: num_workers + dedicated scheduler CUs */
   const mpk_task_info* tasks;
-  const int32_t* event_count;  /* [num_events] signals per iteration */
+  const int32_t* event_count;  /* [num_events] publishing tasks per iteration */
   const int32_t* event_op;     /* [num_events] producing operator */
-  const int32_t* queue_len;    /* [num_workers] */
-  const int32_t* queues;       /* [num_workers][max_queue] task ids in execution order */
+  const int32_t* queue_len;    /* [num_queues] */
+  const int32_t* queues;       /* [num_queues][max_queue] task ids in execution order */
 } mpk_graph_info;
 
 int mpk_get_graph_info(mpk_graph_t graph, mpk_graph_info* info);
 
-/* Run the graph's dependency protocol on host threads (one per worker), with
- * every task body replaced by a random sleep of up to jitter_us microseconds
- * (seeded).  Writes one mpk_trace_record per (iteration, task) into
- * host_trace (num_iterations * num_tasks records; times in ns).  Returns
- * MPK_ERR_DEVICE_TIMEOUT if any wait exceeds timeout_ms, which is how a
- * malformed graph shows up as a deadlock.  For tests of the builder. */
-int mpk_simulate(mpk_graph_t graph, int32_t num_iterations, uint32_t seed, int32_t jitter_us,
-                 int32_t timeout_ms, mpk_trace_record* host_trace);
+/* Host model of the device's dependency protocol (tests of the builder and
+ * of the protocol; no device call).  One host thread per CU queue walks the
+ * queue's tasks, iteration by iteration, with each task body replaced by a
+ * seeded random sleep of up to jitter_us microseconds.  As on the device, a
+ * task waits for exactly the stamped 64-bit words it reads (payload + stamp
+ * iter_base + s + 1 of iteration s), the attention split owning the
+ * position gathers the other splits' partial words, the owner stores the
+ * K/V row of the position before it publishes, and the argmax task writes
+ * tokens / step and the token word the next iteration's embedding waits for
+ * (P1 "How MPK Works").  The word buffers, K/V rows and meta tensors live in
+ * a simulation state that persists across mpk_simulate calls, like device
+ * buffers across launches.  Checks: every accepted word carries the payload
+ * its producer wrote in this iteration of this call (a stale word that
+ * passes the stamp check is reported), every K/V row read was written (or
+ * pre-filled) before, token words agree with tokens.  Planted faults show
+ * that the checks fire. */
+typedef struct mpk_sim_s* mpk_sim_t;
+
+enum {
+  MPK_SIM_NO_FAULT = 0,
+  MPK_SIM_FAULT_KV_AFTER_PUBLISH = 1, /* the owner split publishes before storing the K/V row */
+  MPK_SIM_FAULT_SKIP_WAIT = 2,        /* attention reads its q/k/v words without waiting (QKV tiles late) */
+  MPK_SIM_FAULT_DROP_PUBLISH = 3      /* LM-head tile 0 never publishes (a wait must time out) */
+};
+
+typedef struct {
+  int32_t num_iterations;
+  uint32_t iter_base;  /* stamp of iteration s is iter_base + s + 1; the caller advances it by
+                          num_iterations per call, as the library does per launch */
+  uint32_t seed;
+  int32_t jitter_us;
+  int32_t timeout_ms;  /* per wait; a wait past it ends the call with MPK_ERR_DEVICE_TIMEOUT */
+  int32_t fault;       /* MPK_SIM_* */
+} mpk_sim_cfg;
+
+/* Simulation state for `graph` from host copies of step[B], tokens[B][width]
+ * and prompt_len[B]; K/V rows of positions < kv_filled count as pre-filled.
+ * The graph must outlive the state. */
+int mpk_sim_create(mpk_graph_t graph, const int32_t* step, const int32_t* tokens,
+                   const int32_t* prompt_len, int32_t kv_filled, mpk_sim_t* out);
+
+/* One simulated launch of cfg->num_iterations iterations.  Writes one
+ * mpk_trace_record per (iteration, task) into host_trace (times in ns since
+ * the call's start; hw_id = the queue; start_ticket is taken once every word
+ * the task reads is present, before it writes any; attention splits with
+ * nothing to do keep start_ticket all ones).  Returns MPK_OK,
+ * MPK_ERR_SHAPE (the start-of-run rule of mpk_run_steps),
+ * MPK_ERR_DEVICE_TIMEOUT (a wait exceeded timeout_ms) or MPK_ERR_GRAPH (a
+ * protocol check failed; mpk_last_error says which). */
+int mpk_simulate(mpk_sim_t sim, const mpk_sim_cfg* cfg, mpk_trace_record* host_trace);
+
+/* Current step[B] and tokens[B][width] of the simulation (either may be NULL). */
+int mpk_sim_read_meta(mpk_sim_t sim, int32_t* step, int32_t* tokens);
+
+void mpk_sim_destroy(mpk_sim_t sim);
+
+/* The start-of-run rule of mpk_run_steps applied on the host to host copies
+ * of the meta tensors (step[B], tokens[B][width], prompt_len[B] with the
+ * graph's shapes), for callers that keep them: MPK_OK, or MPK_ERR_SHAPE
+ * naming the first request and position that break it.  Pure host work. */
+int mpk_check_run(mpk_graph_t graph, const int32_t* step, const int32_t* tokens,
+                  const int32_t* prompt_len, int32_t num_iterations);
 
 /* Device address of tensor `tensor_id` (attached or library-owned). */
 int mpk_get_tensor_ptr(mpk_exec_t exec, int32_t tensor_id, void** dev_ptr);

@@ -16,8 +16,11 @@ into One Kernel Launch", sections "How MPK Works", "Getting Started" and
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence, Tuple
 
@@ -91,10 +94,18 @@ class mpk_task_info(ctypes.Structure):
 
 class mpk_graph_info(ctypes.Structure):
     _fields_ = [("num_tasks", c_i32), ("num_events", c_i32), ("num_workers", c_i32),
-                ("max_queue", c_i32), ("num_ops", c_i32), ("sink_op", c_i32),
+                ("max_queue", c_i32), ("num_ops", c_i32), ("sink_op", c_i32), ("num_queues", c_i32),
                 ("tasks", ctypes.POINTER(mpk_task_info)), ("event_count", ctypes.POINTER(c_i32)),
                 ("event_op", ctypes.POINTER(c_i32)), ("queue_len", ctypes.POINTER(c_i32)),
                 ("queues", ctypes.POINTER(c_i32))]
+
+
+MPK_SIM_NO_FAULT, MPK_SIM_FAULT_KV_AFTER_PUBLISH, MPK_SIM_FAULT_SKIP_WAIT, MPK_SIM_FAULT_DROP_PUBLISH = 0, 1, 2, 3
+
+
+class mpk_sim_cfg(ctypes.Structure):
+    _fields_ = [("num_iterations", c_i32), ("iter_base", c_u32), ("seed", c_u32), ("jitter_us", c_i32),
+                ("timeout_ms", c_i32), ("fault", c_i32)]
 
 
 TRACE_DTYPE_FIELDS = [("task", "<i4"), ("iteration", "<i4"), ("start_ticket", "<u4"),
@@ -132,7 +143,11 @@ def load_library(path: str = LIB_PATH):
         "mpk_set_abort": (c_i32, [c_vp, c_i32]),
         "mpk_read_trace": (c_i32, [c_vp, c_vp, ctypes.c_size_t, P(ctypes.c_size_t)]),
         "mpk_get_graph_info": (c_i32, [c_vp, P(mpk_graph_info)]),
-        "mpk_simulate": (c_i32, [c_vp, c_i32, c_u32, c_i32, c_i32, c_vp]),
+        "mpk_sim_create": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, P(c_vp)]),
+        "mpk_simulate": (c_i32, [c_vp, P(mpk_sim_cfg), c_vp]),
+        "mpk_sim_read_meta": (c_i32, [c_vp, c_vp, c_vp]),
+        "mpk_sim_destroy": (None, [c_vp]),
+        "mpk_check_run": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32]),
         "mpk_get_tensor_ptr": (c_i32, [c_vp, c_i32, P(c_vp)]),
         "mpk_destroy_exec": (None, [c_vp]),
         "mpk_destroy_graph": (None, [c_vp]),
@@ -146,9 +161,27 @@ def load_library(path: str = LIB_PATH):
     return L
 
 
+# Load order.  torch ships its own HIP runtime; a process holds one runtime
+# per soname, the first one loaded, and every HIP library binds to it.  torch
+# (which the package uses for device memory and streams) is imported first, so
+# the library always runs on torch's runtime.  Importing torch does not
+# initialise the GPU.  The library itself is opened when the package is
+# imported, normally before the GPU runtime is initialised: a library opened
+# later is mapped below the address range the runtime reserves, and its
+# exit-time destructor (which unregisters its device code from the HIP
+# runtime) then runs in an order the runtime's other libraries do not see.
+try:
+    import torch  # noqa: F401
+except ImportError:  # the library then binds to the system HIP runtime
+    pass
+if os.path.exists(LIB_PATH):
+    load_library()
+
+
 EXPORTED = ["mpk_build_graph", "mpk_compile", "mpk_run_steps", "mpk_run_steps_per_op",
             "mpk_get_status", "mpk_set_abort", "mpk_read_trace", "mpk_get_graph_info",
-            "mpk_simulate", "mpk_get_tensor_ptr", "mpk_destroy_exec", "mpk_destroy_graph",
+            "mpk_sim_create", "mpk_simulate", "mpk_sim_read_meta", "mpk_sim_destroy",
+            "mpk_check_run", "mpk_get_tensor_ptr", "mpk_destroy_exec", "mpk_destroy_graph",
             "mpk_last_error"]
 
 
@@ -211,14 +244,43 @@ def mpk_get_graph_info(graph: int) -> mpk_graph_info:
     return info
 
 
-def mpk_simulate(graph: int, num_iterations: int, seed: int = 0, jitter_us: int = 0,
-                 timeout_ms: int = 5000):
+def mpk_sim_create(graph: int, step, tokens, prompt_len, kv_filled: int = 0) -> int:
     import numpy as np
-    info = mpk_get_graph_info(graph)
-    buf = np.empty(num_iterations * info.num_tasks, dtype=np.dtype(TRACE_DTYPE_FIELDS))
-    _check(load_library().mpk_simulate(graph, num_iterations, seed, jitter_us, timeout_ms,
-                                       buf.ctypes.data))
+    a = [np.ascontiguousarray(v, dtype=np.int32) for v in (step, tokens, prompt_len)]
+    out = c_vp()
+    _check(load_library().mpk_sim_create(graph, a[0].ctypes.data, a[1].ctypes.data, a[2].ctypes.data,
+                                         kv_filled, ctypes.byref(out)))
+    return out.value
+
+
+def mpk_simulate(sim: int, num_tasks: int, num_iterations: int, iter_base: int, seed: int = 0,
+                 jitter_us: int = 0, timeout_ms: int = 5000, fault: int = MPK_SIM_NO_FAULT):
+    """One simulated launch; returns the trace records [num_iterations * num_tasks]."""
+    import numpy as np
+    cfg = mpk_sim_cfg(num_iterations, iter_base, seed, jitter_us, timeout_ms, fault)
+    buf = np.empty(num_iterations * num_tasks, dtype=np.dtype(TRACE_DTYPE_FIELDS))
+    _check(load_library().mpk_simulate(sim, ctypes.byref(cfg), buf.ctypes.data))
     return buf
+
+
+def mpk_sim_read_meta(sim: int, batch: int, width: int):
+    import numpy as np
+    step = np.empty(batch, np.int32)
+    toks = np.empty((batch, width), np.int32)
+    _check(load_library().mpk_sim_read_meta(sim, step.ctypes.data, toks.ctypes.data))
+    return step, toks
+
+
+def mpk_sim_destroy(sim: int) -> None:
+    if sim:
+        load_library().mpk_sim_destroy(sim)
+
+
+def mpk_check_run(graph: int, step, tokens, prompt_len, num_iterations: int) -> None:
+    import numpy as np
+    a = [np.ascontiguousarray(v, dtype=np.int32) for v in (step, tokens, prompt_len)]
+    _check(load_library().mpk_check_run(graph, a[0].ctypes.data, a[1].ctypes.data, a[2].ctypes.data,
+                                        num_iterations))
 
 
 def mpk_get_tensor_ptr(exe: int, tensor_id: int) -> int:
@@ -369,18 +431,34 @@ def qwen3_graph(shape, batch: int, ptrs: Dict[str, int], tokens_width: int, max_
     return g, meta
 
 
+# Executables still open when the interpreter exits are closed by an atexit
+# hook, which runs while the HIP runtime (and any profiler attached to it) is
+# still intact; a finaliser running later, during interpreter teardown, makes
+# no HIP call.
+_live = weakref.WeakSet()
+
+
+@atexit.register
+def _close_live_executables():
+    for e in list(_live):
+        e.close()
+
+
 class Executable:
     """Owns a built graph and its compiled executable."""
 
     def __init__(self, spec: GraphSpec, meta: mpk_meta, model: mpk_model_cfg,
                  launch: mpk_launch_cfg, device: int = 0):
         self.spec = spec
+        self.exe = 0
         self.graph = mpk_build_graph(model, launch, spec.c_tensors(), spec.ops, meta)
         try:
             self.exe = mpk_compile(self.graph, device)
         except Exception:
             mpk_destroy_graph(self.graph)
+            self.graph = 0
             raise
+        _live.add(self)
 
     def tensor_ptr(self, name: str) -> int:
         return mpk_get_tensor_ptr(self.exe, self.spec.index[name])
@@ -398,8 +476,11 @@ class Executable:
         mpk_destroy_exec(getattr(self, "exe", 0))
         mpk_destroy_graph(getattr(self, "graph", 0))
         self.exe = self.graph = 0
+        _live.discard(self)
 
     def __del__(self):
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:

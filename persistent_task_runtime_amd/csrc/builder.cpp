@@ -1,5 +1,5 @@
-// Host task-graph builder: operators -> tiles -> tasks, events, per-worker
-// queues; graph checks; a host-thread simulator of the device protocol.
+// Host task-graph builder: operators -> tiles -> tasks, per-CU queues; graph
+// checks; the host form of the start-of-run rule.
 //
 // Sources (web pages on Mirage Persistent Kernel, "MPK"):
 //   P1 "Mirage Persistent Kernel: Fusing Multi-GPU LLM Inference into One
@@ -13,19 +13,16 @@
 // "工作机制"), and advise that each operator's thread-block count be a multiple
 // of the worker count so no worker idles (P1 "The API"; P5 "Grenzen der
 // README-Aussagen").  Here each operator is split into at most one tile per
-// worker CU (256 on MI355X), tiles become tasks, every operator owns one
-// monotonic event counter, and each worker gets a static queue of its tasks
-// in operator order.  A task waits until its producers' events reach
-// count * (iteration + 1) (or count * iteration for reads of the previous
-// iteration's tokens/step), so counters are never reset inside a run.
+// worker CU (256 on MI355X), tiles become tasks, and each CU gets a static
+// queue of its tasks in operator order.  Tasks hand values to each other as
+// stamped words (the device runtime): a task waits for exactly the words it
+// reads, so the graph needs no event counters; the operator-level edges
+// derived here check the graph (producers before consumers, every operator
+// an ancestor of the last) and are kept for introspection.
 #include <algorithm>
-#include <memory>
-#include <atomic>
-#include <chrono>
 #include <cstring>
-#include <random>
+#include <memory>
 #include <set>
-#include <thread>
 
 #include "graph.hpp"
 
@@ -142,6 +139,7 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
     return mpk_fail(MPK_ERR_INVALID_ARG, "unknown sched_mode");
   }
   const int W = g->num_workers;
+  g->num_queues = Lc.num_cus;
 
   // ---- meta tensors ----
   const int B = meta->num_requests;
@@ -310,6 +308,14 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
         act_read(i, o.in[0]);
         reads_meta[i] = 1;
         D.kind = MPK_TK_ATTN;
+        // one attention task per worker at least per (request, kv head): a
+        // split that owns the position gathers the others, so two groups
+        // must never share a queue (an owner could wait on a split queued
+        // behind it)
+        if (B * nkv > W)
+          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": num_requests x n_kv_heads = " +
+                                             std::to_string(B * nkv) + " exceeds the " + std::to_string(W) +
+                                             " workers (one attention task per worker)");
         D.nq = nq, D.nkv = nkv, D.d = d, D.S = M.max_seq;
         D.nsplit = mpk_attn_splits(W, B, nkv, M.max_seq);
         D.ntiles = B * nkv * D.nsplit;
@@ -348,11 +354,10 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
     if (g->dops[i].kind == 0) continue;
     op_ev[i] = (int)g->ev_count.size();
     const mpk_dev_op& D = g->dops[i];
+    // tasks that publish the operator's words (attention: one owner split per group)
     int cnt = D.kind == MPK_TK_ATTN ? B * D.nkv : D.ntiles;
     g->ev_count.push_back(cnt);
     g->ev_op.push_back(i);
-    g->ev_base.push_back(g->n_flags);
-    g->n_flags += cnt;
     g->dops[i].event = op_ev[i];
   }
   int sink = -1;
@@ -428,16 +433,14 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
       T.worker = D.kind == MPK_TK_ATTN ? t
                                        : D.worker_base + (int)(((int64_t)t * (W - D.worker_base)) / D.ntiles);
       T.split = -1;
-      T.out_flag = g->ev_base[op_ev[i]] + t;
       if (D.kind == MPK_TK_ATTN) {
         int per_req = D.nkv * D.nsplit;
         T.row0 = t / per_req;                   // request
         T.nrows = (t % per_req) / D.nsplit;     // kv head
         T.split = t % D.nsplit;
-        T.last_only = 1;
-        T.out_flag = g->ev_base[op_ev[i]] + T.row0 * D.nkv + T.nrows;
       } else if (D.kind == MPK_TK_ARGMAX) {
-        T.worker = 0;
+        // co-resident mode: worker 0; dedicated mode: the first scheduler CU
+        T.worker = g->num_queues > W ? W : 0;
         T.row0 = 0;
         T.nrows = D.N0;
       } else {
@@ -447,15 +450,10 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
         T.row0 = u0 * a;
         T.nrows = (u1 - u0) * a;
       }
-      T.n_deps = (int)deps[i].size();
-      for (int k = 0; k < MPK_MAX_DEPS; ++k) T.dep_base[k] = T.dep_n[k] = T.dep_prev[k] = -1;
       mpk_task_info I{};
       for (int k = 0; k < MPK_MAX_DEPS; ++k) I.dep_event[k] = I.dep_count[k] = I.dep_prev[k] = -1;
-      for (int k = 0; k < T.n_deps; ++k) {
+      for (int k = 0; k < (int)deps[i].size(); ++k) {
         const int e = op_ev[deps[i][k].first];
-        T.dep_base[k] = g->ev_base[e];
-        T.dep_n[k] = g->ev_count[e];
-        T.dep_prev[k] = deps[i][k].second;
         I.dep_event[k] = e;
         I.dep_count[k] = g->ev_count[e];
         I.dep_prev[k] = deps[i][k].second;
@@ -466,18 +464,20 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
       g->info.push_back(I);
     }
   }
-  // ---- per-worker queues in operator order ----
-  std::vector<std::vector<int>> q(W);
+  // ---- per-CU queues in operator order (dedicated scheduler CUs hold the
+  // argmax task or nothing) ----
+  const int NQ = g->num_queues;
+  std::vector<std::vector<int>> q(NQ);
   for (size_t k = 0; k < g->tasks.size(); ++k) q[g->tasks[k].worker].push_back((int)k);
-  g->qlen.assign(W, 0);
+  g->qlen.assign(NQ, 0);
   g->max_queue = 1;
-  for (int w = 0; w < W; ++w) {
+  for (int w = 0; w < NQ; ++w) {
     g->qlen[w] = (int)q[w].size();
     g->max_queue = std::max(g->max_queue, g->qlen[w]);
   }
-  g->queues.assign((size_t)W * g->max_queue, mpk_dev_qentry{-1});
-  g->queue_ids.assign((size_t)W * g->max_queue, -1);
-  for (int w = 0; w < W; ++w) {
+  g->queues.assign((size_t)NQ * g->max_queue, mpk_dev_qentry{-1});
+  g->queue_ids.assign((size_t)NQ * g->max_queue, -1);
+  for (int w = 0; w < NQ; ++w) {
     const int n = g->qlen[w];
     for (int k = 0; k < n; ++k) {
       g->queues[(size_t)w * g->max_queue + k] = mpk_dev_qentry{q[w][k]};
@@ -494,6 +494,7 @@ extern "C" int mpk_get_graph_info(mpk_graph_t g, mpk_graph_info* info) {
   info->num_tasks = (int)g->tasks.size();
   info->num_events = (int)g->ev_count.size();
   info->num_workers = g->num_workers;
+  info->num_queues = g->num_queues;
   info->max_queue = g->max_queue;
   info->num_ops = (int)g->dops.size();
   info->sink_op = g->sink;
@@ -507,69 +508,29 @@ extern "C" int mpk_get_graph_info(mpk_graph_t g, mpk_graph_info* info) {
 
 extern "C" void mpk_destroy_graph(mpk_graph_t g) { delete g; }
 
-// ---- host-thread simulation of the device protocol ----------------------
-extern "C" int mpk_simulate(mpk_graph_t g, int32_t n_iter, uint32_t seed, int32_t jitter_us,
-                            int32_t timeout_ms, mpk_trace_record* trace) {
+// The start-of-run rule of mpk_begin_run (device) on host copies of the meta
+// tensors: positions inside tokens and the KV cache, and every id the run
+// reads from tokens inside the vocabulary.
+extern "C" int mpk_check_run(mpk_graph_t g, const int32_t* step, const int32_t* tokens,
+                             const int32_t* prompt_len, int32_t n_iter) {
   mpk_clear_error();
-  if (!g || n_iter <= 0 || !trace || jitter_us < 0 || timeout_ms <= 0)
-    return mpk_fail(MPK_ERR_INVALID_ARG, "mpk_simulate: bad argument");
-  const int W = g->num_workers, NT = (int)g->tasks.size();
-  std::vector<std::atomic<uint32_t>> flags(g->n_flags);
-  for (auto& e : flags) e.store(0);
-  // last-arriver groups of attention: (op, request, kv head)
-  std::vector<std::atomic<uint32_t>> grp(NT);
-  for (auto& e : grp) e.store(0);
-  std::atomic<uint32_t> ticket{0};
-  std::atomic<int> failed{0};
-  for (int64_t i = 0; i < (int64_t)n_iter * NT; ++i) trace[i] = mpk_trace_record{-1, -1, 0, 0, 0, 0, 0, 0, 0};
-  auto t0 = std::chrono::steady_clock::now();
-  auto now_ns = [&] {
-    return (uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(
-               std::chrono::steady_clock::now() - t0).count();
-  };
-  auto worker = [&](int w) {
-    std::mt19937 rng(seed * 7919u + (uint32_t)w);
-    for (int s = 0; s < n_iter && !failed.load(); ++s) {
-      for (int k = 0; k < g->qlen[w]; ++k) {
-        const int tid = g->queues[(size_t)w * g->max_queue + k].task;
-        const mpk_dev_task& T = g->tasks[tid];
-        auto start = std::chrono::steady_clock::now();
-        for (int d = 0; d < T.n_deps; ++d) {
-          const uint32_t target = (uint32_t)(s + 1 - T.dep_prev[d]);
-          for (int f = T.dep_base[d]; f < T.dep_base[d] + T.dep_n[d]; ++f) {
-            while (flags[f].load(std::memory_order_acquire) < target) {
-              if (failed.load()) return;
-              if (std::chrono::steady_clock::now() - start > std::chrono::milliseconds(timeout_ms)) {
-                failed.store(1);
-                return;
-              }
-              std::this_thread::yield();
-            }
-          }
-        }
-        mpk_trace_record& R = trace[(int64_t)s * NT + tid];
-        R.task = tid;
-        R.iteration = s;
-        R.start_ticket = ticket.fetch_add(1);
-        R.t_start = now_ns();
-        R.hw_id = (uint32_t)w;
-        if (jitter_us) std::this_thread::sleep_for(std::chrono::microseconds(rng() % (jitter_us + 1)));
-        bool signal = true;
-        const mpk_dev_op& D = g->dops[T.op];
-        if (T.last_only) {
-          const int group = g->op_first_task[T.op] + (T.row0 * D.nkv + T.nrows) * D.nsplit;
-          const uint32_t old = grp[group].fetch_add(1, std::memory_order_acq_rel);
-          signal = (old % (uint32_t)D.nsplit) == (uint32_t)D.nsplit - 1;
-        }
-        R.end_ticket = ticket.fetch_add(1);
-        R.t_end = now_ns();
-        if (signal) flags[T.out_flag].store((uint32_t)(s + 1), std::memory_order_release);
-      }
+  if (!g || !step || !tokens || !prompt_len) return mpk_fail(MPK_ERR_INVALID_ARG, "mpk_check_run: NULL argument");
+  if (n_iter <= 0) return mpk_fail(MPK_ERR_INVALID_ARG, "num_iterations must be positive");
+  const int B = g->meta.num_requests;
+  const int64_t width = g->tensors[g->meta.tokens].dims[1];
+  for (int r = 0; r < B; ++r) {
+    const int p0 = step[r];
+    if (p0 < 0 || (int64_t)p0 + n_iter >= width || (int64_t)p0 + n_iter > g->model.max_seq)
+      return mpk_fail(MPK_ERR_SHAPE, "request " + std::to_string(r) + ": step " + std::to_string(p0) + " + " +
+                                         std::to_string(n_iter) +
+                                         " iterations leaves the tokens tensor or the KV cache");
+    const int q_end = std::min(p0 + n_iter, std::max(prompt_len[r], p0 + 1));
+    for (int q = p0; q < q_end; ++q) {
+      const int t = tokens[(int64_t)r * width + q];
+      if (t < 0 || t >= g->model.vocab)
+        return mpk_fail(MPK_ERR_SHAPE, "request " + std::to_string(r) + ": token id " + std::to_string(t) +
+                                           " at position " + std::to_string(q) + " is outside the vocabulary");
     }
-  };
-  std::vector<std::thread> th;
-  for (int w = 0; w < W; ++w) th.emplace_back(worker, w);
-  for (auto& t : th) t.join();
-  if (failed.load()) return mpk_fail(MPK_ERR_DEVICE_TIMEOUT, "simulated dependency wait timed out");
+  }
   return MPK_OK;
 }

@@ -16,7 +16,8 @@ struct mpk_graph_s {
   std::vector<mpk_op> ops;
 
   // derived by the builder
-  int num_workers = 0;
+  int num_workers = 0;   // CUs that take tiles
+  int num_queues = 0;    // CUs of the launch grid (workers + dedicated scheduler CUs)
   int sink = -1;
   std::vector<int> producer;        // per tensor: producing op, -1
   std::vector<int> embed_src;       // per tensor: E tensor id if output of an EMBED op, else -1
@@ -24,13 +25,12 @@ struct mpk_graph_s {
   std::vector<int> op_first_task, op_ntasks;
   std::vector<mpk_dev_task> tasks;
   std::vector<mpk_task_info> info;
-  std::vector<int> ev_count, ev_op, ev_base;  // per event: producers (flags), operator, first flag
-  int n_flags = 0;
+  std::vector<int> ev_count, ev_op;  // per event (an operator's output words): publishing tasks, operator
   int argmax_op = -1;                           // internal operator appended after the LM head
   std::vector<int> qlen;
   int max_queue = 0;
-  std::vector<mpk_dev_qentry> queues;  // [num_workers][max_queue]
-  std::vector<int32_t> queue_ids;      // [num_workers][max_queue] task ids (introspection)
+  std::vector<mpk_dev_qentry> queues;  // [num_queues][max_queue]
+  std::vector<int32_t> queue_ids;      // [num_queues][max_queue] task ids (introspection)
 };
 
 // Thread-local error reporting shared by both translation units.

@@ -67,9 +67,8 @@ typedef struct {
   int64_t logits_iters;
 } mpk_dev_op;
 
-/* One task (a tile of an operator).  The dependency fields describe the
- * operator-level graph (introspection and the host simulation); on the
- * device a task waits for the stamped words it reads. */
+/* One task (a tile of an operator).  A task carries no dependency fields: it
+ * waits for exactly the stamped words its body reads. */
 typedef struct {
   int32_t kind;
   int32_t op;
@@ -77,13 +76,7 @@ typedef struct {
   int32_t worker;
   int32_t row0, nrows; /* GEMV: virtual rows; ATTN: request, kv head */
   int32_t split;       /* ATTN split */
-  int32_t n_deps;
-  int32_t dep_base[MPK_MAX_DEPS]; /* first flag of the producer operator */
-  int32_t dep_n[MPK_MAX_DEPS];    /* number of flags of the producer operator */
-  int32_t dep_prev[MPK_MAX_DEPS]; /* 1: wait for the previous iteration's stamp */
-  int32_t out_flag;    /* flag this task stamps (attention: its group's last arriver) */
-  int32_t last_only;   /* 1: only the last arriver of the tile group stamps */
-  int32_t pad[1];
+  int32_t pad;
 } mpk_dev_task;
 
 /* Per queue entry: the task id. */
@@ -122,7 +115,9 @@ typedef struct {
   int32_t rope_half;
   float rms_eps;
   int32_t vocab;
-  int32_t pos0[MPK_MAX_BATCH];  /* step[r] at launch: position of request r in iteration s is pos0[r] + s */
+  int32_t max_seq;
+  int32_t* pos0;                /* [B] step[r] at launch, written by the run's first kernel: position
+                                   of request r in iteration s is pos0[r] + s */
   uint32_t iter_base;           /* stamp of iteration s is iter_base + s + 1 */
 } mpk_kparams;
 

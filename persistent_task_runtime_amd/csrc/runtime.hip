@@ -278,6 +278,7 @@ DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 #define LDS_POS (LDS_BEST + 512)         // [8] int: position of request r in the current iteration
 #define LDS_TOK (LDS_POS + 32)           // [8] int: token of request r in the current iteration
 #define LDS_SYNCED (LDS_TOK + 32)        // int: a task of this iteration has received inputs of it
+#define LDS_POS0 (LDS_SYNCED + 32)       // [8] int: position of request r in the launch's first iteration
 // control words: [0] stop flag, [8, 40) wait-round slots, [40] row claims
 #define LDS_OUT 2048
 #define LDS_OUT_FLOATS 1024
@@ -310,11 +311,16 @@ DEV int cur_pos(const char* smem, int b) {
   return __builtin_amdgcn_readfirstlane(lvi(smem, LDS_POS)[b]);
 }
 
-// Scheduler wavefront: positions of iteration s into LDS_POS (uniform
-// indices into the kernel-argument array).
+// Scheduler wavefront, once per launch: the positions of the launch's first
+// iteration (written by mpk_begin_run ahead of the launch) into LDS_POS0.
+DEV void load_positions(const mpk_kparams& P, char* smem, int lane) {
+  if (lane < P.B) lvi(smem, LDS_POS0)[lane] = ld_devi(P.pos0 + lane);
+}
+
+// Scheduler wavefront: positions of iteration s into LDS_POS.
 DEV void set_positions(const mpk_kparams& P, char* smem, int s, int lane) {
   if (lane == 0)
-    for (int b = 0; b < P.B; ++b) lvi(smem, LDS_POS)[b] = P.pos0[b] + s;
+    for (int b = 0; b < P.B; ++b) lvi(smem, LDS_POS)[b] = lvi(smem, LDS_POS0)[b] + s;
 }
 
 // Per-lane forms: the position of request b (b may differ between lanes), and
@@ -474,8 +480,11 @@ DEV int resolve_tokens(const mpk_kparams& P, char* smem, int tid, int s, int tas
     const int rc = wait_round(P, Wt, need, s, task_id, smem, tid);
     if (rc <= 0) {
       if (rc == 0 && tid < P.B) {
+        // every id a run consumes is checked by mpk_begin_run before the
+        // run starts (a failed check stops the run); the clamp only keeps an
+        // id that the caller changed during the run inside the table
         const int t = tok[tid];
-        tok[tid] = t < 0 ? 0 : (t >= P.vocab ? P.vocab - 1 : t);  // ids are checked on the host; stay in bounds
+        tok[tid] = t < 0 ? 0 : (t >= P.vocab ? P.vocab - 1 : t);
       }
       __syncthreads();
       return rc;
@@ -1816,8 +1825,11 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_persistent(mpk_kparams P) 
   const bool sched = wave == MPK_NW;
   cqent* Q = (cqent*)(const void*)P.queues + (int64_t)blockIdx.x * P.qstride;
   const int qlen = ((const CAS int32_t*)(const void*)P.qlen)[blockIdx.x];
+  // a failed start-of-run check (or a stop already recorded): no work at all
+  if (uni(__hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0) return;
   lds_vi* ctl = lvi(smem, LDS_CTL);
   if (tid == 0) ctl[0] = 0;
+  if (sched) load_positions(P, smem, lane);
   for (int s = 0; s < P.n_iter; ++s) {
     for (int k = 0; k < qlen; ++k) {
       const int task_id = Q[k].task;
@@ -1866,19 +1878,59 @@ __global__ __launch_bounds__(MPK_THREADS, 1) void mpk_op_kernel(mpk_kparams P, i
   const bool sched = wave == MPK_NW;
   const int task_id = first_task + blockIdx.x;
   ctask& T = tasks_of(P)[task_id];
+  if (uni(__hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0) return;
   lds_vi* ctl = lvi(smem, LDS_CTL);
   if (tid == 0) ctl[0] = 0;
   // every earlier launch (every earlier iteration) has ended
   if (tid == 0) *lvi(smem, LDS_SYNCED) = 1;
+  if (sched) load_positions(P, smem, lane);
   if (sched) set_positions(P, smem, s, lane);
   __syncthreads();
   run_task<NB>(P, T, task_id, s, smem, tid, sched, -1);
   vm_wait<0>();
 }
 
-__global__ void mpk_zero_u32(uint32_t* p, int64_t n) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
+// First kernel of every run, on the run's stream: clears the status word
+// (not the host's stop request) and the trace ticket counter, records each
+// request's position at launch (pos0) for the run's kernels, and checks what
+// the run will consume: 0 <= step[r], step[r] + n < tokens width,
+// step[r] + n <= max_seq, and every token id read from `tokens` (position
+// step[r], and the prompt ids at step[r] + 1 .. step[r] + n - 1 that the
+// iterations feed forward) inside [0, vocab).  A failed check records
+// MPK_ERR_SHAPE with iteration -1 and the request as the task; every kernel
+// of the run then returns at once.  Same rule as mpk_check_run on the host.
+// One workgroup of 64 threads.
+__global__ void mpk_begin_run(mpk_kparams P, int n_iter) {
+  const int lane = threadIdx.x;
+  if (lane == 0) {
+    P.status->code = 0;
+    P.status->iteration = 0;
+    P.status->task = 0;
+    *P.ticket_ctr = 0u;
+  }
+  __syncthreads();
+  for (int r = 0; r < P.B; ++r) {
+    const int p0 = P.step[r];
+    const int plen = P.prompt_len[r];
+    bool bad = p0 < 0 || (int64_t)p0 + n_iter >= P.tokens_width || (int64_t)p0 + n_iter > P.max_seq;
+    if (!bad) {
+      // ids read from tokens: position p0, and q in (p0, p0 + n) below the prompt's end
+      const int q_end = min(p0 + n_iter, max(plen, p0 + 1));
+      for (int q = p0 + lane; q < q_end; q += 64) {
+        const int t = P.tokens[(int64_t)r * P.tokens_width + q];
+        bad |= t < 0 || t >= P.vocab;
+      }
+    }
+    if (__ballot(bad) != 0) {
+      if (lane == 0) {
+        P.status->code = MPK_ERR_SHAPE;
+        P.status->iteration = -1;
+        P.status->task = r;
+      }
+      return;
+    }
+    if (lane == 0) P.pos0[r] = p0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1899,6 +1951,7 @@ struct mpk_exec_s {
   std::vector<uint64_t*> ll_ptr;     // per tensor: stamped words of an operator output, or NULL
   float* d_rope = nullptr;
   mpk_dev_status* d_status = nullptr;
+  int32_t* d_pos0 = nullptr;         // [MPK_MAX_BATCH] positions at launch (mpk_begin_run)
   mpk_trace_record* d_trace = nullptr;
   int64_t trace_cap = 0;  // records
   int last_iters = 0;
@@ -1952,15 +2005,13 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   mpk_clear_error();
   if (!g || !out) return mpk_fail(MPK_ERR_INVALID_ARG, "mpk_compile: NULL argument");
   *out = nullptr;
-  if (g->launch.sched_mode != MPK_SCHED_CORESIDENT)
-    return mpk_fail(MPK_ERR_SPLIT, "only the co-resident scheduler mode is implemented");
   HIPCHK(hipSetDevice(device));
   hipDeviceProp_t prop;
   HIPCHK(hipGetDeviceProperties(&prop, device));
-  if (prop.multiProcessorCount != g->num_workers)
-    return mpk_fail(MPK_ERR_SPLIT, "graph built for " + std::to_string(g->num_workers) +
-                                       " workers, device has " +
-                                       std::to_string(prop.multiProcessorCount) + " CUs");
+  if (prop.multiProcessorCount != g->num_queues)
+    return mpk_fail(MPK_ERR_SPLIT, "graph built for " + std::to_string(g->num_queues) +
+                                       " CUs, device has " +
+                                       std::to_string(prop.multiProcessorCount));
   int coop = 0;
   HIPCHK(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, device));
   if (!coop) return mpk_fail(MPK_ERR_NOT_CORESIDENT, "device has no cooperative launch");
@@ -2078,6 +2129,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   if ((rc = dalloc(x.get(), &x->d_qlen, g->qlen.size() * 4))) return rc;
   HIPCHK(hipMemcpy(x->d_qlen, g->qlen.data(), g->qlen.size() * 4, hipMemcpyHostToDevice));
   if ((rc = dalloc(x.get(), &x->d_status, sizeof(mpk_dev_status)))) return rc;
+  if ((rc = dalloc(x.get(), &x->d_pos0, MPK_MAX_BATCH * sizeof(int32_t)))) return rc;
 
   // RoPE table, fp64 angles rounded to fp32 (pair i of a head: angle p * theta^(-2i/d))
   const int half = M.head_dim / 2;
@@ -2115,6 +2167,8 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   K.rope_half = half;
   K.rms_eps = M.rms_eps;
   K.vocab = M.vocab;
+  K.max_seq = M.max_seq;
+  K.pos0 = x->d_pos0;
   // The zero fills above (hipMemset) are ordered on the null stream only;
   // a run on another stream must never see a buffer before it is zeroed (a
   // reused allocation could still hold words stamped by an earlier
@@ -2130,33 +2184,17 @@ static std::atomic<uint64_t> g_stamps{0};
 static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
   if (!x) return mpk_fail(MPK_ERR_INVALID_ARG, "NULL exec");
   if (n_iter <= 0) return mpk_fail(MPK_ERR_INVALID_ARG, "num_iterations must be positive");
-  HIPCHK(hipSetDevice(x->device));
-  // bounds of tokens / KV cache for every request
-  std::vector<int32_t> step(x->B);
-  HIPCHK(hipMemcpyAsync(step.data(), x->kp.step, x->B * 4, hipMemcpyDeviceToHost, st));
-  HIPCHK(hipStreamSynchronize(st));
-  std::vector<int32_t> toks((size_t)x->B * x->kp.tokens_width);
-  HIPCHK(hipMemcpyAsync(toks.data(), x->kp.tokens, toks.size() * 4, hipMemcpyDeviceToHost, st));
-  HIPCHK(hipStreamSynchronize(st));
-  for (int r = 0; r < x->B; ++r) {
-    int64_t last = (int64_t)step[r] + n_iter;
-    if (step[r] >= 0 && step[r] < x->kp.tokens_width) {
-      const int32_t t = toks[(size_t)r * x->kp.tokens_width + step[r]];
-      if (t < 0 || t >= x->g->model.vocab)
-        return mpk_fail(MPK_ERR_SHAPE, "request " + std::to_string(r) + ": token id " + std::to_string(t) +
-                                           " at position " + std::to_string(step[r]) + " is outside the vocabulary");
-    }
-    if (step[r] < 0 || last >= x->kp.tokens_width || last > x->g->model.max_seq)
-      return mpk_fail(MPK_ERR_SHAPE, "request " + std::to_string(r) + ": step " + std::to_string(step[r]) +
-                                         " + " + std::to_string(n_iter) +
-                                         " iterations leaves the tokens tensor or the KV cache");
-  }
+  // Checks that need no device value; positions and token ids are checked
+  // on the device by mpk_begin_run (no host round trip per launch).
+  if ((int64_t)n_iter >= x->kp.tokens_width || n_iter > x->g->model.max_seq)
+    return mpk_fail(MPK_ERR_SHAPE, std::to_string(n_iter) + " iterations leave the tokens tensor or the KV cache");
   for (size_t i = 0; i < x->g->dops.size(); ++i) {
     const mpk_dev_op& D = x->g->dops[i];
     if (D.kind == MPK_TK_LMHEAD && x->g->ops[i].out[0] >= 0 && D.logits_iters < n_iter)
       return mpk_fail(MPK_ERR_SHAPE, "logits tensor holds fewer iterations than requested");
   }
-  // trace buffer
+  HIPCHK(hipSetDevice(x->device));
+  // trace buffer (allocated by the first traced run that needs more room)
   x->kp.trace = nullptr;
   if (x->g->launch.trace) {
     int64_t need = (int64_t)n_iter * x->kp.n_tasks;
@@ -2171,12 +2209,6 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
     x->kp.trace = x->d_trace;
     x->kp.trace_tickets = x->g->launch.trace == 1;
   }
-  // positions at launch: request r is at step[r] + s in iteration s (the
-  // LM-head argmax advances step by one per iteration, on the device)
-  for (int r = 0; r < x->B; ++r) x->kp.pos0[r] = step[r];
-  // positions at launch: request r is at step[r] + s in iteration s (the
-  // LM-head argmax advances step by one per iteration, on the device)
-  for (int r = 0; r < x->B; ++r) x->kp.pos0[r] = step[r];
   x->kp.n_iter = n_iter;
   x->last_iters = n_iter;
   // stamps of this run: base + 1 .. base + n_iter, taken from a counter
@@ -2186,9 +2218,8 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
   if (base + (uint64_t)n_iter >= 0xffffffffull)
     return mpk_fail(MPK_ERR_STATE, "iteration stamps exhausted (2^32 iterations per process)");
   x->kp.iter_base = (uint32_t)base;
-  hipLaunchKernelGGL(mpk_zero_u32, dim3(1), dim3(64), 0, st, x->d_ticket_ctr, (int64_t)1);
-  // clear code / iteration / task; a stop request (abort_req) stays until cleared
-  hipLaunchKernelGGL(mpk_zero_u32, dim3(1), dim3(64), 0, st, (uint32_t*)x->d_status, (int64_t)3);
+  // status, trace ticket, positions at launch, checks of step / tokens
+  hipLaunchKernelGGL(mpk_begin_run, dim3(1), dim3(64), 0, st, x->kp, (int)n_iter);
   HIPCHK(hipGetLastError());
   return MPK_OK;
 }
@@ -2199,7 +2230,7 @@ extern "C" int mpk_run_steps(mpk_exec_t x, int32_t n_iter, void* stream) {
   int rc = prepare_run(x, n_iter, st);
   if (rc) return rc;
   void* args[] = {&x->kp};
-  HIPCHK(hipLaunchCooperativeKernel(x->kernel_persistent, dim3(x->g->num_workers), dim3(MPK_THREADS), args,
+  HIPCHK(hipLaunchCooperativeKernel(x->kernel_persistent, dim3(x->g->num_queues), dim3(MPK_THREADS), args,
                                     x->lds_bytes, st));
   return MPK_OK;
 }

@@ -68,7 +68,7 @@ class Session:
 
     def __init__(self, w: "synth.Workload", model: DeviceModel, logits_iters: int = 0,
                  trace: bool = False, max_seq: Optional[int] = None, kv=None,
-                 spin_timeout_ns: int = 0, x_in=None):
+                 spin_timeout_ns: int = 0, x_in=None, launch=None):
         import torch
 
         dev = _dev()
@@ -114,7 +114,8 @@ class Session:
                                      x_out_ptr=self.x_out.data_ptr() if self.x_out is not None else 0)
         num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
         mcfg = mpk.model_cfg(sh, B, self.max_seq)
-        lcfg = mpk.launch_cfg(num_cus, trace=trace, spin_timeout_ns=spin_timeout_ns)
+        lcfg = launch if launch is not None else mpk.launch_cfg(num_cus, trace=trace,
+                                                                  spin_timeout_ns=spin_timeout_ns)
         self.model = model
         self.exe = mpk.Executable(spec, meta, mcfg, lcfg)
 
@@ -137,11 +138,11 @@ class Session:
 
 
 def run_workload(w: "synth.Workload", n_iter: int, want_logits: bool = False, per_op: bool = False,
-                 trace: bool = False, model: Optional[DeviceModel] = None) -> dict:
+                 trace: bool = False, model: Optional[DeviceModel] = None, launch=None) -> dict:
     import torch
 
     model = model or DeviceModel(w.shape, w.seed, w.gains)
-    sess = Session(w, model, logits_iters=n_iter if want_logits else 0, trace=trace)
+    sess = Session(w, model, logits_iters=n_iter if want_logits else 0, trace=trace, launch=launch)
     sess.run(n_iter, per_op=per_op)
     torch.cuda.synchronize()
     sess.check_status()

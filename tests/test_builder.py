@@ -53,8 +53,8 @@ def info_arrays(g):
     tasks = [info.tasks[i] for i in range(info.num_tasks)]
     ev_cnt = [info.event_count[i] for i in range(info.num_events)]
     ev_op = [info.event_op[i] for i in range(info.num_events)]
-    qlen = [info.queue_len[w] for w in range(info.num_workers)]
-    queues = [[info.queues[w * info.max_queue + k] for k in range(qlen[w])] for w in range(info.num_workers)]
+    qlen = [info.queue_len[w] for w in range(info.num_queues)]
+    queues = [[info.queues[w * info.max_queue + k] for k in range(qlen[w])] for w in range(info.num_queues)]
     return info, tasks, ev_cnt, ev_op, queues
 
 
@@ -135,35 +135,6 @@ def test_dependencies_follow_the_decoder_chain():
         assert deps[1] == ((sink, 1),)
         for i in range(2, len(kinds) + 1):
             assert deps[i] == ((i - 1, 0),), (i, deps[i])
-    finally:
-        mpk.mpk_destroy_graph(g)
-
-
-def test_simulated_protocol_respects_every_edge_under_jitter():
-    shape = synth.TINY
-    g, spec = build(shape, num_cus=32, tokens_width=16, max_seq=16)
-    try:
-        info, tasks, ev_cnt, ev_op, queues = info_arrays(g)
-        n_iter = 3
-        tr = mpk.mpk_simulate(g, n_iter, seed=7, jitter_us=200, timeout_ms=20000)
-        assert (tr["task"] >= 0).all(), "every task ran in every iteration"
-        NT = info.num_tasks
-        tr = tr.reshape(n_iter, NT)
-        kinds = [o.kind for o in spec.ops]
-        by_op = {}
-        for i, t in enumerate(tasks):
-            by_op.setdefault(t.op, []).append(i)
-        # edges derived from the decoder's operator order, not from the builder tables
-        chain = [i for i, k in enumerate(kinds) if k != mpk.MPK_OP_EMBED] + [len(kinds)]
-        for s in range(n_iter):
-            for a, b in zip(chain, chain[1:]):
-                end_a = max(tr[s, i]["end_ticket"] for i in by_op[a])
-                start_b = min(tr[s, i]["start_ticket"] for i in by_op[b])
-                assert end_a < start_b, (s, a, b)
-            if s:
-                end_lm = max(tr[s - 1, i]["end_ticket"] for i in by_op[chain[-1]])
-                start_first = min(tr[s, i]["start_ticket"] for i in by_op[chain[0]])
-                assert end_lm < start_first
     finally:
         mpk.mpk_destroy_graph(g)
 
@@ -253,5 +224,59 @@ def test_single_layer_graph_without_embedding_or_lm_head():
         first = [t for t in tasks if t.op == 0]
         # no producer: waits for the previous iteration's last operator
         assert {(ev_op[t.dep_event[0]], t.dep_prev[0]) for t in first} == {(info.sink_op, 1)}
+    finally:
+        mpk.mpk_destroy_graph(g)
+
+
+def test_more_attention_groups_than_workers_is_a_shape_error():
+    # B x n_kv attention groups need one worker each at least (an owner split
+    # must never queue behind another group's split)
+    sh = synth.ModelShape(1, 256, 16, 16, 16, 256, 256)
+    with pytest.raises(mpk.MPKError) as e:
+        build(sh, num_cus=8)
+    assert e.value.code == mpk.MPK_ERR_SHAPE and "attention" in mpk.mpk_last_error()
+    g, _ = build(sh, num_cus=16)
+    mpk.mpk_destroy_graph(g)
+
+
+def test_host_run_check_follows_the_start_of_run_rule():
+    """mpk_check_run: positions inside tokens and the KV cache; every id the
+    run reads from tokens (the one at step, then the prompt ids it feeds
+    forward) inside the vocabulary; generated slots past the prompt are not
+    read."""
+    V = synth.TINY.vocab
+    g, spec = build(synth.TINY, B=2, tokens_width=64, max_seq=60)
+    try:
+        toks = np.full((2, 64), -1, np.int32)
+        toks[0, :10] = 5
+        toks[1, :4] = 7
+        plen = np.array([10, 4], np.int32)
+        step = np.zeros(2, np.int32)
+        mpk.mpk_check_run(g, step, toks, plen, 30)
+        bad = toks.copy()
+        bad[0, 9] = V
+        with pytest.raises(mpk.MPKError) as e:
+            mpk.mpk_check_run(g, step, bad, plen, 30)
+        assert e.value.code == mpk.MPK_ERR_SHAPE and "request 0" in str(e.value) and "position 9" in str(e.value)
+        mpk.mpk_check_run(g, step, bad, plen, 9)  # position 9 is not read by 9 iterations from 0
+        bad = toks.copy()
+        bad[1, 2] = -3
+        with pytest.raises(mpk.MPKError) as e:
+            mpk.mpk_check_run(g, step, bad, plen, 3)
+        assert "request 1" in str(e.value)
+        # a generating request reads only the id at its position
+        s2 = np.array([10, 4], np.int32)
+        t2 = toks.copy()
+        t2[0, 10] = 1
+        t2[1, 4] = 2
+        mpk.mpk_check_run(g, s2, t2, plen, 20)
+        t2[1, 4] = V + 1
+        with pytest.raises(mpk.MPKError):
+            mpk.mpk_check_run(g, s2, t2, plen, 20)
+        # positions: tokens width 64, KV capacity 60
+        with pytest.raises(mpk.MPKError, match="leaves"):
+            mpk.mpk_check_run(g, np.array([0, 4], np.int32), toks, plen, 61)
+        with pytest.raises(mpk.MPKError, match="leaves"):
+            mpk.mpk_check_run(g, np.array([-1, 4], np.int32), toks, plen, 1)
     finally:
         mpk.mpk_destroy_graph(g)

@@ -1,0 +1,140 @@
+"""The host model of the device protocol (mpk_simulate): stamped words, the
+per-launch stamp base, owner-split gathers and K/V rows stored before the
+word that orders their readers, run on host threads over the builder's own
+operator and task tables (no GPU).
+
+Positions 58..69 of a tiny decoder with 32 CUs: the attention context grows
+from one split of 64 positions to two at position 64, so the split that
+owns the position (and gathers the other's partial) changes mid-run."""
+import numpy as np
+import pytest
+
+import synth
+import persistent_task_runtime_amd as mpk
+
+from test_builder import build, info_arrays
+
+NONE = 0xFFFFFFFF
+WIDTH = MAX_SEQ = 200
+P0 = 58
+
+
+def _graph():
+    g, spec = build(synth.TINY, num_cus=32, tokens_width=WIDTH, max_seq=MAX_SEQ)
+    return g, spec
+
+
+def _meta():
+    toks = np.full((1, WIDTH), -1, np.int32)
+    toks[0, :P0 + 1] = synth.uniform_ids(0, "sim.prompt", P0 + 1, synth.TINY.vocab)
+    return np.array([P0], np.int32), toks, np.array([20], np.int32)
+
+
+@pytest.fixture
+def sim():
+    g, spec = _graph()
+    step, toks, plen = _meta()
+    s = mpk.mpk_sim_create(g, step, toks, plen, kv_filled=P0)
+    yield g, spec, s
+    mpk.mpk_sim_destroy(s)
+    mpk.mpk_destroy_graph(g)
+
+
+def _run(g, s, n, base, **kw):
+    info = mpk.mpk_get_graph_info(g)
+    return mpk.mpk_simulate(s, info.num_tasks, n, base, **kw).reshape(n, info.num_tasks)
+
+
+def test_every_data_edge_is_ordered_under_jitter(sim):
+    g, spec, s = sim
+    n = 12
+    tr = _run(g, s, n, 1000, seed=7, jitter_us=300, timeout_ms=20000)
+    info, tasks, _, _, _ = info_arrays(g)
+    NT = info.num_tasks
+    assert (tr["task"] == np.arange(NT)[None, :]).all(), "every task exactly once per iteration"
+    kinds = [o.kind for o in spec.ops]
+    by_op = {}
+    for i, t in enumerate(tasks):
+        by_op.setdefault(t.op, []).append(i)
+    sh = synth.TINY
+    d, G = sh.head_dim, sh.n_q // sh.n_kv
+
+    def group_rows(j):
+        rows = set(range(j * G * d, (j + 1) * G * d))
+        rows |= set(range(sh.n_q * d + j * d, sh.n_q * d + (j + 1) * d))
+        rows |= set(range((sh.n_q + sh.n_kv) * d + j * d, (sh.n_q + sh.n_kv) * d + (j + 1) * d))
+        return rows
+
+    # edges from the decoder's operator order (not from the builder's tables):
+    # embed -> [qkv -> attention -> o -> gate/up -> down] x L -> LM head -> argmax -> next iteration
+    chain = [i for i, k in enumerate(kinds) if k != mpk.MPK_OP_EMBED] + [len(kinds)]
+    two_splits = 0
+    for it in range(n):
+        st = tr[it]["start_ticket"]
+        for a, b in zip(chain, chain[1:]):
+            pa = [t for t in by_op[a] if st[t] != NONE]
+            pb = [t for t in by_op[b] if st[t] != NONE]
+            assert pa and pb
+            if b < len(kinds) and kinds[b] == mpk.MPK_OP_ATTENTION:
+                two_splits += len(pb) == 2 * sh.n_kv
+                for t in pb:
+                    rows = group_rows(tasks[t].nrows)
+                    prod = [q for q in pa if rows & set(range(tasks[q].row0, tasks[q].row0 + tasks[q].nrows))]
+                    assert prod and max(st[q] for q in prod) < st[t]
+            else:
+                assert max(st[t] for t in pa) < min(st[t] for t in pb), (it, a, b)
+        if it:
+            prev = tr[it - 1]["start_ticket"][by_op[chain[-1]]].max()
+            assert prev < tr[it]["start_ticket"][by_op[chain[0]]].min()
+    # positions 58..63 use one split, 64..69 two (the owner gathers the other)
+    assert two_splits == 6 * 2  # 6 iterations x 2 layers
+    step, toks = mpk.mpk_sim_read_meta(s, 1, WIDTH)
+    assert step[0] == P0 + n
+    assert ((toks[0, P0 + 1:P0 + n + 1] >= 0) & (toks[0, P0 + 1:P0 + n + 1] < synth.TINY.vocab)).all()
+    assert (toks[0, P0 + n + 1:] == -1).all()
+
+
+def test_buffers_reused_across_launches_never_pass_a_stale_word(sim):
+    g, spec, s = sim
+    # consecutive launches, stamp base advanced by each launch's iterations (as
+    # the library does): every word a task accepts is this iteration's
+    _run(g, s, 5, 100, seed=1, jitter_us=100, timeout_ms=20000)
+    _run(g, s, 4, 105, seed=2, jitter_us=100, timeout_ms=20000)
+    # a base that repeats the last launch's stamps: the words that launch left
+    # behind carry the stamp the next launch waits for, and are caught
+    with pytest.raises(mpk.MPKError) as e:
+        _run(g, s, 3, 108, seed=3, jitter_us=0, timeout_ms=20000)
+    assert e.value.code == mpk.MPK_ERR_GRAPH and "not this iteration" in str(e.value)
+
+
+def test_kv_row_stored_after_the_publish_is_caught(sim):
+    g, spec, s = sim
+    with pytest.raises(mpk.MPKError) as e:
+        _run(g, s, 4, 10, fault=mpk.MPK_SIM_FAULT_KV_AFTER_PUBLISH, timeout_ms=20000)
+    assert e.value.code == mpk.MPK_ERR_GRAPH and "K/V row" in str(e.value)
+
+
+def test_a_skipped_wait_is_caught(sim):
+    g, spec, s = sim
+    with pytest.raises(mpk.MPKError) as e:
+        _run(g, s, 3, 10, fault=mpk.MPK_SIM_FAULT_SKIP_WAIT, timeout_ms=20000)
+    assert e.value.code == mpk.MPK_ERR_GRAPH
+
+
+def test_a_word_never_published_times_out_and_the_next_launch_recovers(sim):
+    g, spec, s = sim
+    with pytest.raises(mpk.MPKError) as e:
+        _run(g, s, 3, 10, fault=mpk.MPK_SIM_FAULT_DROP_PUBLISH, timeout_ms=300)
+    assert e.value.code == mpk.MPK_ERR_DEVICE_TIMEOUT
+    # relaunch from the state the stopped run left (a fresh stamp base)
+    step, _ = mpk.mpk_sim_read_meta(s, 1, WIDTH)
+    _run(g, s, 3, 20, seed=4, jitter_us=50, timeout_ms=20000)
+    step2, _ = mpk.mpk_sim_read_meta(s, 1, WIDTH)
+    assert step2[0] == step[0] + 3
+
+
+def test_start_of_run_rule_applies(sim):
+    g, spec, s = sim
+    with pytest.raises(mpk.MPKError) as e:
+        _run(g, s, WIDTH, 10)
+    assert e.value.code == mpk.MPK_ERR_SHAPE

@@ -14,14 +14,19 @@ from test_builder import build, info_arrays
 
 def _simulated(n_iter=3):
     g, spec = build(synth.TINY, num_cus=32, tokens_width=16, max_seq=16)
+    sim = 0
     try:
         info, tasks, _, _, _ = info_arrays(g)
-        tr = mpk.mpk_simulate(g, n_iter, seed=3, jitter_us=50, timeout_ms=20000)
+        toks = np.full((1, 16), -1, np.int32)
+        toks[0, :4] = [1, 2, 3, 4]
+        sim = mpk.mpk_sim_create(g, np.zeros(1, np.int32), toks, np.array([4], np.int32))
+        tr = mpk.mpk_simulate(sim, info.num_tasks, n_iter, 0, seed=3, jitter_us=50, timeout_ms=20000)
         # copies: the task table belongs to the graph, destroyed below
         tasks = [SimpleNamespace(**{f: getattr(t, f) for f in ("op", "tile", "worker", "row0", "nrows", "split")})
                  for t in tasks]
         return tr, tasks, info.num_tasks, [o.kind for o in spec.ops]
     finally:
+        mpk.mpk_sim_destroy(sim)
         mpk.mpk_destroy_graph(g)
 
 
