@@ -175,6 +175,12 @@ def main():
     import persistent_task_runtime_amd as mpk
     from persistent_task_runtime_amd import runner
 
+    # The native libraries are opened before the GPU runtime initialises, so
+    # they map above the address range it reserves, like every other HIP
+    # library of the process; their exit-time destructors (a HIP library's
+    # unregisters its device code) then run in the usual order.
+    mpk.load_library()
+    synth._load()
     assert torch.cuda.is_available(), "no GPU visible"
     if args.workload == "long":
         return bench_long(args)

@@ -195,6 +195,23 @@ int mpk_compile(mpk_graph_t graph, int32_t device, mpk_exec_t* out);
  * caches are unchanged. */
 int mpk_run_steps(mpk_exec_t exec, int32_t num_iterations, void* stream);
 
+/* mpk_run_steps for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same kernels, same results; the call allocates nothing and makes no
+ * host-device round trip.  The run scratch (the stamped words between tasks,
+ * attention split partials, LM-head tile maxima, token words, status word and
+ * positions: mpk_compile sizes it per graph) lives in one static device array
+ * of the library per GPU, 64 MiB, held until the process ends; mpk_compile
+ * prepares the executable's table into it.  Every call on a GPU shares that
+ * GPU's array and leaves its contents behind: runs that overlap on one GPU
+ * race (one allocation-free run per GPU at a time).  Stop requests stay per
+ * executable.  Returns MPK_ERR_SHAPE (nothing launched) when the graph's run
+ * scratch exceeds 64 MiB (e.g. batch 1 of the 8B shape at 32768 positions fits;
+ * larger batches may not), MPK_ERR_INVALID_ARG for a traced graph (the trace
+ * buffer would need an allocation), and otherwise what mpk_run_steps
+ * returns; mpk_get_status reports this run's status. */
+int mpk_run_steps_static(mpk_exec_t exec, int32_t num_iterations, void* stream);
+
 /* The same task bodies launched one kernel per operator per iteration (the
  * comparison the pages make against per-operator kernels, P1 "Alternative").
  * Same tiles, same reduction order: results are bitwise equal to

@@ -70,12 +70,6 @@ def lib():
     return _lib
 
 
-# opened at import, before any GPU runtime initialisation (see the package
-# binding's note on load order)
-if os.path.exists(_SO):
-    lib()
-
-
 def _p(a: np.ndarray) -> int:
     assert a.flags.c_contiguous
     return a.ctypes.data

@@ -131,6 +131,15 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         from . import build as _build
         _build.build(force=False)
+    # Load order: torch ships its own HIP runtime, and a process holds one
+    # runtime per soname (the first loaded) to which every HIP library binds.
+    # torch, which provides the device memory and streams, is imported first,
+    # so the library always runs on torch's runtime.  (Importing torch does
+    # not initialise the GPU.)
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # then the system HIP runtime
+        pass
     L = ctypes.CDLL(path)
     P = ctypes.POINTER
     sig = {
@@ -138,6 +147,7 @@ def load_library(path: str = LIB_PATH):
                                     P(mpk_op), c_i32, P(mpk_meta), P(c_vp)]),
         "mpk_compile": (c_i32, [c_vp, c_i32, P(c_vp)]),
         "mpk_run_steps": (c_i32, [c_vp, c_i32, c_vp]),
+        "mpk_run_steps_static": (c_i32, [c_vp, c_i32, c_vp]),
         "mpk_run_steps_per_op": (c_i32, [c_vp, c_i32, c_vp]),
         "mpk_get_status": (c_i32, [c_vp, P(c_i32), P(c_i32), P(c_i32)]),
         "mpk_set_abort": (c_i32, [c_vp, c_i32]),
@@ -161,24 +171,7 @@ def load_library(path: str = LIB_PATH):
     return L
 
 
-# Load order.  torch ships its own HIP runtime; a process holds one runtime
-# per soname, the first one loaded, and every HIP library binds to it.  torch
-# (which the package uses for device memory and streams) is imported first, so
-# the library always runs on torch's runtime.  Importing torch does not
-# initialise the GPU.  The library itself is opened when the package is
-# imported, normally before the GPU runtime is initialised: a library opened
-# later is mapped below the address range the runtime reserves, and its
-# exit-time destructor (which unregisters its device code from the HIP
-# runtime) then runs in an order the runtime's other libraries do not see.
-try:
-    import torch  # noqa: F401
-except ImportError:  # the library then binds to the system HIP runtime
-    pass
-if os.path.exists(LIB_PATH):
-    load_library()
-
-
-EXPORTED = ["mpk_build_graph", "mpk_compile", "mpk_run_steps", "mpk_run_steps_per_op",
+EXPORTED = ["mpk_build_graph", "mpk_compile", "mpk_run_steps", "mpk_run_steps_static", "mpk_run_steps_per_op",
             "mpk_get_status", "mpk_set_abort", "mpk_read_trace", "mpk_get_graph_info",
             "mpk_sim_create", "mpk_simulate", "mpk_sim_read_meta", "mpk_sim_destroy",
             "mpk_check_run", "mpk_get_tensor_ptr", "mpk_destroy_exec", "mpk_destroy_graph",
@@ -214,6 +207,10 @@ def mpk_compile(graph: int, device: int = 0) -> int:
 
 def mpk_run_steps(exe: int, num_iterations: int, stream: int = 0) -> None:
     _check(load_library().mpk_run_steps(exe, num_iterations, stream))
+
+
+def mpk_run_steps_static(exe: int, num_iterations: int, stream: int = 0) -> None:
+    _check(load_library().mpk_run_steps_static(exe, num_iterations, stream))
 
 
 def mpk_run_steps_per_op(exe: int, num_iterations: int, stream: int = 0) -> None:

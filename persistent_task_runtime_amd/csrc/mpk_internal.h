@@ -102,7 +102,8 @@ typedef struct {
   const int32_t* prompt_len;
   const float* rope_cos;        /* [max_seq][d/2] */
   const float* rope_sin;
-  mpk_dev_status* status;
+  mpk_dev_status* status;       /* code / iteration / task of the run */
+  int32_t* abort_req;           /* the executable's stop request (mpk_set_abort) */
   mpk_trace_record* trace;      /* NULL = off */
   int32_t trace_tickets;        /* 1: also take global tickets (slower) */
   uint32_t* ticket_ctr;

@@ -32,6 +32,7 @@
 #include <cmath>
 #include <cstring>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -388,7 +389,7 @@ DEV int wait_round(const mpk_kparams& P, Waiter& Wt, bool pending, int s, int ta
   if (tid == 0 && (Wt.rounds & 7) == 2) {
     int mine = 0;
     const int code = __hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int abort_req = __hip_atomic_load(&P.status->abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int abort_req = __hip_atomic_load(P.abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     if (abort_req) mine = MPK_ERR_ABORTED;
     else if (Wt.t0 != 0 && clock_now() - Wt.t0 > P.timeout_ticks) mine = MPK_ERR_DEVICE_TIMEOUT;
     if (mine) {
@@ -428,7 +429,7 @@ DEV bool wave_watch(const mpk_kparams& P, Waiter& Wt, int s, int task_id, char* 
     Wt.t0 = clock_now();
   } else if ((Wt.rounds & 7) == 0) {
     const int code = __hip_atomic_load(&P.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int abort_req = __hip_atomic_load(&P.status->abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int abort_req = __hip_atomic_load(P.abort_req, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     const int mine = abort_req ? MPK_ERR_ABORTED
                                : (clock_now() - Wt.t0 > P.timeout_ticks ? MPK_ERR_DEVICE_TIMEOUT : 0);
     if (mine && lane == 0) {
@@ -1960,6 +1961,15 @@ struct mpk_exec_s {
   const void* kernel_op = nullptr;
   int lds_bytes = 0;
   mpk_kparams kp{};
+  // Run scratch: every buffer the run's kernels write besides the caller's
+  // tensors (stamped words, split partials, tile maxima, token words,
+  // status, ticket, positions), in allocation order; mpk_run_steps_static
+  // places the same buffers at the same offsets in the static array.
+  std::vector<std::pair<void*, size_t>> scratch;
+  size_t scratch_bytes = 0;           // their total, each rounded up to 256 bytes
+  mpk_dev_op* d_ops_static = nullptr; // operator table pointing into the static array (NULL: does not fit)
+  mpk_kparams kp_static{};
+  mpk_dev_status* last_status = nullptr;  // status word of the last run (own or static)
 };
 
 #define HIPCHK(x)                                                                          \
@@ -1992,6 +2002,92 @@ static int dalloc(mpk_exec_s* x, T** p, size_t bytes) {
   HIPCHK(hipMemset(q, 0, bytes ? bytes : 16));
   x->owned.push_back(q);
   *p = reinterpret_cast<T*>(q);
+  return MPK_OK;
+}
+
+// A buffer the run's kernels write (see mpk_exec_s::scratch).
+template <typename T>
+static int salloc(mpk_exec_s* x, T** p, size_t bytes) {
+  const int rc = dalloc(x, p, bytes);
+  if (rc) return rc;
+  x->scratch.emplace_back((void*)*p, bytes);
+  x->scratch_bytes += (bytes + 255) & ~(size_t)255;
+  return MPK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free runs (mpk_run_steps_static).  The run scratch lives in one
+// file-scope device array per GPU, held until the process ends.  Host code
+// never uses the array's name as an address: its device address is taken
+// once per device with hipGetSymbolAddress (at the first mpk_compile on that
+// device, with the device current) and kept per device.
+// ---------------------------------------------------------------------------
+#define MPK_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+#define MPK_MAX_DEVICES 64
+static __device__ __align__(256) unsigned char scratch[MPK_STATIC_SCRATCH_BYTES];
+
+__global__ void mpk_fill_zero(uint4* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[MPK_MAX_DEVICES];
+
+// Device address of the static array on `device` (current), cleared once:
+// stamped words left in it by earlier runs of this process carry stamps no
+// later run uses, but the array's first contents are unknown.
+static int static_scratch(int device, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (device < 0 || device >= MPK_MAX_DEVICES) return mpk_fail(MPK_ERR_INVALID_ARG, "device ordinal out of range");
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    hipLaunchKernelGGL(mpk_fill_zero, dim3(1024), dim3(256), 0, 0, (uint4*)p,
+                       (int64_t)(MPK_STATIC_SCRATCH_BYTES / sizeof(uint4)));
+    HIPCHK(hipGetLastError());
+    HIPCHK(hipDeviceSynchronize());
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return MPK_OK;
+}
+
+// The static operator table and kernel parameters of x: the same buffers at
+// the same offsets in the static array.  Left unset when they do not fit.
+static int build_static_tables(mpk_exec_s* x, const std::vector<mpk_dev_op>& dops) {
+  if (x->scratch_bytes > MPK_STATIC_SCRATCH_BYTES) return MPK_OK;
+  void* base = nullptr;
+  int rc = static_scratch(x->device, &base);
+  if (rc) return rc;
+  std::vector<std::pair<void*, char*>> map;  // own buffer -> static address
+  size_t off = 0;
+  for (const auto& b : x->scratch) {
+    map.emplace_back(b.first, (char*)base + off);
+    off += (b.second + 255) & ~(size_t)255;
+  }
+  auto remap = [&](auto* p) -> decltype(p) {
+    if (!p) return p;
+    for (const auto& m : map)
+      if ((const void*)p == m.first) return reinterpret_cast<decltype(p)>(m.second);
+    return p;  // caller memory (attached tensors) is not scratch
+  };
+  std::vector<mpk_dev_op> sops = dops;
+  for (mpk_dev_op& D : sops) {
+    D.xll = remap(D.xll);
+    D.rll = remap(D.rll);
+    D.yll = remap(D.yll);
+    D.pll = remap(D.pll);
+  }
+  if ((rc = dalloc(x, &x->d_ops_static, sops.size() * sizeof(mpk_dev_op)))) return rc;
+  HIPCHK(hipMemcpy(x->d_ops_static, sops.data(), sops.size() * sizeof(mpk_dev_op), hipMemcpyHostToDevice));
+  mpk_kparams& K = x->kp_static;
+  K = x->kp;
+  K.ops = x->d_ops_static;
+  K.tok_ll = remap(x->kp.tok_ll);
+  K.status = remap(x->kp.status);
+  K.ticket_ctr = remap(x->kp.ticket_ctr);
+  K.pos0 = remap(x->kp.pos0);
   return MPK_OK;
 }
 
@@ -2042,7 +2138,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
     const bool produced = g->producer[i] >= 0 && g->embed_src[i] < 0;
     if (produced && t.dtype == MPK_F32) {
       const int64_t n = tensor_bytes(t) / 4;
-      if ((rc = dalloc(x.get(), &x->ll_ptr[i], (size_t)n * 8))) return rc;
+      if ((rc = salloc(x.get(), &x->ll_ptr[i], (size_t)n * 8))) return rc;
     }
     if (t.dev_ptr) {
       x->tensor_ptr[i] = t.dev_ptr;
@@ -2060,8 +2156,8 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   const int B = x->B;
 
   std::vector<mpk_dev_op> dops = g->dops;
-  if ((rc = dalloc(x.get(), &x->d_ticket_ctr, 4))) return rc;
-  if ((rc = dalloc(x.get(), &x->d_tok_ll, (size_t)B * 8))) return rc;
+  if ((rc = salloc(x.get(), &x->d_ticket_ctr, 4))) return rc;
+  if ((rc = salloc(x.get(), &x->d_tok_ll, (size_t)B * 8))) return rc;
 
   for (size_t i = 0; i < dops.size(); ++i) {
     mpk_dev_op& D = dops[i];
@@ -2079,7 +2175,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
       const int G = D.nq / D.nkv;
       if (G > ATT_MAXG) return mpk_fail(MPK_ERR_SHAPE, "more than 4 query heads per kv head");
       if (D.d > 128) return mpk_fail(MPK_ERR_SHAPE, "head_dim above 128");
-      if ((rc = dalloc(x.get(), &D.pll, (size_t)B * D.nkv * D.nsplit * G * (D.d + 2) * 8))) return rc;
+      if ((rc = salloc(x.get(), &D.pll, (size_t)B * D.nkv * D.nsplit * G * (D.d + 2) * 8))) return rc;
       continue;
     }
     const int e_in = o.in[0];
@@ -2111,7 +2207,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
     } else {  // LM head
       D.W0 = (const uint16_t*)P(o.in[2]);
       D.logits = o.out[0] >= 0 ? (float*)P(o.out[0]) : nullptr;
-      if ((rc = dalloc(x.get(), &D.pll, (size_t)D.ntiles * B * 2 * 8))) return rc;
+      if ((rc = salloc(x.get(), &D.pll, (size_t)D.ntiles * B * 2 * 8))) return rc;
     }
   }
   if (g->argmax_op >= 0) {
@@ -2128,8 +2224,8 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   HIPCHK(hipMemcpy(x->d_queues, g->queues.data(), g->queues.size() * sizeof(mpk_dev_qentry), hipMemcpyHostToDevice));
   if ((rc = dalloc(x.get(), &x->d_qlen, g->qlen.size() * 4))) return rc;
   HIPCHK(hipMemcpy(x->d_qlen, g->qlen.data(), g->qlen.size() * 4, hipMemcpyHostToDevice));
-  if ((rc = dalloc(x.get(), &x->d_status, sizeof(mpk_dev_status)))) return rc;
-  if ((rc = dalloc(x.get(), &x->d_pos0, MPK_MAX_BATCH * sizeof(int32_t)))) return rc;
+  if ((rc = salloc(x.get(), &x->d_status, sizeof(mpk_dev_status)))) return rc;
+  if ((rc = salloc(x.get(), &x->d_pos0, MPK_MAX_BATCH * sizeof(int32_t)))) return rc;
 
   // RoPE table, fp64 angles rounded to fp32 (pair i of a head: angle p * theta^(-2i/d))
   const int half = M.head_dim / 2;
@@ -2156,6 +2252,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   K.rope_cos = x->d_rope;
   K.rope_sin = x->d_rope + (size_t)M.max_seq * half;
   K.status = x->d_status;
+  K.abort_req = &x->d_status->abort_req;
   K.trace = nullptr;
   K.ticket_ctr = x->d_ticket_ctr;
   uint64_t ns = g->launch.spin_timeout_ns ? g->launch.spin_timeout_ns : 2000000000ull;
@@ -2173,6 +2270,8 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   // a run on another stream must never see a buffer before it is zeroed (a
   // reused allocation could still hold words stamped by an earlier
   // executable).
+  x->last_status = x->d_status;
+  if ((rc = build_static_tables(x.get(), dops))) return rc;
   HIPCHK(hipDeviceSynchronize());
   *out = x.release();
   return MPK_OK;
@@ -2181,12 +2280,13 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
 // Iteration stamps handed out so far in this process (see prepare_run).
 static std::atomic<uint64_t> g_stamps{0};
 
-static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
-  if (!x) return mpk_fail(MPK_ERR_INVALID_ARG, "NULL exec");
+// Host checks, stamps and the start-of-run kernel of a run with parameters
+// K (x->kp, or x->kp_static for an allocation-free run).
+static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st, mpk_kparams& K) {
   if (n_iter <= 0) return mpk_fail(MPK_ERR_INVALID_ARG, "num_iterations must be positive");
   // Checks that need no device value; positions and token ids are checked
   // on the device by mpk_begin_run (no host round trip per launch).
-  if ((int64_t)n_iter >= x->kp.tokens_width || n_iter > x->g->model.max_seq)
+  if ((int64_t)n_iter >= K.tokens_width || n_iter > x->g->model.max_seq)
     return mpk_fail(MPK_ERR_SHAPE, std::to_string(n_iter) + " iterations leave the tokens tensor or the KV cache");
   for (size_t i = 0; i < x->g->dops.size(); ++i) {
     const mpk_dev_op& D = x->g->dops[i];
@@ -2195,9 +2295,9 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
   }
   HIPCHK(hipSetDevice(x->device));
   // trace buffer (allocated by the first traced run that needs more room)
-  x->kp.trace = nullptr;
+  K.trace = nullptr;
   if (x->g->launch.trace) {
-    int64_t need = (int64_t)n_iter * x->kp.n_tasks;
+    int64_t need = (int64_t)n_iter * K.n_tasks;
     if (need > x->trace_cap) {
       void* p = nullptr;
       HIPCHK(hipMalloc(&p, (size_t)need * sizeof(mpk_trace_record)));
@@ -2206,10 +2306,10 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
       x->trace_cap = need;
     }
     HIPCHK(hipMemsetAsync(x->d_trace, 0xff, (size_t)need * sizeof(mpk_trace_record), st));
-    x->kp.trace = x->d_trace;
-    x->kp.trace_tickets = x->g->launch.trace == 1;
+    K.trace = x->d_trace;
+    K.trace_tickets = x->g->launch.trace == 1;
   }
-  x->kp.n_iter = n_iter;
+  K.n_iter = n_iter;
   x->last_iters = n_iter;
   // stamps of this run: base + 1 .. base + n_iter, taken from a counter
   // shared by every executable of the process, so no two runs (of this or
@@ -2217,17 +2317,19 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st) {
   const uint64_t base = g_stamps.fetch_add((uint64_t)n_iter);
   if (base + (uint64_t)n_iter >= 0xffffffffull)
     return mpk_fail(MPK_ERR_STATE, "iteration stamps exhausted (2^32 iterations per process)");
-  x->kp.iter_base = (uint32_t)base;
+  K.iter_base = (uint32_t)base;
   // status, trace ticket, positions at launch, checks of step / tokens
-  hipLaunchKernelGGL(mpk_begin_run, dim3(1), dim3(64), 0, st, x->kp, (int)n_iter);
+  hipLaunchKernelGGL(mpk_begin_run, dim3(1), dim3(64), 0, st, K, (int)n_iter);
   HIPCHK(hipGetLastError());
+  x->last_status = K.status == x->kp.status ? x->d_status : x->kp_static.status;
   return MPK_OK;
 }
 
 extern "C" int mpk_run_steps(mpk_exec_t x, int32_t n_iter, void* stream) {
   mpk_clear_error();
+  if (!x) return mpk_fail(MPK_ERR_INVALID_ARG, "NULL exec");
   hipStream_t st = (hipStream_t)stream;
-  int rc = prepare_run(x, n_iter, st);
+  int rc = prepare_run(x, n_iter, st, x->kp);
   if (rc) return rc;
   void* args[] = {&x->kp};
   HIPCHK(hipLaunchCooperativeKernel(x->kernel_persistent, dim3(x->g->num_queues), dim3(MPK_THREADS), args,
@@ -2235,10 +2337,29 @@ extern "C" int mpk_run_steps(mpk_exec_t x, int32_t n_iter, void* stream) {
   return MPK_OK;
 }
 
+extern "C" int mpk_run_steps_static(mpk_exec_t x, int32_t n_iter, void* stream) {
+  mpk_clear_error();
+  if (!x) return mpk_fail(MPK_ERR_INVALID_ARG, "NULL exec");
+  if (!x->d_ops_static)
+    return mpk_fail(MPK_ERR_SHAPE, "the run scratch of this graph needs " + std::to_string(x->scratch_bytes) +
+                                       " bytes; the static array holds " +
+                                       std::to_string(MPK_STATIC_SCRATCH_BYTES));
+  if (x->g->launch.trace)
+    return mpk_fail(MPK_ERR_INVALID_ARG, "a traced graph needs a trace buffer; the allocation-free run has none");
+  hipStream_t st = (hipStream_t)stream;
+  int rc = prepare_run(x, n_iter, st, x->kp_static);
+  if (rc) return rc;
+  void* args[] = {&x->kp_static};
+  HIPCHK(hipLaunchCooperativeKernel(x->kernel_persistent, dim3(x->g->num_queues), dim3(MPK_THREADS), args,
+                                    x->lds_bytes, st));
+  return MPK_OK;
+}
+
 extern "C" int mpk_run_steps_per_op(mpk_exec_t x, int32_t n_iter, void* stream) {
   mpk_clear_error();
+  if (!x) return mpk_fail(MPK_ERR_INVALID_ARG, "NULL exec");
   hipStream_t st = (hipStream_t)stream;
-  int rc = prepare_run(x, n_iter, st);
+  int rc = prepare_run(x, n_iter, st, x->kp);
   if (rc) return rc;
   x->kp.trace = nullptr;
   const mpk_graph_s* g = x->g;
@@ -2257,7 +2378,7 @@ extern "C" int mpk_get_status(mpk_exec_t x, int32_t* code, int32_t* iteration, i
   if (!x) return mpk_fail(MPK_ERR_INVALID_ARG, "NULL exec");
   mpk_dev_status s{};
   HIPCHK(hipSetDevice(x->device));
-  HIPCHK(hipMemcpy(&s, x->d_status, sizeof(s), hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(&s, x->last_status, sizeof(s), hipMemcpyDeviceToHost));
   if (code) *code = s.code;
   if (iteration) *iteration = s.code ? s.iteration : -1;
   if (task) *task = s.code ? s.task : -1;

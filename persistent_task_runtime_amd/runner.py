@@ -119,12 +119,14 @@ class Session:
         self.model = model
         self.exe = mpk.Executable(spec, meta, mcfg, lcfg)
 
-    def run(self, n_iter: int, per_op: bool = False, stream=None):
+    def run(self, n_iter: int, per_op: bool = False, stream=None, static: bool = False):
         import torch
 
         s = torch.cuda.current_stream() if stream is None else stream
         if per_op:
             self.exe.run_per_op(n_iter, s.cuda_stream)
+        elif static:
+            mpk.mpk_run_steps_static(self.exe.exe, n_iter, s.cuda_stream)
         else:
             self.exe.run(n_iter, s.cuda_stream)
 

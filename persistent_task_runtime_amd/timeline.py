@@ -182,8 +182,10 @@ def main(argv=None) -> int:
     import torch
 
     import synth
-    from . import mpk_get_graph_info, mpk_read_trace
+    from . import load_library, mpk_get_graph_info, mpk_read_trace
     from . import runner
+
+    load_library()  # before the GPU runtime initialises (see load_library)
 
     if args.workload == "qwen3_8b_long":
         warm = 2 if args.warmup is None else args.warmup

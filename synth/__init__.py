@@ -67,12 +67,6 @@ def _load():
     return _lib
 
 
-# opened at import, before any GPU runtime initialisation (see the package
-# binding's note on load order)
-if os.path.exists(_SO):
-    _load()
-
-
 def key(seed: int, name: str) -> int:
     return _load().synth_key(seed, name.encode())
 
