@@ -155,9 +155,11 @@ def parse_args(argv=None):
     ap.add_argument("--no-per-op", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for profiles)")
-    ap.add_argument("--workload", choices=("qwen3_8b", "long"), default="qwen3_8b",
+    ap.add_argument("--workload", choices=("qwen3_8b", "long", "b8"), default="qwen3_8b",
                     help="long: the same model with each layer's K/V cache pre-filled N(0,1) to "
-                         "32768 positions, 128 decode iterations from there (attention-heavy)")
+                         "32768 positions, 128 decode iterations from there (attention-heavy); "
+                         "b8: batch 8, prompt lengths uniform in [16, 512] ingested per request, "
+                         "then 256 lockstep greedy iterations (MFMA linear tasks)")
     return ap.parse_args(argv)
 
 
@@ -184,6 +186,8 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     if args.workload == "long":
         return bench_long(args)
+    if args.workload == "b8":
+        return bench_b8(args)
     sh = synth.QWEN3_8B
     P = PROMPT_TOKENS
     K, W = timed_tokens(args.steps), args.warmup
@@ -387,6 +391,127 @@ def bench_long(args):
         "kernel": "mpk_persistent<1>", "launch_ms": round(launch_avg, 4),
         "bound_ms_per_token": round(bound_ms, 5), "frac_of_bound": round(bound_ms / ms_tok, 4),
         "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_b8(args):
+    """Batch 8: 8 requests with seeded prompt lengths uniform in [16, 512]
+    (tokens [8, 4096]); each prompt is ingested at batch 1 into the batch-8
+    session's own tensors (untimed), then the 8 requests decode in lockstep,
+    each at its own position, 256 greedy iterations timed in launches of
+    --launch-iters.  A step is one batch-8 iteration (a token for each of the
+    8 requests)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from persistent_task_runtime_amd import runner
+
+    sh = synth.QWEN3_8B
+    K = 256
+    w = synth.workload("qwen3_8b_b8")
+    P = w.prompt_len.astype(np.int64)
+    launches = plan_launches(K, args.launch_iters)
+    t0 = time.time()
+    weights = synth.make_model(sh, seed=w.seed)
+    model = runner.DeviceModel(sh, weights=weights)
+    sess = runner.Session(w, model)
+    torch.cuda.synchronize()
+    log("weights and batch-8 session ready in %.1f s" % (time.time() - t0))
+    # prompts: request r alone (batch 1) over positions 0 .. P_r - 2, in the
+    # batch-8 tensors; then step[r] = P_r - 1 (the first batched iteration
+    # consumes the last prompt id)
+    t1 = time.time()
+    sess.step.zero_()
+    for r in range(w.batch):
+        view = runner.RequestView(sess, r)
+        view.run(int(P[r]) - 1)
+        torch.cuda.synchronize()
+        code, it, task = view.exe.status()
+        assert code == 0, (r, code, it, task)
+        view.close()
+    step0 = sess.step.cpu().numpy()
+    assert np.array_equal(step0, P - 1), (step0, P - 1)
+    toks0 = sess.tokens.clone()
+    log("prompts (%d ids) ingested at batch 1 in %.1f s" % (int(P.sum()), time.time() - t1))
+    stream = torch.cuda.current_stream()
+    if args.warmup:
+        sess.run(args.warmup)
+        torch.cuda.synchronize()
+        sess.check_status()
+        sess.step.copy_(torch.from_numpy(step0.astype(np.int32)).to(sess.step.device))
+        sess.tokens.copy_(toks0)
+        log("warm-up: %d batch-8 iterations" % args.warmup)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
+    torch.cuda.synchronize()
+    for (a, b), L in zip(ev, launches):
+        a.record(stream)
+        sess.run(L)
+        b.record(stream)
+    torch.cuda.synchronize()
+    sess.check_status()
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = ev[0][0].elapsed_time(ev[-1][1])
+    ms_it = ms / K
+    assert np.array_equal(sess.step.cpu().numpy(), step0 + K)
+    toks = sess.tokens.cpu().numpy()
+    for r in range(w.batch):
+        gen = toks[r, int(P[r]):int(P[r]) + K]
+        assert ((gen >= 0) & (gen < sh.vocab)).all()
+    kvp = kv_bytes_per_position(sh)
+
+    def it_bytes(s):
+        return sh.streamed_weight_bytes() + sum(kvp * (int(step0[r]) + s + 1) + 2 * sh.hidden for r in range(8))
+
+    pos = 0
+    launch_bytes = []
+    for L in launches:
+        launch_bytes.append(sum(it_bytes(pos + i) for i in range(L)))
+        pos += L
+    alg = sum(launch_bytes)
+    achieved = sum(b / (t / 1e3) for b, t in zip(launch_bytes, launch_ms)) / len(launches) / 1e9
+    bound_ms = alg / K / (HBM_PEAK_GBS * 1e9) * 1e3
+    tok_s = 8 * K / (ms / 1e3)
+    log("batch 8: %.4f ms/iteration (%.1f tokens/s) over launches %s, %.1f GB/s algorithmic (%.1f%% of %.0f "
+        "GB/s), bound %.4f ms/iteration" % (ms_it, tok_s, launches, achieved, 100 * achieved / HBM_PEAK_GBS,
+                                            HBM_PEAK_GBS, bound_ms))
+    sess.close()
+    del sess, model
+    torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        n_cpu = 2
+        om = oracle.Model(sh, weights)
+        wc = synth.Workload("b8_cpu", sh, 8, n_cpu, n_cpu + 2, np.full(8, n_cpu + 1, np.int32),
+                            np.zeros(8, np.int32))
+        st = oracle.State(sh, synth.make_tokens(wc), wc.step0, wc.prompt_len, n_cpu + 1)
+        t2 = time.time()
+        oracle.decode(om, st, n_cpu, want_logits=False)
+        dt = time.time() - t2
+        cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+        cpu = {"value": dt / n_cpu * 1e3, "unit": "ms/iteration", "cores": cores, "kind": "oracle",
+               "sample": "%d batch-8 iterations (8 requests each, positions 0-%d) of the same model, fp64 C "
+                         "oracle, OpenMP over output rows" % (n_cpu, n_cpu - 1)}
+        log("cpu oracle: %.1f ms per batch-8 iteration on %d threads" % (cpu["value"], cores))
+    out = {
+        "metric": "ms/iteration decode latency at batch 8 (Qwen3-8B shape) + % of HBM roofline",
+        "value": round(ms_it, 5), "unit": "ms/iteration", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_it, 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 MFMA (hi/lo inputs), f32 accumulate", "data": "synthetic",
+        "config": {"workload": "qwen3_8b_batch8_prompts16to512_greedy", "layers": sh.layers, "hidden": sh.hidden,
+                   "q_heads": sh.n_q, "kv_heads": sh.n_kv, "head_dim": sh.head_dim, "ffn": sh.ffn,
+                   "vocab": sh.vocab, "tied_lm_head": True, "batch": 8,
+                   "prompt_lengths": [int(x) for x in P], "generated_tokens_per_request": K,
+                   "iterations_per_launch": launches[0], "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16"},
+        "tokens_per_s": round(tok_s, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "kernel": "mpk_persistent<8>", "launch_ms": round(sum(launch_ms) / len(launches), 4),
+        "bound_ms_per_iteration": round(bound_ms, 5), "frac_of_bound": round(bound_ms / ms_it, 4),
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

@@ -51,7 +51,7 @@ typedef enum {
   MPK_ERR_INVALID_ARG = -1,    /* NULL handle/pointer, bad enum, bad count */
   MPK_ERR_SHAPE = -2,          /* tensor dims disagree with the model or operator */
   MPK_ERR_DTYPE = -3,          /* tensor dtype not the one the operator takes */
-  MPK_ERR_ALIGN = -4,          /* device pointer not 16-byte aligned */
+  MPK_ERR_ALIGN = -4,          /* device pointer not 16-byte aligned (int32 tensors: 4-byte) */
   MPK_ERR_SPLIT = -5,          /* worker / scheduler counts break the CU rule */
   MPK_ERR_NOT_CORESIDENT = -6, /* the workers cannot all be resident at once */
   MPK_ERR_HIP = -7,            /* a HIP runtime call failed */

@@ -81,8 +81,10 @@ int check_tensor(const mpk_graph_s* g, int id, int dtype, std::initializer_list<
                                          std::to_string(want));
     ++i;
   }
-  if (t.dev_ptr && ((uintptr_t)t.dev_ptr & 15))
-    return mpk_fail(MPK_ERR_ALIGN, "tensor " + tname(g, id) + " is not 16-byte aligned");
+  // bf16 / f32 tensors are read in 16-byte units; int32 meta tensors by element
+  const uintptr_t align = t.dtype == MPK_I32 ? 4 : 16;
+  if (t.dev_ptr && ((uintptr_t)t.dev_ptr & (align - 1)))
+    return mpk_fail(MPK_ERR_ALIGN, "tensor " + tname(g, id) + " is not " + std::to_string(align) + "-byte aligned");
   return MPK_OK;
 }
 
@@ -143,8 +145,8 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
 
   // ---- meta tensors ----
   const int B = meta->num_requests;
-  if (B <= 0 || B > M.max_batch || B > MPK_MAX_BATCH)
-    return mpk_fail(MPK_ERR_SHAPE, "num_requests must be in [1, min(max_batch, 8)]");
+  if (B <= 0 || B > M.max_batch || B > MPK_MAX_BATCH || (B > 2 && B != MPK_MAX_BATCH))
+    return mpk_fail(MPK_ERR_SHAPE, "num_requests must be 1, 2 or 8 (and at most max_batch)");
   int rc;
   if ((rc = check_tensor(g, meta->tokens, MPK_I32, {B, -1}, "tokens", -1))) return rc;
   if ((rc = check_tensor(g, meta->step, MPK_I32, {B}, "step", -1))) return rc;
@@ -287,12 +289,30 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
                                              " rows cannot give " + std::to_string(T) +
                                              " tiles of >= " + std::to_string(min_units) + " rows");
         D.ntiles = T;
-        if (D.kind == MPK_TK_GEMV && (int64_t)B * ((U + T - 1) / T) * a > 512)
-          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) +
-                                             ": rows per tile x num_requests exceed 512");
-        if ((int64_t)B * ((U + T - 1) / T) * a * 32 > (B == 1 ? 28 * 1024 : 40 * 1024))
-          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) +
-                                             ": rows per tile x num_requests exceed the partial-sum buffer");
+        const int tile_rows = ((U + T - 1) / T) * a;  // largest tile, virtual rows
+        if (B == MPK_MAX_BATCH) {
+          // batch 8 runs the MFMA bodies: x staged in LDS per 4096-column
+          // pass, 16-row blocks split over the waves (1 or 2 blocks: all
+          // waves split K; up to 6: two row groups; the LM head: up to 40
+          // blocks, one row group per wave), 8 x outputs staged in 4 KB
+          if (K % 4096)
+            return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": at batch 8 the input width K = " +
+                                               std::to_string(K) + " must be a multiple of 4096");
+          const int nblk = (tile_rows + 15) / 16;
+          const int max_blk = D.epi == MPK_EPI_ARGMAX ? 40 : 6;
+          if (nblk > max_blk || (D.epi != MPK_EPI_ARGMAX && 8 * (D.pairs ? tile_rows / 2 : tile_rows) > 1024))
+            return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": " + std::to_string(tile_rows) +
+                                               " rows per tile exceed the batch-8 tile");
+        } else if (B > 2) {
+          return mpk_fail(MPK_ERR_SHAPE, "num_requests must be 1, 2 or 8");
+        } else {
+          if (D.kind == MPK_TK_GEMV && (int64_t)B * tile_rows > 512)
+            return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) +
+                                               ": rows per tile x num_requests exceed 512");
+          if ((int64_t)B * tile_rows * 32 > (B == 1 ? 28 * 1024 : 40 * 1024))
+            return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) +
+                                               ": rows per tile x num_requests exceed the partial-sum buffer");
+        }
         break;
       }
       case MPK_OP_ATTENTION: {

@@ -294,6 +294,13 @@ struct Lay {
   // the gathered split partials); one workgroup per CU, so the whole LDS
   static constexpr int TOTAL = 156 * 1024;
 };
+// batch 8: linear tasks stage x per 4096-column pass (gemv8_body)
+template <>
+struct Lay<8> {
+  static constexpr int XS = 0;
+  static constexpr int RES = LDS_X;
+  static constexpr int TOTAL = 156 * 1024;
+};
 static_assert(Lay<1>::RES + LDS_RES_BYTES <= Lay<1>::TOTAL, "LDS budget");
 static_assert(Lay<2>::RES + LDS_RES_BYTES <= Lay<2>::TOTAL, "LDS budget");
 
@@ -1806,6 +1813,371 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 }
 
 // ---------------------------------------------------------------------------
+// Batch-8 linear tasks on MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+//
+// y[r][row] = W[row] . x[r] for the 8 requests as steps of [16 rows] x [32
+// columns of W] x [16 MFMA columns].  The 16 MFMA columns carry each
+// request's input twice: its bf16 value (hi) and the bf16 value of what hi
+// leaves (lo = x - hi), so an input keeps about 16 significant bits while
+// the MFMA forms the hi and lo products in one instruction (padding 8
+// requests to 16 columns would otherwise waste them); y = D[row][r] +
+// D[row][r + 8].  The products of bf16 pairs are exact in fp32.
+//
+// A tile's rows form 16-row blocks; rows past the tile repeat its last row
+// (the same cache lines as a real row: no extra HBM traffic; discarded).  x
+// is staged in LDS in passes of 4096 columns as MFMA B operands: 1 KB per
+// 32-column k-step, lane l's 16 bytes at 16 l holding request l % 8 (hi for
+// l % 16 < 8, lo otherwise), columns 8 (l / 16) .. + 7 of the step; with a
+// norm, times the gain, and 1 / rms is applied to the sums.  Worker wave w
+// takes the blocks w / WK + (8 / WK) j (j < NBW) and the k-steps
+// [(w % WK) KS, (w % WK + 1) KS) of every pass, KS = 128 / WK; each lane loads
+// 16 bytes of weights per (block, k-step) straight into the A operand (row
+// l % 16 of the block, columns 8 (l / 16) .. + 7 of the step: 16 rows x 64
+// bytes per load, and the next k-step continues the same rows), RG k-steps
+// of loads in flight, the first RG issued before the inputs are awaited.
+// With WK > 1 the waves' partial sums meet in LDS and are added in wave
+// order: the result does not depend on timing (bitwise reproducible).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+#define G8_PASS 4096               // columns of x staged per pass
+#define G8_KSTEPS (G8_PASS / 32)   // MFMA k-steps per pass
+#define G8_ITEMS (8 * G8_PASS / 8) // (request, 8-column group) staging items per pass
+#define G8_NI ((G8_ITEMS + MPK_THREADS - 1) / MPK_THREADS)
+static_assert(MPK_THREADS % 8 == 0, "a thread's staging items share one request");
+static_assert(LDS_X + G8_KSTEPS * 1024 <= 156 * 1024, "a staged pass must fit the LDS");
+
+// hi and lo bf16 parts (round to nearest even) of 8 values, 16 bytes each
+DEV void split_hilo8(const float (&v)[8], u32x4& hi, u32x4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t h0 = f2bf(v[2 * e]), h1 = f2bf(v[2 * e + 1]);
+    const uint16_t l0 = f2bf(v[2 * e] - bf16f(h0)), l1 = f2bf(v[2 * e + 1] - bf16f(h1));
+    h[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
+// Weight row of virtual row vr (rows of W0, W1, W2 in order; gate/up pairs
+// interleaved).
+DEV const uint16_t* vrow_ptr(cop& D, int vr) {
+  if (D.pairs) return ((vr & 1) ? D.W1 : D.W0) + (int64_t)(vr >> 1) * D.K;
+  if (vr < D.N0) return D.W0 + (int64_t)vr * D.K;
+  if (vr < D.N0 + D.N1) return D.W1 + (int64_t)(vr - D.N0) * D.K;
+  return D.W2 + (int64_t)(vr - D.N0 - D.N1) * D.K;
+}
+
+// Stage pass p of the 8 requests' x into LDS (B operands), every thread of
+// the workgroup taking part.  Item i = tid + MPK_THREADS j covers request
+// i % 8 (the same for all of a thread's items) and columns 8 (i / 8) .. + 7
+// of the pass.  With a norm, each item's sum of squares of the raw values (in
+// column order) goes to LDS at G8_SQ, [request][item group].  Each
+// wavefront polls its own stamped words and the workgroup meets at the end.
+// Returns -1 on stop.
+#define G8_SQ (LDS_X + G8_KSTEPS * 1024)  // [8][512] floats
+static_assert(G8_SQ + 8 * 512 * 4 <= 156 * 1024, "staging sums exceed the LDS");
+DEV int stage_pass8(const mpk_kparams& P, cop& D, int p, char* smem, int tid, int s, int task_id, Waiter& Wt,
+                    uint32_t st) {
+  const int lane = tid & 63;
+  const uint32_t xb = lds_addr(smem) + LDS_X;
+  const uint32_t sqb = lds_addr(smem) + G8_SQ;
+  const int b = tid & 7;
+  uint32_t need = 0;
+  for (int j = 0; j < G8_NI; ++j)
+    if (tid + MPK_THREADS * j < G8_ITEMS) need |= 1u << j;
+  const int64_t xrow = (int64_t)b * D.K + (int64_t)p * G8_PASS;
+  const uint16_t* erow = D.x_embed ? D.E + (int64_t)cur_token_v(smem, b) * D.K + (int64_t)p * G8_PASS : nullptr;
+  for (;;) {
+#pragma unroll 1
+    for (int j = 0; j < G8_NI; ++j) {
+      if (!((need >> j) & 1u)) continue;
+      const int q = (tid + MPK_THREADS * j) >> 3;  // 8-column group within the pass
+      float v[8];
+      if (D.xll) {
+        uint64_t w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = ld_ll(D.xll + xrow + 8 * q + e);
+        bool ok = true;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ok &= ll_ok(w[e], st);
+          v[e] = ll_f(w[e]);
+        }
+        if (!ok) continue;
+      } else if (erow) {
+        unpack8(gldv<u32x4>(erow + 8 * q), v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = gld(D.x + xrow + 8 * q + e);
+      }
+      need &= ~(1u << j);
+      if (D.has_norm) {
+        float ssq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ssq = fmaf(v[e], v[e], ssq);
+        lds_write_f32(sqb + (uint32_t)(b * 512 + q) * 4u, ssq);
+        float gf[8];
+        unpack8(gldv<u32x4>(D.gain + p * G8_PASS + 8 * q), gf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= gf[e];
+      }
+      u32x4 hi, lo;
+      split_hilo8(v, hi, lo);
+      const uint32_t a = xb + (uint32_t)(q >> 2) * 1024u + (uint32_t)(16 * (q & 3) + b) * 16u;
+      lds_write_u32x4(a, hi);
+      lds_write_u32x4(a + 128u, lo);
+    }
+    if (__ballot(need != 0) == 0) break;
+    if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  lds_barrier();
+  return *lvi(smem, LDS_CTL) ? -1 : 0;
+}
+
+// 1 / rms of the 8 requests into LDS_INV (1 without a norm), from the items'
+// sums of squares: wave r < 8 adds request r's 512 item sums, 8 per lane in
+// column order, then across lanes in a fixed order.  Read back with a
+// per-lane request index, so the values live in LDS, not in a register
+// array.
+DEV void rms8(const mpk_kparams& P, cop& D, char* smem, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  float* inv = reinterpret_cast<float*>(smem + LDS_INV);
+  if (D.has_norm && wave < 8) {
+    const float* sq = reinterpret_cast<const float*>(smem + G8_SQ) + wave * 512 + lane * 8;
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t += sq[e];
+    t = wave_sum(t);
+    if (lane == 0) inv[wave] = 1.0f / sqrtf(t / (float)D.K + P.rms_eps);
+  } else if (!D.has_norm && tid < 8) {
+    inv[tid] = 1.0f;
+  }
+  __syncthreads();
+}
+
+// Residuals of an EPI_RESID tile into LDS_OUT ([request][output row], the
+// layout the epilogue then overwrites with the outputs): polled stamped
+// words, embedding rows, or a plain tensor.  Element idx goes to thread
+// idx % MPK_THREADS (the thread that later adds its sum); each wavefront polls
+// its own words with the watchdog.  Returns -1 on stop.
+DEV int gather_resid8(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, int s, int task_id, Waiter& Wt,
+                      uint32_t st, int n_out_tile) {
+  const int lane = tid & 63;
+  const uint32_t ob = lds_addr(smem) + LDS_OUT;
+  constexpr int PER = (8 * 128 + MPK_THREADS - 1) / MPK_THREADS;  // outputs per thread at most
+  uint32_t need = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = tid + k * MPK_THREADS;
+    if (idx >= 8 * n_out_tile) continue;
+    const int r = idx / n_out_tile, row = T.row0 + idx - r * n_out_tile;
+    if (D.res_embed) {
+      lds_write_f32(ob + (uint32_t)idx * 4u, bf16f(gld16(D.E + (int64_t)cur_token_v(smem, r) * D.n_out + row)));
+    } else if (!D.rll) {
+      lds_write_f32(ob + (uint32_t)idx * 4u, gld(D.resid + (int64_t)r * D.n_out + row));
+    } else {
+      need |= 1u << k;
+    }
+  }
+  for (;;) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (!((need >> k) & 1u)) continue;
+      const int idx = tid + k * MPK_THREADS;
+      const int r = idx / n_out_tile, row = T.row0 + idx - r * n_out_tile;
+      const uint64_t w = ld_ll(D.rll + (int64_t)r * D.n_out + row);
+      if (ll_ok(w, st)) {
+        lds_write_f32(ob + (uint32_t)idx * 4u, ll_f(w));
+        need &= ~(1u << k);
+      }
+    }
+    if (__ballot(need != 0) == 0) break;
+    if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  lds_barrier();
+  return *lvi(smem, LDS_CTL) ? -1 : 0;
+}
+
+template <int NBW, int WK>
+DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, char* smem, int tid, bool sched) {
+  constexpr int WR = MPK_NW / WK;       // row groups of waves
+  constexpr int KSW = G8_KSTEPS / WK;   // k-steps per wave per pass
+  constexpr int RG = NBW == 1 ? 8 : (NBW <= 3 ? 4 : 2);  // k-steps of weight loads in flight
+  static_assert(KSW % RG == 0, "passes hold whole ring rounds");
+  const int wave = uni(tid >> 6), lane = tid & 63;
+  const int wr = wave / WK, wk = wave % WK;
+  const int nrows = uni(T.nrows), row0 = uni(T.row0);
+  const int nblk = (nrows + 15) >> 4;
+  const int npass = uni(D.K / G8_PASS);
+  const int U = npass * KSW;  // this wave's k-steps over the task
+  const uint32_t st = stamp_of(P, s);
+  const uint32_t lb = lds_addr(smem);
+  const uint32_t xb = lb + LDS_X;
+  // weight row of each of this wave's blocks for this lane, at its first column
+  const gu32x4* wrow[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    int lr = (wr + WR * j) * 16 + (lane & 15);
+    lr = lr < nrows ? lr : nrows - 1;
+    wrow[j] = (const gu32x4*)(const void*)(vrow_ptr(D, row0 + lr) + 8 * (lane >> 4) + wk * KSW * 32);
+  }
+  // the ring: k-step u of this wave reads columns (u / KSW) G8_PASS + (u % KSW) 32 past wrow
+  u32x4 ring[RG][NBW];
+  auto issue = [&](int u, u32x4(&r)[NBW]) {
+    const int pp = u / KSW, t = u - pp * KSW;
+    const int off = (pp * G8_PASS + t * 32) / 8;  // in 16-byte units
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) r[j] = wrow[j][off];
+  };
+  if (!sched) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g) issue(g, ring[g]);
+  }
+  Waiter Wt = waiter_start();
+  if (D.x_embed || D.res_embed) {
+    const int rc = resolve_tokens(P, smem, tid, s, task_id, Wt);
+    if (rc) return rc;
+  }
+  {
+    const int rc = stage_pass8(P, D, 0, smem, tid, s, task_id, Wt, st);
+    if (rc) return rc;
+  }
+  rms8(P, D, smem, tid);
+  const float* inv = reinterpret_cast<const float*>(smem + LDS_INV);
+  mark_ready(P, s, task_id, tid);
+  if (tid == 0) *lvi(smem, LDS_SYNCED) = 1;
+  f32x4 acc[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u0 = 0; u0 < U; u0 += RG) {
+    if (u0 > 0 && u0 % KSW == 0) {
+      // next pass: every wave is done with the staged one
+      lds_barrier();
+      const int rc = stage_pass8(P, D, u0 / KSW, smem, tid, s, task_id, Wt, st);
+      if (rc) {
+        vm_wait<0>();
+        return rc;
+      }
+    }
+    if (!sched) {
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        const int ks = wk * KSW + (u0 + g) % KSW;
+        const u32x4 B = lds_read_u32x4(xb + (uint32_t)ks * 1024u + (uint32_t)lane * 16u);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ring[g][j]),
+                                                           __builtin_bit_cast(bf16x8, B), acc[j], 0, 0, 0);
+        if (u0 + g + RG < U) issue(u0 + g + RG, ring[g]);
+      }
+    }
+  }
+  // hi + lo: lanes with l % 16 < 8 hold request l % 16, rows 4 (l / 16) + i of each block
+#pragma unroll
+  for (int j = 0; j < NBW; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] += __shfl_xor(acc[j][i], 8);
+  const int n = lane & 15, g4 = lane >> 4;
+  const uint32_t ob = lb + LDS_OUT;
+  if (D.epi == MPK_EPI_ARGMAX) {
+    // ---- LM head (WK = 1): logits, this wave's best row per request ----
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    if (!sched && n < 8) {
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int blk = wr + WR * j;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int lr = blk * 16 + 4 * g4 + i;
+          if (lr < nrows) {
+            const float logit = acc[j][i] * inv[n];
+            if (D.logits && s < D.logits_iters) gst(D.logits + ((int64_t)s * P.B + n) * D.N0 + row0 + lr, logit);
+            if (logit > bv || (logit == bv && row0 + lr < bi)) bv = logit, bi = row0 + lr;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) bv = ov, bi = oi;
+    }
+    float* bvs = reinterpret_cast<float*>(smem + LDS_BEST);
+    int* bis = reinterpret_cast<int*>(smem + LDS_BEST + MPK_NW * 8 * 4);
+    if (!sched && lane < 8) bvs[wave * 8 + lane] = bv, bis[wave * 8 + lane] = bi;
+    __syncthreads();
+    if (tid < 8) {
+      float v = -INFINITY;
+      int ix = 0x7fffffff;
+      for (int w = 0; w < MPK_NW; ++w) {
+        const float vv = bvs[w * 8 + tid];
+        const int ii = bis[w * 8 + tid];
+        if (vv > v || (vv == v && ii < ix)) v = vv, ix = ii;
+      }
+      uint64_t* pw = D.pll + ((int64_t)T.tile * 8 + tid) * 2;
+      st_ll(pw, v, st);
+      st_lli(pw + 1, ix, st);
+    }
+    return 0;
+  }
+  // ---- cross-wave sums (in wave order) into LDS, then the epilogue ----
+  lds_barrier();  // every wave is done with the staged x: its area takes the partial sums
+  float* red = reinterpret_cast<float*>(smem + LDS_X);  // [WK][nblk][16 rows][8 requests]
+  if (!sched && n < 8) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int blk = wr + WR * j;
+      if (blk < nblk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[((wk * nblk + blk) * 16 + 4 * g4 + i) * 8 + n] = acc[j][i];
+    }
+  }
+  __syncthreads();
+  const int n_out_tile = D.pairs ? nrows / 2 : nrows;
+  if (D.epi == MPK_EPI_RESID) {
+    const int rc = gather_resid8(P, D, T, smem, tid, s, task_id, Wt, st, n_out_tile);
+    if (rc) return rc;
+  }
+  // output o of the tile, request r: its rows' sums over the waves
+  auto rowsum = [&](int lr, int r) {
+    float v = 0.f;
+    for (int k = 0; k < WK; ++k) v += red[((k * nblk + (lr >> 4)) * 16 + (lr & 15)) * 8 + r];
+    return v;
+  };
+  for (int idx = tid; idx < 8 * n_out_tile; idx += MPK_THREADS) {
+    const int r = idx / n_out_tile, o = idx - r * n_out_tile;
+    const uint32_t a = ob + (uint32_t)idx * 4u;
+    float y;
+    if (D.epi == MPK_EPI_SILU) {
+      y = silu(rowsum(2 * o, r) * inv[r]) * (rowsum(2 * o + 1, r) * inv[r]);
+    } else if (D.epi == MPK_EPI_RESID) {
+      y = lds_read_f32(a) + rowsum(o, r);  // this thread's own residual (gather_resid8)
+    } else {
+      y = rowsum(o, r) * inv[r];
+    }
+    lds_write_f32(a, y);
+  }
+  __syncthreads();
+  publish_tile<8>(P, D, T, lb, s, st, tid);
+  return 0;
+}
+
+// Batch-8 linear task: the work split for the tile's blocks.
+DEV int gemv8_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, char* smem, int tid, bool sched) {
+  const int nblk = (uni(T.nrows) + 15) >> 4;
+  if (D.epi == MPK_EPI_ARGMAX) return gemv8_body<5, 1>(P, T, D, s, task_id, smem, tid, sched);
+  if (nblk == 1) return gemv8_body<1, 8>(P, T, D, s, task_id, smem, tid, sched);
+  if (nblk == 2) return gemv8_body<2, 8>(P, T, D, s, task_id, smem, tid, sched);
+  return gemv8_body<3, 4>(P, T, D, s, task_id, smem, tid, sched);
+}
+
+// ---------------------------------------------------------------------------
 // dispatch of one task body; returns -1 when the run must stop
 // ---------------------------------------------------------------------------
 template <int NB>
@@ -1813,7 +2185,12 @@ DEV int run_task(const mpk_kparams& P, ctask& T, int task_id, int s, char* smem,
   cop& D = ops_of(P)[T.op];
   if (T.kind == MPK_TK_ATTN) return attn_task(P, T, D, smem, tid, sched, s, task_id);
   if (T.kind == MPK_TK_ARGMAX) return argmax_task<NB>(P, D, smem, tid, s, task_id);
-  return gemv_task<NB>(P, T, D, s, task_id, smem, tid, sched, next);
+  if constexpr (NB == 8) {
+    (void)next;
+    return gemv8_task(P, T, D, s, task_id, smem, tid, sched);
+  } else {
+    return gemv_task<NB>(P, T, D, s, task_id, smem, tid, sched, next);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1990,8 +2367,9 @@ static int select_kernels(int B, const void** pers, const void** op, int* lds) {
   switch (B) {
     case 1: kernels_for<1>(pers, op, lds); return MPK_OK;
     case 2: kernels_for<2>(pers, op, lds); return MPK_OK;
+    case 8: kernels_for<8>(pers, op, lds); return MPK_OK;
     default:
-      return mpk_fail(MPK_ERR_SHAPE, "this build runs num_requests in {1, 2}");
+      return mpk_fail(MPK_ERR_SHAPE, "this build runs num_requests in {1, 2, 8}");
   }
 }
 

@@ -139,6 +139,37 @@ class Session:
         self.exe.close()
 
 
+class RequestView:
+    """Request r of a batched Session as a batch-1 executable over views of
+    the session's own tensors (its tokens row, step and prompt_len entries,
+    and its slice of every layer's K/V cache, contiguous in the
+    [B, n_kv, S, d] layout): runs of it advance that request in place, e.g.
+    to ingest its prompt before batched decoding."""
+
+    def __init__(self, sess: "Session", r: int):
+        import torch
+
+        sh, m = sess.w.shape, sess.model
+        ptrs = m.ptrs()
+        for l in m.layer_ids:
+            ptrs["l%d.kcache" % l] = sess.kc[l][r].data_ptr()
+            ptrs["l%d.vcache" % l] = sess.vc[l][r].data_ptr()
+        ptrs.update(tokens=sess.tokens[r].data_ptr(), step=sess.step[r:r + 1].data_ptr(),
+                    prompt_len=sess.prompt_len[r:r + 1].data_ptr())
+        spec, meta = mpk.qwen3_graph(sh, 1, ptrs, sess.tokens.shape[1], sess.max_seq, layers=m.layer_ids)
+        num_cus = torch.cuda.get_device_properties(_dev()).multi_processor_count
+        self.exe = mpk.Executable(spec, meta, mpk.model_cfg(sh, 1, sess.max_seq), mpk.launch_cfg(num_cus))
+
+    def run(self, n_iter: int, stream=None):
+        import torch
+
+        s = torch.cuda.current_stream() if stream is None else stream
+        self.exe.run(n_iter, s.cuda_stream)
+
+    def close(self):
+        self.exe.close()
+
+
 def run_workload(w: "synth.Workload", n_iter: int, want_logits: bool = False, per_op: bool = False,
                  trace: bool = False, model: Optional[DeviceModel] = None, launch=None) -> dict:
     import torch

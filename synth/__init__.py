@@ -14,6 +14,10 @@ pages give no weights, so weights are seeded random, see ``make_model``):
                   positions with N(0,1) bf16, fp32 input h ~ N(0,1), one step.
 * ``wide1``       one Qwen3-8B-shaped layer with a 16384-id tied embedding /
                   LM head; 4 random prompt ids, 5 greedy tokens.
+* ``narrow8``     2 layers at the widths the batch-8 linear tasks take (hidden
+                  4096, 32 q / 8 kv heads of 128, FFN 4096) with a 4096-id
+                  vocabulary; batch 8, prompt lengths uniform in [3, 10],
+                  greedy to 14 iterations.
 * ``qwen3_8b``    36 layers + tied 151936-row embedding / LM head, batch 1,
                   39 random prompt ids, 512 greedy tokens.
 * ``qwen3_8b_b8`` same model at batch 8, prompt lengths uniform in [16, 512],
@@ -211,6 +215,12 @@ def workload(name: str, seed: int = 0, gains: str = "ones", **over) -> Workload:
         w = Workload("wide1", sh, 1, n_iter=(P - 1) + 5, tokens_width=P + 5,
                      prompt_len=np.array([P], np.int32), step0=np.zeros(1, np.int32),
                      seed=seed, gains=gains)
+    elif name == "narrow8":
+        B = 8
+        sh = ModelShape(2, 4096, 32, 8, 128, 4096, 4096)
+        P = uniform_int(seed, "narrow8.prompt_len", B, 3, 10)
+        w = Workload("narrow8", sh, B, n_iter=14, tokens_width=26, prompt_len=P,
+                     step0=np.zeros(B, np.int32), seed=seed, gains=gains)
     elif name == "qwen3_8b":
         P = 39
         w = Workload("qwen3_8b", QWEN3_8B, 1, n_iter=(P - 1) + 512, tokens_width=P + 512,

@@ -280,3 +280,36 @@ def test_host_run_check_follows_the_start_of_run_rule():
             mpk.mpk_check_run(g, np.array([-1, 4], np.int32), toks, plen, 1)
     finally:
         mpk.mpk_destroy_graph(g)
+
+
+def test_batch8_tiles_and_refusals():
+    """Batch 8 (the MFMA linear tasks): the same row tiles as batch 1 (QKV 24
+    rows = two 16-row blocks, o / down 16, gate/up 48 pairs, LM head 593/594),
+    attention 8 requests x 8 kv heads x 4 splits = 256 tasks; input widths
+    must be multiples of 4096 (the 256-wide tiny decoder is refused), and
+    batch sizes other than 1, 2 and 8 are refused."""
+    g, spec = build(synth.QWEN3_8B, B=8, tokens_width=4096, max_seq=800)
+    try:
+        info, tasks, _, _, _ = info_arrays(g)
+        kinds = [o.kind for o in spec.ops]
+        rows = {}
+        for t in tasks:
+            if t.op < len(kinds):
+                rows.setdefault(kinds[t.op], set()).add(t.nrows)
+        assert rows[mpk.MPK_OP_RMSNORM_LINEAR] == {24}
+        assert rows[mpk.MPK_OP_RMSNORM_GATEUP] == {96}
+        assert rows[mpk.MPK_OP_LINEAR_RESIDUAL] == {16}
+        assert rows[mpk.MPK_OP_LMHEAD_ARGMAX] == {593, 594}
+        attn = [t for t in tasks if t.op == 2]
+        assert len(attn) == 256 and {t.row0 for t in attn} == set(range(8))
+        assert {t.split for t in attn} == {0, 1, 2, 3}
+    finally:
+        mpk.mpk_destroy_graph(g)
+    g, _ = build(synth.workload("narrow8").shape, B=8, tokens_width=26, max_seq=26)
+    mpk.mpk_destroy_graph(g)
+    with pytest.raises(mpk.MPKError) as e:
+        build(synth.TINY, B=8)
+    assert e.value.code == mpk.MPK_ERR_SHAPE and "4096" in str(e.value)
+    with pytest.raises(mpk.MPKError) as e:
+        build(synth.TINY, B=3)
+    assert e.value.code == mpk.MPK_ERR_SHAPE
