@@ -1843,6 +1843,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #define G8_KSTEPS (G8_PASS / 32)   // MFMA k-steps per pass
 #define G8_ITEMS (8 * G8_PASS / 8) // (request, 8-column group) staging items per pass
 #define G8_NI ((G8_ITEMS + MPK_THREADS - 1) / MPK_THREADS)
+#define G8_IG 2  // staging items per thread whose words are in flight together
+static_assert(G8_NI % G8_IG == 0, "staging rounds hold whole item groups");
 static_assert(MPK_THREADS % 8 == 0, "a thread's staging items share one request");
 static_assert(LDS_X + G8_KSTEPS * 1024 <= 156 * 1024, "a staged pass must fit the LDS");
 
@@ -1890,20 +1892,31 @@ DEV int stage_pass8(const mpk_kparams& P, cop& D, int p, char* smem, int tid, in
   const int64_t xrow = (int64_t)b * D.K + (int64_t)p * G8_PASS;
   const uint16_t* erow = D.x_embed ? D.E + (int64_t)cur_token_v(smem, b) * D.K + (int64_t)p * G8_PASS : nullptr;
   for (;;) {
+    // G8_IG items per round: their stamped words are all in flight together
 #pragma unroll 1
-    for (int j = 0; j < G8_NI; ++j) {
+    for (int j0 = 0; j0 < G8_NI; j0 += G8_IG) {
+      uint64_t w[G8_IG][8];
+      if (D.xll) {
+#pragma unroll
+        for (int jj = 0; jj < G8_IG; ++jj) {
+          const int q = (tid + MPK_THREADS * (j0 + jj)) >> 3;
+          if ((need >> (j0 + jj)) & 1u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[jj][e] = ld_ll(D.xll + xrow + 8 * q + e);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < G8_IG; ++jj) {
+      const int j = j0 + jj;
       if (!((need >> j) & 1u)) continue;
       const int q = (tid + MPK_THREADS * j) >> 3;  // 8-column group within the pass
       float v[8];
       if (D.xll) {
-        uint64_t w[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = ld_ll(D.xll + xrow + 8 * q + e);
         bool ok = true;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          ok &= ll_ok(w[e], st);
-          v[e] = ll_f(w[e]);
+          ok &= ll_ok(w[jj][e], st);
+          v[e] = ll_f(w[jj][e]);
         }
         if (!ok) continue;
       } else if (erow) {
@@ -1928,6 +1941,9 @@ DEV int stage_pass8(const mpk_kparams& P, cop& D, int p, char* smem, int tid, in
       const uint32_t a = xb + (uint32_t)(q >> 2) * 1024u + (uint32_t)(16 * (q & 3) + b) * 16u;
       lds_write_u32x4(a, hi);
       lds_write_u32x4(a + 128u, lo);
+      }
+      // the next round's loads are issued after this round's words are used
+      asm volatile("" ::: "memory");
     }
     if (__ballot(need != 0) == 0) break;
     if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
@@ -2006,7 +2022,12 @@ template <int NBW, int WK>
 DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, char* smem, int tid, bool sched) {
   constexpr int WR = MPK_NW / WK;       // row groups of waves
   constexpr int KSW = G8_KSTEPS / WK;   // k-steps per wave per pass
-  constexpr int RG = NBW == 1 ? 8 : (NBW <= 3 ? 4 : 2);  // k-steps of weight loads in flight
+  // k-steps of weight loads in flight: the stream rate is set by the bytes in
+  // flight, the ring by the registers (168 per lane with three wavefronts on
+  // a SIMD, no spills): 16 loads of 1 KB per wave for one block, 8 for two,
+  // 12 for three, 10 for five.  Half of them are issued before the inputs
+  // are staged (registers for the staging), the rest after.
+  constexpr int RG = NBW == 1 ? 16 : (NBW == 2 ? 4 : (NBW == 3 ? 4 : 2));
   static_assert(KSW % RG == 0, "passes hold whole ring rounds");
   const int wave = uni(tid >> 6), lane = tid & 63;
   const int wr = wave / WK, wk = wave % WK;
@@ -2035,7 +2056,7 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
   };
   if (!sched) {
 #pragma unroll
-    for (int g = 0; g < RG; ++g) issue(g, ring[g]);
+    for (int g = 0; g < RG / 2; ++g) issue(g, ring[g]);
   }
   Waiter Wt = waiter_start();
   if (D.x_embed || D.res_embed) {
@@ -2045,6 +2066,11 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
   {
     const int rc = stage_pass8(P, D, 0, smem, tid, s, task_id, Wt, st);
     if (rc) return rc;
+  }
+  if (!sched) {
+#pragma unroll
+    for (int g = RG / 2; g < RG; ++g)
+      if (g < U) issue(g, ring[g]);
   }
   rms8(P, D, smem, tid);
   const float* inv = reinterpret_cast<const float*>(smem + LDS_INV);

@@ -177,6 +177,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=None, help="default: the prompt iterations (2 for long)")
     ap.add_argument("--iters", type=int, default=8)
     ap.add_argument("--out", default="timeline.json")
+    ap.add_argument("--batch", type=int, default=1, choices=(1, 2, 8),
+                    help="requests decoded together (qwen3_8b: each with its own seeded 39-id prompt)")
     args = ap.parse_args(argv)
 
     import torch
@@ -192,6 +194,10 @@ def main(argv=None) -> int:
     else:
         warm = int(synth.workload(args.workload).prompt_len[0]) - 1 if args.warmup is None else args.warmup
     w = synth.workload(args.workload, n_iter=warm + args.iters)
+    if args.batch > 1:
+        w = synth.Workload(w.name + "_b%d" % args.batch, w.shape, args.batch, w.n_iter, w.tokens_width,
+                           np.repeat(w.prompt_len[:1], args.batch), np.repeat(w.step0[:1], args.batch),
+                           kv_prefill=w.kv_prefill, seed=w.seed, gains=w.gains)
     model = runner.DeviceModel(w.shape, weights=synth.make_model(w.shape, seed=w.seed))
     sess = runner.Session(w, model, trace=2)
     if warm:
