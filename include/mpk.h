@@ -63,8 +63,9 @@ typedef enum {
 
 typedef enum { MPK_BF16 = 1, MPK_F32 = 2, MPK_I32 = 3 } mpk_dtype_t;
 
-/* Decoder shape and the two scalars the pages leave open (see the design
- * notes: RMSNorm eps inside the root, RoPE base). */
+/* Decoder shape (head_dim 64 or 128: the attention kernel is specialised
+ * for these; MPK_ERR_SHAPE otherwise) and two scalars the pages leave open:
+ * the RMSNorm epsilon (added inside the square root) and the RoPE base. */
 typedef struct {
   int32_t num_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
   float rms_eps;

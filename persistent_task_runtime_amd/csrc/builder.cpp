@@ -115,8 +115,8 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
     return mpk_fail(MPK_ERR_INVALID_ARG, "model config has a non-positive field");
   if (M.n_q_heads % M.n_kv_heads)
     return mpk_fail(MPK_ERR_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
-  if (M.head_dim % 16 || M.head_dim > 128 || M.head_dim < 16)
-    return mpk_fail(MPK_ERR_SHAPE, "head_dim must be a multiple of 16 in [16, 128]");
+  // the attention kernel is specialised for these two head sizes
+  if (M.head_dim != 64 && M.head_dim != 128) return mpk_fail(MPK_ERR_SHAPE, "head_dim must be 64 or 128");
   if (M.n_q_heads / M.n_kv_heads > MPK_NW)
     return mpk_fail(MPK_ERR_SHAPE, "more than 8 query heads per kv head");
 

@@ -41,6 +41,7 @@
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef const void __attribute__((address_space(1)))* gptr_t;
 typedef void __attribute__((address_space(3)))* lptr_t;
 
@@ -102,12 +103,13 @@ DEV float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 DEV float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 DEV float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bf16 bits, round to nearest even
-DEV uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// float -> bf16 bits, round to nearest even (NaN stays NaN): the hardware
+// conversion v_cvt_pk_bf16_f32, two values per instruction in f2bf2 (low
+// half a, high half b)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+DEV uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+DEV uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
 }
 
 template <int CTRL>
@@ -187,18 +189,6 @@ DEV void lds_read_2f4_near(uint32_t a, f32x4& x0, f32x4& x1) {
                : "=&v"(x0), "=&v"(x1)
                : "v"(a)
                : "memory");
-}
-
-// K and V of two position rounds from an LDS ring slot: [K0][K1][V0][V1],
-// 1 KB each, this lane's 16 bytes at a (early-clobber outputs, see
-// lds_read_2f4).
-DEV void lds_read_kv2(uint32_t a, u32x4 (&K)[2], u32x4 (&V)[2]) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
-      "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\ts_waitcnt lgkmcnt(0)"
-      : "=&v"(K[0]), "=&v"(K[1]), "=&v"(V[0]), "=&v"(V[1])
-      : "v"(a)
-      : "memory");
 }
 
 DEV float lds_read_f32(uint32_t a) {
@@ -1401,46 +1391,130 @@ DEV int argmax_task(const mpk_kparams& P, cop& D, char* smem, int tid, int s, in
 // ---------------------------------------------------------------------------
 // Attention task (request r, kv head j, split c of nsplit): per-head RMSNorm
 // of q and k, RoPE at the request's position p, K/V of p into the caches
-// (by the split that owns p), an online softmax over this split's positions
-// kept per lane group in registers, and one merge across the wavefronts.
-// The context [0, p] is cut into na = min(nsplit, ceil((p + 1) / 64))
-// splits; splits c >= na have nothing to do this iteration.  With one split
-// the task writes the attention output of the group's query heads; with
-// several, splits publish stamped partials (m, l, acc) and the split that
-// owns p merges them into the output.  Returns -1 on stop.
+// (by the split that owns p), then softmax(q K^T) V over this split's
+// positions on MFMA, and one merge across the wavefronts.  The context
+// [0, p] is cut into na = min(nsplit, ceil((p + 1) / 64)) splits; splits
+// c >= na have nothing to do this iteration.  With one split the task writes
+// the attention output of the group's query heads; with several, splits
+// publish stamped partials (m, l, acc) and the split that owns p merges them
+// into the output.  Returns -1 on stop.
+//
+// The split's positions go in steps of 16 (wave w of the eight worker waves
+// takes steps w, w + 8, ...):
+//   S = K q on v_mfma_f32_16x16x32_bf16: the step's K rows are the A operand
+//     (16 positions x 32 dims per instruction), q the B operand: columns 0..3 the bf16 (hi) parts of the group's heads,
+//     columns 4..7 the bf16 parts of what hi leaves (lo), so q keeps about 16
+//     bits; S = column h + column h + 4.  Scores are in base 2 (q carries
+//     log2(e) / sqrt(d)).
+//   An online softmax per head: the reference maximum moves only when a
+//     score exceeds it by 8 (weights stay below 2^8, most steps skip the
+//     rescale); any reference gives the same softmax once l and acc share
+//     it.
+//   O^T += V^T P on v_mfma_f32_16x16x16_bf16: the step's V rows land in LDS
+//     by global->LDS DMA (1 KB = 512 / d rows per instruction, 32 bytes of
+//     padding between instructions) and are read transposed, 4 positions of
+//     one dim per lane, as the A operand; P (hi / lo columns again) is the B
+//     operand, taken from the score layout with one exchange.
+//   K and V of a step land in LDS by global->LDS DMA (device scope): K as
+//     the score MFMA's A operand, 1 KB per 32 dims in lane order (a
+//     conflict-free 16-byte read per lane), V as rows (above).  at_ring(DH)
+//     steps per wave are in flight.  With no loads into registers in the
+//     fold, every wait on them is explicit (the compiler's own waits on a
+//     register ring fall back to full drains across this loop).
+// Position p itself is not read from the cache: its K/V are in LDS; the
+// scheduler wavefront scores it and it joins the merge as a ninth partial.
+// Idle positions (past the split, or p) read row lo and score -inf.
 // ---------------------------------------------------------------------------
 #define ATT_MAXG 4
-#define ATT_ROUNDS 2    // position rounds per wavefront whose K/V rows are loaded together
-#define ATT_GROUPS 64   // position groups per workgroup at most (NW waves x 64 / LP, d >= 64)
-#define ATT_RING 2      // LDS ring slots (steps of K/V rows) per wavefront, multi-step splits
-#define ATT_SLOT (2 * ATT_ROUNDS * 1024)  // one ring slot: K and V of a step, 1 KB per round each
-static_assert(ATT_ROUNDS == 2, "lds_read_kv2 reads two rounds");
-static_assert((ATT_RING & (ATT_RING - 1)) == 0 && ATT_RING >= 2, "ring slots are indexed with i & (ATT_RING - 1)");
-// the ring overlays the group accumulators and what follows them
-static_assert(LDS_X + (ATT_MAXG * 128 + 256 + 2 * ATT_GROUPS * ATT_MAXG) * 4 + MPK_NW * ATT_RING * ATT_SLOT <=
-                  Lay<1>::TOTAL,
-              "attention K/V ring exceeds the LDS");
+#define AT_VRING (LDS_X + 3 * 1024)    // after q [4][128] and the k / v row of p
+// one step's K (DH / 32 KB) and V (16 rows in 1 KB DMA chunks + 32 bytes of
+// padding each) in the ring, and the steps in flight per wave
+constexpr int at_slot(int dh) { return dh * 32 + (dh / 32) * 1056; }
+constexpr int at_ring(int dh) { return dh == 128 ? 2 : 3; }
+static_assert(AT_VRING + MPK_NW * at_ring(128) * at_slot(128) <= 156 * 1024, "attention ring exceeds the LDS");
+static_assert(AT_VRING + MPK_NW * at_ring(64) * at_slot(64) <= 156 * 1024, "attention ring exceeds the LDS");
+static_assert(AT_VRING + (9 * ATT_MAXG * 128 + 2 * 9 * ATT_MAXG) * 4 + 64 * 1024 <= 156 * 1024,
+              "attention merge area and partial gather exceed the LDS");
 
-// Sum over the LP lanes of a position group (lanes [g*LP, (g+1)*LP)), every
-// lane of the group receiving the same value (quad swaps, then half-row and
-// row mirrors: DPP, no LDS round trip).
-DEV float group_sum(float v, int LP) {
-  v += dpp<0xB1>(v);                  // quad_perm [1,0,3,2]
-  if (LP >= 4) v += dpp<0x4E>(v);     // quad_perm [2,3,0,1]
-  if (LP >= 8) v += dpp<0x141>(v);    // row_half_mirror
-  if (LP >= 16) v += dpp<0x140>(v);   // row_mirror
-  return v;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// hi and lo bf16 parts (round to nearest even) of 8 values, 16 bytes each
+DEV void split_hilo8(const float (&v)[8], u32x4& hi, u32x4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f2bf2(v[2 * e], v[2 * e + 1]);
+    l[e] = f2bf2(v[2 * e] - __uint_as_float(h[e] << 16), v[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
-struct SoftState {
-  float m[ATT_MAXG], l[ATT_MAXG], acc[ATT_MAXG][8];
-};
 
+// bf16 hi part of 4 values (packed pairs) and of what hi leaves (lo)
+DEV void split_hilo4(const float (&v)[4], u32x2& hi, u32x2& lo) {
+  const uint32_t h0 = f2bf2(v[0], v[1]), h1 = f2bf2(v[2], v[3]);
+  hi = u32x2{h0, h1};
+  lo = u32x2{f2bf2(v[0] - __uint_as_float(h0 << 16), v[1] - __uint_as_float(h0 & 0xffff0000u)),
+             f2bf2(v[2] - __uint_as_float(h1 << 16), v[3] - __uint_as_float(h1 & 0xffff0000u))};
+}
+
+// The transposed A operand of V^T P for two 16-dim blocks: 4 positions of one
+// dim each, at a (block b0: rows a, a + RS, a + 2 RS, a + 3 RS) and a + 32.
+// Zero-extending 16-bit reads, packed in pairs afterwards (the d16 forms do
+// not keep the other half of the register when SRAM ECC is on).  asm LDS
+// reads: a compiler-visible LDS read after the DMAs would wait for every DMA
+// in flight.
+template <int RS>
+DEV void lds_read_vt2(uint32_t a, u32x2& x, u32x2& y) {
+  uint32_t v[8];
+  asm volatile(
+      "ds_read_u16 %0, %8\n\tds_read_u16 %1, %8 offset:%9\n\t"
+      "ds_read_u16 %2, %8 offset:%10\n\tds_read_u16 %3, %8 offset:%11\n\t"
+      "ds_read_u16 %4, %8 offset:32\n\tds_read_u16 %5, %8 offset:%12\n\t"
+      "ds_read_u16 %6, %8 offset:%13\n\tds_read_u16 %7, %8 offset:%14\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a), "n"(RS), "n"(2 * RS), "n"(3 * RS), "n"(32 + RS), "n"(32 + 2 * RS), "n"(32 + 3 * RS)
+      : "memory");
+  x = u32x2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+  y = u32x2{v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+}
+
+// The A operand of a step's scores: KS 16-byte reads at a, a + 1 KB, ...
+// (early-clobber outputs, see lds_read_2f4)
+template <int KS>
+DEV void lds_read_k(uint32_t a, u32x4 (&k)[KS]) {
+  static_assert(KS == 2 || KS == 4, "head_dim 64 or 128");
+  if constexpr (KS == 2) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(k[0]), "=&v"(k[1])
+                 : "v"(a)
+                 : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+        : "v"(a)
+        : "memory");
+  }
+}
+
+template <int DH>
 DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, bool sched, int s, int task_id) {
+  constexpr int KS = DH / 32;    // k-steps of a score MFMA
+  constexpr int DB = DH / 16;    // 16-dim blocks of V
+  constexpr int PPI = 512 / DH;  // V rows per 1 KB DMA chunk
+  constexpr int LPR = DH / 8;    // lanes per V row (16 bytes each)
+  constexpr int OPS = KS + 16 / PPI;  // vector-memory operations per step (K and V DMAs)
+  constexpr int AT_R = at_ring(DH), SLOT = at_slot(DH), KBYTES = DH * 32;
+  static_assert(DB % 2 == 0, "V^T blocks are read in pairs");
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g4 = lane >> 4, cn = lane & 15;  // MFMA lane: row group, column
   const int r = T.row0, j = T.nrows, c = T.split, NS = D.nsplit;
-  const int d = D.d, G = D.nq / D.nkv, half = d >> 1, LP = d >> 3, PPR = 64 / LP;
-  const int step = MPK_NW * PPR * ATT_ROUNDS;  // positions per step of all wavefronts
+  const int G = D.nq / D.nkv, half = DH >> 1;
   const int p = cur_pos(smem, r);
   const int n = p + 1;
   const int na = min(NS, (n + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT);
@@ -1448,56 +1522,57 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   const int lo = (int)(((int64_t)c * n) / na), hi = (int)(((int64_t)(c + 1) * n) / na);
   const bool owner = c == na - 1;  // the split holding position p
   const uint32_t st = stamp_of(P, s);
-  // position groups: lanes [g*LP, (g+1)*LP) of a wavefront take one position
-  // (LP lanes x 8 dims); NG = NW * PPR groups per workgroup
-  const int NG = MPK_NW * PPR;
-  float* qs = reinterpret_cast<float*>(smem + LDS_X);  // [G][d]
-  float* kv = qs + ATT_MAXG * 128;                      // k [d], v [d] (bf16-rounded)
-  float* wm = kv + 256;                                 // [NG][G] group maxima
-  float* wl = wm + ATT_GROUPS * ATT_MAXG;               // [NG][G] group sums
-  float* wacc = wl + ATT_GROUPS * ATT_MAXG;             // [NG][G][d] group accumulators
-  uint32_t* gath = reinterpret_cast<uint32_t*>(wacc + ATT_GROUPS * ATT_MAXG * 64);  // gathered partials
+  const uint32_t lb = lds_addr(smem);
+  float* qs = reinterpret_cast<float*>(smem + LDS_X);  // [G][DH], scaled for base-2 scores
+  float* kv = qs + ATT_MAXG * 128;                      // k [DH], v [DH] of p (bf16-rounded)
+  float* mo = reinterpret_cast<float*>(smem + AT_VRING);  // merge: [9][G][DH] (over the ring)
+  float* mm = mo + 9 * ATT_MAXG * 128;                    // [9][G] maxima
+  float* ml = mm + 9 * ATT_MAXG;                          // [9][G] sums
+  uint32_t* gath = reinterpret_cast<uint32_t*>(ml + 9 * ATT_MAXG);  // gathered split partials
   float* outs = reinterpret_cast<float*>(smem + LDS_OUT);               // partial, then o
   uint32_t* kvrow = reinterpret_cast<uint32_t*>(smem + LDS_OUT) + 640;  // bf16 K row, then V row
-  const int qkv_w = (D.nq + 2 * D.nkv) * d;
-  uint16_t* kc = D.kc + ((int64_t)(r * D.nkv + j) * D.S) * d;
-  uint16_t* vc = D.vc + ((int64_t)(r * D.nkv + j) * D.S) * d;
-  const int dim0 = (lane % LP) * 8;
-  const int pg = lane / LP;
-  // scores are kept in base-2 units, s * log2(e) / sqrt(d): every
-  // exponential below is one exp2.  The factor is applied to q once, when
-  // q is staged, rather than to every score.
-  const float scale = 1.4426950408889634f / sqrtf((float)d);
+  const int qkv_w = (D.nq + 2 * D.nkv) * DH;
+  uint16_t* kc = D.kc + ((int64_t)(r * D.nkv + j) * D.S) * DH;
+  uint16_t* vc = D.vc + ((int64_t)(r * D.nkv + j) * D.S) * DH;
+  // base-2 scores: log2(e) / sqrt(d) is applied to q once, when it is staged
+  const float scale = 1.4426950408889634f / sqrtf((float)DH);
 
-  SoftState sm;
+  // ---- the fold's steps: wave w takes steps w, w + 8, ... of 16 positions ----
+  const int nst = (hi - lo + 15) >> 4;
+  const int nmine = nst > wave ? (nst - wave + MPK_NW - 1) / MPK_NW : 0;
+  const uint32_t ring = lb + AT_VRING + (uint32_t)wave * (AT_R * SLOT);
+  // step i of this wave: positions t0 .. t0 + 15, t0 = lo + 16 (wave + 8 i),
+  // into ring slot `slot` (K, then V)
+  auto issue = [&](int i, uint32_t slot) {
+    const int t0 = lo + 16 * (wave + MPK_NW * i);
+    const int tk = t0 + cn;
+    const int rk = tk < hi && tk != p ? tk : lo;
 #pragma unroll
-  for (int h = 0; h < ATT_MAXG; ++h) {
-    sm.m[h] = -INFINITY, sm.l[h] = 0.f;
+    for (int kk = 0; kk < KS; ++kk)
+      __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(kc + (int64_t)rk * DH + 32 * kk + 8 * g4),
+                                       lds_ptr(slot + kk * 1024), 16, 0, 16 /* sc1: device scope */);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.acc[h][e] = 0.f;
-  }
-  // K/V rows of this wave's first rounds.  The cache rows below p were
-  // written by earlier iterations, all ended once any input of this
-  // iteration has arrived.  If an earlier task of this iteration on this CU
-  // has already waited for one (LDS_SYNCED), the rows are loaded before
-  // this task's own wait; otherwise (nothing before it on this queue, or only
-  // tasks with nothing to do) after it.
-  // (Splits of more than one step stream their rows through an LDS ring
-  // instead, below.)
-  const bool multi = hi - lo > step;
-  u32x4 kr[ATT_ROUNDS], vr[ATT_ROUNDS];
-  auto load_into = [&](u32x4(&K)[ATT_ROUNDS], u32x4(&V)[ATT_ROUNDS], int base) {
-#pragma unroll
-    for (int q = 0; q < ATT_ROUNDS; ++q) {
-      const int t = base + (wave + MPK_NW * q) * PPR + pg;
-      const int tc = t < hi && t != p ? t : lo;  // in-bounds row for idle lanes
-      K[q] = ld_dev16(kc + (int64_t)tc * d + dim0);
-      V[q] = ld_dev16(vc + (int64_t)tc * d + dim0);
+    for (int c4 = 0; c4 < 16 / PPI; ++c4) {
+      const int tv = t0 + c4 * PPI + lane / LPR;
+      const int rv = tv < hi && tv != p ? tv : lo;
+      __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(vc + (int64_t)rv * DH + 8 * (lane % LPR)),
+                                       lds_ptr(slot + KBYTES + c4 * 1056), 16, 0, 16 /* sc1: device scope */);
     }
   };
-  auto load_rounds = [&](int base) { load_into(kr, vr, base); };
-  const bool early = uni(*lvi(smem, LDS_SYNCED)) != 0;
-  if (!sched && lo < hi && !multi && early) load_rounds(lo);
+  // The cache rows below p were written by earlier iterations, all ended once
+  // any input of this iteration has arrived.  If an earlier task of this
+  // iteration on this CU has already waited for one, the first steps are
+  // issued before this task's own wait; otherwise after it.
+  // (Whatever earlier tasks left in flight is waited for first: the
+  // compiler's waits would otherwise drain these loads as well, at once.)
+  vm_drain_known();
+  int pre = 0;
+  if (!sched && uni(*lvi(smem, LDS_SYNCED)) != 0) {
+#pragma unroll
+    for (int i = 0; i < AT_R - 1; ++i)
+      if (i < nmine) issue(i, ring + i * SLOT);
+    pre = min(AT_R - 1, nmine);
+  }
 
   // ---- q / k / v words of the group: wave hh < G + 2 takes one head vector ----
   const int hh = wave;
@@ -1514,7 +1589,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   Waiter Wt = waiter_start();
   const bool mine = !sched && hh < G + 2 && lane < half;
   const uint64_t* src = D.xll + (int64_t)r * qkv_w +
-                        (hh < G ? (j * G + hh) * d : (hh == G ? D.nq * d + j * d : (D.nq + D.nkv) * d + j * d));
+                        (hh < G ? (j * G + hh) * DH : (hh == G ? D.nq * DH + j * DH : (D.nq + D.nkv) * DH + j * DH));
   uint64_t wa = 0, wb = 0;
   {
     // each wavefront polls its own head vector; the workgroup meets once
@@ -1533,10 +1608,9 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     if (*lvi(smem, LDS_CTL)) return -1;
   }
   if (tid == 0) *lvi(smem, LDS_SYNCED) = 1;
-  if (!sched && lo < hi && !multi && !early) load_rounds(lo);
-  // The K/V rows, RoPE factors and gains above are loads issued before the
+  // the K/V steps, RoPE factors and gains above are loads issued before the
   // device-scope polls: complete them here (see vm_drain_known; they were
-  // issued first, so this costs little).
+  // issued first, so this costs little)
   vm_drain_known();
   mark_ready(P, s, task_id, tid);
 
@@ -1546,15 +1620,15 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     const float b = lane < half ? ll_f(wb) : 0.f;
     if (hh <= G) {
       const float ss = wave_sum(a * a + b * b);
-      const float inv = 1.0f / sqrtf(ss / (float)d + P.rms_eps);
+      const float inv = 1.0f / sqrtf(ss / (float)DH + P.rms_eps);
       if (lane < half) {
         const float ya = ga * (a * inv);
         const float yb = gb * (b * inv);
         const float ra = ya * cs - yb * sn;
         const float rb = yb * cs + ya * sn;
         if (hh < G) {
-          qs[hh * d + lane] = ra * scale;
-          qs[hh * d + lane + half] = rb * scale;
+          qs[hh * DH + lane] = ra * scale;
+          qs[hh * DH + lane + half] = rb * scale;
         } else {
           const uint16_t ka = f2bf(ra), kb = f2bf(rb);
           kv[lane] = bf16f(ka);
@@ -1565,200 +1639,181 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       }
     } else if (lane < half) {
       const uint16_t va = f2bf(a), vb = f2bf(b);
-      kv[d + lane] = bf16f(va);
-      kv[d + lane + half] = bf16f(vb);
-      reinterpret_cast<uint16_t*>(kvrow)[d + lane] = va;
-      reinterpret_cast<uint16_t*>(kvrow)[d + lane + half] = vb;
+      kv[DH + lane] = bf16f(va);
+      kv[DH + lane + half] = bf16f(vb);
+      reinterpret_cast<uint16_t*>(kvrow)[DH + lane] = va;
+      reinterpret_cast<uint16_t*>(kvrow)[DH + lane + half] = vb;
     }
   }
   __syncthreads();
-  // the owner's scheduler wavefront writes K/V of p into the caches while the
-  // workers score; its stores complete before the output is published (next
-  // iteration's readers are ordered after that output)
-  if (sched && owner) {
-    uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * d);
-    uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * d);
-    for (int i = lane; i < d / 2; i += 64) {
-      st_devu(kdst + i, kvrow[i]);
-      st_devu(vdst + i, kvrow[d / 2 + i]);
-    }
-    vm_drain();
-  }
 
-  // ---- scores and online softmax over this wave's positions ----
-  if (!sched) {
-    // q is read from LDS in each step (asm reads: not hoisted into 32 more
-    // live registers across the loop)
-    const uint32_t qa = lds_addr(qs) + (uint32_t)dim0 * 4u;
-    const uint32_t kva = lds_addr(kv) + (uint32_t)dim0 * 4u;
-    // one base step: its positions folded into the running (m, l, acc)
-    auto fold = [&](u32x4(&K)[ATT_ROUNDS], u32x4(&V)[ATT_ROUNDS], int base) {
-      // this round's ATT_ROUNDS positions per lane group are folded into the
-      // running (m, l, acc) together: one rescale per head per base step
-      float kf[ATT_ROUNDS][8], vf[ATT_ROUNDS][8];
-      bool valid[ATT_ROUNDS];
+  float m = -INFINITY, l = 0.f;  // workers, head cn (lanes cn < G): running reference and this lane's sum
+  f32x4 acc[DB];
 #pragma unroll
-      for (int q = 0; q < ATT_ROUNDS; ++q) {
-        const int t = base + (wave + MPK_NW * q) * PPR + pg;
-        valid[q] = t < hi;
-        // The loaded rows are unpacked on every lane (the wait for them is
-        // then in straight-line code, not in a branch that all lanes may
-        // skip, which would leave them outstanding into the next step's
-        // loads).  Row p comes from LDS; an idle lane (its row is not this
-        // split's) takes it too, so no value outside the rows in [lo, p)
-        // reaches the sums, whatever the cache holds there.
-        unpack8(K[q], kf[q]);
-        unpack8(V[q], vf[q]);
-        if (t == p || !valid[q]) {
-          // (asm reads: a compiler-visible LDS read here would wait for
-          // every K/V ring DMA in flight)
-          f32x4 k0, k1, v0, v1;
-          lds_read_2f4_near(kva, k0, k1);
-          lds_read_2f4_near(kva + (uint32_t)d * 4u, v0, v1);
-          kf[q][0] = k0.x, kf[q][1] = k0.y, kf[q][2] = k0.z, kf[q][3] = k0.w;
-          kf[q][4] = k1.x, kf[q][5] = k1.y, kf[q][6] = k1.z, kf[q][7] = k1.w;
-          vf[q][0] = v0.x, vf[q][1] = v0.y, vf[q][2] = v0.z, vf[q][3] = v0.w;
-          vf[q][4] = v1.x, vf[q][5] = v1.y, vf[q][6] = v1.z, vf[q][7] = v1.w;
-        }
+  for (int b = 0; b < DB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float spv[ATT_MAXG];  // scheduler wave: scores of position p
+  if (sched) {
+    // the owner's K/V of p into the caches (its stores complete before the
+    // output is published; next iteration's readers are ordered after that
+    // output), then the scores of position p, the merge's ninth partial
+    if (owner) {
+      uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * DH);
+      uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * DH);
+      for (int i = lane; i < DH / 2; i += 64) {
+        st_devu(kdst + i, kvrow[i]);
+        st_devu(vdst + i, kvrow[DH / 2 + i]);
       }
-#pragma unroll
-      for (int h = 0; h < ATT_MAXG; ++h) {
-        if (h < G) {
-          f32x4 q0, q1;  // q of head h, dims dim0 .. dim0 + 7
-          lds_read_2f4_near(qa + (uint32_t)(h * d) * 4u, q0, q1);
-          const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-          float sc[ATT_ROUNDS];
-          float Mx = -INFINITY;
-#pragma unroll
-          for (int q = 0; q < ATT_ROUNDS; ++q) {
-            float part = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part = fmaf(qv[e], kf[q][e], part);
-            part = group_sum(part, LP);  // all lanes of a group share valid[q]
-            sc[q] = valid[q] ? part : -INFINITY;
-            Mx = fmaxf(Mx, sc[q]);
-          }
-          // (m, l, acc) hold the sums relative to a reference m that moves
-          // only when a score exceeds it by more than 8 (base 2; always for
-          // the first score, m = -inf): weights stay below 2^8, and most
-          // steps skip the rescale.  Any reference gives the same softmax
-          // once l and acc share it, which the merges below rely on.
-          // (exponentials: the hardware's v_exp_f32, which maps -inf to 0;
-          // no weight here needs a denormal result)
-          if (Mx > sm.m[h] + 8.f) {
-            const float co = __builtin_amdgcn_exp2f(sm.m[h] - Mx);  // 0 for m = -inf
-            sm.l[h] *= co;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm.acc[h][e] *= co;
-            sm.m[h] = Mx;
-          }
-          if (Mx != -INFINITY) {
-            float L = sm.l[h];
-#pragma unroll
-            for (int q = 0; q < ATT_ROUNDS; ++q) {
-              const float w = __builtin_amdgcn_exp2f(sc[q] - sm.m[h]);  // 0 for an idle position
-              L += w;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) sm.acc[h][e] = fmaf(w, vf[q][e], sm.acc[h][e]);
-            }
-            sm.l[h] = L;
-          }
-        }
-      }
-    };
-    if (!multi) {
-      fold(kr, vr, lo);
-    } else {
-      // K/V rows through a ring of ATT_RING steps per wavefront in LDS,
-      // filled by global->LDS DMA: ATT_RING - 1 steps stay in flight while
-      // one is folded, and no registers are held by loads in flight.  The
-      // ring overlays the group accumulators (written below, after every
-      // wavefront has left this loop) and the gathered partials.  Past the
-      // end, steps re-read row lo (folded with weight 0).  Waits are exact
-      // counts: the loop issues no other vector-memory operation, and its
-      // LDS reads are asm, which the compiler does not hold for the DMAs.
-      const uint32_t ring = lds_addr(wacc) + (uint32_t)wave * (ATT_RING * ATT_SLOT);
-      auto dma_step = [&](int i) {
-        const int base = lo + i * step;
-        const uint32_t slot = ring + (uint32_t)(i & (ATT_RING - 1)) * ATT_SLOT;
-#pragma unroll
-        for (int q = 0; q < ATT_ROUNDS; ++q) {
-          const int t = base + (wave + MPK_NW * q) * PPR + pg;
-          const int tc = t < hi && t != p ? t : lo;  // in-bounds row for idle lanes
-          __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(kc + (int64_t)tc * d + dim0),
-                                           lds_ptr(slot + q * 1024), 16, 0, 16 /* sc1: device scope */);
-          __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(vc + (int64_t)tc * d + dim0),
-                                           lds_ptr(slot + (ATT_ROUNDS + q) * 1024), 16, 0, 16);
-        }
-      };
-      const int nst = (hi - lo + step - 1) / step;
-#pragma unroll
-      for (int i = 0; i < ATT_RING - 1; ++i) dma_step(i);
-      for (int i = 0; i < nst; ++i) {
-        dma_step(i + ATT_RING - 1);
-        vm_wait_known<(ATT_RING - 1) * 2 * ATT_ROUNDS>();  // step i has landed
-        u32x4 K[ATT_ROUNDS], V[ATT_ROUNDS];
-        lds_read_kv2(ring + (uint32_t)(i & (ATT_RING - 1)) * ATT_SLOT + (uint32_t)lane * 16u, K, V);
-        fold(K, V, lo + i * step);
-      }
-      vm_drain_known();
+      vm_drain();
     }
-  }
-  // every wavefront is done with the ring before the accumulators over it
-  // are written
-  if (multi) __syncthreads();
-  if (!sched) {
-    // each position group's (m, l, acc) to LDS: merged across groups and
-    // wavefronts below in one pass
-    const int grp = wave * PPR + pg;
 #pragma unroll
     for (int h = 0; h < ATT_MAXG; ++h) {
-      if (h < G) {
-        if ((lane % LP) == 0) {
-          wm[grp * ATT_MAXG + h] = sm.m[h];
-          wl[grp * ATT_MAXG + h] = sm.l[h];
+      float part = 0.f;
+      if (h < G)
+        for (int i = lane; i < DH; i += 64) part = fmaf(qs[h * DH + i], kv[i], part);
+      spv[h] = wave_sum(part);
+    }
+  } else {
+    // ---- the MFMA fold over this wave's steps ----
+    // q as the B operand of the scores, per 32-dim k-step
+    u32x4 qb[KS];
+    {
+      const int h = cn & 3;
+      const bool has = cn < 8 && h < G;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        float qv[8];
+        f32x4 q0, q1;
+        lds_read_2f4_near(lb + LDS_X + (uint32_t)(h * DH + 32 * kk + 8 * g4) * 4u, q0, q1);
+        qv[0] = q0.x, qv[1] = q0.y, qv[2] = q0.z, qv[3] = q0.w;
+        qv[4] = q1.x, qv[5] = q1.y, qv[6] = q1.z, qv[7] = q1.w;
+        u32x4 hi8, lo8;
+        split_hilo8(qv, hi8, lo8);
+        qb[kk] = !has ? u32x4{0u, 0u, 0u, 0u} : (cn < 4 ? hi8 : lo8);
+      }
+    }
+    // the rest of the first AT_R - 1 steps
+#pragma unroll
+    for (int i = 0; i < AT_R - 1; ++i)
+      if (i >= pre && i < nmine) issue(i, ring + i * SLOT);
+    for (int i0 = 0; i0 < nmine; i0 += AT_R) {
+#pragma unroll
+      for (int sl = 0; sl < AT_R; ++sl) {
+        const int i = i0 + sl;
+        if (i >= nmine) break;
+        const int nx = (sl + AT_R - 1) % AT_R;
+        if (i + AT_R - 1 < nmine) issue(i + AT_R - 1, ring + nx * SLOT);
+        // step i has landed (loads complete in issue order: only the later
+        // steps' operations may still be in flight)
+        const int later = min(AT_R - 1, nmine - 1 - i);
+        if (later >= 2) vm_wait_known<2 * OPS>();
+        else if (later == 1) vm_wait_known<OPS>();
+        else vm_wait_known<0>();
+        const int t0 = lo + 16 * (wave + MPK_NW * i);
+        // scores of the step's 16 positions: lane (g4, cn) holds positions
+        // t0 + 4 g4 + e of column cn; hi + lo columns
+        const uint32_t slot = ring + sl * SLOT;
+        u32x4 kr[KS];
+        lds_read_k<KS>(slot + lane * 16, kr);
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]),
+                                                       __builtin_bit_cast(bf16x8, qb[kk]), sa, 0, 0, 0);
+        float sv[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = sa[e] + __shfl_xor(sa[e], 4);
+          const int t = t0 + 4 * g4 + e;
+          sv[e] = cn < G && t < hi && t != p ? v : -INFINITY;
+          mx = fmaxf(mx, sv[e]);
         }
-        float* dst = wacc + (grp * ATT_MAXG + h) * d + dim0;
-        *reinterpret_cast<float4*>(dst) = float4{sm.acc[h][0], sm.acc[h][1], sm.acc[h][2], sm.acc[h][3]};
-        *reinterpret_cast<float4*>(dst + 4) = float4{sm.acc[h][4], sm.acc[h][5], sm.acc[h][6], sm.acc[h][7]};
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool mv = mx > m + 8.f;  // (always for the first score: m = -inf)
+        if (__ballot(mv) != 0) {
+          const float mn = mv ? mx : m;
+          const float co = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+          l *= co;
+          m = mn;
+          // columns cn and cn + 4 belong to head cn & 3
+          const float cc = __shfl(co, (lane & 0x30) | (lane & 3));
+#pragma unroll
+          for (int b = 0; b < DB; ++b) acc[b] *= cc;
+        }
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m);
+          l += pv[e];
+        }
+        // P as the B operand: lane (g4, cn) takes positions 4 g4 .. + 3 of
+        // column cn: the hi parts for cn < 4, the lo parts (from lane - 4) for
+        // cn in 4..7, zero beyond
+        u32x2 ph, pl;
+        split_hilo4(pv, ph, pl);
+        const int srcl = cn >= 4 && cn < 8 ? lane - 4 : lane;
+        const uint32_t l0 = __shfl(pl.x, srcl), l1 = __shfl(pl.y, srcl);
+        const u32x2 pb = cn < 4 ? ph : (cn < 8 ? u32x2{l0, l1} : u32x2{0u, 0u});
+        // O^T += V^T P: the A operand of block b is V[4 g4 .. + 3][16 b + cn]
+        const uint32_t va = slot + KBYTES + (uint32_t)((4 * g4) / PPI) * 1056u +
+                            (uint32_t)((4 * g4) % PPI) * (2 * DH) + (uint32_t)cn * 2u;
+#pragma unroll
+        for (int b = 0; b < DB; b += 2) {
+          u32x2 x0, x1;
+          lds_read_vt2<2 * DH>(va + b * 32, x0, x1);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, x0),
+                                                             __builtin_bit_cast(bf16x4, pb), acc[b], 0, 0, 0);
+          acc[b + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, x1),
+                                                                 __builtin_bit_cast(bf16x4, pb), acc[b + 1], 0, 0,
+                                                                 0);
+        }
       }
+    }
+    // O[h][d] = column h + column h + 4; this wave's sums per head
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[b][e] += __shfl_xor(acc[b][e], 4);
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+  }
+  // every wave's V ring is drained before the merge area over it is written
+  vm_drain_known();
+  lds_barrier();
+  if (sched) {
+    for (int h = 0; h < G; ++h) {
+      for (int i = lane; i < DH; i += 64) mo[(MPK_NW * ATT_MAXG + h) * 128 + i] = owner ? kv[DH + i] : 0.f;
+      if (lane == 0) {
+        mm[MPK_NW * ATT_MAXG + h] = owner ? spv[h] : -INFINITY;
+        ml[MPK_NW * ATT_MAXG + h] = owner ? 1.f : 0.f;
+      }
+    }
+  } else if (cn < G) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+      *reinterpret_cast<float4*>(mo + (wave * ATT_MAXG + cn) * 128 + 16 * b + 4 * g4) =
+          float4{acc[b][0], acc[b][1], acc[b][2], acc[b][3]};
+    if (g4 == 0) {
+      mm[wave * ATT_MAXG + cn] = m;
+      ml[wave * ATT_MAXG + cn] = l;
     }
   }
   __syncthreads();
-  // ---- merge the position groups: this split's (m, l, acc) per head ----
-  // wave h (< G) turns the groups' maxima into per-group weights once
-  float* hML = reinterpret_cast<float*>(smem + LDS_RED);  // [G][2]: M, L per head
-  if (!sched && wave < G) {
-    const int h = wave;
-    float mg = -INFINITY, lg = 0.f;
+  // ---- merge the nine partials (eight waves, position p) per head ----
+  const int stride = DH + 2;
+  const int64_t o_base = (int64_t)r * D.nq * DH + (int64_t)j * G * DH;
+  for (int idx = tid; idx < G * DH && !sched; idx += MPK_NW * 64) {
+    const int h = idx / DH, i = idx - h * DH;
     float M = -INFINITY;
-    for (int g0 = 0; g0 < NG; g0 += 64) {
-      const int g = g0 + lane;
-      M = fmaxf(M, g < NG ? wm[g * ATT_MAXG + h] : -INFINITY);
+    for (int w = 0; w <= MPK_NW; ++w) M = fmaxf(M, mm[w * ATT_MAXG + h]);
+    float A = 0.f, L = 0.f;
+    for (int w = 0; w <= MPK_NW; ++w) {
+      const float mw = mm[w * ATT_MAXG + h];
+      const float cw = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      A = fmaf(mo[(w * ATT_MAXG + h) * 128 + i], cw, A);
+      L = fmaf(ml[w * ATT_MAXG + h], cw, L);
     }
-    M = wave_max(M);
-    float L = 0.f;
-    for (int g0 = 0; g0 < NG; g0 += 64) {
-      const int g = g0 + lane;
-      if (g < NG) {
-        mg = wm[g * ATT_MAXG + h];
-        lg = wl[g * ATT_MAXG + h];
-      }
-      const float cg = g < NG && mg != -INFINITY ? exp2f(mg - M) : 0.f;
-      L += lg * cg;
-      if (g < NG) wm[g * ATT_MAXG + h] = cg;  // the group's weight replaces its reference m
-    }
-    L = wave_sum(L);
-    if (lane == 0) hML[2 * h] = M, hML[2 * h + 1] = L;
-  }
-  __syncthreads();
-  const int stride = d + 2;
-  const int64_t o_base = (int64_t)r * D.nq * d + (int64_t)j * G * d;
-  for (int idx = tid; idx < G * d && !sched; idx += MPK_NW * 64) {
-    const int h = idx / d, i = idx - h * d;
-    float A = 0.f;
-    for (int g = 0; g < NG; ++g) A = fmaf(wacc[(g * ATT_MAXG + h) * d + i], wm[g * ATT_MAXG + h], A);
-    const float M = hML[2 * h], L = hML[2 * h + 1];
     if (na == 1) {
       put_out(D, o_base + idx, A / L, st);  // the whole context in one split
     } else {
@@ -1780,8 +1835,8 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   // owner: merge the other splits' partials (gathered in chunks) into its own,
   // in split order: o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M)
   const int idx = tid;
-  const bool mine_o = !sched && idx < G * d;
-  const int h = mine_o ? idx / d : 0, i = mine_o ? idx - h * d : 0;
+  const bool mine_o = !sched && idx < G * DH;
+  const int h = mine_o ? idx / DH : 0, i = mine_o ? idx - h * DH : 0;
   float M = mine_o ? outs[h * stride] : 0.f;
   float L = mine_o ? outs[h * stride + 1] : 0.f;
   float O = mine_o ? outs[h * stride + 2 + i] : 0.f;
@@ -1838,7 +1893,6 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 // With WK > 1 the waves' partial sums meet in LDS and are added in wave
 // order: the result does not depend on timing (bitwise reproducible).
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #define G8_PASS 4096               // columns of x staged per pass
 #define G8_KSTEPS (G8_PASS / 32)   // MFMA k-steps per pass
 #define G8_ITEMS (8 * G8_PASS / 8) // (request, 8-column group) staging items per pass
@@ -1847,20 +1901,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 static_assert(G8_NI % G8_IG == 0, "staging rounds hold whole item groups");
 static_assert(MPK_THREADS % 8 == 0, "a thread's staging items share one request");
 static_assert(LDS_X + G8_KSTEPS * 1024 <= 156 * 1024, "a staged pass must fit the LDS");
-
-// hi and lo bf16 parts (round to nearest even) of 8 values, 16 bytes each
-DEV void split_hilo8(const float (&v)[8], u32x4& hi, u32x4& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint16_t h0 = f2bf(v[2 * e]), h1 = f2bf(v[2 * e + 1]);
-    const uint16_t l0 = f2bf(v[2 * e] - bf16f(h0)), l1 = f2bf(v[2 * e + 1] - bf16f(h1));
-    h[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-  }
-  hi = u32x4{h[0], h[1], h[2], h[3]};
-  lo = u32x4{l[0], l[1], l[2], l[3]};
-}
 
 // Weight row of virtual row vr (rows of W0, W1, W2 in order; gate/up pairs
 // interleaved).
@@ -2209,7 +2249,9 @@ DEV int gemv8_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
 template <int NB>
 DEV int run_task(const mpk_kparams& P, ctask& T, int task_id, int s, char* smem, int tid, bool sched, int next) {
   cop& D = ops_of(P)[T.op];
-  if (T.kind == MPK_TK_ATTN) return attn_task(P, T, D, smem, tid, sched, s, task_id);
+  if (T.kind == MPK_TK_ATTN)
+    return D.d == 128 ? attn_task<128>(P, T, D, smem, tid, sched, s, task_id)
+                      : attn_task<64>(P, T, D, smem, tid, sched, s, task_id);
   if (T.kind == MPK_TK_ARGMAX) return argmax_task<NB>(P, D, smem, tid, s, task_id);
   if constexpr (NB == 8) {
     (void)next;
@@ -2578,7 +2620,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
       D.yll = PL(o.out[0]);
       const int G = D.nq / D.nkv;
       if (G > ATT_MAXG) return mpk_fail(MPK_ERR_SHAPE, "more than 4 query heads per kv head");
-      if (D.d > 128) return mpk_fail(MPK_ERR_SHAPE, "head_dim above 128");
+      if (D.d != 64 && D.d != 128) return mpk_fail(MPK_ERR_SHAPE, "head_dim must be 64 or 128");
       if ((rc = salloc(x.get(), &D.pll, (size_t)B * D.nkv * D.nsplit * G * (D.d + 2) * 8))) return rc;
       continue;
     }

@@ -118,7 +118,11 @@ def boundary_gaps(records: np.ndarray, tasks, num_tasks: int, chain: Sequence[in
       a CU already waits at b while a is still running);
     - "last_start":  last start of b minus the last end of a;
     - "span_b":      last end of b minus the last end of a (the boundary plus
-      b's own duration: the critical path of the chain runs through these).
+      b's own duration: the critical path of the chain runs through these);
+    - "last_ready":  last time a task of b had all its inputs, minus the last
+      end of a (how long b's inputs took to arrive);
+    - "work_med", "work_max": median and maximum over b's tasks of end minus
+      ready (a task's own work once its inputs are there).
 
     Arrays have shape [iterations, len(chain) - 1]; operators whose tasks
     did not run in an iteration (e.g. attention splits beyond the context)
@@ -129,7 +133,8 @@ def boundary_gaps(records: np.ndarray, tasks, num_tasks: int, chain: Sequence[in
         by_op.setdefault(tasks[i].op, []).append(i)
     us = ns_per_tick / 1000.0
     n_it, n_b = recs.shape[0], len(chain) - 1
-    out = {k: np.full((n_it, n_b), np.nan) for k in ("first_start", "last_start", "span_b")}
+    out = {k: np.full((n_it, n_b), np.nan)
+           for k in ("first_start", "last_start", "span_b", "last_ready", "work_med", "work_max")}
     for s in range(n_it):
         r = recs[s]
         for k, (a, b) in enumerate(zip(chain, chain[1:])):
@@ -143,6 +148,12 @@ def boundary_gaps(records: np.ndarray, tasks, num_tasks: int, chain: Sequence[in
             out["first_start"][s, k] = (int(rb["t_start"].min()) - end_a) * us
             out["last_start"][s, k] = (int(rb["t_start"].max()) - end_a) * us
             out["span_b"][s, k] = (int(rb["t_end"].max()) - end_a) * us
+            ready = rb[rb["t_ready"] != np.iinfo(np.uint64).max]
+            if len(ready):
+                out["last_ready"][s, k] = (int(ready["t_ready"].max()) - end_a) * us
+                work = (ready["t_end"].astype(np.int64) - ready["t_ready"].astype(np.int64)) * us
+                out["work_med"][s, k] = float(np.median(work))
+                out["work_max"][s, k] = float(work.max())
     return out
 
 
@@ -222,13 +233,15 @@ def main(argv=None) -> int:
     gaps = boundary_gaps(tr, tasks, NT, chain)
     print("%d task events over %d iterations (%.3f ms/iteration traced) -> %s"
           % (n, args.iters, wall / args.iters, args.out))
-    print("%-10s %12s %12s %12s" % ("operator", "first_start", "last_start", "span"))
+    cols = ("first_start", "last_start", "span_b", "last_ready", "work_med", "work_max")
+    print("%-10s" % "operator" + "".join("%13s" % c for c in ("first_start", "last_start", "span", "last_ready",
+                                                             "work_med", "work_max")))
     per = {}
     for k, b in enumerate(chain[1:]):
         per.setdefault(labels[b], []).append(k)
     for name, ks in per.items():
-        med = [float(np.nanmedian(gaps[f][:, ks])) for f in ("first_start", "last_start", "span_b")]
-        print("%-10s %10.2f us %10.2f us %10.2f us" % (name, *med))
+        med = [float(np.nanmedian(gaps[f][:, ks])) for f in cols]
+        print("%-10s" % name + "".join("%10.2f us" % v for v in med))
     print("boundary span histogram (us):", gap_histogram(gaps["span_b"]))
     sess.close()
     return 0

@@ -24,7 +24,7 @@ def test_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
     src = f.read_text()
     f.write_text("// a new comment line\n" + src.replace("\n", "\n  ", 3) + "\n/* trailing\n block */\n")
     assert bench.code_digest() == base
-    f.write_text(src.replace("#define ATT_ROUNDS 2", "#define ATT_ROUNDS 3", 1))
+    f.write_text(src.replace("#define ATT_MAXG 4", "#define ATT_MAXG 8", 1))
     assert bench.code_digest() != base
 
 

@@ -193,6 +193,12 @@ def test_shape_and_graph_errors_are_reported():
     with pytest.raises(mpk.MPKError) as e:
         mpk.mpk_build_graph(mcfg, lcfg, spec.c_tensors(), ops, meta)
     assert e.value.code in (mpk.MPK_ERR_GRAPH,)
+    # a head size the attention kernel is not built for
+    m96 = mpk.model_cfg(shape, 1, 64)
+    m96.head_dim = 96
+    with pytest.raises(mpk.MPKError) as e:
+        mpk.mpk_build_graph(m96, lcfg, spec.c_tensors(), spec.ops, meta)
+    assert e.value.code == mpk.MPK_ERR_SHAPE and "head_dim" in mpk.mpk_last_error()
     # too many tiles for the rows
     ops = list(spec.ops)
     ops[1].num_tiles = 256
@@ -231,7 +237,7 @@ def test_single_layer_graph_without_embedding_or_lm_head():
 def test_more_attention_groups_than_workers_is_a_shape_error():
     # B x n_kv attention groups need one worker each at least (an owner split
     # must never queue behind another group's split)
-    sh = synth.ModelShape(1, 256, 16, 16, 16, 256, 256)
+    sh = synth.ModelShape(1, 1024, 16, 16, 64, 256, 256)
     with pytest.raises(mpk.MPKError) as e:
         build(sh, num_cus=8)
     assert e.value.code == mpk.MPK_ERR_SHAPE and "attention" in mpk.mpk_last_error()
