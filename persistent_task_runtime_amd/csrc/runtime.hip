@@ -527,6 +527,49 @@ DEV int gather_ll(const mpk_kparams& P, const uint64_t* src, int n, uint32_t* ds
   return *lvi(smem, LDS_CTL) ? -1 : 0;
 }
 
+// Stamped words src[0, n) (n even, src 16 bytes aligned) into LDS at byte
+// address dst, 8 bytes per word, by global->LDS DMA (device scope): 1 KB
+// chunks (whole chunks are written: ceil(8 n / 1 KB) KB must be free at dst),
+// chunk k taken by wavefront k % 9.  Each wavefront checks the stamps of its
+// own chunks and fetches the stale ones again, so all chunks are in flight at
+// once and nothing is held in registers.  Every thread of the workgroup
+// calls it; returns -1 on stop.
+DEV int gather_ll_dma(const mpk_kparams& P, const uint64_t* src, int n, uint32_t dst, uint32_t st, Waiter& Wt,
+                      int s, int task_id, char* smem, int tid) {
+  constexpr int NWAVES = MPK_THREADS / 64, MAXC = 16;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int nch = (n * 8 + 1023) >> 10, npiece = n >> 1;
+  uint32_t need = 0;  // bit k: chunk wave + 9 k is still to fetch
+#pragma unroll
+  for (int k = 0; k < MAXC; ++k)
+    if (wave + NWAVES * k < nch) need |= 1u << k;
+  while (need) {
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k)
+      if ((need >> k) & 1u) {
+        const int pc = min((wave + NWAVES * k) * 64 + lane, npiece - 1);  // lanes past the end repeat the last piece
+        __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(src + 2 * pc),
+                                         lds_ptr(dst + (uint32_t)(wave + NWAVES * k) * 1024u), 16, 0,
+                                         16 /* sc1: device scope */);
+      }
+    vm_drain_known();
+    uint32_t stale = 0;
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k)
+      if ((need >> k) & 1u) {
+        const int piece = (wave + NWAVES * k) * 64 + lane;
+        const u32x4 v = lds_read_u32x4(dst + (uint32_t)(wave + NWAVES * k) * 1024u + lane * 16u);
+        if (__ballot(piece < npiece && (v.y != st || v.w != st)) != 0) stale |= 1u << k;
+      }
+    need = stale;
+    if (!need) break;
+    if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  lds_barrier();
+  return *lvi(smem, LDS_CTL) ? -1 : 0;
+}
+
 // ---------------------------------------------------------------------------
 // weight units (GEMV and LM-head tiles)
 //   A tile covers virtual rows [row0, row0 + nrows).  Rows go to the worker
@@ -1433,8 +1476,12 @@ constexpr int at_slot(int dh) { return dh * 32 + (dh / 32) * 1056; }
 constexpr int at_ring(int dh) { return dh == 128 ? 2 : 3; }
 static_assert(AT_VRING + MPK_NW * at_ring(128) * at_slot(128) <= 156 * 1024, "attention ring exceeds the LDS");
 static_assert(AT_VRING + MPK_NW * at_ring(64) * at_slot(64) <= 156 * 1024, "attention ring exceeds the LDS");
-static_assert(AT_VRING + (9 * ATT_MAXG * 128 + 2 * 9 * ATT_MAXG) * 4 + 64 * 1024 <= 156 * 1024,
-              "attention merge area and partial gather exceed the LDS");
+// the merge area ([9][G][128] partial sums, [9][G] maxima, [9][G] sums) over
+// the ring, then the split partials gathered by DMA (whole KB chunks, at most
+// 9 x 16 of them)
+#define AT_GATH (AT_VRING + (9 * ATT_MAXG * 128 + 2 * 9 * ATT_MAXG) * 4)
+static_assert(AT_GATH % 16 == 0 && AT_GATH + 64 * 1024 <= 156 * 1024 && (156 * 1024 - AT_GATH) / 1024 <= 9 * 16,
+              "attention merge area and partial gather do not fit the LDS");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -1528,7 +1575,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   float* mo = reinterpret_cast<float*>(smem + AT_VRING);  // merge: [9][G][DH] (over the ring)
   float* mm = mo + 9 * ATT_MAXG * 128;                    // [9][G] maxima
   float* ml = mm + 9 * ATT_MAXG;                          // [9][G] sums
-  uint32_t* gath = reinterpret_cast<uint32_t*>(ml + 9 * ATT_MAXG);  // gathered split partials
+  uint32_t* gath = reinterpret_cast<uint32_t*>(smem + AT_GATH);        // gathered split partials
   float* outs = reinterpret_cast<float*>(smem + LDS_OUT);               // partial, then o
   uint32_t* kvrow = reinterpret_cast<uint32_t*>(smem + LDS_OUT) + 640;  // bf16 K row, then V row
   const int qkv_w = (D.nq + 2 * D.nkv) * DH;
@@ -1537,14 +1584,17 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   // base-2 scores: log2(e) / sqrt(d) is applied to q once, when it is staged
   const float scale = 1.4426950408889634f / sqrtf((float)DH);
 
-  // ---- the fold's steps: wave w takes steps w, w + 8, ... of 16 positions ----
+  // ---- the fold's steps of 16 positions: wave w starts with steps w, w + 8,
+  // ... (AT_R - 1 of them), then claims the next free step from a workgroup
+  // counter each time it frees a ring slot (waves whose data arrives sooner
+  // take more steps) ----
   const int nst = (hi - lo + 15) >> 4;
-  const int nmine = nst > wave ? (nst - wave + MPK_NW - 1) / MPK_NW : 0;
+  if (tid == 0) *lvi(smem, LDS_CLAIM) = MPK_NW * (AT_R - 1);  // read only after the barriers below
   const uint32_t ring = lb + AT_VRING + (uint32_t)wave * (AT_R * SLOT);
-  // step i of this wave: positions t0 .. t0 + 15, t0 = lo + 16 (wave + 8 i),
-  // into ring slot `slot` (K, then V)
-  auto issue = [&](int i, uint32_t slot) {
-    const int t0 = lo + 16 * (wave + MPK_NW * i);
+  // step k: positions t0 .. t0 + 15, t0 = lo + 16 k, into ring slot `slot`
+  // (K, then V)
+  auto issue = [&](int k, uint32_t slot) {
+    const int t0 = lo + 16 * k;
     const int tk = t0 + cn;
     const int rk = tk < hi && tk != p ? tk : lo;
 #pragma unroll
@@ -1566,12 +1616,14 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   // (Whatever earlier tasks left in flight is waited for first: the
   // compiler's waits would otherwise drain these loads as well, at once.)
   vm_drain_known();
-  int pre = 0;
-  if (!sched && uni(*lvi(smem, LDS_SYNCED)) != 0) {
+  int sq[AT_R];  // the step in each ring slot, -1: none (steps are taken in slot order)
+#pragma unroll
+  for (int i = 0; i < AT_R; ++i) sq[i] = i < AT_R - 1 && wave + MPK_NW * i < nst ? wave + MPK_NW * i : -1;
+  const bool early = !sched && uni(*lvi(smem, LDS_SYNCED)) != 0;
+  if (early) {
 #pragma unroll
     for (int i = 0; i < AT_R - 1; ++i)
-      if (i < nmine) issue(i, ring + i * SLOT);
-    pre = min(AT_R - 1, nmine);
+      if (sq[i] >= 0) issue(sq[i], ring + i * SLOT);
   }
 
   // ---- q / k / v words of the group: wave hh < G + 2 takes one head vector ----
@@ -1691,24 +1743,37 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
         qb[kk] = !has ? u32x4{0u, 0u, 0u, 0u} : (cn < 4 ? hi8 : lo8);
       }
     }
-    // the rest of the first AT_R - 1 steps
+    if (!early) {
 #pragma unroll
-    for (int i = 0; i < AT_R - 1; ++i)
-      if (i >= pre && i < nmine) issue(i, ring + i * SLOT);
-    for (int i0 = 0; i0 < nmine; i0 += AT_R) {
+      for (int i = 0; i < AT_R - 1; ++i)
+        if (sq[i] >= 0) issue(sq[i], ring + i * SLOT);
+    }
+    for (bool more = sq[0] >= 0; more;) {
 #pragma unroll
       for (int sl = 0; sl < AT_R; ++sl) {
-        const int i = i0 + sl;
-        if (i >= nmine) break;
+        if (sq[sl] < 0) {
+          more = false;
+          break;
+        }
+        // the slot freed by the previous step takes the next free step
+        // (none once a claim has come back empty: the last slot filled is -1)
         const int nx = (sl + AT_R - 1) % AT_R;
-        if (i + AT_R - 1 < nmine) issue(i + AT_R - 1, ring + nx * SLOT);
-        // step i has landed (loads complete in issue order: only the later
-        // steps' operations may still be in flight)
-        const int later = min(AT_R - 1, nmine - 1 - i);
+        int k = -1;
+        if (sq[(sl + AT_R - 2) % AT_R] >= 0) {
+          k = claim_unit(smem, lane);
+          if (k >= nst) k = -1;
+        }
+        sq[nx] = k;
+        if (k >= 0) issue(k, ring + nx * SLOT);
+        // this step has landed (loads complete in issue order: only the
+        // later steps' operations may still be in flight)
+        int later = 0;
+#pragma unroll
+        for (int q = 1; q < AT_R; ++q) later += sq[(sl + q) % AT_R] >= 0;
         if (later >= 2) vm_wait_known<2 * OPS>();
         else if (later == 1) vm_wait_known<OPS>();
         else vm_wait_known<0>();
-        const int t0 = lo + 16 * (wave + MPK_NW * i);
+        const int t0 = lo + 16 * sq[sl];
         // scores of the step's 16 positions: lane (g4, cn) holds positions
         // t0 + 4 g4 + e of column cn; hi + lo columns
         const uint32_t slot = ring + sl * SLOT;
@@ -1832,36 +1897,55 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     for (int i = tid; i < G * stride; i += MPK_THREADS) st_ll(pgrp + (int64_t)c * G * stride + i, outs[i], st);
     return 0;
   }
-  // owner: merge the other splits' partials (gathered in chunks) into its own,
-  // in split order: o = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M)
+  // owner: merge the other splits' partials into its own, as many per round
+  // as the LDS holds (gathered by DMA): o = sum_c acc_c 2^(m_c - M) /
+  // sum_c l_c 2^(m_c - M), with M the largest m_c; a round's weights
+  // 2^(m_c - M) are computed once per head and partial
   const int idx = tid;
   const bool mine_o = !sched && idx < G * DH;
   const int h = mine_o ? idx / DH : 0, i = mine_o ? idx - h * DH : 0;
-  float M = mine_o ? outs[h * stride] : 0.f;
   float L = mine_o ? outs[h * stride + 1] : 0.f;
   float O = mine_o ? outs[h * stride + 2 + i] : 0.f;
-  const int chunk = (Lay<1>::TOTAL - (int)((char*)gath - smem)) / 4 / (G * stride);
+  float* mrun = mm;  // [G] running reference per head (the merge area is free now)
+  float* wt = mo;    // [chunk + 1][G]: the partials' weights, then the running sums' rescale
+  if (tid < G) mrun[tid] = outs[tid * stride];  // (read after the gather's barrier)
+  const float* gf = reinterpret_cast<const float*>(gath);  // word w's payload at gf[2 w]
+  const int avail = (Lay<1>::TOTAL - (int)((char*)gath - smem)) & ~1023;
+  const int chunk = avail / (G * stride * 8);
   for (int c0 = 0; c0 < na - 1; c0 += chunk) {
     const int nc = min(chunk, na - 1 - c0);
-    const int rc =
-        gather_ll<16>(P, pgrp + (int64_t)c0 * G * stride, nc * G * stride, gath, st, Wt, s, task_id, smem, tid);
+    const int rc = gather_ll_dma(P, pgrp + (int64_t)c0 * G * stride, nc * G * stride, lds_addr(gath), st, Wt, s,
+                                 task_id, smem, tid);
     if (rc) return rc;
-    if (mine_o) {
-      for (int cc = 0; cc < nc; ++cc) {
-        const float mc = __uint_as_float(gath[(cc * G + h) * stride]);
-        const float lc = __uint_as_float(gath[(cc * G + h) * stride + 1]);
-        const float ac = __uint_as_float(gath[(cc * G + h) * stride + 2 + i]);
-        if (lc > 0.f) {
-          const float Mn = fmaxf(M, mc);
-          const float ca = M == -INFINITY ? 0.f : exp2f(M - Mn);
-          const float cb = exp2f(mc - Mn);
-          L = L * ca + lc * cb;
-          O = O * ca + ac * cb;
-          M = Mn;
-        }
+    if (!sched && wave < G) {
+      // worker wave hh: head hh, one lane per partial
+      const int hh = wave;
+      const float Mo = mrun[hh];
+      float Mn = Mo;
+      for (int cc = lane; cc < nc; cc += 64)
+        if (gf[2 * ((cc * G + hh) * stride + 1)] > 0.f) Mn = fmaxf(Mn, gf[2 * (cc * G + hh) * stride]);
+      Mn = wave_max(Mn);
+      for (int cc = lane; cc < nc; cc += 64) {
+        const float mc = gf[2 * (cc * G + hh) * stride], lc = gf[2 * ((cc * G + hh) * stride + 1)];
+        wt[cc * G + hh] = lc > 0.f ? exp2f(mc - Mn) : 0.f;
+      }
+      if (lane == 0) {
+        wt[nc * G + hh] = exp2f(Mo - Mn);
+        mrun[hh] = Mn;
       }
     }
-    __syncthreads();  // the gather area is reused by the next chunk
+    __syncthreads();
+    if (mine_o) {
+      const float ca = wt[nc * G + h];
+      L *= ca;
+      O *= ca;
+      for (int cc = 0; cc < nc; ++cc) {
+        const float w = wt[cc * G + h];
+        L = fmaf(gf[2 * ((cc * G + h) * stride + 1)], w, L);
+        O = fmaf(gf[2 * ((cc * G + h) * stride + 2 + i)], w, O);
+      }
+    }
+    __syncthreads();  // the gather area and the weights are reused by the next round
   }
   if (mine_o) put_out(D, o_base + idx, O / L, st);
   return 0;
