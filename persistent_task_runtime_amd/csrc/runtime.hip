@@ -238,15 +238,14 @@ DEV void st_devi(int32_t* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED,
 DEV void st_devu(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 16 bytes written earlier in the launch by another CU, possibly on another
-// XCD (the K/V rows of earlier positions): device-scope loads, since a plain
-// load may hit a line of this XCD's L2 that predates the write.
-DEV u32x4 ld_dev16(const void* p) {
-  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<void*>(p));
-  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
-}
+// Cache-policy bits of a load (global->LDS DMA, buffer load): sc1 makes it
+// device scope (coherent with device-scope stores of other CUs on any XCD),
+// nt marks data read once.  Streams of data read once reach a higher HBM
+// rate with nt (about 6.8 against 6.0 TB/s in a 256-CU streaming test of
+// 8 KB steps), also together with sc1.
+#define CPOL_NT 2
+#define CPOL_SC1 16
+
 // all vector-memory operations of this wavefront complete (the scheduler
 // wavefront issues no weight loads, so this waits only for its own stores)
 DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -550,7 +549,7 @@ DEV int gather_ll_dma(const mpk_kparams& P, const uint64_t* src, int n, uint32_t
         const int pc = min((wave + NWAVES * k) * 64 + lane, npiece - 1);  // lanes past the end repeat the last piece
         __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(src + 2 * pc),
                                          lds_ptr(dst + (uint32_t)(wave + NWAVES * k) * 1024u), 16, 0,
-                                         16 /* sc1: device scope */);
+                                         CPOL_SC1);
       }
     vm_drain_known();
     uint32_t stale = 0;
@@ -831,7 +830,7 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       for (uint32_t m = need; m; m &= m - 1) {
         const int c = wave + MPK_NW * __builtin_ctz(m);
         __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.xll + c * 128 + lane * 2), lds_ptr(lb + land + c * 1024),
-                                         16, 0, 16 /* sc1: device scope */);
+                                         16, 0, CPOL_SC1);
       }
       uint64_t wr = 0;
       if (need_r) wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
@@ -1258,7 +1257,7 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
 #pragma unroll
             for (int u = 0; u < MPK_RING; ++u)
               __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(wp + u * 64),
-                                               lds_ptr(pf + (rr * MPK_RING + u) * 1024), 16, 0, 0);
+                                               lds_ptr(pf + (rr * MPK_RING + u) * 1024), 16, 0, CPOL_NT);
           }
         }
       }
@@ -1600,13 +1599,13 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
       __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(kc + (int64_t)rk * DH + 32 * kk + 8 * g4),
-                                       lds_ptr(slot + kk * 1024), 16, 0, 16 /* sc1: device scope */);
+                                       lds_ptr(slot + kk * 1024), 16, 0, CPOL_SC1 | CPOL_NT);
 #pragma unroll
     for (int c4 = 0; c4 < 16 / PPI; ++c4) {
       const int tv = t0 + c4 * PPI + lane / LPR;
       const int rv = tv < hi && tv != p ? tv : lo;
       __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(vc + (int64_t)rv * DH + 8 * (lane % LPR)),
-                                       lds_ptr(slot + KBYTES + c4 * 1056), 16, 0, 16 /* sc1: device scope */);
+                                       lds_ptr(slot + KBYTES + c4 * 1056), 16, 0, CPOL_SC1 | CPOL_NT);
     }
   };
   // The cache rows below p were written by earlier iterations, all ended once
