@@ -130,6 +130,26 @@ class Session:
         else:
             self.exe.run(n_iter, s.cuda_stream)
 
+    def replace_request(self, r: int, prompt) -> None:
+        """Slot r takes a new request between runs (the request that held it
+        leaves): its tokens row becomes the new prompt (-1 past it), its step
+        0 and its prompt length len(prompt).  The other slots go on where
+        they were.  The slot's K/V cache is not cleared: the new request
+        reads a position only after it has written it.  Ordered with the runs
+        on the current stream."""
+        import torch
+
+        prompt = np.asarray(prompt, dtype=np.int32)
+        W = self.tokens.shape[1]
+        if not 1 <= prompt.size < W:
+            raise ValueError("prompt of %d ids does not fit a tokens row of %d" % (prompt.size, W))
+        row = np.full(W, -1, np.int32)
+        row[:prompt.size] = prompt
+        dev = self.tokens.device
+        self.tokens[r].copy_(torch.from_numpy(row).to(dev))
+        self.step[r:r + 1].fill_(0)
+        self.prompt_len[r:r + 1].fill_(int(prompt.size))
+
     def check_status(self):
         code, it, task = self.exe.status()
         if code != 0:

@@ -100,6 +100,66 @@ def test_batch8_persistent_equals_per_op_and_itself(narrow):
         x["session"].close()
 
 
+def test_requests_leave_and_join_between_launches(narrow):
+    """Dynamic batch: after a first launch two requests leave and new ones
+    (new prompts, step 0) take their slots for the second launch while the
+    other six go on.  Every request's whole history - the leavers' first
+    launch, the joiners' second, the stayers' both - is compared with the
+    oracle run on that request alone, teacher-forced on its own tokens."""
+    import torch
+    from persistent_task_runtime_amd import runner
+
+    w, weights, model = narrow
+    n1, n2 = 6, 12
+    S = w.tokens_width  # K/V capacity for the stayers' n1 + n2 positions
+    sess = runner.Session(w, model, logits_iters=max(n1, n2), max_seq=S)
+    sess.run(n1)
+    torch.cuda.synchronize()
+    sess.check_status()
+    lg1 = sess.logits.cpu().numpy()[:n1].copy()
+    tok1 = sess.tokens.cpu().numpy().copy()
+    step1 = sess.step.cpu().numpy().copy()
+    leave = (2, 5)
+    new_prompts = {r: synth.uniform_int(0, "join.prompt%d" % r, 3 + 2 * k, 0, w.shape.vocab - 1)
+                   for k, r in enumerate(leave)}
+    for r, pr in new_prompts.items():
+        sess.replace_request(r, pr)
+    sess.run(n2)
+    torch.cuda.synchronize()
+    sess.check_status()
+    lg2 = sess.logits.cpu().numpy()[:n2].copy()
+    tok2 = sess.tokens.cpu().numpy().copy()
+    step2 = sess.step.cpu().numpy().copy()
+    sess.close()
+    log("join/leave: slots %s replaced after %d iterations, then %d more" % (list(leave), n1, n2))
+    om = oracle.Model(w.shape, weights)
+    prompts0 = synth.make_tokens(w)
+
+    def check(r, prompt_row, plen, s0, n, glog, gtok, gstep, what):
+        ol, oam, omg = parity.teacher_forced(om, w.shape, gtok[None], np.array([s0], np.int32), n, S)
+        rep = parity.compare(prompt_row[None], np.array([plen], np.int32), np.array([s0], np.int32), n,
+                             glog[:, None], gtok[None], np.array([gstep], np.int32), ol, oam, omg)
+        log("  request %d (%s): %s" % (r, what, rep))
+        assert rep.compared == n
+        return rep
+
+    checked = 0
+    for r in range(w.batch):
+        if r in leave:
+            check(r, prompts0[r], int(w.prompt_len[r]), int(w.step0[r]), n1, lg1[:, r], tok1[r], step1[r], "left")
+            pr = new_prompts[r]
+            row = np.full(prompts0.shape[1], -1, np.int32)
+            row[:pr.size] = pr
+            rep = check(r, row, pr.size, 0, n2, lg2[:, r], tok2[r], step2[r], "joined")
+            assert step2[r] == n2
+        else:
+            glog = np.concatenate([lg1[:, r], lg2[:, r]])
+            rep = check(r, prompts0[r], int(w.prompt_len[r]), int(w.step0[r]), n1 + n2, glog, tok2[r], step2[r],
+                        "stayed")
+        checked += rep.checked
+    assert checked >= 80
+
+
 @pytest.fixture(scope="module")
 def full_weights_b8():
     t0 = time.time()
