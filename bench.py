@@ -153,6 +153,8 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-op", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prompt-ingestion comparison (one position per iteration vs chunks of 8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for profiles)")
     ap.add_argument("--workload", choices=("qwen3_8b", "long", "b8"), default="qwen3_8b",
@@ -161,6 +163,55 @@ def parse_args(argv=None):
                          "b8: batch 8, prompt lengths uniform in [16, 512] ingested per request, "
                          "then 256 lockstep greedy iterations (MFMA linear tasks)")
     return ap.parse_args(argv)
+
+
+def bench_prefill(sess, n_prompt, restart, stream, rows=8):
+    """Prompt ingestion (positions 0 .. P-2, untimed in the decode figure):
+    one position per persistent iteration, against chunks of `rows`
+    positions per iteration (rows_per_request: the batch-8 kernels) followed
+    by the remaining positions one at a time.  Each is warmed up once, then
+    timed with HIP events around its launches."""
+    import torch
+    from persistent_task_runtime_amd import runner
+
+    pc = runner.PromptChunks(sess, 0, rows)
+    restart()
+    nch = pc.chunks_left()
+    rest = n_prompt - rows * nch
+
+    def one_by_one():
+        sess.run(n_prompt)
+
+    def chunked():
+        pc.run(nch)
+        if rest:
+            sess.run(rest)
+
+    out = {}
+    for name, fn in (("one_per_iteration", one_by_one), ("chunked", chunked)):
+        restart()
+        fn()
+        torch.cuda.synchronize()
+        restart()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        sess.check_status()
+        code = pc.exe.status()[0]
+        assert code == 0, "prompt chunks: device status %d" % code
+        assert int(sess.step.cpu()[0]) == n_prompt
+        out[name] = a.elapsed_time(b)
+    pc.close()
+    res = {"positions": n_prompt, "rows_per_iteration": rows, "chunk_iterations": nch,
+           "decode_iterations": rest, "ms_chunked": round(out["chunked"], 3),
+           "ms_one_per_iteration": round(out["one_per_iteration"], 3),
+           "speedup": round(out["one_per_iteration"] / out["chunked"], 3)}
+    log("prompt ingestion (%d positions): %.3f ms one per iteration, %.3f ms in %d chunks of %d + %d "
+        "iterations (%.2fx)" % (n_prompt, out["one_per_iteration"], out["chunked"], nch, rows, rest,
+                                res["speedup"]))
+    return res
 
 
 def main():
@@ -279,6 +330,9 @@ def main():
         sess.check_status()
         per_op = e0.elapsed_time(e1) / Kp
         log("one launch per operator: %.4f ms/token over %d steps" % (per_op, Kp))
+    prefill = None
+    if not args.no_prefill:
+        prefill = bench_prefill(sess, n_prompt, restart, stream)
     sess.close()
     del sess, model
     torch.cuda.synchronize()
@@ -328,6 +382,7 @@ def main():
         "frac_of_bound": round(bound_ms / ms_tok, 4),
         "per_op_ms_per_token": round(per_op, 5) if per_op else None,
         "speedup_vs_per_op": round(per_op / ms_tok, 3) if per_op else None,
+        "prompt_ingestion": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

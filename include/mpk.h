@@ -111,7 +111,8 @@ typedef struct {
 } mpk_tensor;
 
 /* Operator kinds and their operands (tensor ids into the table; -1 = none).
- * B = num_requests, K = input width, N = output rows.
+ * B = rows = num_requests x rows_per_request (see mpk_meta), K = input width,
+ * N = output rows.
  *
  * MPK_OP_EMBED            in  {E[V,H] bf16}
  *                         out {x[B,H] f32}: x[r] = E[tokens[r][step[r]]].  Never
@@ -120,7 +121,7 @@ typedef struct {
  *                         out {y[B,N0+N1+N2] f32}: y = [W0;W1;W2] . RMSNorm(x; gain)
  *                         (P1 "The API"; P5 "Grenzen der README-Aussagen").
  * MPK_OP_ATTENTION        in  {qkv[B,(nq+2nkv)d] f32, q_norm[d] bf16, k_norm[d] bf16,
- *                              kcache[B,nkv,S,d] bf16, vcache[B,nkv,S,d] bf16}
+ *                              kcache[num_requests,nkv,S,d] bf16, vcache[same] bf16}
  *                         out {o[B,nq*d] f32}: per-head RMSNorm of q and k, RoPE at
  *                         step[r], K/V of position step[r] stored in the caches,
  *                         causal grouped-query attention over positions 0..step[r].
@@ -160,10 +161,21 @@ typedef struct {
  * seq_length] i32 holding prompts and generated ids, step[num_requests] i32
  * (the position each request consumes next) and prompt_len[num_requests] i32.
  * All three are caller-owned device memory (attached); tokens and step are
- * advanced on the device. */
+ * advanced on the device.
+ *
+ * rows_per_request R (0 or 1: decode): with R > 1 every iteration takes R
+ * consecutive prompt positions of each request at once (batched prompt
+ * ingestion, the step before decoding the pages' 39-token prompt of P3
+ * Figure 1): rows r R .. r R + R - 1 are positions step[r] .. step[r] + R - 1
+ * of request r, attention of row r R + i covers positions 0 .. step[r] + i,
+ * every row writes its K/V row, and step[r] advances by R per iteration.
+ * No token is generated: a run of n iterations needs step[r] + R n <=
+ * prompt_len[r] - 1 for every request (MPK_ERR_SHAPE otherwise), so the
+ * position after every consumed one is still a prompt position. */
 typedef struct {
   int32_t tokens, step, prompt_len; /* tensor ids */
   int32_t num_requests;
+  int32_t rows_per_request;         /* R; rows B = num_requests x R must be 1, 2 or 8 */
 } mpk_meta;
 
 /* Validate the tensors and operators, split each operator into tiles for the

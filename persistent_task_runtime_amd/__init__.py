@@ -77,7 +77,8 @@ class mpk_op(ctypes.Structure):
 
 
 class mpk_meta(ctypes.Structure):
-    _fields_ = [("tokens", c_i32), ("step", c_i32), ("prompt_len", c_i32), ("num_requests", c_i32)]
+    _fields_ = [("tokens", c_i32), ("step", c_i32), ("prompt_len", c_i32), ("num_requests", c_i32),
+                ("rows_per_request", c_i32)]
 
 
 class mpk_trace_record(ctypes.Structure):
@@ -371,25 +372,32 @@ _LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_nor
 def qwen3_graph(shape, batch: int, ptrs: Dict[str, int], tokens_width: int, max_seq: int,
                 layers: Optional[Sequence[int]] = None, with_embedding: bool = True,
                 with_lm_head: bool = True, logits_iters: int = 0, x_in_ptr: int = 0,
-                x_out_ptr: int = 0) -> Tuple[GraphSpec, mpk_meta]:
+                x_out_ptr: int = 0, rows_per_request: int = 1) -> Tuple[GraphSpec, mpk_meta]:
     """Tensor table and operator list of a Qwen3-style decoder, in layer order.
 
-    ``ptrs`` maps weight names (``E``, ``final_norm``, ``l{i}.wq`` ...), the KV
-    caches (``l{i}.kcache`` / ``l{i}.vcache``, each [B, n_kv, max_seq, d] bf16),
-    ``tokens``, ``step``, ``prompt_len`` and optionally ``logits`` to device
-    addresses.  Without the embedding the first layer reads the f32 tensor at
-    ``x_in_ptr`` ([B, hidden]); without the LM head the last layer writes
-    ``x_out_ptr`` when given.  Activations between operators are
+    ``batch`` is the rows B of an iteration: B / rows_per_request requests,
+    each taking rows_per_request consecutive positions per iteration (> 1:
+    batched prompt ingestion, see mpk_meta).  ``ptrs`` maps weight names
+    (``E``, ``final_norm``, ``l{i}.wq`` ...), the KV caches (``l{i}.kcache`` /
+    ``l{i}.vcache``, each [requests, n_kv, max_seq, d] bf16), ``tokens``,
+    ``step``, ``prompt_len`` (per request) and optionally ``logits`` to
+    device addresses.  Without the embedding the first layer reads the f32
+    tensor at ``x_in_ptr`` ([B, hidden]); without the LM head the last layer
+    writes ``x_out_ptr`` when given.  Activations between operators are
     library-owned."""
     g = GraphSpec()
     H, d, F = shape.hidden, shape.head_dim, shape.ffn
     B = batch
+    if rows_per_request < 1 or B % rows_per_request:
+        raise ValueError("rows_per_request must divide the rows per iteration")
+    NR = B // rows_per_request
     layer_ids = list(range(shape.layers)) if layers is None else list(layers)
-    tok = g.tensor("tokens", MPK_I32, (B, tokens_width), ptrs["tokens"])
-    stp = g.tensor("step", MPK_I32, (B,), ptrs["step"])
-    pl = g.tensor("prompt_len", MPK_I32, (B,), ptrs["prompt_len"])
+    tok = g.tensor("tokens", MPK_I32, (NR, tokens_width), ptrs["tokens"])
+    stp = g.tensor("step", MPK_I32, (NR,), ptrs["step"])
+    pl = g.tensor("prompt_len", MPK_I32, (NR,), ptrs["prompt_len"])
     meta = mpk_meta()
-    meta.tokens, meta.step, meta.prompt_len, meta.num_requests = tok, stp, pl, B
+    meta.tokens, meta.step, meta.prompt_len, meta.num_requests = tok, stp, pl, NR
+    meta.rows_per_request = rows_per_request
     if with_embedding:
         E = g.tensor("E", MPK_BF16, (shape.vocab, H), ptrs["E"])
         x = g.tensor("x0", MPK_F32, (B, H))
@@ -403,8 +411,8 @@ def qwen3_graph(shape, batch: int, ptrs: Dict[str, int], tokens_width: int, max_
                              ("wv", (shape.kv_rows, H)), ("q_norm", (d,)), ("k_norm", (d,)),
                              ("wo", (H, shape.q_rows)), ("ffn_norm", (H,)), ("wg", (F, H)),
                              ("wu", (F, H)), ("wd", (H, F)))}
-        kc = g.tensor("l%d.kcache" % l, MPK_BF16, (B, shape.n_kv, max_seq, d), ptrs["l%d.kcache" % l])
-        vc = g.tensor("l%d.vcache" % l, MPK_BF16, (B, shape.n_kv, max_seq, d), ptrs["l%d.vcache" % l])
+        kc = g.tensor("l%d.kcache" % l, MPK_BF16, (NR, shape.n_kv, max_seq, d), ptrs["l%d.kcache" % l])
+        vc = g.tensor("l%d.vcache" % l, MPK_BF16, (NR, shape.n_kv, max_seq, d), ptrs["l%d.vcache" % l])
         qkv = g.tensor("l%d.qkv" % l, MPK_F32, (B, qkv_w))
         o = g.tensor("l%d.o" % l, MPK_F32, (B, shape.q_rows))
         h1 = g.tensor("l%d.h_attn" % l, MPK_F32, (B, H))

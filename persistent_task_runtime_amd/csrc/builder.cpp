@@ -144,13 +144,21 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
   g->num_queues = Lc.num_cus;
 
   // ---- meta tensors ----
-  const int B = meta->num_requests;
-  if (B <= 0 || B > M.max_batch || B > MPK_MAX_BATCH || (B > 2 && B != MPK_MAX_BATCH))
-    return mpk_fail(MPK_ERR_SHAPE, "num_requests must be 1, 2 or 8 (and at most max_batch)");
+  // B rows per iteration: R consecutive positions of each of NR requests
+  const int NR = meta->num_requests;
+  const int R = meta->rows_per_request > 0 ? meta->rows_per_request : 1;
+  if (NR <= 0 || meta->rows_per_request < 0 || (int64_t)NR * R > MPK_MAX_BATCH)
+    return mpk_fail(MPK_ERR_SHAPE, "num_requests x rows_per_request must be 1, 2 or 8 (and at most max_batch)");
+  const int B = NR * R;
+  if (B > M.max_batch || (B > 2 && B != MPK_MAX_BATCH))
+    return mpk_fail(MPK_ERR_SHAPE, "num_requests x rows_per_request must be 1, 2 or 8 (and at most max_batch)");
+  g->rows = B;
+  g->rpr = R;
+  g->meta.rows_per_request = R;
   int rc;
-  if ((rc = check_tensor(g, meta->tokens, MPK_I32, {B, -1}, "tokens", -1))) return rc;
-  if ((rc = check_tensor(g, meta->step, MPK_I32, {B}, "step", -1))) return rc;
-  if ((rc = check_tensor(g, meta->prompt_len, MPK_I32, {B}, "prompt_len", -1))) return rc;
+  if ((rc = check_tensor(g, meta->tokens, MPK_I32, {NR, -1}, "tokens", -1))) return rc;
+  if ((rc = check_tensor(g, meta->step, MPK_I32, {NR}, "step", -1))) return rc;
+  if ((rc = check_tensor(g, meta->prompt_len, MPK_I32, {NR}, "prompt_len", -1))) return rc;
   for (int id : {meta->tokens, meta->step, meta->prompt_len})
     if (!g->tensors[id].dev_ptr)
       return mpk_fail(MPK_ERR_INVALID_ARG, "meta tensors must be attached caller memory");
@@ -319,8 +327,8 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
         if ((rc = check_tensor(g, o.in[0], MPK_F32, {B, qkv_w}, "qkv", i))) return rc;
         if ((rc = check_tensor(g, o.in[1], MPK_BF16, {d}, "q_norm", i))) return rc;
         if ((rc = check_tensor(g, o.in[2], MPK_BF16, {d}, "k_norm", i))) return rc;
-        if ((rc = check_tensor(g, o.in[3], MPK_BF16, {B, nkv, M.max_seq, d}, "kcache", i))) return rc;
-        if ((rc = check_tensor(g, o.in[4], MPK_BF16, {B, nkv, M.max_seq, d}, "vcache", i))) return rc;
+        if ((rc = check_tensor(g, o.in[3], MPK_BF16, {NR, nkv, M.max_seq, d}, "kcache", i))) return rc;
+        if ((rc = check_tensor(g, o.in[4], MPK_BF16, {NR, nkv, M.max_seq, d}, "vcache", i))) return rc;
         if (!g->tensors[o.in[3]].dev_ptr || !g->tensors[o.in[4]].dev_ptr)
           return mpk_fail(MPK_ERR_INVALID_ARG, "KV caches must be attached caller memory");
         if ((rc = check_tensor(g, o.out[0], MPK_F32, {B, nq * d}, "o", i))) return rc;
@@ -333,7 +341,7 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
         // must never share a queue (an owner could wait on a split queued
         // behind it)
         if (B * nkv > W)
-          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": num_requests x n_kv_heads = " +
+          return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": rows x n_kv_heads = " +
                                              std::to_string(B * nkv) + " exceeds the " + std::to_string(W) +
                                              " workers (one attention task per worker)");
         D.nq = nq, D.nkv = nkv, D.d = d, D.S = M.max_seq;
@@ -529,22 +537,28 @@ extern "C" int mpk_get_graph_info(mpk_graph_t g, mpk_graph_info* info) {
 extern "C" void mpk_destroy_graph(mpk_graph_t g) { delete g; }
 
 // The start-of-run rule of mpk_begin_run (device) on host copies of the meta
-// tensors: positions inside tokens and the KV cache, and every id the run
-// reads from tokens inside the vocabulary.
+// tensors: positions inside tokens and the KV cache, every id the run reads
+// from tokens inside the vocabulary, and with R rows per request (batched
+// prompt ingestion) every consumed position followed by a prompt position.
 extern "C" int mpk_check_run(mpk_graph_t g, const int32_t* step, const int32_t* tokens,
                              const int32_t* prompt_len, int32_t n_iter) {
   mpk_clear_error();
   if (!g || !step || !tokens || !prompt_len) return mpk_fail(MPK_ERR_INVALID_ARG, "mpk_check_run: NULL argument");
   if (n_iter <= 0) return mpk_fail(MPK_ERR_INVALID_ARG, "num_iterations must be positive");
-  const int B = g->meta.num_requests;
+  const int NR = g->meta.num_requests, R = g->rpr;
   const int64_t width = g->tensors[g->meta.tokens].dims[1];
-  for (int r = 0; r < B; ++r) {
+  const int64_t n_pos = (int64_t)R * n_iter;  // positions each request consumes
+  for (int r = 0; r < NR; ++r) {
     const int p0 = step[r];
-    if (p0 < 0 || (int64_t)p0 + n_iter >= width || (int64_t)p0 + n_iter > g->model.max_seq)
+    if (p0 < 0 || p0 + n_pos >= width || p0 + n_pos > g->model.max_seq)
       return mpk_fail(MPK_ERR_SHAPE, "request " + std::to_string(r) + ": step " + std::to_string(p0) + " + " +
-                                         std::to_string(n_iter) +
-                                         " iterations leaves the tokens tensor or the KV cache");
-    const int q_end = std::min(p0 + n_iter, std::max(prompt_len[r], p0 + 1));
+                                         std::to_string(n_pos) +
+                                         " positions leaves the tokens tensor or the KV cache");
+    if (R > 1 && p0 + n_pos > (int64_t)prompt_len[r] - 1)
+      return mpk_fail(MPK_ERR_SHAPE, "request " + std::to_string(r) + ": " + std::to_string(n_pos) +
+                                         " positions from step " + std::to_string(p0) +
+                                         " reach past the prompt (batched ingestion generates no token)");
+    const int q_end = R > 1 ? (int)(p0 + n_pos) : std::min(p0 + n_iter, std::max(prompt_len[r], p0 + 1));
     for (int q = p0; q < q_end; ++q) {
       const int t = tokens[(int64_t)r * width + q];
       if (t < 0 || t >= g->model.vocab)

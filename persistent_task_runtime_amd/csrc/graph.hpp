@@ -16,6 +16,8 @@ struct mpk_graph_s {
   std::vector<mpk_op> ops;
 
   // derived by the builder
+  int rows = 1;          // rows per iteration: num_requests x rows_per_request
+  int rpr = 1;           // rows per request (1: decode; > 1: batched prompt ingestion)
   int num_workers = 0;   // CUs that take tiles
   int num_queues = 0;    // CUs of the launch grid (workers + dedicated scheduler CUs)
   int sink = -1;

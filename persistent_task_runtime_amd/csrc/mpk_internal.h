@@ -111,14 +111,14 @@ typedef struct {
   int32_t qstride;
   int32_t n_iter;
   int32_t n_tasks;
-  int32_t B;
+  int32_t B;                    /* rows per iteration */
+  int32_t rpr;                  /* rows per request: row b is position pos0[b / rpr] + rpr s + b % rpr */
   int32_t tokens_width;
   int32_t rope_half;
   float rms_eps;
   int32_t vocab;
   int32_t max_seq;
-  int32_t* pos0;                /* [B] step[r] at launch, written by the run's first kernel: position
-                                   of request r in iteration s is pos0[r] + s */
+  int32_t* pos0;                /* [requests] step[r] at launch, written by the run's first kernel */
   uint32_t iter_base;           /* stamp of iteration s is iter_base + s + 1 */
 } mpk_kparams;
 

@@ -302,7 +302,7 @@ DEV void lds_write_f32x2(uint32_t a, float2 v) {
 
 DEV int xperm(int k) { return (k & ~511) + ((k & 4) << 6) + (((k & 511) >> 3) << 2) + (k & 3); }
 
-// Position of request b in the current iteration (written into LDS_POS by the
+// Position of row b in the current iteration (written into LDS_POS by the
 // scheduler wavefront at the start of each iteration).
 DEV int cur_pos(const char* smem, int b) {
   return __builtin_amdgcn_readfirstlane(lvi(smem, LDS_POS)[b]);
@@ -311,13 +311,16 @@ DEV int cur_pos(const char* smem, int b) {
 // Scheduler wavefront, once per launch: the positions of the launch's first
 // iteration (written by mpk_begin_run ahead of the launch) into LDS_POS0.
 DEV void load_positions(const mpk_kparams& P, char* smem, int lane) {
-  if (lane < P.B) lvi(smem, LDS_POS0)[lane] = ld_devi(P.pos0 + lane);
+  if (lane < P.B / P.rpr) lvi(smem, LDS_POS0)[lane] = ld_devi(P.pos0 + lane);
 }
 
-// Scheduler wavefront: positions of iteration s into LDS_POS.
+// Scheduler wavefront: positions of iteration s into LDS_POS.  Row b is
+// position pos0[r] + rpr s + i of request r = b / rpr, i = b % rpr (rpr = 1:
+// one position per request and iteration).
 DEV void set_positions(const mpk_kparams& P, char* smem, int s, int lane) {
   if (lane == 0)
-    for (int b = 0; b < P.B; ++b) lvi(smem, LDS_POS)[b] = lvi(smem, LDS_POS0)[b] + s;
+    for (int b = 0; b < P.B; ++b)
+      lvi(smem, LDS_POS)[b] = lvi(smem, LDS_POS0)[b / P.rpr] + P.rpr * s + b % P.rpr;
 }
 
 // Per-lane forms: the position of request b (b may differ between lanes), and
@@ -463,7 +466,7 @@ DEV int resolve_tokens(const mpk_kparams& P, char* smem, int tid, int s, int tas
   bool need = false;
   if (tid < P.B) {
     if (s == 0) {
-      tok[tid] = ld_devi(P.tokens + (int64_t)tid * P.tokens_width + cur_pos_v(smem, tid));
+      tok[tid] = ld_devi(P.tokens + (int64_t)(tid / P.rpr) * P.tokens_width + cur_pos_v(smem, tid));
     } else {
       need = true;
     }
@@ -1417,12 +1420,21 @@ DEV int argmax_task(const mpk_kparams& P, cop& D, char* smem, int tid, int s, in
       if (lane == 0) {
         const int p = cur_pos(smem, b);
         int next = ix;
-        if (p + 1 >= ld_devi(P.prompt_len + b)) {
-          st_devi(P.tokens + (int64_t)b * P.tokens_width + p + 1, ix);
+        if (P.rpr == 1) {
+          if (p + 1 >= ld_devi(P.prompt_len + b)) {
+            st_devi(P.tokens + (int64_t)b * P.tokens_width + p + 1, ix);
+          } else {
+            next = ld_devi(P.tokens + (int64_t)b * P.tokens_width + p + 1);  // teacher-forced prompt token
+          }
+          st_devi(P.step + b, p + 1);
         } else {
-          next = ld_devi(P.tokens + (int64_t)b * P.tokens_width + p + 1);  // teacher-forced prompt token
+          // batched prompt ingestion: the row's next position p + rpr is a
+          // prompt position in every iteration of the run (checked at its
+          // start); the request's last row advances its step past the chunk
+          const int r = b / P.rpr;
+          next = s + 1 < P.n_iter ? ld_devi(P.tokens + (int64_t)r * P.tokens_width + p + P.rpr) : 0;
+          if (b % P.rpr == P.rpr - 1) st_devi(P.step + r, p + 1);
         }
-        st_devi(P.step + b, p + 1);
         st_lli(P.tok_ll + b, next, st);
       }
     }
@@ -1561,12 +1573,16 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   const int g4 = lane >> 4, cn = lane & 15;  // MFMA lane: row group, column
   const int r = T.row0, j = T.nrows, c = T.split, NS = D.nsplit;
   const int G = D.nq / D.nkv, half = DH >> 1;
+  // row r is position p of request rq, the off-th row of the request in this
+  // iteration: rows r - off .. r are positions p - off .. p, taken from this
+  // iteration's q/k/v words; the splits fold the cache positions before them
+  const int rq = r / P.rpr, off = r % P.rpr;
   const int p = cur_pos(smem, r);
-  const int n = p + 1;
-  const int na = min(NS, (n + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT);
+  const int nf = p - off;
+  const int na = max(1, min(NS, (nf + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT));
   if (c >= na) return 0;  // uniform over the workgroup: nothing to do this iteration
-  const int lo = (int)(((int64_t)c * n) / na), hi = (int)(((int64_t)(c + 1) * n) / na);
-  const bool owner = c == na - 1;  // the split holding position p
+  const int lo = (int)(((int64_t)c * nf) / na), hi = (int)(((int64_t)(c + 1) * nf) / na);
+  const bool owner = c == na - 1;  // the split that adds positions p - off .. p and merges
   const uint32_t st = stamp_of(P, s);
   const uint32_t lb = lds_addr(smem);
   float* qs = reinterpret_cast<float*>(smem + LDS_X);  // [G][DH], scaled for base-2 scores
@@ -1578,8 +1594,8 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   float* outs = reinterpret_cast<float*>(smem + LDS_OUT);               // partial, then o
   uint32_t* kvrow = reinterpret_cast<uint32_t*>(smem + LDS_OUT) + 640;  // bf16 K row, then V row
   const int qkv_w = (D.nq + 2 * D.nkv) * DH;
-  uint16_t* kc = D.kc + ((int64_t)(r * D.nkv + j) * D.S) * DH;
-  uint16_t* vc = D.vc + ((int64_t)(r * D.nkv + j) * D.S) * DH;
+  uint16_t* kc = D.kc + ((int64_t)(rq * D.nkv + j) * D.S) * DH;
+  uint16_t* vc = D.vc + ((int64_t)(rq * D.nkv + j) * D.S) * DH;
   // base-2 scores: log2(e) / sqrt(d) is applied to q once, when it is staged
   const float scale = 1.4426950408889634f / sqrtf((float)DH);
 
@@ -1595,7 +1611,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   auto issue = [&](int k, uint32_t slot) {
     const int t0 = lo + 16 * k;
     const int tk = t0 + cn;
-    const int rk = tk < hi && tk != p ? tk : lo;
+    const int rk = tk < hi ? tk : lo;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
       __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(kc + (int64_t)rk * DH + 32 * kk + 8 * g4),
@@ -1603,7 +1619,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 #pragma unroll
     for (int c4 = 0; c4 < 16 / PPI; ++c4) {
       const int tv = t0 + c4 * PPI + lane / LPR;
-      const int rv = tv < hi && tv != p ? tv : lo;
+      const int rv = tv < hi ? tv : lo;
       __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(vc + (int64_t)rv * DH + 8 * (lane % LPR)),
                                        lds_ptr(slot + KBYTES + c4 * 1056), 16, 0, CPOL_SC1 | CPOL_NT);
     }
@@ -1702,28 +1718,77 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   f32x4 acc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float spv[ATT_MAXG];  // scheduler wave: scores of position p
-  if (sched) {
-    // the owner's K/V of p into the caches (its stores complete before the
-    // output is published; next iteration's readers are ordered after that
-    // output), then the scores of position p, the merge's ninth partial
-    if (owner) {
-      uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * DH);
-      uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * DH);
-      for (int i = lane; i < DH / 2; i += 64) {
-        st_devu(kdst + i, kvrow[i]);
-        st_devu(vdst + i, kvrow[DH / 2 + i]);
-      }
-      vm_drain();
-    }
+  // Scheduler wave of the owner: positions p - off .. p, the merge's ninth
+  // partial, as a running maximum cm, sum cl and weighted V co per head (a
+  // lane holds dims lane and lane + half of co; lanes < half).
+  float cm[ATT_MAXG], cl[ATT_MAXG], co[ATT_MAXG][2];
 #pragma unroll
-    for (int h = 0; h < ATT_MAXG; ++h) {
-      float part = 0.f;
-      if (h < G)
-        for (int i = lane; i < DH; i += 64) part = fmaf(qs[h * DH + i], kv[i], part);
-      spv[h] = wave_sum(part);
+  for (int h = 0; h < ATT_MAXG; ++h) cm[h] = -INFINITY, cl[h] = 0.f, co[h][0] = co[h][1] = 0.f;
+  if (sched && owner) {
+    // K/V of p into the caches (the stores complete before the output is
+    // published; next iteration's readers are ordered after that output)
+    uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * DH);
+    uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * DH);
+    for (int i = lane; i < DH / 2; i += 64) {
+      st_devu(kdst + i, kvrow[i]);
+      st_devu(vdst + i, kvrow[DH / 2 + i]);
     }
-  } else {
+    vm_drain();
+    const bool pl = lane < half;
+    auto fold_pos = [&](float ka, float kb, float va, float vb) {
+#pragma unroll
+      for (int h = 0; h < ATT_MAXG; ++h) {
+        if (h < G) {
+          const float sc = wave_sum(pl ? fmaf(qs[h * DH + lane], ka, qs[h * DH + lane + half] * kb) : 0.f);
+          const float mn = fmaxf(cm[h], sc);
+          const float a1 = cm[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(cm[h] - mn);
+          const float a2 = __builtin_amdgcn_exp2f(sc - mn);
+          cl[h] = fmaf(cl[h], a1, a2);
+          co[h][0] = fmaf(co[h][0], a1, va * a2);
+          co[h][1] = fmaf(co[h][1], a1, vb * a2);
+          cm[h] = mn;
+        }
+      }
+    };
+    // the request's earlier rows in this iteration (positions p - off ..
+    // p - 1): K and V from their q/k/v words, K normalised and rotated as the
+    // rows' own tasks do, both rounded to bf16 as the cache holds them
+    for (int bb = r - off; bb < r; ++bb) {
+      const uint64_t* kw = D.xll + (int64_t)bb * qkv_w + (D.nq + j) * DH;
+      const uint64_t* vw = kw + D.nkv * DH;
+      uint64_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+      bool need = pl;
+      for (;;) {
+        if (need) {
+          w0 = ld_ll(kw + lane), w1 = ld_ll(kw + lane + half);
+          w2 = ld_ll(vw + lane), w3 = ld_ll(vw + lane + half);
+          need = !(ll_ok(w0, st) && ll_ok(w1, st) && ll_ok(w2, st) && ll_ok(w3, st));
+        }
+        if (__ballot(need) == 0) break;
+        if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const float a = pl ? ll_f(w0) : 0.f, b = pl ? ll_f(w1) : 0.f;
+      const float ss = wave_sum(a * a + b * b);
+      const float inv = 1.0f / sqrtf(ss / (float)DH + P.rms_eps);
+      float ka = 0.f, kb = 0.f, va = 0.f, vb = 0.f;
+      if (pl) {
+        const int pb = cur_pos(smem, bb);
+        const float cs = gld(P.rope_cos + (int64_t)pb * half + lane);
+        const float sn = gld(P.rope_sin + (int64_t)pb * half + lane);
+        const float ya = bf16f(gld16(D.kn + lane)) * (a * inv);
+        const float yb = bf16f(gld16(D.kn + lane + half)) * (b * inv);
+        ka = bf16f(f2bf(ya * cs - yb * sn));
+        kb = bf16f(f2bf(yb * cs + ya * sn));
+        va = bf16f(f2bf(ll_f(w2)));
+        vb = bf16f(f2bf(ll_f(w3)));
+      }
+      fold_pos(ka, kb, va, vb);
+    }
+    // position p (its K/V in LDS)
+    fold_pos(pl ? kv[lane] : 0.f, pl ? kv[lane + half] : 0.f, pl ? kv[DH + lane] : 0.f,
+             pl ? kv[DH + lane + half] : 0.f);
+  } else if (!sched) {
     // ---- the MFMA fold over this wave's steps ----
     // q as the B operand of the scores, per 32-dim k-step
     u32x4 qb[KS];
@@ -1789,7 +1854,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
         for (int e = 0; e < 4; ++e) {
           const float v = sa[e] + __shfl_xor(sa[e], 4);
           const int t = t0 + 4 * g4 + e;
-          sv[e] = cn < G && t < hi && t != p ? v : -INFINITY;
+          sv[e] = cn < G && t < hi ? v : -INFINITY;
           mx = fmaxf(mx, sv[e]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -1845,12 +1910,19 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   // every wave's V ring is drained before the merge area over it is written
   vm_drain_known();
   lds_barrier();
+  if (*lvi(smem, LDS_CTL)) return -1;  // (a wait above ended the run)
   if (sched) {
-    for (int h = 0; h < G; ++h) {
-      for (int i = lane; i < DH; i += 64) mo[(MPK_NW * ATT_MAXG + h) * 128 + i] = owner ? kv[DH + i] : 0.f;
-      if (lane == 0) {
-        mm[MPK_NW * ATT_MAXG + h] = owner ? spv[h] : -INFINITY;
-        ml[MPK_NW * ATT_MAXG + h] = owner ? 1.f : 0.f;
+#pragma unroll
+    for (int h = 0; h < ATT_MAXG; ++h) {
+      if (h < G) {
+        if (lane < half) {
+          mo[(MPK_NW * ATT_MAXG + h) * 128 + lane] = co[h][0];
+          mo[(MPK_NW * ATT_MAXG + h) * 128 + lane + half] = co[h][1];
+        }
+        if (lane == 0) {
+          mm[MPK_NW * ATT_MAXG + h] = cm[h];
+          ml[MPK_NW * ATT_MAXG + h] = cl[h];
+        }
       }
     }
   } else if (cn < G) {
@@ -2438,13 +2510,16 @@ __global__ void mpk_begin_run(mpk_kparams P, int n_iter) {
     *P.ticket_ctr = 0u;
   }
   __syncthreads();
-  for (int r = 0; r < P.B; ++r) {
+  const int64_t n_pos = (int64_t)P.rpr * n_iter;  // positions each request consumes
+  for (int r = 0; r < P.B / P.rpr; ++r) {
     const int p0 = P.step[r];
     const int plen = P.prompt_len[r];
-    bool bad = p0 < 0 || (int64_t)p0 + n_iter >= P.tokens_width || (int64_t)p0 + n_iter > P.max_seq;
+    bool bad = p0 < 0 || p0 + n_pos >= P.tokens_width || p0 + n_pos > P.max_seq ||
+               (P.rpr > 1 && p0 + n_pos > plen - 1);
     if (!bad) {
-      // ids read from tokens: position p0, and q in (p0, p0 + n) below the prompt's end
-      const int q_end = min(p0 + n_iter, max(plen, p0 + 1));
+      // ids read from tokens: position p0, and q in (p0, p0 + n) below the
+      // prompt's end; batched ingestion reads every consumed position
+      const int q_end = P.rpr > 1 ? (int)(p0 + n_pos) : min(p0 + n_iter, max(plen, p0 + 1));
       for (int q = p0 + lane; q < q_end; q += 64) {
         const int t = P.tokens[(int64_t)r * P.tokens_width + q];
         bad |= t < 0 || t >= P.vocab;
@@ -2646,7 +2721,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   });
   x->device = device;
   x->g = g;
-  x->B = g->meta.num_requests;
+  x->B = g->rows;
   int rc = select_kernels(x->B, &x->kernel_persistent, &x->kernel_op, &x->lds_bytes);
   if (rc) return rc;
   HIPCHK(hipFuncSetAttribute(x->kernel_persistent, hipFuncAttributeMaxDynamicSharedMemorySize, x->lds_bytes));
@@ -2789,6 +2864,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   K.qstride = g->max_queue;
   K.n_tasks = (int)g->tasks.size();
   K.B = B;
+  K.rpr = g->rpr;
   K.tokens_width = (int)g->tensors[g->meta.tokens].dims[1];
   K.rope_half = half;
   K.rms_eps = M.rms_eps;
@@ -2815,7 +2891,7 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st, mpk_kparams
   if (n_iter <= 0) return mpk_fail(MPK_ERR_INVALID_ARG, "num_iterations must be positive");
   // Checks that need no device value; positions and token ids are checked
   // on the device by mpk_begin_run (no host round trip per launch).
-  if ((int64_t)n_iter >= K.tokens_width || n_iter > x->g->model.max_seq)
+  if ((int64_t)K.rpr * n_iter >= K.tokens_width || (int64_t)K.rpr * n_iter > x->g->model.max_seq)
     return mpk_fail(MPK_ERR_SHAPE, std::to_string(n_iter) + " iterations leave the tokens tensor or the KV cache");
   for (size_t i = 0; i < x->g->dops.size(); ++i) {
     const mpk_dev_op& D = x->g->dops[i];

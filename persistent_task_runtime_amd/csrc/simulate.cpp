@@ -100,6 +100,8 @@ extern "C" int mpk_sim_create(mpk_graph_t g, const int32_t* step, const int32_t*
   *out = nullptr;
   std::unique_ptr<mpk_sim_s> s(new mpk_sim_s());
   s->g = g;
+  if (g->rpr != 1)
+    return mpk_fail(MPK_ERR_SHAPE, "the simulator models decode graphs (one row per request) only");
   s->B = g->meta.num_requests;
   s->width = g->tensors[g->meta.tokens].dims[1];
   s->S = g->model.max_seq;
@@ -319,10 +321,12 @@ extern "C" int mpk_simulate(mpk_sim_t sim, const mpk_sim_cfg* cfg, mpk_trace_rec
           }
         } else if (T.kind == MPK_TK_ATTN) {
           const int r = T.row0, j = T.nrows, c = T.split, NS = D.nsplit, d = D.d, G = D.nq / D.nkv;
-          const int p = pos0[r] + s, n = p + 1;
-          const int na = std::min(NS, (n + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT);
+          // the splits fold positions 0 .. p - 1 from the cache; the owner
+          // adds p (the device's split rule)
+          const int p = pos0[r] + s, nf = p;
+          const int na = std::max(1, std::min(NS, (nf + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT));
           if (c < na) {
-            const int lo = (int)((int64_t)c * n / na), hi = (int)((int64_t)(c + 1) * n / na);
+            const int lo = (int)((int64_t)c * nf / na), hi = (int)((int64_t)(c + 1) * nf / na);
             const bool owner = c == na - 1;
             // q of the group's heads, k and v of kv head j
             Words& X = sim->tensor_words[O.in[0]];
@@ -338,11 +342,11 @@ extern "C" int mpk_simulate(mpk_sim_t sim, const mpk_sim_cfg* cfg, mpk_trace_rec
             if (!ok) return;
             R.start_ticket = ticket.fetch_add(1);
             R.t_ready = now_ns();
-            // K/V rows of this split's positions other than p: written by an
-            // earlier iteration's owner split (or pre-filled)
+            // K/V rows of this split's positions: written by an earlier
+            // iteration's owner split (or pre-filled)
             std::atomic<uint32_t>* ver = sim->kv_ver[T.op].get() + ((size_t)r * D.nkv + j) * sim->S;
             for (int t = lo; t < hi; ++t)
-              if (t != p && ver[t].load(std::memory_order_acquire) == 0u) {
+              if (ver[t].load(std::memory_order_acquire) == 0u) {
                 fail(MPK_ERR_GRAPH, "task " + std::to_string(tid) + " iteration " + std::to_string(s) +
                                         ": read the K/V row of position " + std::to_string(t) +
                                         " before it was written");

@@ -190,6 +190,52 @@ class RequestView:
         self.exe.close()
 
 
+class PromptChunks:
+    """Batched prompt ingestion for request r of a Session: every iteration
+    takes `rows` consecutive prompt positions of the request as `rows` rows
+    (mpk_meta rows_per_request), over views of the session's own tensors
+    (its tokens row, step and prompt_len entries, its K/V caches), so a run
+    advances the request in place by `rows` positions per iteration.  With
+    logits_iters > 0 the logits of every row are kept ([iteration, row, V]:
+    row i of iteration s is position step + rows s + i)."""
+
+    def __init__(self, sess: "Session", r: int, rows: int = 8, logits_iters: int = 0):
+        import torch
+
+        sh, m = sess.w.shape, sess.model
+        self.sess, self.r, self.rows = sess, r, rows
+        ptrs = m.ptrs()
+        for l in m.layer_ids:
+            ptrs["l%d.kcache" % l] = sess.kc[l][r].data_ptr()
+            ptrs["l%d.vcache" % l] = sess.vc[l][r].data_ptr()
+        ptrs.update(tokens=sess.tokens[r].data_ptr(), step=sess.step[r:r + 1].data_ptr(),
+                    prompt_len=sess.prompt_len[r:r + 1].data_ptr())
+        self.logits = None
+        if logits_iters:
+            self.logits = torch.zeros((logits_iters, rows, sh.vocab), dtype=torch.float32, device=_dev())
+            ptrs["logits"] = self.logits.data_ptr()
+        spec, meta = mpk.qwen3_graph(sh, rows, ptrs, sess.tokens.shape[1], sess.max_seq, layers=m.layer_ids,
+                                     logits_iters=logits_iters, rows_per_request=rows)
+        num_cus = torch.cuda.get_device_properties(_dev()).multi_processor_count
+        self.exe = mpk.Executable(spec, meta, mpk.model_cfg(sh, rows, sess.max_seq), mpk.launch_cfg(num_cus))
+
+    def chunks_left(self) -> int:
+        """Whole chunks that fit before the prompt's last position (batched
+        ingestion generates no token: the last prompt position is decoded)."""
+        step = int(self.sess.step[self.r].item())
+        plen = int(self.sess.prompt_len[self.r].item())
+        return max(0, (plen - 1 - step) // self.rows)
+
+    def run(self, n_iter: int, stream=None):
+        import torch
+
+        s = torch.cuda.current_stream() if stream is None else stream
+        self.exe.run(n_iter, s.cuda_stream)
+
+    def close(self):
+        self.exe.close()
+
+
 def run_workload(w: "synth.Workload", n_iter: int, want_logits: bool = False, per_op: bool = False,
                  trace: bool = False, model: Optional[DeviceModel] = None, launch=None) -> dict:
     import torch

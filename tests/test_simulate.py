@@ -86,8 +86,9 @@ def test_every_data_edge_is_ordered_under_jitter(sim):
         if it:
             prev = tr[it - 1]["start_ticket"][by_op[chain[-1]]].max()
             assert prev < tr[it]["start_ticket"][by_op[chain[0]]].min()
-    # positions 58..63 use one split, 64..69 two (the owner gathers the other)
-    assert two_splits == 6 * 2  # 6 iterations x 2 layers
+    # the splits cover positions 0 .. p - 1: 58..64 take one split, 65..69 two
+    # (the owner gathers the other)
+    assert two_splits == 5 * 2  # 5 iterations x 2 layers
     step, toks = mpk.mpk_sim_read_meta(s, 1, WIDTH)
     assert step[0] == P0 + n
     assert ((toks[0, P0 + 1:P0 + n + 1] >= 0) & (toks[0, P0 + 1:P0 + n + 1] < synth.TINY.vocab)).all()
