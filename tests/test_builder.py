@@ -38,11 +38,12 @@ class FakePtrs(dict):
 
 
 def build(shape, B=1, tokens_width=64, max_seq=64, num_cus=256, layers=None, logits_iters=0,
-          with_embedding=True, with_lm_head=True, launch=None):
+          with_embedding=True, with_lm_head=True, launch=None, rows_per_request=1):
     ptrs = FakePtrs()
     spec, meta = mpk.qwen3_graph(shape, B, ptrs, tokens_width, max_seq, layers=layers,
                                  logits_iters=logits_iters, with_embedding=with_embedding,
-                                 with_lm_head=with_lm_head, x_in_ptr=ptrs["x_in"])
+                                 with_lm_head=with_lm_head, x_in_ptr=ptrs["x_in"],
+                                 rows_per_request=rows_per_request)
     g = mpk.mpk_build_graph(mpk.model_cfg(shape, B, max_seq), launch or mpk.launch_cfg(num_cus),
                             spec.c_tensors(), spec.ops, meta)
     return g, spec
@@ -286,6 +287,39 @@ def test_host_run_check_follows_the_start_of_run_rule():
             mpk.mpk_check_run(g, np.array([-1, 4], np.int32), toks, plen, 1)
     finally:
         mpk.mpk_destroy_graph(g)
+
+
+def test_rows_per_request_graph_and_run_rule():
+    """Batched prompt ingestion (rows_per_request R): B rows are R positions
+    of B / R requests - meta tensors and K/V caches per request, activations
+    and attention tasks per row - and a run must end inside the prompt:
+    step + R n <= prompt_len - 1, every consumed id in the vocabulary."""
+    V = synth.TINY.vocab
+    g, spec = build(synth.TINY, B=2, tokens_width=64, max_seq=60, rows_per_request=2)
+    try:
+        assert spec.tensors[spec.index["tokens"]].dims == (1, 64)
+        assert spec.tensors[spec.index["l0.kcache"]].dims[0] == 1
+        info, tasks, _, _, _ = info_arrays(g)
+        att = [t for t in tasks if t.split >= 0]
+        assert {t.row0 for t in att} == {0, 1}  # one attention group per row
+        toks = np.full((1, 64), -1, np.int32)
+        toks[0, :39] = 3
+        plen = np.array([39], np.int32)
+        mpk.mpk_check_run(g, np.array([0], np.int32), toks, plen, 19)  # positions 0..37
+        with pytest.raises(mpk.MPKError, match="past the prompt"):
+            mpk.mpk_check_run(g, np.array([0], np.int32), toks, plen, 20)
+        with pytest.raises(mpk.MPKError, match="past the prompt"):
+            mpk.mpk_check_run(g, np.array([1], np.int32), toks, plen, 19)
+        bad = toks.copy()
+        bad[0, 37] = V
+        with pytest.raises(mpk.MPKError, match="position 37"):
+            mpk.mpk_check_run(g, np.array([0], np.int32), bad, plen, 19)
+    finally:
+        mpk.mpk_destroy_graph(g)
+    # rows must be 1, 2 or 8 and divisible into requests
+    with pytest.raises(mpk.MPKError) as e:
+        build(synth.TINY, B=4, rows_per_request=4)
+    assert e.value.code == mpk.MPK_ERR_SHAPE
 
 
 def test_batch8_tiles_and_refusals():
