@@ -2052,8 +2052,6 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 #define G8_KSTEPS (G8_PASS / 32)   // MFMA k-steps per pass
 #define G8_ITEMS (8 * G8_PASS / 8) // (request, 8-column group) staging items per pass
 #define G8_NI ((G8_ITEMS + MPK_THREADS - 1) / MPK_THREADS)
-#define G8_IG 2  // staging items per thread whose words are in flight together
-static_assert(G8_NI % G8_IG == 0, "staging rounds hold whole item groups");
 static_assert(MPK_THREADS % 8 == 0, "a thread's staging items share one request");
 static_assert(LDS_X + G8_KSTEPS * 1024 <= 156 * 1024, "a staged pass must fit the LDS");
 
@@ -2066,81 +2064,82 @@ DEV const uint16_t* vrow_ptr(cop& D, int vr) {
   return D.W2 + (int64_t)(vr - D.N0 - D.N1) * D.K;
 }
 
-// Stage pass p of the 8 requests' x into LDS (B operands), every thread of
-// the workgroup taking part.  Item i = tid + MPK_THREADS j covers request
-// i % 8 (the same for all of a thread's items) and columns 8 (i / 8) .. + 7
-// of the pass.  With a norm, each item's sum of squares of the raw values (in
-// column order) goes to LDS at G8_SQ, [request][item group].  Each
-// wavefront polls its own stamped words and the workgroup meets at the end.
-// Returns -1 on stop.
+// Stage pass p of the 8 rows' x into LDS as B operands, every thread of the
+// workgroup taking part.  The B operand of k-step t holds, in the 16 bytes of
+// lane 16 (q & 3) + r (hi) and lane 16 (q & 3) + r + 8 (lo), the 8 columns of
+// item q = 4 t + (q & 3) of row r.  With a norm, each item's sum of squares
+// of the raw values goes to LDS at G8_SQ, [row][item].  Returns -1 on stop.
 #define G8_SQ (LDS_X + G8_KSTEPS * 1024)  // [8][512] floats
 static_assert(G8_SQ + 8 * 512 * 4 <= 156 * 1024, "staging sums exceed the LDS");
-DEV int stage_pass8(const mpk_kparams& P, cop& D, int p, char* smem, int tid, int s, int task_id, Waiter& Wt,
-                    uint32_t st) {
-  const int lane = tid & 63;
-  const uint32_t xb = lds_addr(smem) + LDS_X;
-  const uint32_t sqb = lds_addr(smem) + G8_SQ;
-  const int b = tid & 7;
+
+DEV void lds_write_u32_nw(uint32_t a, uint32_t v) { asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory"); }
+
+// Stamped x: 1 KB units, unit u = row u % 8, columns 128 (u / 8) .. + 127 of
+// the pass: one coalesced 16-byte device-scope load per lane (two words:
+// columns 2 l, 2 l + 1 of the unit); four lanes cover an item and write 4
+// bytes each of its hi and lo slots.  Wavefront w polls units w + 9 k, up to
+// IG of them in flight together, and fetches a unit again while any of its
+// words is stale; the workgroup meets at the end.
+DEV int stage_pass8_ll(const mpk_kparams& P, cop& D, int p, char* smem, int tid, int s, int task_id, Waiter& Wt,
+                       uint32_t st) {
+  constexpr int NWAVES = MPK_THREADS / 64;
+  constexpr int NU = 8 * G8_PASS / 128;           // units per pass
+  constexpr int UPW = (NU + NWAVES - 1) / NWAVES;  // units per wavefront
+  constexpr int IG = 8;                            // units in flight per wavefront
+  static_assert(UPW <= 32, "a wavefront's units fit one mask");
+  const int wave = uni(tid >> 6), lane = tid & 63;
+  const int pc = lane & 3, qi = lane >> 2;  // this lane's piece of its item, the item within the unit
+  const uint32_t xb = lds_addr(smem) + LDS_X, sqb = lds_addr(smem) + G8_SQ;
+  const int K = D.K;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(D.xll), (short)0, 8 * K * 8, 0x00020000);
   uint32_t need = 0;
-  for (int j = 0; j < G8_NI; ++j)
-    if (tid + MPK_THREADS * j < G8_ITEMS) need |= 1u << j;
-  const int64_t xrow = (int64_t)b * D.K + (int64_t)p * G8_PASS;
-  const uint16_t* erow = D.x_embed ? D.E + (int64_t)cur_token_v(smem, b) * D.K + (int64_t)p * G8_PASS : nullptr;
+  for (int k = 0; k < UPW; ++k)
+    if (wave + NWAVES * k < NU) need |= 1u << k;
   for (;;) {
-    // G8_IG items per round: their stamped words are all in flight together
-#pragma unroll 1
-    for (int j0 = 0; j0 < G8_NI; j0 += G8_IG) {
-      uint64_t w[G8_IG][8];
-      if (D.xll) {
+    uint32_t left = need;
+    while (left) {
+      int ks[IG];
 #pragma unroll
-        for (int jj = 0; jj < G8_IG; ++jj) {
-          const int q = (tid + MPK_THREADS * (j0 + jj)) >> 3;
-          if ((need >> (j0 + jj)) & 1u)
+      for (int i = 0; i < IG; ++i) {
+        ks[i] = left ? __builtin_ctz(left) : -1;
+        left &= left - 1;
+      }
+      u32x4 v[IG];
+      uint32_t g[IG];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[jj][e] = ld_ll(D.xll + xrow + 8 * q + e);
+      for (int i = 0; i < IG; ++i) {
+        if (ks[i] >= 0) {
+          const int u = wave + NWAVES * ks[i];
+          const int col = p * G8_PASS + (u >> 3) * 128 + 2 * lane;
+          v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((u & 7) * K + col) * 8, 0, CPOL_SC1);
+          g[i] = D.has_norm ? gldv<uint32_t>(D.gain + col) : 0u;
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < G8_IG; ++jj) {
-      const int j = j0 + jj;
-      if (!((need >> j) & 1u)) continue;
-      const int q = (tid + MPK_THREADS * j) >> 3;  // 8-column group within the pass
-      float v[8];
-      if (D.xll) {
-        bool ok = true;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ok &= ll_ok(w[jj][e], st);
-          v[e] = ll_f(w[jj][e]);
+      for (int i = 0; i < IG; ++i) {
+        if (ks[i] < 0) continue;
+        if (__ballot(v[i].y != st || v[i].w != st) != 0) continue;  // fetched again next round
+        need &= ~(1u << ks[i]);
+        const int u = wave + NWAVES * ks[i];
+        const int r = u & 7, q = (u >> 3) * 16 + qi;
+        float x0 = __uint_as_float(v[i].x), x1 = __uint_as_float(v[i].z);
+        if (D.has_norm) {
+          float ssq = fmaf(x0, x0, x1 * x1);
+          ssq += __shfl_xor(ssq, 1);
+          ssq += __shfl_xor(ssq, 2);
+          if (pc == 0) lds_write_u32_nw(sqb + (uint32_t)(r * 512 + q) * 4u, __float_as_uint(ssq));
+          x0 *= bf16lo(g[i]);
+          x1 *= bf16hi(g[i]);
         }
-        if (!ok) continue;
-      } else if (erow) {
-        unpack8(gldv<u32x4>(erow + 8 * q), v);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = gld(D.x + xrow + 8 * q + e);
+        const uint32_t hi = f2bf2(x0, x1);
+        const uint32_t lo = f2bf2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
+        const uint32_t a = xb + (uint32_t)(q >> 2) * 1024u + (uint32_t)(16 * (q & 3) + r) * 16u + 4u * pc;
+        lds_write_u32_nw(a, hi);
+        lds_write_u32_nw(a + 128u, lo);
       }
-      need &= ~(1u << j);
-      if (D.has_norm) {
-        float ssq = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ssq = fmaf(v[e], v[e], ssq);
-        lds_write_f32(sqb + (uint32_t)(b * 512 + q) * 4u, ssq);
-        float gf[8];
-        unpack8(gldv<u32x4>(D.gain + p * G8_PASS + 8 * q), gf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= gf[e];
-      }
-      u32x4 hi, lo;
-      split_hilo8(v, hi, lo);
-      const uint32_t a = xb + (uint32_t)(q >> 2) * 1024u + (uint32_t)(16 * (q & 3) + b) * 16u;
-      lds_write_u32x4(a, hi);
-      lds_write_u32x4(a + 128u, lo);
-      }
-      // the next round's loads are issued after this round's words are used
-      asm volatile("" ::: "memory");
     }
-    if (__ballot(need != 0) == 0) break;
+    if (need == 0) break;
     if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -2148,11 +2147,48 @@ DEV int stage_pass8(const mpk_kparams& P, cop& D, int p, char* smem, int tid, in
   return *lvi(smem, LDS_CTL) ? -1 : 0;
 }
 
-// 1 / rms of the 8 requests into LDS_INV (1 without a norm), from the items'
-// sums of squares: wave r < 8 adds request r's 512 item sums, 8 per lane in
-// column order, then across lanes in a fixed order.  Read back with a
-// per-lane request index, so the values live in LDS, not in a register
-// array.
+// Unstamped x (an embedding row, or a plain input tensor): item i = tid +
+// MPK_THREADS j covers row i % 8 and columns 8 (i / 8) .. + 7 of the pass.
+DEV int stage_pass8(const mpk_kparams& P, cop& D, int p, char* smem, int tid, int s, int task_id, Waiter& Wt,
+                    uint32_t st) {
+  if (D.xll) return stage_pass8_ll(P, D, p, smem, tid, s, task_id, Wt, st);
+  const uint32_t xb = lds_addr(smem) + LDS_X;
+  const uint32_t sqb = lds_addr(smem) + G8_SQ;
+  const int b = tid & 7;
+  const int64_t xrow = (int64_t)b * D.K + (int64_t)p * G8_PASS;
+  const uint16_t* erow = D.x_embed ? D.E + (int64_t)cur_token_v(smem, b) * D.K + (int64_t)p * G8_PASS : nullptr;
+#pragma unroll 1
+  for (int j = 0; j < G8_NI; ++j) {
+    if (tid + MPK_THREADS * j >= G8_ITEMS) continue;
+    const int q = (tid + MPK_THREADS * j) >> 3;  // 8-column group within the pass
+    float v[8];
+    if (erow) {
+      unpack8(gldv<u32x4>(erow + 8 * q), v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = gld(D.x + xrow + 8 * q + e);
+    }
+    if (D.has_norm) {
+      float ssq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ssq = fmaf(v[e], v[e], ssq);
+      lds_write_f32(sqb + (uint32_t)(b * 512 + q) * 4u, ssq);
+      float gf[8];
+      unpack8(gldv<u32x4>(D.gain + p * G8_PASS + 8 * q), gf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= gf[e];
+    }
+    u32x4 hi, lo;
+    split_hilo8(v, hi, lo);
+    const uint32_t a = xb + (uint32_t)(q >> 2) * 1024u + (uint32_t)(16 * (q & 3) + b) * 16u;
+    lds_write_u32x4(a, hi);
+    lds_write_u32x4(a + 128u, lo);
+  }
+  (void)s, (void)task_id, (void)Wt, (void)st;
+  lds_barrier();
+  return *lvi(smem, LDS_CTL) ? -1 : 0;
+}
+
 DEV void rms8(const mpk_kparams& P, cop& D, char* smem, int tid) {
   const int wave = tid >> 6, lane = tid & 63;
   float* inv = reinterpret_cast<float*>(smem + LDS_INV);
