@@ -2277,7 +2277,10 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
     lr = lr < nrows ? lr : nrows - 1;
     wrow[j] = (const gu32x4*)(const void*)(vrow_ptr(D, row0 + lr) + 8 * (lane >> 4) + wk * KSW * 32);
   }
-  // the ring: k-step u of this wave reads columns (u / KSW) G8_PASS + (u % KSW) 32 past wrow
+  // the ring: k-step u of this wave reads columns (u / KSW) G8_PASS + (u % KSW) 32 past wrow.
+  // Plain loads, not nontemporal: a row's 128-byte line is read as two 64-byte
+  // halves by consecutive k-steps, and the cache has to keep it in between
+  // (nontemporal measured 5.50 against 5.18 ms per batch-8 iteration).
   u32x4 ring[RG][NBW];
   auto issue = [&](int u, u32x4(&r)[NBW]) {
     const int pp = u / KSW, t = u - pp * KSW;
