@@ -1470,8 +1470,9 @@ DEV int argmax_task(const mpk_kparams& P, cop& D, char* smem, int tid, int s, in
 //     one dim per lane, as the A operand; P (hi / lo columns again) is the B
 //     operand, taken from the score layout with one exchange.
 //   K and V of a step land in LDS by global->LDS DMA (device scope): K as
-//     the score MFMA's A operand, 1 KB per 32 dims in lane order (a
-//     conflict-free 16-byte read per lane), V as rows (above).  at_ring(DH)
+//     whole rows (each DMA reads whole lines), its 16-byte segments placed by
+//     an XOR of segment and row so the A operand's reads (one row per lane
+//     column) are conflict-free, V as rows (above).  at_ring(DH)
 //     steps per wave are in flight.  With no loads into registers in the
 //     fold, every wait on them is explicit (the compiler's own waits on a
 //     register ring fall back to full drains across this loop).
@@ -1540,22 +1541,22 @@ DEV void lds_read_vt2(uint32_t a, u32x2& x, u32x2& y) {
   y = u32x2{v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
 }
 
-// The A operand of a step's scores: KS 16-byte reads at a, a + 1 KB, ...
+// The A operand of a step's scores: KS 16-byte reads at a[0 .. KS-1]
 // (early-clobber outputs, see lds_read_2f4)
 template <int KS>
-DEV void lds_read_k(uint32_t a, u32x4 (&k)[KS]) {
+DEV void lds_read_k(const uint32_t (&a)[KS], u32x4 (&k)[KS]) {
   static_assert(KS == 2 || KS == 4, "head_dim 64 or 128");
   if constexpr (KS == 2) {
-    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
                  : "=&v"(k[0]), "=&v"(k[1])
-                 : "v"(a)
+                 : "v"(a[0]), "v"(a[1])
                  : "memory");
   } else {
     asm volatile(
-        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
-        "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\ts_waitcnt lgkmcnt(0)"
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
         : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
-        : "v"(a)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
   }
 }
@@ -1568,6 +1569,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   constexpr int LPR = DH / 8;    // lanes per V row (16 bytes each)
   constexpr int OPS = KS + 16 / PPI;  // vector-memory operations per step (K and V DMAs)
   constexpr int AT_R = at_ring(DH), SLOT = at_slot(DH), KBYTES = DH * 32;
+  constexpr int KSEG = DH / 8, KRPC = 64 / KSEG;  // K: 16-byte segments per row, rows per 1 KB chunk
   static_assert(DB % 2 == 0, "V^T blocks are read in pairs");
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g4 = lane >> 4, cn = lane & 15;  // MFMA lane: row group, column
@@ -1610,12 +1612,17 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   // (K, then V)
   auto issue = [&](int k, uint32_t slot) {
     const int t0 = lo + 16 * k;
-    const int tk = t0 + cn;
-    const int rk = tk < hi ? tk : lo;
+    // K: chunk j holds rows KRPC j .. + KRPC - 1 whole (coalesced lines);
+    // lane l takes row KRPC j + l / KSEG, segment (l % KSEG) ^ (row % KSEG)
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(kc + (int64_t)rk * DH + 32 * kk + 8 * g4),
-                                       lds_ptr(slot + kk * 1024), 16, 0, CPOL_SC1 | CPOL_NT);
+    for (int kj = 0; kj < KS; ++kj) {
+      const int rr = KRPC * kj + lane / KSEG;
+      const int tk = t0 + rr;
+      const int rk = tk < hi ? tk : lo;
+      const int seg = (lane % KSEG) ^ (rr % KSEG);
+      __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(kc + (int64_t)rk * DH + 8 * seg),
+                                       lds_ptr(slot + kj * 1024), 16, 0, CPOL_SC1 | CPOL_NT);
+    }
 #pragma unroll
     for (int c4 = 0; c4 < 16 / PPI; ++c4) {
       const int tv = t0 + c4 * PPI + lane / LPR;
@@ -1842,7 +1849,14 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
         // t0 + 4 g4 + e of column cn; hi + lo columns
         const uint32_t slot = ring + sl * SLOT;
         u32x4 kr[KS];
-        lds_read_k<KS>(slot + lane * 16, kr);
+        // row cn, segment 4 kk + g4: chunk cn / KRPC, slot KSEG (cn % KRPC) +
+        // (segment ^ (cn % KSEG)) (the XOR keeps a 16-lane read conflict-free)
+        uint32_t ka[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          ka[kk] = slot + (uint32_t)(cn / KRPC) * 1024u +
+                   (uint32_t)(KSEG * (cn % KRPC) + ((4 * kk + g4) ^ (cn % KSEG))) * 16u;
+        lds_read_k<KS>(ka, kr);
         f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
