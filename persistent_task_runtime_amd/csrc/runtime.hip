@@ -1732,15 +1732,16 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
 #pragma unroll
   for (int h = 0; h < ATT_MAXG; ++h) cm[h] = -INFINITY, cl[h] = 0.f, co[h][0] = co[h][1] = 0.f;
   if (sched && owner) {
-    // K/V of p into the caches (the stores complete before the output is
-    // published; next iteration's readers are ordered after that output)
+    // K/V of p into the caches.  The stores complete before the output is
+    // published (next iteration's readers are ordered after that output):
+    // this wavefront waits for them after the merge area is written, before
+    // the barrier that precedes the publish, so the wait overlaps the fold.
     uint32_t* kdst = reinterpret_cast<uint32_t*>(kc + (int64_t)p * DH);
     uint32_t* vdst = reinterpret_cast<uint32_t*>(vc + (int64_t)p * DH);
     for (int i = lane; i < DH / 2; i += 64) {
       st_devu(kdst + i, kvrow[i]);
       st_devu(vdst + i, kvrow[DH / 2 + i]);
     }
-    vm_drain();
     const bool pl = lane < half;
     auto fold_pos = [&](float ka, float kb, float va, float vb) {
 #pragma unroll
@@ -1921,8 +1922,9 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
   }
-  // every wave's V ring is drained before the merge area over it is written
-  vm_drain_known();
+  // every worker wave's ring is drained before the merge area over it is
+  // written (the scheduler wave's K/V stores are waited for further down)
+  if (!sched) vm_drain_known();
   lds_barrier();
   if (*lvi(smem, LDS_CTL)) return -1;  // (a wait above ended the run)
   if (sched) {
@@ -1949,6 +1951,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       ml[wave * ATT_MAXG + cn] = l;
     }
   }
+  if (sched) vm_drain();  // the owner's K/V stores, before any output is published
   __syncthreads();
   // ---- merge the nine partials (eight waves, position p) per head ----
   const int stride = DH + 2;
