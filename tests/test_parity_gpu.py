@@ -374,13 +374,17 @@ def test_watchdog_and_abort_end_the_run(torch_dev):
     s.close()
 
 
-@pytest.mark.parametrize("ctx", [512, 10300])
+@pytest.mark.parametrize("ctx", [0, 1, 15, 16, 63, 64, 65, 512, 1000, 10300, 32768])
 def test_one_layer_matches_oracle(torch_dev, ctx):
     """One Qwen3-8B-shaped layer, KV cache pre-filled N(0,1) to ctx positions,
-    input h ~ N(0,1), one decode step at position ctx.  At 512 every
-    attention split is one step of 64 positions (register path); at 10300
-    the 32 splits hold 321-322 positions: six steps through the two-slot
-    LDS ring (it wraps twice), the last one ragged (1-2 positions)."""
+    input h ~ N(0,1), one decode step at position ctx.  The attention splits
+    fold the ctx cached positions in steps of 16 (position ctx itself is the
+    owner's own partial), cut into splits of at least 64 positions: 0 (an
+    empty cache: only the new position), 1, 15 and 16 (one step, ragged or
+    whole), 63 / 64 / 65 (the last step ragged, whole, a single position;
+    65 also takes a second split, merged by the owner), 512, 1000 (several
+    splits, ragged), 10300 (32 splits of 321-322 positions, the two-step ring
+    wrapping), 32768 (32 splits of 1024)."""
     import torch
     from persistent_task_runtime_amd import runner
 
