@@ -187,22 +187,33 @@ def test_batch8_full_model_against_oracle(rocm_device, full_weights_b8):
     _oracle_check(w, n, full_weights_b8, res, min_checked=25, min_written=10, chunk=2)
 
 
-def test_batch8_one_layer_matches_oracle(rocm_device):
+@pytest.mark.parametrize("positions", ["spread", "edges"])
+def test_batch8_one_layer_matches_oracle(rocm_device, positions):
     """One Qwen3-8B-shaped layer at batch 8, K/V pre-filled N(0,1) to 512
-    positions, each request at its own position (512 - 40 r), inputs h ~
-    N(0,1): every request's output h'' against the oracle's layer.  With one
-    layer there is no cascade, so this pins the MFMA linear tasks' precision
-    (bf16 hi/lo inputs: about 16 significant bits, fp32 sums)."""
+    positions, each request at its own position, inputs h ~ N(0,1): every
+    request's output h'' against the oracle's layer.  With one layer there is
+    no cascade, so this pins the MFMA linear tasks' precision (bf16 hi/lo
+    inputs: about 16 significant bits, fp32 sums).  "spread": positions
+    512 - 40 r; "edges": 0, 1, 15, 16, 63, 64, 65 and 500 in one batch (an
+    empty cache, ragged and whole attention steps, split boundaries).  The
+    error grows towards position 0 (measured 1.9e-3 there, 5e-5 at 500):
+    the new V row is rounded to bf16 from fp32 sums whose last bits differ
+    from the oracle's, and with few positions the output is that row itself
+    rather than an average over many."""
     import torch
     from persistent_task_runtime_amd import runner
 
     B = 8
     sh = synth.ModelShape(1, 4096, 32, 8, 128, 12288, 151936)
-    pos = np.array([512 - 40 * r for r in range(B)], np.int32)
-    w = synth.Workload("one_layer_b8", sh, B, 1, 514, pos + 1, pos, kv_prefill=512)
+    if positions == "spread":
+        pos = np.array([512 - 40 * r for r in range(B)], np.int32)
+    else:
+        pos = np.array([0, 1, 15, 16, 63, 64, 65, 500], np.int32)
+    n_fill = int(pos.max())  # positions below every request's own are pre-filled
+    w = synth.Workload("one_layer_b8", sh, B, 1, 514, pos + 1, pos, kv_prefill=n_fill)
     weights = synth.make_model(sh, seed=0, with_embedding=False)
     x = synth.normal_f32(0, "one_layer_b8.h", (B, sh.hidden), 1.0)
-    K, V = synth.make_kv_prefill(sh, B, w.max_seq, 512, seed=0)
+    K, V = synth.make_kv_prefill(sh, B, w.max_seq, n_fill, seed=0)
     model = runner.DeviceModel(sh, weights=weights)
     sess = runner.Session(w, model, kv=(K, V), x_in=torch.from_numpy(x).to("cuda:0"))
     sess.run(1)
@@ -211,11 +222,12 @@ def test_batch8_one_layer_matches_oracle(rocm_device):
     h_gpu = sess.x_out.cpu().numpy().astype(np.float64)
     om = oracle.Model(sh, weights)
     st = oracle.State(sh, np.zeros((B, 514), np.int32), pos, pos + 1, w.max_seq, K, V)
-    worst = 0.0
+    errs = []
     for r in range(B):
         h_or = oracle.layer(om, 0, st, r, int(pos[r]), x[r])
         err = float(np.max(np.abs(h_gpu[r] - h_or)))
-        worst = max(worst, err)
+        errs.append(err)
         assert err <= parity.LOGIT_TOL, "request %d: h max-abs error %g" % (r, err)
-    log("one layer at batch 8: h max-abs err %.3g (|h| max %.3g)" % (worst, float(np.abs(h_gpu).max())))
+    log("one layer at batch 8 (positions %s): h max-abs err per request %s (|h| max %.3g)"
+        % ([int(q) for q in pos], ["%.2g" % e for e in errs], float(np.abs(h_gpu).max())))
     sess.close()
