@@ -682,9 +682,21 @@ DEV void cursor_step(Cursor& C, int wave) {
 // words, an embedding row, or a plain input tensor), times the RMSNorm gain
 // when the operator normalises, and the tile's residual rows; inv receives
 // 1 / rms per request (1 without a norm) in every thread.  Every thread of
-// the workgroup takes part.  issue_ring() issues the calling wavefront's
-// first weight loads (ring_ops vector-memory operations: 8, 16 or 24): it is
-// called once, as early as the input wait allows.  Returns -1 on stop.
+// the workgroup takes part.  The calling wavefront's first weight loads
+// (ring_ops vector-memory operations: 8, 16 or 24) go out while the inputs
+// are awaited: issue_ring() issues the register ring's first group
+// (MPK_RING loads) with the first poll round; issue_step(i), i >= 1, issues
+// PF_STEP more (the rows of an LDS assignment unit), one step per later
+// round, the rest after the inputs arrive.  Returns -1 on stop.
+//
+// Why in steps: a CU's requests share its XCD's queue to memory with every
+// other CU of the XCD, and the producer's last output stores and this
+// task's polls wait behind whatever that queue holds.  Issuing the whole
+// prefetch at once (up to 192 KB per CU) keeps that queue several
+// microseconds deep exactly while the last inputs are on their way; a step
+// per round keeps the prefetch flowing while the polls stay near the head
+// of the queue.
+#define PF_STEP 4
 #define XCH 8    // stamped x words per thread per gather pass (register path)
 #define XGMAX 4  // chunks per wavefront whose gains and values stay in registers (DMA path)
 
@@ -722,9 +734,9 @@ DEV uint32_t lds_read_u32(uint32_t a) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
   return v;
 }
-template <int NB, class Ring>
+template <int NB, class Ring, class Step>
 DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, int s, int task_id,
-                     float (&inv)[NB], int ring_ops, Ring&& issue_ring) {
+                     float (&inv)[NB], int ring_ops, Ring&& issue_ring, Step&& issue_step) {
   float* xs = reinterpret_cast<float*>(smem + LDS_X);
   float* res = reinterpret_cast<float*>(smem + Lay<NB>::RES);
   float* red = reinterpret_cast<float*>(smem + LDS_RED);
@@ -752,7 +764,8 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
   const int land = Lay<NB>::RES + LDS_RES_BYTES;
   const int nchunk = (NE + 127) >> 7;
   const int nres = D.epi == MPK_EPI_RESID ? NB * T.nrows : 0;
-  const bool dma = dma_chunks<NB>(D) > 0;
+  // (the DMA path leaves the residual rows to the scheduler wavefront)
+  const bool dma = dma_chunks<NB>(D) > 0 && nres <= 64;
   // zero padding columns of x (K not a multiple of 512); no gather writes them
   for (int i = K + (worker ? tid : Kpad); i < Kpad; i += MPK_NW * 64)
 #pragma unroll
@@ -761,7 +774,7 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
   // path the scheduler wavefront's lanes take them: it streams no weights,
   // so waiting for a residual word (its count of loads in flight unknown to
   // the compiler: a full drain) waits behind no weight ring.
-  const bool rsched = dma && nres <= 64;
+  const bool rsched = dma;
   const int rt = rsched ? tid - MPK_NW * 64 : tid;
   bool need_r = false;
   float rv = 0.f;
@@ -821,73 +834,98 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       }
       need = __builtin_amdgcn_readfirstlane(need);
     };
-    bool first = true, published = false;
-    for (;;) {
-      if (first) {
-        // stale landing data must not pass the stamp check before the first
-        // round's DMA has landed: clear the landing stamps first
-        for (uint32_t m = need; m; m &= m - 1)
-          lds_write_u32x4(lb + land + (wave + MPK_NW * __builtin_ctz(m)) * 1024 + lane * 16, u32x4{0u, 0u, 0u, 0u});
-        lds_wait();
-      }
-      for (uint32_t m = need; m; m &= m - 1) {
-        const int c = wave + MPK_NW * __builtin_ctz(m);
-        __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.xll + c * 128 + lane * 2), lds_ptr(lb + land + c * 1024),
-                                         16, 0, CPOL_SC1);
-      }
-      uint64_t wr = 0;
-      if (need_r) wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
-      if (first) {
-        // the weights go out behind this round's words; wait for the words
-        // only (loads complete in issue order)
-        issue_ring();
-        // (ring group, and the rows of an LDS assignment unit)
-        if (worker && ring_ops == 3 * MPK_RING) vm_wait_known<3 * MPK_RING>();
-        else if (worker && ring_ops == 2 * MPK_RING) vm_wait_known<2 * MPK_RING>();
-        else if (worker) vm_wait_known<MPK_RING>();
-        // the gains are in LDS
-        if (D.has_norm) {
+    // Rounds: the first fetches every chunk; after a round that fetched
+    // every missing chunk, the next fetches only the lowest missing one (a
+    // probe: waiting wavefronts re-reading all their stale chunks every
+    // round would load the memory system with polls), and once a probe
+    // comes back current the next round fetches all that are still missing.
+    const int nsteps = worker ? 1 + (ring_ops - MPK_RING) / PF_STEP : 0;
+    int step = 0;
+    bool first = true, published = false, fetch_all = true;
+    if (worker) {
+      for (;;) {
+        if (first) {
+          // stale landing data must not pass the stamp check before the
+          // first round's DMA has landed: clear the landing stamps first
+          for (uint32_t m = need; m; m &= m - 1)
+            lds_write_u32x4(lb + land + (wave + MPK_NW * __builtin_ctz(m)) * 1024 + lane * 16, u32x4{0u, 0u, 0u, 0u});
+          lds_wait();
+        }
+        const uint32_t fetch = fetch_all ? need : (need & (0u - need));
+        for (uint32_t m = fetch; m; m &= m - 1) {
+          const int c = wave + MPK_NW * __builtin_ctz(m);
+          __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.xll + c * 128 + lane * 2),
+                                           lds_ptr(lb + land + c * 1024), 16, 0, CPOL_SC1);
+        }
+        // the next prefetch step goes out behind this round's words; wait
+        // for the words only (loads complete in issue order)
+        if (first) {
+          issue_ring();
+          step = 1;
+          vm_wait_known<MPK_RING>();
+        } else if (step < nsteps) {
+          issue_step(step);
+          ++step;
+          vm_wait_known<PF_STEP>();
+        } else {
+          vm_drain_known();
+        }
+        if (first && D.has_norm) {
+          // the gains are in LDS
 #pragma unroll
           for (int i = 0; i < XGMAX; ++i)
             if ((mine >> i) & 1u) gp[i] = lds_read_u32(gla + (wave + MPK_NW * i) * 256 + lane * 4);
         }
-      } else if (worker) {
-        vm_drain_known();
-      }
-      take(need);
-      if (D.has_norm && worker && need == 0 && !published) {
-        published = true;
-        // this wavefront's chunks are all in: its RMS partials, in chunk order
-        float ss[NB];
+        take(fetch);
+        fetch_all = fetch_all ? false : (need & fetch) == 0;
+        if (D.has_norm && need == 0 && !published) {
+          published = true;
+          // this wavefront's chunks are all in: its RMS partials, in chunk order
+          float ss[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+          for (int b = 0; b < NB; ++b) ss[b] = 0.f;
 #pragma unroll
-        for (int i = 0; i < XGMAX; ++i) {
-          if ((mine >> i) & 1u) {
-            const int b = (wave + MPK_NW * i) * 128 / K;
-            const float q = fmaf(xv[i].x, xv[i].x, xv[i].y * xv[i].y);
+          for (int i = 0; i < XGMAX; ++i) {
+            if ((mine >> i) & 1u) {
+              const int b = (wave + MPK_NW * i) * 128 / K;
+              const float q = fmaf(xv[i].x, xv[i].x, xv[i].y * xv[i].y);
 #pragma unroll
-            for (int bb = 0; bb < NB; ++bb) ss[bb] += bb == b ? q : 0.f;
+              for (int bb = 0; bb < NB; ++bb) ss[bb] += bb == b ? q : 0.f;
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const float t = wave_sum(ss[b]);
+            if (lane == 0) lds_write_f32(lb + LDS_RED + (uint32_t)(wave * 8 + b) * 4u, t);
           }
         }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float t = wave_sum(ss[b]);
-          if (lane == 0) lds_write_f32(lb + LDS_RED + (uint32_t)(wave * 8 + b) * 4u, t);
-        }
+        first = false;
+        if (need == 0) break;
+        if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+        __builtin_amdgcn_s_sleep(1);
       }
-      if (need_r && ll_ok(wr, st)) res[rt] = ll_f(wr), need_r = false;
-      if (first && rt >= 0 && rt < nres && !D.rll) res[rt] = rv;
-      first = false;
-      if (need == 0 && __ballot(need_r) == 0) break;
-      if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
-      __builtin_amdgcn_s_sleep(1);
+      // the prefetch steps not issued during the wait
+      for (step = max(step, 1); step < nsteps; ++step) issue_step(step);
+    } else {
+      // the scheduler wavefront: the tile's residual rows (its loads share
+      // no register with a worker's, so no wait of theirs covers them)
+      if (rt >= 0 && rt < nres && !D.rll) res[rt] = rv;
+      for (;;) {
+        if (need_r) {
+          const uint64_t wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
+          if (ll_ok(wr, st)) res[rt] = ll_f(wr), need_r = false;
+        }
+        if (__ballot(need_r) == 0) break;
+        if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
     }
     // every wavefront's inputs are in, or the workgroup stops
     lds_barrier();
     if (*lvi(smem, LDS_CTL)) return -1;
   } else {
-    issue_ring();
+    if (worker) issue_ring();
+    for (int i = 1; worker && i < 1 + (ring_ops - MPK_RING) / PF_STEP; ++i) issue_step(i);
     // RMSNorm gains of this thread's columns (k = tid + 512 j), loaded before
     // the inputs are awaited when K fits one gather pass
     const bool gains_early = K <= XCH * MPK_NW * 64;
@@ -1238,32 +1276,36 @@ DEV int gemv_task(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, ch
   float inv[NB];
   {
     const int ring_ops = MPK_RING + (lds_pending ? a_pre * MPK_RING : 0);
+    // First weight loads: the ring's first group, then (steps 1, 2, ...)
+    // the rows of the LDS assignment unit, PF_STEP units per step.
+    static_assert(MPK_RING % PF_STEP == 0, "LDS unit steps");
+    Cursor C2;  // the LDS assignment unit's rows
     const int rc = stage_inputs<NB>(P, D, T, smem, tid, s, task_id, inv, ring_ops, [&]() {
-      if (!sched && whole) {
+      if (sched) return;
+      if (whole) {
         // units 0..7 of the wavefront's first row (of W0 when it has none)
         const gu32x4* wp = unit_ptr(I, 0, lane);
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) b[j] = __builtin_nontemporal_load(wp + j * 64);
-      } else if (!sched) {
+      } else {
 #pragma unroll
         for (int j = 0; j < MPK_RING; ++j) {
           b[j] = load_unit(I, lane);
           cursor_step(I, wave);
         }
       }
-      if (!sched) {
-        if (lds_pending) {
-          Cursor C2 = I;
-          for (int rr = 0; rr < a_pre; ++rr) {
-            cursor_goto(C2, MPK_NW + wave, rr, 0, wave);
-            const gu32x4* wp = unit_ptr(C2, 0, lane);
-#pragma unroll
-            for (int u = 0; u < MPK_RING; ++u)
-              __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(wp + u * 64),
-                                               lds_ptr(pf + (rr * MPK_RING + u) * 1024), 16, 0, CPOL_NT);
-          }
-        }
+    }, [&](int step) {
+      if (sched) return;
+      const int q = (step - 1) * PF_STEP;  // first unit of the step within the LDS assignment unit
+      if (q % MPK_RING == 0) {
+        C2 = I;
+        cursor_goto(C2, MPK_NW + wave, q / MPK_RING, 0, wave);
       }
+      const gu32x4* wp = unit_ptr(C2, 0, lane);
+#pragma unroll
+      for (int u = 0; u < PF_STEP; ++u)
+        __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(wp + (q % MPK_RING + u) * 64),
+                                         lds_ptr(pf + (q + u) * 1024), 16, 0, CPOL_NT);
     });
     if (rc) return rc;
   }
