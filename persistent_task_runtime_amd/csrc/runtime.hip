@@ -689,13 +689,12 @@ DEV void cursor_step(Cursor& C, int wave) {
 // PF_STEP more (the rows of an LDS assignment unit), one step per later
 // round, the rest after the inputs arrive.  Returns -1 on stop.
 //
-// Why in steps: a CU's requests share its XCD's queue to memory with every
-// other CU of the XCD, and the producer's last output stores and this
-// task's polls wait behind whatever that queue holds.  Issuing the whole
-// prefetch at once (up to 192 KB per CU) keeps that queue several
-// microseconds deep exactly while the last inputs are on their way; a step
-// per round keeps the prefetch flowing while the polls stay near the head
-// of the queue.
+// Why in steps: every request a CU sends waits behind the requests already
+// queued to memory, its own and its XCD's.  Issuing the whole prefetch at
+// once (up to 192 KB per CU) made the polls of the tasks that start last
+// (their inputs all present at the first round) wait behind it; in steps
+// of 4 KB per wavefront the last inputs of an operator are staged about
+// 1 us earlier (2 to 8 KB steps measured the same).
 #define PF_STEP 4
 #define XCH 8    // stamped x words per thread per gather pass (register path)
 #define XGMAX 4  // chunks per wavefront whose gains and values stay in registers (DMA path)
@@ -834,14 +833,13 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       }
       need = __builtin_amdgcn_readfirstlane(need);
     };
-    // Rounds: the first fetches every chunk; after a round that fetched
-    // every missing chunk, the next fetches only the lowest missing one (a
-    // probe: waiting wavefronts re-reading all their stale chunks every
-    // round would load the memory system with polls), and once a probe
-    // comes back current the next round fetches all that are still missing.
+    // Every round fetches all of the wavefront's chunks still missing.
+    // (Probing one missing chunk per round and fetching the rest once it is
+    // current measured 0.6 % slower: the last inputs then take an extra
+    // round.)
     const int nsteps = worker ? 1 + (ring_ops - MPK_RING) / PF_STEP : 0;
     int step = 0;
-    bool first = true, published = false, fetch_all = true;
+    bool first = true, published = false;
     if (worker) {
       for (;;) {
         if (first) {
@@ -851,7 +849,7 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
             lds_write_u32x4(lb + land + (wave + MPK_NW * __builtin_ctz(m)) * 1024 + lane * 16, u32x4{0u, 0u, 0u, 0u});
           lds_wait();
         }
-        const uint32_t fetch = fetch_all ? need : (need & (0u - need));
+        const uint32_t fetch = need;
         for (uint32_t m = fetch; m; m &= m - 1) {
           const int c = wave + MPK_NW * __builtin_ctz(m);
           __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.xll + c * 128 + lane * 2),
@@ -877,7 +875,6 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
             if ((mine >> i) & 1u) gp[i] = lds_read_u32(gla + (wave + MPK_NW * i) * 256 + lane * 4);
         }
         take(fetch);
-        fetch_all = fetch_all ? false : (need & fetch) == 0;
         if (D.has_norm && need == 0 && !published) {
           published = true;
           // this wavefront's chunks are all in: its RMS partials, in chunk order
