@@ -56,6 +56,12 @@ typedef struct {
   const uint64_t* rll;    /* stamped residual words, or NULL */
   float* y;               /* plain output (tensor attached by the caller), or NULL */
   uint64_t* yll;          /* stamped output words */
+  /* Packed words (one per element: value rounded to 24 bits, 8-bit stamp)
+   * beside the stamped ones, for the input gathers of GEMV tasks: xpk, when
+   * set, holds the same input as xll; ypk receives the outputs also written
+   * to yll.  NULL when unused. */
+  const uint32_t* xpk;
+  uint32_t* ypk;
   const uint16_t* E; /* embedding rows for x_embed / res_embed */
   const uint16_t* qn;
   const uint16_t* kn;

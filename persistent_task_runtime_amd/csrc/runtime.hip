@@ -299,6 +299,9 @@ DEV void lds_write_f32(uint32_t a, float v) {
 DEV void lds_write_f32x2(uint32_t a, float2 v) {
   asm volatile("ds_write_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(v) : "memory");
 }
+DEV void lds_write_f32x4(uint32_t a, f32x4 v) {
+  asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(v) : "memory");
+}
 
 DEV int xperm(int k) { return (k & ~511) + ((k & 4) << 6) + (((k & 511) >> 3) << 2) + (k & 3); }
 
@@ -356,6 +359,31 @@ DEV uint64_t ld_ll(const uint64_t* p) {
 }
 DEV bool ll_ok(uint64_t w, uint32_t st) { return (uint32_t)(w >> 32) == st; }
 DEV float ll_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// Packed words: one 32-bit word per element, the fp32 value rounded to
+// nearest (ties to even) at 15 mantissa bits in the upper 24 bits and an
+// 8-bit stamp in the low byte, so an input gather moves half the bytes.  A
+// 32-bit device-scope store is single-copy atomic like the 64-bit one.  The
+// 8-bit stamp of iteration stamp st is st mod 255 + 1 (never 0: zeroed
+// buffers hold no current word).  Within a run it is enough: a consumer
+// reads its words every iteration, so a word it reads holds this
+// iteration's value or the previous one's (it saw that one, and every word
+// is rewritten once per iteration after all of the previous iteration's
+// reads of it), and consecutive stamps differ.  Across runs the host
+// clears the packed buffers before a run whenever a stale word could be 255
+// or more stamps old (see prepare_run).
+DEV uint32_t stamp8(uint32_t st) { return st % 255u + 1u; }
+DEV uint32_t pk_word(float v, uint32_t s8) {
+  const uint32_t u = __float_as_uint(v);
+  return ((u + 0x7fu + ((u >> 8) & 1u)) & 0xffffff00u) | s8;
+}
+DEV float pk_f(uint32_t w) { return __uint_as_float(w & 0xffffff00u); }
+DEV void st_pk(uint32_t* p, float v, uint32_t s8) {
+  __hip_atomic_store(p, pk_word(v, s8), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV uint32_t ld_pk(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Workgroup barrier over LDS data only: this wavefront's LDS operations are
 // complete first, its vector-memory loads need not be (the barrier that
@@ -699,22 +727,26 @@ DEV void cursor_step(Cursor& C, int wave) {
 #define XCH 8    // stamped x words per thread per gather pass (register path)
 #define XGMAX 4  // chunks per wavefront whose gains and values stay in registers (DMA path)
 
-// DMA staging: the landing zone beyond the residual rows (1 KB per chunk of
-// 128 stamped words) and, with a norm, the gains of each chunk's columns
-// (256 bytes per chunk), which go into the staged-x area beyond x when they
-// fit there (they are read before x is complete) and after the landing zone
-// otherwise.
+// DMA staging: the landing zone beyond the residual rows (1 KB per chunk:
+// 128 stamped words, or 256 packed words when the input has them) and, with
+// a norm, the gains of each chunk's columns (2 bytes per column), which go
+// into the staged-x area beyond x when they fit there (they are read before
+// x is complete) and after the landing zone otherwise.
+DEV int chunk_cols(cop& D) { return D.xpk ? 256 : 128; }
+template <int NB>
+DEV int n_chunks(cop& D) {
+  return (NB * D.K + chunk_cols(D) - 1) / chunk_cols(D);
+}
 template <int NB>
 DEV bool gains_in_xs(cop& D) {
   const int Kpad = ((D.K + 511) / 512) * 512;
-  const int nchunk = (NB * D.K + 127) >> 7;
-  return LDS_X + NB * Kpad * 4 + nchunk * 256 <= Lay<NB>::RES;
+  return LDS_X + NB * Kpad * 4 + n_chunks<NB>(D) * chunk_cols(D) * 2 <= Lay<NB>::RES;
 }
 // bytes the DMA staging occupies from the landing zone's start
 template <int NB>
 DEV int land_bytes(cop& D) {
-  const int nchunk = (NB * D.K + 127) >> 7;
-  return nchunk * 1024 + (D.has_norm && !gains_in_xs<NB>(D) ? nchunk * 256 : 0);
+  const int nchunk = n_chunks<NB>(D);
+  return nchunk * 1024 + (D.has_norm && !gains_in_xs<NB>(D) ? nchunk * chunk_cols(D) * 2 : 0);
 }
 
 // Chunks in which the task's x arrives by global->LDS DMA, or 0 when it
@@ -722,8 +754,8 @@ DEV int land_bytes(cop& D) {
 template <int NB>
 DEV int dma_chunks(cop& D) {
   const int land = Lay<NB>::RES + LDS_RES_BYTES;
-  const int nchunk = (NB * D.K + 127) >> 7;
-  const bool ok = D.xll && (D.K & 127) == 0 && land + land_bytes<NB>(D) <= Lay<NB>::TOTAL &&
+  const int nchunk = n_chunks<NB>(D);
+  const bool ok = D.xll && (D.K % chunk_cols(D)) == 0 && land + land_bytes<NB>(D) <= Lay<NB>::TOTAL &&
                   nchunk <= 32 * MPK_NW && (!D.has_norm || nchunk <= XGMAX * MPK_NW);
   return ok ? nchunk : 0;
 }
@@ -761,7 +793,7 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
   // publishes its RMS partial sums once all of them are in; the sums run in
   // a fixed order whatever the arrival order (deterministic).
   const int land = Lay<NB>::RES + LDS_RES_BYTES;
-  const int nchunk = (NE + 127) >> 7;
+  const int nchunk = n_chunks<NB>(D);
   const int nres = D.epi == MPK_EPI_RESID ? NB * T.nrows : 0;
   // (the DMA path leaves the residual rows to the scheduler wavefront)
   const bool dma = dma_chunks<NB>(D) > 0 && nres <= 64;
@@ -792,43 +824,74 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       for (int i = 0; wave + MPK_NW * i < nchunk; ++i) need |= 1u << i;
     need = __builtin_amdgcn_readfirstlane(need);
     const uint32_t mine = need;
-    // Gains of this lane's two columns in chunks i < XGMAX (packed bf16
-    // pair), by DMA into LDS after the landing zone: as loads into registers
-    // the compiler would wait for them with a full drain (the ring behind
-    // them has a path-dependent length).
+    // A chunk is 1 KB: 128 stamped words (2 per lane), or with packed
+    // words 256 of them (4 per lane).
+    const bool pk = D.xpk != nullptr;
+    const int cc = pk ? 256 : 128;  // columns per chunk
+    const uint32_t s8 = stamp8(st);
+    // Gains of this lane's columns in chunks i < XGMAX (packed bf16 pairs:
+    // one, or two with packed words at +256 bytes), by DMA into LDS after the
+    // landing zone: as loads into registers the compiler would wait for them
+    // with a full drain (the ring behind them has a path-dependent length).
     const uint32_t gla = lb + (gains_in_xs<NB>(D) ? LDS_X + NB * Kpad * 4 : land + nchunk * 1024);
-    uint32_t gp[XGMAX];
-    float2 xv[XGMAX];
+    uint32_t gp[XGMAX], gq[XGMAX];
+    float sq[XGMAX];  // a chunk's sum of squares (the RMS partials, in chunk order)
 #pragma unroll
     for (int i = 0; i < XGMAX; ++i) {
       const int c = wave + MPK_NW * i;
-      const int k = (c * 128) % K;
-      if (D.has_norm && ((mine >> i) & 1u))
-        __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.gain + k + lane * 2), lds_ptr(gla + c * 256), 4, 0, 0);
+      const int k = (c * cc) % K;
+      if (D.has_norm && ((mine >> i) & 1u)) {
+        const uint32_t gd = gla + c * cc * 2;
+        if (pk) {
+          __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.gain + k + lane * 4), lds_ptr(gd), 4, 0, 0);
+          __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.gain + k + lane * 4 + 2), lds_ptr(gd + 256), 4, 0,
+                                           0);
+        } else {
+          __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.gain + k + lane * 2), lds_ptr(gd), 4, 0, 0);
+        }
+      }
       gp[i] = 0u;
-      xv[i] = float2{0.f, 0.f};
+      gq[i] = 0u;
+      sq[i] = 0.f;
     }
     // Chunks of this wavefront in LDS (mask m): take each whose words are
-    // all current (with a norm the raw values also stay in registers for
-    // the RMS sums).
+    // all current.
     auto take = [&](uint32_t m) {
       for (; m; m &= m - 1) {
         const int i = __builtin_ctz(m), c = wave + MPK_NW * i;
         const u32x4 w = lds_read_u32x4(lb + land + c * 1024 + lane * 16);
-        if (__ballot(w.y != st || w.w != st) == 0) {
+        const bool stale = pk ? ((w.x & 0xffu) != s8) | ((w.y & 0xffu) != s8) | ((w.z & 0xffu) != s8) |
+                                    ((w.w & 0xffu) != s8)
+                              : (w.y != st) | (w.w != st);
+        if (__ballot(stale) == 0) {
           need &= ~(1u << i);
-          const int e = c * 128 + lane * 2;
+          const int e = c * cc + lane * (pk ? 4 : 2);
           const int b = e / K, k = e - b * K;
-          float2 x{__uint_as_float(w.x), __uint_as_float(w.z)};
-          if (D.has_norm) {
-            // i < XGMAX here (checked with dma)
-#pragma unroll
-            for (int j = 0; j < XGMAX; ++j)
-              if (j == i) xv[j] = x, x = float2{x.x * bf16lo(gp[j]), x.y * bf16hi(gp[j])};
-          }
+          const uint32_t xa = lb + LDS_X + (uint32_t)(b * Kpad + xperm(k)) * 4u;
           // (LDS stores written in asm: after a global->LDS DMA the
           // compiler puts a full vmcnt drain before its own LDS stores)
-          lds_write_f32x2(lb + LDS_X + (uint32_t)(b * Kpad + xperm(k)) * 4u, x);
+          if (pk) {
+            f32x4 x = f32x4{pk_f(w.x), pk_f(w.y), pk_f(w.z), pk_f(w.w)};
+            if (D.has_norm) {
+              // i < XGMAX here (checked with dma)
+              const float q = fmaf(x.x, x.x, x.y * x.y) + fmaf(x.z, x.z, x.w * x.w);
+#pragma unroll
+              for (int j = 0; j < XGMAX; ++j)
+                if (j == i)
+                  sq[j] = q, x = f32x4{x.x * bf16lo(gp[j]), x.y * bf16hi(gp[j]), x.z * bf16lo(gq[j]),
+                                       x.w * bf16hi(gq[j])};
+            }
+            lds_write_f32x4(xa, x);
+          } else {
+            float2 x{__uint_as_float(w.x), __uint_as_float(w.z)};
+            if (D.has_norm) {
+              const float q = fmaf(x.x, x.x, x.y * x.y);
+#pragma unroll
+              for (int j = 0; j < XGMAX; ++j)
+                if (j == i) sq[j] = q, x = float2{x.x * bf16lo(gp[j]), x.y * bf16hi(gp[j])};
+            }
+            lds_write_f32x2(xa, x);
+          }
         }
       }
       need = __builtin_amdgcn_readfirstlane(need);
@@ -852,8 +915,8 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
         const uint32_t fetch = need;
         for (uint32_t m = fetch; m; m &= m - 1) {
           const int c = wave + MPK_NW * __builtin_ctz(m);
-          __builtin_amdgcn_global_load_lds((gptr_t)(const void*)(D.xll + c * 128 + lane * 2),
-                                           lds_ptr(lb + land + c * 1024), 16, 0, CPOL_SC1);
+          const void* src = pk ? (const void*)(D.xpk + c * 256 + lane * 4) : (const void*)(D.xll + c * 128 + lane * 2);
+          __builtin_amdgcn_global_load_lds((gptr_t)src, lds_ptr(lb + land + c * 1024), 16, 0, CPOL_SC1);
         }
         // the next prefetch step goes out behind this round's words; wait
         // for the words only (loads complete in issue order)
@@ -871,8 +934,13 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
         if (first && D.has_norm) {
           // the gains are in LDS
 #pragma unroll
-          for (int i = 0; i < XGMAX; ++i)
-            if ((mine >> i) & 1u) gp[i] = lds_read_u32(gla + (wave + MPK_NW * i) * 256 + lane * 4);
+          for (int i = 0; i < XGMAX; ++i) {
+            if ((mine >> i) & 1u) {
+              const uint32_t gd = gla + (wave + MPK_NW * i) * cc * 2 + lane * 4;
+              gp[i] = lds_read_u32(gd);
+              if (pk) gq[i] = lds_read_u32(gd + 256);
+            }
+          }
         }
         take(fetch);
         if (D.has_norm && need == 0 && !published) {
@@ -884,10 +952,9 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
 #pragma unroll
           for (int i = 0; i < XGMAX; ++i) {
             if ((mine >> i) & 1u) {
-              const int b = (wave + MPK_NW * i) * 128 / K;
-              const float q = fmaf(xv[i].x, xv[i].x, xv[i].y * xv[i].y);
+              const int b = (wave + MPK_NW * i) * cc / K;
 #pragma unroll
-              for (int bb = 0; bb < NB; ++bb) ss[bb] += bb == b ? q : 0.f;
+              for (int bb = 0; bb < NB; ++bb) ss[bb] += bb == b ? sq[i] : 0.f;
             }
           }
 #pragma unroll
@@ -944,19 +1011,26 @@ DEV int stage_inputs(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid
       for (int j = 0; j < XCH; ++j)
         if (worker && base + tid + j * MPK_NW * 64 < NE) need |= 1u << j;
       if (D.xll) {
+        // packed words when the input has them (the same values the DMA
+        // path of a smaller batch reads)
+        const bool pk = D.xpk != nullptr;
+        const uint32_t s8 = stamp8(st);
         for (;;) {
           uint64_t v[XCH];
 #pragma unroll
-          for (int j = 0; j < XCH; ++j)
-            if ((need >> j) & 1u) v[j] = ld_ll(D.xll + base + tid + j * MPK_NW * 64);
+          for (int j = 0; j < XCH; ++j) {
+            const int e = base + tid + j * MPK_NW * 64;
+            if ((need >> j) & 1u) v[j] = pk ? (uint64_t)ld_pk(D.xpk + e) : ld_ll(D.xll + e);
+          }
           uint64_t wr = 0;
           if (need_r) wr = ld_ll(D.rll + (int64_t)rb * D.n_out + rrow);
           // (request, column) of element j, stepped from j = 0 without divisions
           int eb = (base + tid) / K, ek = base + tid - eb * K;
 #pragma unroll
           for (int j = 0; j < XCH; ++j) {
-            if (((need >> j) & 1u) && ll_ok(v[j], st)) {
-              xs[eb * Kpad + xperm(ek)] = ll_f(v[j]);
+            const bool cur = pk ? ((uint32_t)v[j] & 0xffu) == s8 : ll_ok(v[j], st);
+            if (((need >> j) & 1u) && cur) {
+              xs[eb * Kpad + xperm(ek)] = pk ? pk_f((uint32_t)v[j]) : ll_f(v[j]);
               need &= ~(1u << j);
             }
             ek += MPK_NW * 64;
@@ -1056,8 +1130,9 @@ DEV void unpack8(const u32x4 w, float (&f)[8]) {
 
 // Publish one output element: its stamped word for consumer tasks, and the
 // plain value when the tensor is attached by the caller.
-DEV void put_out(cop& D, int64_t i, float v, uint32_t st) {
+DEV void put_out(cop& D, int64_t i, float v, uint32_t st, uint32_t s8) {
   st_ll(D.yll + i, v, st);
+  if (D.ypk) st_pk(D.ypk + i, v, s8);
   if (D.y) gst(D.y + i, v);
 }
 
@@ -1164,9 +1239,10 @@ DEV void publish_tile(const mpk_kparams& P, cop& D, ctask& T, uint32_t lb, int s
   }
   const int n_out_tile = D.pairs ? T.nrows / 2 : T.nrows;
   const int orow0 = D.pairs ? T.row0 / 2 : T.row0;
+  const uint32_t s8 = stamp8(st);
   for (int i = tid; i < NB * n_out_tile; i += MPK_THREADS) {
     const int b = i / n_out_tile, ol = i - b * n_out_tile;
-    put_out(D, (int64_t)b * D.n_out + orow0 + ol, lds_read_f32(ob + (uint32_t)(b * n_out_tile + ol) * 4u), st);
+    put_out(D, (int64_t)b * D.n_out + orow0 + ol, lds_read_f32(ob + (uint32_t)(b * n_out_tile + ol) * 4u), st, s8);
   }
 }
 
@@ -2007,7 +2083,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
       L = fmaf(ml[w * ATT_MAXG + h], cw, L);
     }
     if (na == 1) {
-      put_out(D, o_base + idx, A / L, st);  // the whole context in one split
+      put_out(D, o_base + idx, A / L, st, stamp8(st));  // the whole context in one split
     } else {
       outs[h * stride + 2 + i] = A;
       if (i == 0) {
@@ -2074,7 +2150,7 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
     }
     __syncthreads();  // the gather area and the weights are reused by the next round
   }
-  if (mine_o) put_out(D, o_base + idx, O / L, st);
+  if (mine_o) put_out(D, o_base + idx, O / L, st, stamp8(st));
   return 0;
 }
 
@@ -2648,6 +2724,10 @@ struct mpk_exec_s {
   uint32_t* d_ticket_ctr = nullptr;  // trace ticket counter
   uint64_t* d_tok_ll = nullptr;      // [B] stamped next token
   std::vector<uint64_t*> ll_ptr;     // per tensor: stamped words of an operator output, or NULL
+  std::vector<uint32_t*> pk_ptr;     // per tensor: packed twin of ll_ptr, or NULL
+  std::pair<void*, size_t> pk_buf{nullptr, 0};  // the packed twins (one allocation; run scratch)
+  void* pk_buf_static = nullptr;     // the same in the static array
+  uint64_t pk_clear_base = 0;        // stamp counter when the own packed twins were last cleared
   float* d_rope = nullptr;
   mpk_dev_status* d_status = nullptr;
   int32_t* d_pos0 = nullptr;         // [MPK_MAX_BATCH] positions at launch (mpk_begin_run)
@@ -2732,6 +2812,11 @@ __global__ void mpk_fill_zero(uint4* p, int64_t n) {
 
 static std::mutex g_scratch_mu;
 static void* g_scratch_ptr[MPK_MAX_DEVICES];
+// Per device: the executable whose allocation-free run used the static
+// array last, and the stamp counter when its packed twins there were
+// cleared (see prepare_run).
+static const void* g_static_owner[MPK_MAX_DEVICES];
+static uint64_t g_static_pk_base[MPK_MAX_DEVICES];
 
 // Device address of the static array on `device` (current), cleared once:
 // stamped words left in it by earlier runs of this process carry stamps no
@@ -2759,16 +2844,24 @@ static int build_static_tables(mpk_exec_s* x, const std::vector<mpk_dev_op>& dop
   void* base = nullptr;
   int rc = static_scratch(x->device, &base);
   if (rc) return rc;
-  std::vector<std::pair<void*, char*>> map;  // own buffer -> static address
+  struct span {
+    const char* own;
+    size_t bytes;
+    char* at;  // static address
+  };
+  std::vector<span> map;  // own buffer -> static address
   size_t off = 0;
   for (const auto& b : x->scratch) {
-    map.emplace_back(b.first, (char*)base + off);
+    map.push_back({(const char*)b.first, b.second, (char*)base + off});
     off += (b.second + 255) & ~(size_t)255;
   }
+  // a pointer into a scratch buffer (its start or inside it, as the packed
+  // twins that share one allocation) moves with the buffer
   auto remap = [&](auto* p) -> decltype(p) {
     if (!p) return p;
+    const char* c = (const char*)(const void*)p;
     for (const auto& m : map)
-      if ((const void*)p == m.first) return reinterpret_cast<decltype(p)>(m.second);
+      if (c >= m.own && c < m.own + m.bytes) return reinterpret_cast<decltype(p)>(m.at + (c - m.own));
     return p;  // caller memory (attached tensors) is not scratch
   };
   std::vector<mpk_dev_op> sops = dops;
@@ -2777,6 +2870,8 @@ static int build_static_tables(mpk_exec_s* x, const std::vector<mpk_dev_op>& dop
     D.rll = remap(D.rll);
     D.yll = remap(D.yll);
     D.pll = remap(D.pll);
+    D.xpk = remap(D.xpk);
+    D.ypk = remap(D.ypk);
   }
   if ((rc = dalloc(x, &x->d_ops_static, sops.size() * sizeof(mpk_dev_op)))) return rc;
   HIPCHK(hipMemcpy(x->d_ops_static, sops.data(), sops.size() * sizeof(mpk_dev_op), hipMemcpyHostToDevice));
@@ -2787,8 +2882,12 @@ static int build_static_tables(mpk_exec_s* x, const std::vector<mpk_dev_op>& dop
   K.status = remap(x->kp.status);
   K.ticket_ctr = remap(x->kp.ticket_ctr);
   K.pos0 = remap(x->kp.pos0);
+  x->pk_buf_static = remap(x->pk_buf.first);
   return MPK_OK;
 }
+
+// Iteration stamps handed out so far in this process (see prepare_run).
+static std::atomic<uint64_t> g_stamps{0};
 
 static int64_t tensor_bytes(const mpk_tensor& t) {
   int64_t n = 1;
@@ -2851,6 +2950,40 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   // plain pointer of an attached tensor (NULL for library-owned stamped ones)
   auto PA = [&](int id) -> void* { return id >= 0 && g->tensors[id].dev_ptr ? x->tensor_ptr[id] : nullptr; };
   auto PL = [&](int id) -> uint64_t* { return id >= 0 ? x->ll_ptr[id] : nullptr; };
+  // Packed twins (mpk_dev_op::xpk) of the stamped outputs that GEMV tasks
+  // gather as their input x, batch 1 and 2 (the batch-8 staging reads the
+  // stamped words): the outputs of attention, linear + residual and
+  // gate/up operators, when the consumer's K is a multiple of 256.
+  // All twins share one allocation (cleared in one pass, see prepare_run).
+  x->pk_ptr.assign(NTEN, nullptr);
+  if (x->B <= 2) {
+    std::vector<size_t> off(NTEN, SIZE_MAX);
+    size_t total = 0;
+    for (size_t i = 0; i < g->ops.size(); ++i) {
+      const mpk_op& o = g->ops[i];
+      const bool gemv_in = o.kind == MPK_OP_RMSNORM_LINEAR || o.kind == MPK_OP_LINEAR_RESIDUAL ||
+                           o.kind == MPK_OP_RMSNORM_GATEUP || o.kind == MPK_OP_LMHEAD_ARGMAX;
+      if (!gemv_in || o.in[0] < 0 || !x->ll_ptr[o.in[0]] || g->dops[i].K % 256 != 0) continue;
+      const int src = o.in[0];
+      const int prod = g->producer[src];
+      if (prod < 0) continue;
+      const int pkind = g->ops[prod].kind;
+      if (pkind != MPK_OP_ATTENTION && pkind != MPK_OP_LINEAR_RESIDUAL && pkind != MPK_OP_RMSNORM_GATEUP) continue;
+      if (off[src] == SIZE_MAX) {
+        off[src] = total;
+        total += ((size_t)tensor_bytes(g->tensors[src]) + 255) & ~(size_t)255;  // one 32-bit word per f32
+      }
+    }
+    if (total) {
+      uint32_t* blk = nullptr;
+      if ((rc = salloc(x.get(), &blk, total))) return rc;
+      for (int t = 0; t < NTEN; ++t)
+        if (off[t] != SIZE_MAX) x->pk_ptr[t] = (uint32_t*)((char*)blk + off[t]);
+      x->pk_buf = {(void*)blk, total};
+    }
+  }
+  x->pk_clear_base = g_stamps.load();
+  auto PK = [&](int id) -> uint32_t* { return id >= 0 ? x->pk_ptr[id] : nullptr; };
   const mpk_model_cfg& M = g->model;
   const int B = x->B;
 
@@ -2871,6 +3004,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
       D.vc = (uint16_t*)P(o.in[4]);
       D.y = (float*)PA(o.out[0]);
       D.yll = PL(o.out[0]);
+      D.ypk = PK(o.out[0]);
       const int G = D.nq / D.nkv;
       if (G > ATT_MAXG) return mpk_fail(MPK_ERR_SHAPE, "more than 4 query heads per kv head");
       if (D.d != 64 && D.d != 128) return mpk_fail(MPK_ERR_SHAPE, "head_dim must be 64 or 128");
@@ -2879,6 +3013,7 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
     }
     const int e_in = o.in[0];
     D.xll = D.x_embed ? nullptr : PL(e_in);
+    D.xpk = D.x_embed ? nullptr : PK(e_in);
     D.x = D.x_embed || D.xll ? nullptr : (const float*)P(e_in);
     if (D.x_embed) D.E = (const uint16_t*)P(g->embed_src[e_in]);
     D.gain = D.has_norm ? (const uint16_t*)P(o.in[1]) : nullptr;
@@ -2898,11 +3033,13 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
       }
       D.y = (float*)PA(o.out[0]);
       D.yll = PL(o.out[0]);
+      D.ypk = PK(o.out[0]);
     } else if (o.kind == MPK_OP_RMSNORM_GATEUP) {
       D.W0 = (const uint16_t*)P(o.in[2]);
       D.W1 = (const uint16_t*)P(o.in[3]);
       D.y = (float*)PA(o.out[0]);
       D.yll = PL(o.out[0]);
+      D.ypk = PK(o.out[0]);
     } else {  // LM head
       D.W0 = (const uint16_t*)P(o.in[2]);
       D.logits = o.out[0] >= 0 ? (float*)P(o.out[0]) : nullptr;
@@ -2977,8 +3114,6 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   return MPK_OK;
 }
 
-// Iteration stamps handed out so far in this process (see prepare_run).
-static std::atomic<uint64_t> g_stamps{0};
 
 // Host checks, stamps and the start-of-run kernel of a run with parameters
 // K (x->kp, or x->kp_static for an allocation-free run).
@@ -3018,6 +3153,31 @@ static int prepare_run(mpk_exec_t x, int32_t n_iter, hipStream_t st, mpk_kparams
   if (base + (uint64_t)n_iter >= 0xffffffffull)
     return mpk_fail(MPK_ERR_STATE, "iteration stamps exhausted (2^32 iterations per process)");
   K.iter_base = (uint32_t)base;
+  // Packed twins carry 8-bit stamps (st mod 255 + 1).  A word left from an
+  // earlier run was written with a stamp in (clear base, base]; the first
+  // iteration's stamp base + 1 could match it only if it is 255 or more
+  // stamps old, so the twins are cleared (to stamp 0, never current) first
+  // when the counter has moved 255 or more since they were last cleared, and
+  // in the static array also when another executable used it last.
+  if (x->pk_buf.second) {
+    const bool stat = &K == &x->kp_static;
+    void* p = stat ? x->pk_buf_static : x->pk_buf.first;
+    bool clear;
+    if (stat) {
+      std::lock_guard<std::mutex> lk(g_scratch_mu);
+      clear = g_static_owner[x->device] != (const void*)x || base - g_static_pk_base[x->device] >= 255;
+      if (clear) g_static_owner[x->device] = x, g_static_pk_base[x->device] = base;
+    } else {
+      clear = base - x->pk_clear_base >= 255;
+      if (clear) x->pk_clear_base = base;
+    }
+    if (clear) {
+      const int64_t n16 = (int64_t)(x->pk_buf.second / 16);
+      hipLaunchKernelGGL(mpk_fill_zero, dim3((unsigned)std::min<int64_t>(1024, (n16 + 255) / 256)), dim3(256), 0, st,
+                         (uint4*)p, n16);
+      HIPCHK(hipGetLastError());
+    }
+  }
   // status, trace ticket, positions at launch, checks of step / tokens
   hipLaunchKernelGGL(mpk_begin_run, dim3(1), dim3(64), 0, st, K, (int)n_iter);
   HIPCHK(hipGetLastError());

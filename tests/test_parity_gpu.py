@@ -144,6 +144,47 @@ def test_run_to_run_deterministic_and_resumable(torch_dev):
     s1.close(), s2.close()
 
 
+@pytest.mark.parametrize("static", [False, True])
+def test_packed_words_cleared_before_their_stamps_repeat(torch_dev, static):
+    """The packed hand-over words (one 32-bit word per element: value and an
+    8-bit stamp, st mod 255 + 1) left by a run could look current to a later
+    run whose first stamp is 255 after theirs.  Exec A runs 6 iterations,
+    exec C exactly 254, so A's next first stamp has the same 8-bit stamp as
+    every packed word A left; A must clear them first (and in the static
+    array, where C's words overlay A's, because C used it last): its 6 + 24
+    iterations equal bitwise one run of 30 of a fresh exec."""
+    import torch
+    from persistent_task_runtime_amd import runner
+
+    w = synth.workload("tiny")
+    weights = synth.make_model(w.shape, seed=w.seed)
+    model = runner.DeviceModel(w.shape, weights=weights)
+    ref = runner.Session(w, model, logits_iters=30)
+    ref.run(30, static=static)
+    torch.cuda.synchronize()
+    ref.check_status()
+    l_ref = ref.logits.cpu().numpy().copy()
+    toks_ref = ref.tokens.cpu().numpy()
+    ref.close()
+    wc = synth.Workload("tiny_c", w.shape, 1, n_iter=254, tokens_width=300, prompt_len=w.prompt_len.copy(),
+                        step0=np.zeros(1, np.int32))
+    c = runner.Session(wc, model)
+    a = runner.Session(w, model, logits_iters=30)
+    a.run(6, static=static)
+    torch.cuda.synchronize()
+    l_a = a.logits.cpu().numpy()[:6].copy()
+    c.run(254, static=static)
+    torch.cuda.synchronize()
+    c.check_status()
+    a.run(24, static=static)
+    torch.cuda.synchronize()
+    a.check_status()
+    l_b = a.logits.cpu().numpy()[:24]
+    assert np.array_equal(np.concatenate([l_a, l_b]).view(np.uint32), l_ref.view(np.uint32))
+    assert np.array_equal(a.tokens.cpu().numpy(), toks_ref)
+    a.close(), c.close()
+
+
 def test_trace_orders_every_dependency(torch_dev):
     log("trace order")
     n = 6
