@@ -2278,11 +2278,94 @@ DEV int stage_pass8_ll(const mpk_kparams& P, cop& D, int p, char* smem, int tid,
   lds_barrier();
   return *lvi(smem, LDS_CTL) ? -1 : 0;
 }
+// Packed x (mpk_dev_op::xpk): 1 KB units of 256 columns, unit u = row u % 8,
+// columns 256 (u / 8) .. + 255 of the pass; a lane's 16 bytes are four
+// packed words (columns 4 l .. 4 l + 3), two lanes cover an item and write 8
+// bytes each of its hi and lo slots.  Same polling and the same sums of
+// squares (in the same association) as with stamped words.
+DEV void lds_write_u32x2_nw(uint32_t a, uint32_t v0, uint32_t v1) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(u32x2_t{v0, v1}) : "memory");
+}
+DEV int stage_pass8_pk(const mpk_kparams& P, cop& D, int p, char* smem, int tid, int s, int task_id, Waiter& Wt,
+                       uint32_t st) {
+  constexpr int NWAVES = MPK_THREADS / 64;
+  constexpr int NU = 8 * G8_PASS / 256;           // units per pass
+  constexpr int UPW = (NU + NWAVES - 1) / NWAVES;  // units per wavefront
+  constexpr int IG = 8;                            // units in flight per wavefront
+  static_assert(UPW <= 32, "a wavefront's units fit one mask");
+  const int wave = uni(tid >> 6), lane = tid & 63;
+  const int ph = lane & 1, qi = lane >> 1;  // this lane's half of its item, the item within the unit
+  const uint32_t xb = lds_addr(smem) + LDS_X, sqb = lds_addr(smem) + G8_SQ;
+  const int K = D.K;
+  const uint32_t s8 = stamp8(st);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(D.xpk), (short)0, 8 * K * 4, 0x00020000);
+  uint32_t need = 0;
+  for (int k = 0; k < UPW; ++k)
+    if (wave + NWAVES * k < NU) need |= 1u << k;
+  for (;;) {
+    uint32_t left = need;
+    while (left) {
+      int ks[IG];
+#pragma unroll
+      for (int i = 0; i < IG; ++i) {
+        ks[i] = left ? __builtin_ctz(left) : -1;
+        left &= left - 1;
+      }
+      u32x4 v[IG];
+      uint32_t g0[IG], g1[IG];
+#pragma unroll
+      for (int i = 0; i < IG; ++i) {
+        if (ks[i] >= 0) {
+          const int u = wave + NWAVES * ks[i];
+          const int col = p * G8_PASS + (u >> 3) * 256 + 4 * lane;
+          v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((u & 7) * K + col) * 4, 0, CPOL_SC1);
+          g0[i] = D.has_norm ? gldv<uint32_t>(D.gain + col) : 0u;
+          g1[i] = D.has_norm ? gldv<uint32_t>(D.gain + col + 2) : 0u;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < IG; ++i) {
+        if (ks[i] < 0) continue;
+        const bool stale = ((v[i].x & 0xffu) != s8) | ((v[i].y & 0xffu) != s8) | ((v[i].z & 0xffu) != s8) |
+                           ((v[i].w & 0xffu) != s8);
+        if (__ballot(stale) != 0) continue;  // fetched again next round
+        need &= ~(1u << ks[i]);
+        const int u = wave + NWAVES * ks[i];
+        const int r = u & 7, q = (u >> 3) * 32 + qi;
+        float x0 = pk_f(v[i].x), x1 = pk_f(v[i].y), x2 = pk_f(v[i].z), x3 = pk_f(v[i].w);
+        if (D.has_norm) {
+          float ssq = fmaf(x0, x0, x1 * x1) + fmaf(x2, x2, x3 * x3);
+          ssq += __shfl_xor(ssq, 1);
+          if (ph == 0) lds_write_u32_nw(sqb + (uint32_t)(r * 512 + q) * 4u, __float_as_uint(ssq));
+          x0 *= bf16lo(g0[i]);
+          x1 *= bf16hi(g0[i]);
+          x2 *= bf16lo(g1[i]);
+          x3 *= bf16hi(g1[i]);
+        }
+        const uint32_t h0 = f2bf2(x0, x1), h1 = f2bf2(x2, x3);
+        const uint32_t l0 = f2bf2(x0 - __uint_as_float(h0 << 16), x1 - __uint_as_float(h0 & 0xffff0000u));
+        const uint32_t l1 = f2bf2(x2 - __uint_as_float(h1 << 16), x3 - __uint_as_float(h1 & 0xffff0000u));
+        const uint32_t a = xb + (uint32_t)(q >> 2) * 1024u + (uint32_t)(16 * (q & 3) + r) * 16u + 8u * ph;
+        lds_write_u32x2_nw(a, h0, h1);
+        lds_write_u32x2_nw(a + 128u, l0, l1);
+      }
+    }
+    if (need == 0) break;
+    if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  lds_barrier();
+  return *lvi(smem, LDS_CTL) ? -1 : 0;
+}
+
 
 // Unstamped x (an embedding row, or a plain input tensor): item i = tid +
 // MPK_THREADS j covers row i % 8 and columns 8 (i / 8) .. + 7 of the pass.
 DEV int stage_pass8(const mpk_kparams& P, cop& D, int p, char* smem, int tid, int s, int task_id, Waiter& Wt,
                     uint32_t st) {
+  if (D.xpk) return stage_pass8_pk(P, D, p, smem, tid, s, task_id, Wt, st);
   if (D.xll) return stage_pass8_ll(P, D, p, smem, tid, s, task_id, Wt, st);
   const uint32_t xb = lds_addr(smem) + LDS_X;
   const uint32_t sqb = lds_addr(smem) + G8_SQ;
@@ -2951,12 +3034,11 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
   auto PA = [&](int id) -> void* { return id >= 0 && g->tensors[id].dev_ptr ? x->tensor_ptr[id] : nullptr; };
   auto PL = [&](int id) -> uint64_t* { return id >= 0 ? x->ll_ptr[id] : nullptr; };
   // Packed twins (mpk_dev_op::xpk) of the stamped outputs that GEMV tasks
-  // gather as their input x, batch 1 and 2 (the batch-8 staging reads the
-  // stamped words): the outputs of attention, linear + residual and
+  // gather as their input x: the outputs of attention, linear + residual and
   // gate/up operators, when the consumer's K is a multiple of 256.
   // All twins share one allocation (cleared in one pass, see prepare_run).
   x->pk_ptr.assign(NTEN, nullptr);
-  if (x->B <= 2) {
+  {
     std::vector<size_t> off(NTEN, SIZE_MAX);
     size_t total = 0;
     for (size_t i = 0; i < g->ops.size(); ++i) {
