@@ -2292,7 +2292,7 @@ DEV int stage_pass8_pk(const mpk_kparams& P, cop& D, int p, char* smem, int tid,
   constexpr int NWAVES = MPK_THREADS / 64;
   constexpr int NU = 8 * G8_PASS / 256;           // units per pass
   constexpr int UPW = (NU + NWAVES - 1) / NWAVES;  // units per wavefront
-  constexpr int IG = 8;                            // units in flight per wavefront
+  constexpr int IG = 4;                            // units in flight per wavefront (8 measured 1.6 % slower)
   static_assert(UPW <= 32, "a wavefront's units fit one mask");
   const int wave = uni(tid >> 6), lane = tid & 63;
   const int ph = lane & 1, qi = lane >> 1;  // this lane's half of its item, the item within the unit
@@ -2363,9 +2363,13 @@ DEV int stage_pass8_pk(const mpk_kparams& P, cop& D, int p, char* smem, int tid,
 
 // Unstamped x (an embedding row, or a plain input tensor): item i = tid +
 // MPK_THREADS j covers row i % 8 and columns 8 (i / 8) .. + 7 of the pass.
+// PK = false leaves the packed staging out of the caller: inlined into the
+// LM head's body it made that body's stream 25 % slower (the LM head at
+// batch 8 reads the stamped words).
+template <bool PK>
 DEV int stage_pass8(const mpk_kparams& P, cop& D, int p, char* smem, int tid, int s, int task_id, Waiter& Wt,
                     uint32_t st) {
-  if (D.xpk) return stage_pass8_pk(P, D, p, smem, tid, s, task_id, Wt, st);
+  if (PK && D.xpk) return stage_pass8_pk(P, D, p, smem, tid, s, task_id, Wt, st);
   if (D.xll) return stage_pass8_ll(P, D, p, smem, tid, s, task_id, Wt, st);
   const uint32_t xb = lds_addr(smem) + LDS_X;
   const uint32_t sqb = lds_addr(smem) + G8_SQ;
@@ -2513,7 +2517,7 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
     if (rc) return rc;
   }
   {
-    const int rc = stage_pass8(P, D, 0, smem, tid, s, task_id, Wt, st);
+    const int rc = stage_pass8<(NBW != 5)>(P, D, 0, smem, tid, s, task_id, Wt, st);
     if (rc) return rc;
   }
   if (!sched) {
@@ -2532,7 +2536,7 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
     if (u0 > 0 && u0 % KSW == 0) {
       // next pass: every wave is done with the staged one
       lds_barrier();
-      const int rc = stage_pass8(P, D, u0 / KSW, smem, tid, s, task_id, Wt, st);
+      const int rc = stage_pass8<(NBW != 5)>(P, D, u0 / KSW, smem, tid, s, task_id, Wt, st);
       if (rc) {
         vm_wait<0>();
         return rc;
@@ -3095,7 +3099,8 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
     }
     const int e_in = o.in[0];
     D.xll = D.x_embed ? nullptr : PL(e_in);
-    D.xpk = D.x_embed ? nullptr : PK(e_in);
+    // (the batch-8 LM head stages the stamped words: see stage_pass8)
+    D.xpk = D.x_embed || (B == 8 && o.kind == MPK_OP_LMHEAD_ARGMAX) ? nullptr : PK(e_in);
     D.x = D.x_embed || D.xll ? nullptr : (const float*)P(e_in);
     if (D.x_embed) D.E = (const uint16_t*)P(g->embed_src[e_in]);
     D.gain = D.has_norm ? (const uint16_t*)P(o.in[1]) : nullptr;
