@@ -217,7 +217,10 @@ int mpk_run_steps(mpk_exec_t exec, int32_t num_iterations, void* stream);
  * of the library per GPU, 64 MiB, held until the process ends; mpk_compile
  * prepares the executable's table into it.  Every call on a GPU shares that
  * GPU's array and leaves its contents behind: runs that overlap on one GPU
- * race (one allocation-free run per GPU at a time).  Stop requests stay per
+ * race (one allocation-free run per GPU at a time).  The packed input words
+ * (8-bit stamps) in it are cleared first, by a fill kernel on `stream`,
+ * whenever another executable used the array last or their stamps could
+ * repeat (no allocation either).  Stop requests stay per
  * executable.  Returns MPK_ERR_SHAPE (nothing launched) when the graph's run
  * scratch exceeds 64 MiB (e.g. batch 1 of the 8B shape at 32768 positions fits;
  * larger batches may not), MPK_ERR_INVALID_ARG for a traced graph (the trace
