@@ -706,8 +706,8 @@ DEV void cursor_step(Cursor& C, int wave) {
   }
 }
 
-// Stage the GEMV input into LDS: x (gathered from its producers' stamped
-// words, an embedding row, or a plain input tensor), times the RMSNorm gain
+// Stage the GEMV input into LDS: x (gathered from its producers' packed or
+// stamped words, an embedding row, or a plain input tensor), times the RMSNorm gain
 // when the operator normalises, and the tile's residual rows; inv receives
 // 1 / rms per request (1 without a norm) in every thread.  Every thread of
 // the workgroup takes part.  The calling wavefront's first weight loads
@@ -724,8 +724,8 @@ DEV void cursor_step(Cursor& C, int wave) {
 // of 4 KB per wavefront the last inputs of an operator are staged about
 // 1 us earlier (2 to 8 KB steps measured the same).
 #define PF_STEP 4
-#define XCH 8    // stamped x words per thread per gather pass (register path)
-#define XGMAX 4  // chunks per wavefront whose gains and values stay in registers (DMA path)
+#define XCH 8    // input words per thread per gather pass (register path)
+#define XGMAX 4  // chunks per wavefront whose gains and sums of squares stay in registers (DMA path)
 
 // DMA staging: the landing zone beyond the residual rows (1 KB per chunk:
 // 128 stamped words, or 256 packed words when the input has them) and, with
