@@ -367,6 +367,22 @@ int mpk_get_tensor_ptr(mpk_exec_t exec, int32_t tensor_id, void** dev_ptr);
 void mpk_destroy_exec(mpk_exec_t exec);
 void mpk_destroy_graph(mpk_graph_t graph);
 
+/* Measured HBM read ceiling (a measurement utility, not part of the decode
+ * path).  The decode step is bound by streaming its weights once per
+ * iteration (P3 "Why MPK?", Figure 1: weight bytes over memory bandwidth);
+ * this reads `bytes` at device address `src` once, asynchronously on
+ * `stream`, with the load form of the weight streams (16-byte nontemporal
+ * loads, 8 wavefronts per workgroup, 16 loads in flight per lane), on
+ * `workgroups` workgroups striding over 128 KiB units.  The
+ * caller times it (events on the same stream) to get the stream-read rate
+ * that a roofline fraction can also be stated against.  `sink` is one
+ * caller-owned device word that is written only if the XOR of all the data
+ * read equals a fixed constant (it keeps the loads live).  Errors:
+ * MPK_ERR_INVALID_ARG (NULL pointer, workgroups < 1), MPK_ERR_SHAPE (bytes
+ * not a positive multiple of 131072), MPK_ERR_ALIGN (src not 16-byte or sink
+ * not 4-byte aligned), MPK_ERR_HIP (launch failure). */
+int mpk_stream_read(const void* src, uint64_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
+
 /* Message of the last failure on the calling thread (never NULL). */
 const char* mpk_last_error(void);
 

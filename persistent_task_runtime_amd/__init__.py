@@ -162,6 +162,7 @@ def load_library(path: str = LIB_PATH):
         "mpk_get_tensor_ptr": (c_i32, [c_vp, c_i32, P(c_vp)]),
         "mpk_destroy_exec": (None, [c_vp]),
         "mpk_destroy_graph": (None, [c_vp]),
+        "mpk_stream_read": (c_i32, [c_vp, ctypes.c_uint64, c_i32, c_vp, c_vp]),
         "mpk_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -176,7 +177,7 @@ EXPORTED = ["mpk_build_graph", "mpk_compile", "mpk_run_steps", "mpk_run_steps_st
             "mpk_get_status", "mpk_set_abort", "mpk_read_trace", "mpk_get_graph_info",
             "mpk_sim_create", "mpk_simulate", "mpk_sim_read_meta", "mpk_sim_destroy",
             "mpk_check_run", "mpk_get_tensor_ptr", "mpk_destroy_exec", "mpk_destroy_graph",
-            "mpk_last_error"]
+            "mpk_stream_read", "mpk_last_error"]
 
 
 def mpk_last_error() -> str:
@@ -285,6 +286,10 @@ def mpk_get_tensor_ptr(exe: int, tensor_id: int) -> int:
     p = c_vp()
     _check(load_library().mpk_get_tensor_ptr(exe, tensor_id, ctypes.byref(p)))
     return p.value or 0
+
+
+def mpk_stream_read(src_ptr: int, nbytes: int, workgroups: int, sink_ptr: int, stream: int) -> None:
+    _check(load_library().mpk_stream_read(src_ptr, nbytes, workgroups, sink_ptr, stream))
 
 
 def mpk_destroy_exec(exe: int) -> None:

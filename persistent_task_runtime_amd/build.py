@@ -9,7 +9,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmpk.so")
 
-SOURCES = [os.path.join(CSRC, "builder.cpp"), os.path.join(CSRC, "simulate.cpp"), os.path.join(CSRC, "runtime.hip")]
+SOURCES = [os.path.join(CSRC, "builder.cpp"), os.path.join(CSRC, "simulate.cpp"), os.path.join(CSRC, "runtime.hip"),
+           os.path.join(CSRC, "stream_probe.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

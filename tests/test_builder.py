@@ -222,6 +222,20 @@ def test_null_arguments_are_rejected(lib):
     lib.mpk_destroy_graph(None)
 
 
+def test_stream_read_arguments_are_checked_before_any_launch(lib):
+    """The read-ceiling probe refuses bad arguments on the host (these calls
+    never reach the device: the addresses are never dereferenced)."""
+    fake, sink = 1 << 20, 1 << 21
+    unit = 128 * 1024
+    assert lib.mpk_stream_read(None, unit, 256, sink, None) == mpk.MPK_ERR_INVALID_ARG
+    assert lib.mpk_stream_read(fake, unit, 256, None, None) == mpk.MPK_ERR_INVALID_ARG
+    assert lib.mpk_stream_read(fake, unit, 0, sink, None) == mpk.MPK_ERR_INVALID_ARG
+    assert lib.mpk_stream_read(fake, 0, 256, sink, None) == mpk.MPK_ERR_SHAPE
+    assert lib.mpk_stream_read(fake, unit + 16, 256, sink, None) == mpk.MPK_ERR_SHAPE
+    assert "131072" in mpk.mpk_last_error()
+    assert lib.mpk_stream_read(fake + 8, unit, 256, sink, None) == mpk.MPK_ERR_ALIGN
+
+
 def test_single_layer_graph_without_embedding_or_lm_head():
     sh = synth.ModelShape(1, 4096, 32, 8, 128, 12288, 151936)
     g, spec = build(sh, tokens_width=514, max_seq=513, with_embedding=False, with_lm_head=False)
