@@ -326,7 +326,9 @@ extern "C" int mpk_simulate(mpk_sim_t sim, const mpk_sim_cfg* cfg, mpk_trace_rec
           const int p = pos0[r] + s, nf = p;
           const int na = std::max(1, std::min(NS, (nf + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT));
           if (c < na) {
-            const int lo = (int)((int64_t)c * nf / na), hi = (int)((int64_t)(c + 1) * nf / na);
+            // the owner folds a quarter of another split's share
+            const int64_t den = 4 * (int64_t)na - 3;
+            const int lo = (int)(4 * (int64_t)c * nf / den), hi = c == na - 1 ? nf : (int)(4 * (int64_t)(c + 1) * nf / den);
             const bool owner = c == na - 1;
             // q of the group's heads, k and v of kv head j
             Words& X = sim->tensor_words[O.in[0]];
