@@ -516,6 +516,58 @@ def test_full_model_prompt_and_generated_tokens(torch_dev, full_weights):
 
 
 @pytest.mark.timeout(900)
+def test_benchmark_launch_plan_end_of_generation(torch_dev, full_weights):
+    """The benchmark's own plan at full size: the 39-token prompt through the
+    one-launch-per-operator path, then the 512 generated tokens as eight
+    persistent launches of 64 iterations.  Sampled outputs the oracle
+    computes one by one: the last six iterations (positions 544-549, the
+    end of the eighth launch) against the oracle teacher-forced on the GPU's
+    tokens, with the GPU's own K/V rows of positions 0-543 as its cache;
+    step, the prompt slots and the slots past the last one written are
+    checked whole, and every generated id is a vocabulary id."""
+    import torch
+    from persistent_task_runtime_amd import runner
+
+    sh = synth.QWEN3_8B
+    P, K, L, n_chk = 39, 512, 64, 6
+    n_prompt = P - 1
+    total = n_prompt + K
+    width = total + 2
+    w = synth.Workload("qwen3_8b", sh, 1, n_iter=total, tokens_width=width, prompt_len=np.array([P], np.int32),
+                       step0=np.zeros(1, np.int32))
+    log("benchmark plan: uploading")
+    model = runner.DeviceModel(sh, weights=full_weights)
+    sess = runner.Session(w, model, max_seq=width, logits_iters=L)
+    sess.run(n_prompt, per_op=True)
+    torch.cuda.synchronize()
+    sess.check_status()
+    for i in range(K // L):
+        log("benchmark plan: launch %d of %d iterations" % (i, L))
+        sess.run(L)
+    torch.cuda.synchronize()
+    sess.check_status()
+    tokens = sess.tokens.cpu().numpy()
+    step = sess.step.cpu().numpy()
+    logits = sess.logits.cpu().numpy()  # the last launch's iterations: positions total - L .. total - 1
+    p0 = total - n_chk
+    kv = []
+    for cache in (sess.kc, sess.vc):
+        a = np.stack([cache[l].cpu().numpy().view(np.uint16) for l in model.layer_ids])[:, :, :, :total]
+        a[:, :, :, p0:] = 0  # the oracle writes its own rows from p0 on
+        kv.append(np.ascontiguousarray(a))
+    sess.close()
+    del model
+    assert int(step[0]) == total
+    gen = tokens[0, P:total + 1]
+    assert ((gen >= 0) & (gen < sh.vocab)).all()
+    w_end = synth.Workload("qwen3_8b_end", sh, 1, n_iter=n_chk, tokens_width=width,
+                           prompt_len=np.array([P], np.int32), step0=np.array([p0], np.int32))
+    res = {"tokens": tokens, "step": step, "logits": logits[L - n_chk:]}
+    log("gpu done; oracle at positions %d-%d" % (p0, total - 1))
+    check_against_oracle(w_end, n_chk, full_weights, res, min_checked=1, min_written=1, kv=tuple(kv))
+
+
+@pytest.mark.timeout(900)
 def test_long_context_sampled_steps(torch_dev, full_weights):
     """The long-context configuration: the full model with each layer's K/V
     cache pre-filled N(0,1) to 32768 positions, decoding at positions
