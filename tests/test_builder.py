@@ -336,9 +336,33 @@ def test_rows_per_request_graph_and_run_rule():
     assert e.value.code == mpk.MPK_ERR_SHAPE
 
 
+def test_gemv_after_attention_avoids_merging_splits():
+    """Long context (K/V capacity past 32768 positions): the attention takes
+    all 256 workers (8 kv heads x 32 splits), the split that merges is each
+    group's last task (split 31), and the o projection's tiles stay off those
+    8 CUs (248 tiles of 16-17 rows), so none waits behind a merge."""
+    g, spec = build(synth.QWEN3_8B, B=1, tokens_width=32900, max_seq=32900)
+    try:
+        info, tasks, _, _, _ = info_arrays(g)
+        kinds = [o.kind for o in spec.ops]
+        attn_ops = [i for i, k in enumerate(kinds) if k == mpk.MPK_OP_ATTENTION]
+        for a in attn_ops:
+            at = [t for t in tasks if t.op == a]
+            assert len(at) == 256 and {t.split for t in at} == set(range(32))
+            owners = {t.worker for t in at if t.split == 31}
+            assert owners == {32 * j + 31 for j in range(8)}
+            o = [t for t in tasks if t.op == a + 1]
+            assert kinds[a + 1] == mpk.MPK_OP_LINEAR_RESIDUAL
+            assert len(o) == 248 and {t.nrows for t in o} == {16, 17} and sum(t.nrows for t in o) == 4096
+            assert not owners & {t.worker for t in o} and len({t.worker for t in o}) == 248
+    finally:
+        mpk.mpk_destroy_graph(g)
+
+
 def test_batch8_tiles_and_refusals():
     """Batch 8 (the MFMA linear tasks): the same row tiles as batch 1 (QKV 24
-    rows = two 16-row blocks, o / down 16, gate/up 48 pairs, LM head 593/594),
+    rows = two 16-row blocks, down 16, gate/up 48 pairs, LM head 593/594; o
+    off the merging splits' CUs),
     attention 8 requests x 8 kv heads x 4 splits = 256 tasks; input widths
     must be multiples of 4096 (the 256-wide tiny decoder is refused), and
     batch sizes other than 1, 2 and 8 are refused."""
@@ -352,11 +376,18 @@ def test_batch8_tiles_and_refusals():
                 rows.setdefault(kinds[t.op], set()).add(t.nrows)
         assert rows[mpk.MPK_OP_RMSNORM_LINEAR] == {24}
         assert rows[mpk.MPK_OP_RMSNORM_GATEUP] == {96}
-        assert rows[mpk.MPK_OP_LINEAR_RESIDUAL] == {16}
         assert rows[mpk.MPK_OP_LMHEAD_ARGMAX] == {593, 594}
         attn = [t for t in tasks if t.op == 2]
         assert len(attn) == 256 and {t.row0 for t in attn} == set(range(8))
         assert {t.split for t in attn} == {0, 1, 2, 3}
+        # o (after the attention) avoids the 64 merging splits' CUs: 192
+        # tiles of 21-22 rows; down keeps 256 tiles of 16
+        o_ops = {i for i, k in enumerate(kinds) if k == mpk.MPK_OP_LINEAR_RESIDUAL and kinds[i - 1] == mpk.MPK_OP_ATTENTION}
+        down_ops = {i for i, k in enumerate(kinds) if k == mpk.MPK_OP_LINEAR_RESIDUAL} - o_ops
+        assert {t.nrows for t in tasks if t.op in o_ops} == {21, 22}
+        assert {t.nrows for t in tasks if t.op in down_ops} == {16}
+        owners = {t.worker for t in attn if t.split == 3}
+        assert len(owners) == 64 and not owners & {t.worker for t in tasks if t.op in o_ops}
     finally:
         mpk.mpk_destroy_graph(g)
     g, _ = build(synth.workload("narrow8").shape, B=8, tokens_width=26, max_seq=26)
