@@ -187,6 +187,69 @@ def test_batch8_full_model_against_oracle(rocm_device, full_weights_b8):
     _oracle_check(w, n, full_weights_b8, res, min_checked=25, min_written=10, chunk=2)
 
 
+@pytest.mark.timeout(900)
+def test_batch8_benchmark_plan_end_of_generation(rocm_device, full_weights_b8):
+    """The batch-8 benchmark's own plan at full size: 8 requests with seeded
+    prompt lengths in [16, 512] (tokens [8, 4096]), each prompt ingested at
+    batch 1 into the batch-8 tensors, then 256 lockstep iterations as four
+    persistent launches of 64.  Sampled outputs the oracle computes one by
+    one: every request's last two iterations, against the oracle
+    teacher-forced on the GPU's tokens with the GPU's own K/V rows below
+    them; step, the prompt slots and the slots past the last one written
+    checked whole, every generated id a vocabulary id."""
+    import torch
+    from persistent_task_runtime_amd import runner
+
+    sh = synth.QWEN3_8B
+    w = synth.workload("qwen3_8b_b8")
+    P = w.prompt_len.astype(np.int64)
+    K, L, n_chk = 256, 64, 2
+    log("batch-8 benchmark plan: prompts %s" % list(P))
+    model = runner.DeviceModel(sh, weights=full_weights_b8)
+    sess = runner.Session(w, model, logits_iters=L)
+    sess.step.zero_()
+    for r in range(w.batch):
+        view = runner.RequestView(sess, r)
+        view.run(int(P[r]) - 1)
+        torch.cuda.synchronize()
+        code, it, task = view.exe.status()
+        assert code == 0, (r, code, it, task)
+        view.close()
+    step0 = sess.step.cpu().numpy().astype(np.int64)
+    assert np.array_equal(step0, P - 1)
+    for i in range(K // L):
+        log("batch-8 benchmark plan: launch %d of %d iterations" % (i, L))
+        sess.run(L)
+    torch.cuda.synchronize()
+    sess.check_status()
+    tokens = sess.tokens.cpu().numpy()
+    step = sess.step.cpu().numpy()
+    logits = sess.logits.cpu().numpy()  # the last launch's iterations
+    p_end = (step0 + K - n_chk).astype(np.int32)
+    kv = []
+    for cache in (sess.kc, sess.vc):
+        a = np.stack([cache[l].cpu().numpy().view(np.uint16) for l in model.layer_ids])  # [L][B][n_kv][S][d]
+        for r in range(w.batch):
+            a[:, r, :, int(p_end[r]):] = 0  # the oracle writes its own rows from there on
+        kv.append(np.ascontiguousarray(a))
+    S = sess.max_seq
+    sess.close()
+    del model
+    assert np.array_equal(step, step0 + K)
+    for r in range(w.batch):
+        gen = tokens[r, int(P[r]):int(P[r]) + K]
+        assert ((gen >= 0) & (gen < sh.vocab)).all()
+    log("gpu done; oracle at positions %s .. +%d" % (list(p_end), n_chk - 1))
+    om = oracle.Model(sh, full_weights_b8)
+    t0 = time.time()
+    ol, oam, omg = parity.teacher_forced(om, sh, tokens, p_end, n_chk, S, kv[0], kv[1], chunk=1, progress=log)
+    rep = parity.compare(synth.make_tokens(w), w.prompt_len, p_end, n_chk, logits[L - n_chk:], tokens, step,
+                         ol, oam, omg)
+    log("qwen3_8b_b8 end of generation: %s (oracle %.1f s)" % (rep, time.time() - t0))
+    assert rep.compared == w.batch * n_chk
+    assert rep.checked >= 4 and rep.checked_written >= 4, str(rep)
+
+
 @pytest.mark.parametrize("positions", ["spread", "edges"])
 def test_batch8_one_layer_matches_oracle(rocm_device, positions):
     """One Qwen3-8B-shaped layer at batch 8, K/V pre-filled N(0,1) to 512

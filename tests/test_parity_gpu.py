@@ -568,6 +568,58 @@ def test_benchmark_launch_plan_end_of_generation(torch_dev, full_weights):
 
 
 @pytest.mark.timeout(900)
+def test_long_context_benchmark_plan_end(torch_dev, full_weights):
+    """The long-context benchmark's own plan at full size: K/V pre-filled
+    N(0,1) to 32768 positions, 2 warm-up iterations, then two persistent
+    launches of 63 (positions 32770-32895).  Sampled outputs the oracle
+    computes one by one: the last six iterations (positions 32890-32895)
+    against the oracle teacher-forced on the GPU's tokens, with the GPU's own
+    K/V rows (the prefill and the rows the run wrote) as its cache; at least
+    one of them with a token decision (top-2 margin above 0.1)."""
+    import torch
+    from persistent_task_runtime_amd import runner
+
+    w = synth.workload("qwen3_8b_long")
+    sh = w.shape
+    L, n_chk = 63, 6
+    total = int(w.step0[0]) + 2 + 2 * L
+    log("long-context benchmark plan: uploading (K/V prefill per layer)")
+    model = runner.DeviceModel(sh, weights=full_weights)
+    sess = runner.Session(w, model, logits_iters=L)
+    sess.run(2)
+    for i in range(2):
+        log("long-context benchmark plan: launch %d of %d iterations" % (i, L))
+        sess.run(L)
+    torch.cuda.synchronize()
+    sess.check_status()
+    tokens = sess.tokens.cpu().numpy()
+    step = sess.step.cpu().numpy()
+    logits = sess.logits.cpu().numpy()  # the last launch's iterations
+    p0 = total - n_chk
+    kv = []
+    for cache in (sess.kc, sess.vc):
+        a = np.stack([cache[l].cpu().numpy().view(np.uint16) for l in model.layer_ids])
+        a[:, :, :, p0:] = 0  # the oracle writes its own rows from p0 on
+        kv.append(np.ascontiguousarray(a))
+    S = sess.max_seq
+    sess.close()
+    del model
+    assert int(step[0]) == total
+    gen = tokens[0, int(w.step0[0]) + 1:total + 1]
+    assert ((gen >= 0) & (gen < sh.vocab)).all()
+    log("gpu done; oracle at positions %d-%d" % (p0, total - 1))
+    om = oracle.Model(sh, full_weights)
+    t0 = time.time()
+    p0a = np.array([p0], np.int32)
+    ol, oam, omg = parity.teacher_forced(om, sh, tokens, p0a, n_chk, S, kv[0], kv[1], chunk=1, progress=log)
+    del kv
+    rep = parity.compare(synth.make_tokens(w), w.prompt_len, p0a, n_chk, logits[L - n_chk:], tokens, step,
+                         ol, oam, omg)
+    log("qwen3_8b_long end: %s (oracle %.1f s)" % (rep, time.time() - t0))
+    assert rep.compared == n_chk and rep.checked >= 1, str(rep)
+
+
+@pytest.mark.timeout(900)
 def test_long_context_sampled_steps(torch_dev, full_weights):
     """The long-context configuration: the full model with each layer's K/V
     cache pre-filled N(0,1) to 32768 positions, decoding at positions
