@@ -303,12 +303,21 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
           }
         }
         const int Wt = W - D.worker_base - n_avoid;  // workers this operator's tiles may use
-        int T = o.num_tiles > 0 ? o.num_tiles : std::max(1, std::min(Wt, U / min_units));
+        // Batch 8, linear + residual over several 4096-column passes (the
+        // down projection): split K, one pass per tile, so a CU gathers only
+        // its columns of the 8 rows' x (down: 128 KB instead of 384 KB, as
+        // much as its weights); each row group's last split merges.
+        D.ksplit = B == MPK_MAX_BATCH && o.kind == MPK_OP_LINEAR_RESIDUAL && !D.res_embed && K > 4096 &&
+                           K <= 3 * 4096 && K % 4096 == 0 && o.num_tiles <= 0 && !D.worker_base && !n_avoid
+                       ? K / 4096
+                       : 0;
+        const int ks = std::max(1, (int)D.ksplit);
+        int T = o.num_tiles > 0 ? o.num_tiles : std::max(1, std::min(Wt / ks, U / min_units));
         if (T > Wt || U / T < min_units)
           return mpk_fail(MPK_ERR_SHAPE, "op " + std::to_string(i) + ": " + std::to_string(U) +
                                              " rows cannot give " + std::to_string(T) +
                                              " tiles of >= " + std::to_string(min_units) + " rows");
-        D.ntiles = T;
+        D.ntiles = T * ks;  // T row groups, ks splits each
         const int tile_rows = ((U + T - 1) / T) * a;  // largest tile, virtual rows
         if (B == MPK_MAX_BATCH) {
           // batch 8 runs the MFMA bodies: x staged in LDS per 4096-column
@@ -494,9 +503,11 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
       } else {
         const int a = D.pairs ? 2 : 1;
         const int U = (D.N0 + D.N1 + D.N2) / a;
-        int u0 = (int)((int64_t)t * U / D.ntiles), u1 = (int)((int64_t)(t + 1) * U / D.ntiles);
+        const int ks = std::max(1, (int)D.ksplit), ng = D.ntiles / ks, grp = t / ks;
+        int u0 = (int)((int64_t)grp * U / ng), u1 = (int)((int64_t)(grp + 1) * U / ng);
         T.row0 = u0 * a;
         T.nrows = (u1 - u0) * a;
+        if (D.ksplit > 1) T.split = t % ks;
       }
       mpk_task_info I{};
       for (int k = 0; k < MPK_MAX_DEPS; ++k) I.dep_event[k] = I.dep_count[k] = I.dep_prev[k] = -1;

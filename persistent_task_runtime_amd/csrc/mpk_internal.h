@@ -45,7 +45,12 @@ typedef struct {
    * the tile into LDS (as many as fit beyond the input's landing zone) */
   int32_t worker_base;
   int32_t lds_pre;
-  int32_t pad0;
+  /* ksplit > 1 (batch-8 linear + residual with K = ksplit * 4096): tile t is
+   * row group t / ksplit over columns [4096 k, 4096 k + 4096), k = its split
+   * (t % ksplit); splits k < ksplit - 1 publish their partial sums as
+   * stamped words in pll [ksplit - 1][B][n_out], split ksplit - 1 adds them
+   * (in split order) to its own and applies the epilogue.  0: no split. */
+  int32_t ksplit;
   const float* x;         /* plain input (a graph input tensor), or NULL */
   const uint64_t* xll;    /* stamped input words (output of another operator), or NULL */
   const uint16_t* gain;
@@ -68,7 +73,8 @@ typedef struct {
   uint16_t* kc;
   uint16_t* vc;
   uint64_t* pll;     /* stamped attention split partials [B][nkv][nsplit][G][d + 2];
-                        LM head: per tile and request (value, row) */
+                        LM head: per tile and request (value, row);
+                        split-K linear: partial sums [ksplit - 1][B][n_out] */
   float* logits;     /* LM head: optional [iters][B][V] */
   int64_t logits_iters;
 } mpk_dev_op;

@@ -2480,6 +2480,61 @@ DEV int gather_resid8(const mpk_kparams& P, cop& D, ctask& T, char* smem, int ti
   return *lvi(smem, LDS_CTL) ? -1 : 0;
 }
 
+// Split K, the merging split: the other splits' partial sums of the outputs
+// this thread holds in LDS_OUT (the residuals gather_resid8 left there, same
+// element-to-thread map), polled as stamped words, then added to them as
+// resid + (p_0 + p_1 + ...) in split order.  Returns -1 on stop.
+#define G8_MAXPARTS 2  // splits that publish partials (ksplit <= 3)
+DEV int gather_parts8(const mpk_kparams& P, cop& D, ctask& T, char* smem, int tid, int s, int task_id, Waiter& Wt,
+                      uint32_t st, int n_out_tile) {
+  const int lane = tid & 63;
+  const uint32_t ob = lds_addr(smem) + LDS_OUT;
+  constexpr int PER = (8 * 128 + MPK_THREADS - 1) / MPK_THREADS;  // outputs per thread at most
+  const int np = D.ksplit - 1;
+  float pv[PER][G8_MAXPARTS];
+  uint32_t need = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+#pragma unroll
+    for (int c = 0; c < G8_MAXPARTS; ++c) {
+      pv[k][c] = 0.f;
+      if (tid + k * MPK_THREADS < 8 * n_out_tile && c < np) need |= 1u << (k * G8_MAXPARTS + c);
+    }
+  }
+  for (;;) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = tid + k * MPK_THREADS;
+      const int r = idx / n_out_tile, row = T.row0 + idx - r * n_out_tile;
+#pragma unroll
+      for (int c = 0; c < G8_MAXPARTS; ++c) {
+        if (!((need >> (k * G8_MAXPARTS + c)) & 1u)) continue;
+        const uint64_t w = ld_ll(D.pll + ((int64_t)(c * 8 + r) * D.n_out + row));
+        if (ll_ok(w, st)) {
+          pv[k][c] = ll_f(w);
+          need &= ~(1u << (k * G8_MAXPARTS + c));
+        }
+      }
+    }
+    if (__ballot(need != 0) == 0) break;
+    if (wave_watch(P, Wt, s, task_id, smem, lane)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = tid + k * MPK_THREADS;
+    if (idx >= 8 * n_out_tile) continue;
+    float sum = pv[k][0];
+#pragma unroll
+    for (int c = 1; c < G8_MAXPARTS; ++c)
+      if (c < np) sum += pv[k][c];
+    const uint32_t a = ob + (uint32_t)idx * 4u;
+    lds_write_f32(a, lds_read_f32(a) + sum);
+  }
+  lds_barrier();
+  return *lvi(smem, LDS_CTL) ? -1 : 0;
+}
+
 template <int NBW, int WK>
 DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, char* smem, int tid, bool sched) {
   constexpr int WR = MPK_NW / WK;       // row groups of waves
@@ -2495,7 +2550,9 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
   const int wr = wave / WK, wk = wave % WK;
   const int nrows = uni(T.nrows), row0 = uni(T.row0);
   const int nblk = (nrows + 15) >> 4;
-  const int npass = uni(D.K / G8_PASS);
+  // split K: this tile's one pass is pass kc of the row (kc = 0: all passes)
+  const int kc = D.ksplit > 1 ? uni(T.split) : 0;
+  const int npass = D.ksplit > 1 ? 1 : uni(D.K / G8_PASS);
   const int U = npass * KSW;  // this wave's k-steps over the task
   const uint32_t st = stamp_of(P, s);
   const uint32_t lb = lds_addr(smem);
@@ -2506,7 +2563,7 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
   for (int j = 0; j < NBW; ++j) {
     int lr = (wr + WR * j) * 16 + (lane & 15);
     lr = lr < nrows ? lr : nrows - 1;
-    wrow[j] = (const gu32x4*)(const void*)(vrow_ptr(D, row0 + lr) + 8 * (lane >> 4) + wk * KSW * 32);
+    wrow[j] = (const gu32x4*)(const void*)(vrow_ptr(D, row0 + lr) + kc * G8_PASS + 8 * (lane >> 4) + wk * KSW * 32);
   }
   // the ring: k-step u of this wave reads columns (u / KSW) G8_PASS + (u % KSW) 32 past wrow.
   // Plain loads, not nontemporal: a row's 128-byte line is read as two 64-byte
@@ -2529,7 +2586,7 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
     if (rc) return rc;
   }
   {
-    const int rc = stage_pass8<(NBW != 5)>(P, D, 0, smem, tid, s, task_id, Wt, st);
+    const int rc = stage_pass8<(NBW != 5)>(P, D, kc, smem, tid, s, task_id, Wt, st);
     if (rc) return rc;
   }
   if (!sched) {
@@ -2548,7 +2605,7 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
     if (u0 > 0 && u0 % KSW == 0) {
       // next pass: every wave is done with the staged one
       lds_barrier();
-      const int rc = stage_pass8<(NBW != 5)>(P, D, u0 / KSW, smem, tid, s, task_id, Wt, st);
+      const int rc = stage_pass8<(NBW != 5)>(P, D, kc + u0 / KSW, smem, tid, s, task_id, Wt, st);
       if (rc) {
         vm_wait<0>();
         return rc;
@@ -2631,16 +2688,25 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
   }
   __syncthreads();
   const int n_out_tile = D.pairs ? nrows / 2 : nrows;
-  if (D.epi == MPK_EPI_RESID) {
-    const int rc = gather_resid8(P, D, T, smem, tid, s, task_id, Wt, st, n_out_tile);
-    if (rc) return rc;
-  }
   // output o of the tile, request r: its rows' sums over the waves
   auto rowsum = [&](int lr, int r) {
     float v = 0.f;
     for (int k = 0; k < WK; ++k) v += red[((k * nblk + (lr >> 4)) * 16 + (lr & 15)) * 8 + r];
     return v;
   };
+  if (D.ksplit > 1 && kc < D.ksplit - 1) {
+    // a split that does not merge: its partial sums for the merging split
+    for (int idx = tid; idx < 8 * n_out_tile; idx += MPK_THREADS) {
+      const int r = idx / n_out_tile, o = idx - r * n_out_tile;
+      st_ll(D.pll + ((int64_t)(kc * 8 + r) * D.n_out + row0 + o), rowsum(o, r), st);
+    }
+    return 0;
+  }
+  if (D.epi == MPK_EPI_RESID) {
+    int rc = gather_resid8(P, D, T, smem, tid, s, task_id, Wt, st, n_out_tile);
+    if (!rc && D.ksplit > 1) rc = gather_parts8(P, D, T, smem, tid, s, task_id, Wt, st, n_out_tile);
+    if (rc) return rc;
+  }
   for (int idx = tid; idx < 8 * n_out_tile; idx += MPK_THREADS) {
     const int r = idx / n_out_tile, o = idx - r * n_out_tile;
     const uint32_t a = ob + (uint32_t)idx * 4u;
@@ -3133,6 +3199,10 @@ extern "C" int mpk_compile(mpk_graph_t g, int32_t device, mpk_exec_t* out) {
       D.y = (float*)PA(o.out[0]);
       D.yll = PL(o.out[0]);
       D.ypk = PK(o.out[0]);
+      if (D.ksplit > 1) {
+        if (D.ksplit - 1 > G8_MAXPARTS || B != 8) return mpk_fail(MPK_ERR_SHAPE, "split K beyond its limits");
+        if ((rc = salloc(x.get(), &D.pll, (size_t)(D.ksplit - 1) * B * D.n_out * 8))) return rc;
+      }
     } else if (o.kind == MPK_OP_RMSNORM_GATEUP) {
       D.W0 = (const uint16_t*)P(o.in[2]);
       D.W1 = (const uint16_t*)P(o.in[3]);

@@ -131,6 +131,8 @@ extern "C" int mpk_sim_create(mpk_graph_t g, const int32_t* step, const int32_t*
         s->kv_ver[i][k].store((int)(k % s->S) < kv_filled ? KV_PREFILLED : 0u, std::memory_order_relaxed);
     } else if (D.kind == MPK_TK_LMHEAD) {
       s->op_words[i].alloc((size_t)D.ntiles * s->B * 2);
+    } else if (D.kind == MPK_TK_GEMV && D.ksplit > 1) {
+      s->op_words[i].alloc((size_t)(D.ksplit - 1) * s->B * D.n_out);  // split-K partial sums
     }
   }
   s->tok.alloc(s->B);
@@ -293,10 +295,15 @@ extern "C" int mpk_simulate(mpk_sim_t sim, const mpk_sim_cfg* cfg, mpk_trace_rec
           if (D.x_embed || D.res_embed)
             for (int r = 0; r < B && ok; ++r) ok = token_of(r, pos0[r] + s, s, tid);
           const int xin = O.in[0];
+          // split K: the tile reads its own 4096 columns of each row's x
+          const bool split = D.ksplit > 1;
+          const bool merges = !split || T.split == D.ksplit - 1;
+          const size_t c0 = split ? (size_t)T.split * 4096 : 0, c1 = split ? c0 + 4096 : (size_t)D.K;
           if (ok && !D.x_embed && sim->tensor_words[xin].n)
             for (size_t i = 0; i < sim->tensor_words[xin].n && ok; ++i)
-              ok = take(sim->tensor_words[xin], (uint32_t)xin, i, st, tid, s, false);
-          if (ok && D.epi == MPK_EPI_RESID && !D.res_embed && sim->tensor_words[O.in[2]].n)
+              if (i % (size_t)D.K >= c0 && i % (size_t)D.K < c1)
+                ok = take(sim->tensor_words[xin], (uint32_t)xin, i, st, tid, s, false);
+          if (ok && merges && D.epi == MPK_EPI_RESID && !D.res_embed && sim->tensor_words[O.in[2]].n)
             for (int r = 0; r < B && ok; ++r)
               for (int row = T.row0; row < T.row0 + T.nrows && ok; ++row)
                 ok = take(sim->tensor_words[O.in[2]], (uint32_t)O.in[2], (size_t)r * D.n_out + row, st, tid, s,
@@ -308,7 +315,23 @@ extern "C" int mpk_simulate(mpk_sim_t sim, const mpk_sim_cfg* cfg, mpk_trace_rec
           // ---- outputs ----
           if (cfg->fault == MPK_SIM_FAULT_SKIP_WAIT && D.kind == MPK_TK_GEMV && D.epi == MPK_EPI_STORE && s == 1)
             sleep_us(200000);  // a late QKV producer: a consumer that does not wait reads the old words
-          if (T.kind == MPK_TK_LMHEAD) {
+          if (split && !merges) {
+            // a split that does not merge: its partial sums
+            for (int r = 0; r < B; ++r)
+              for (int row = T.row0; row < T.row0 + T.nrows; ++row)
+                put(sim->op_words[T.op], TAG_OP + T.op, ((size_t)T.split * B + r) * D.n_out + row, st);
+          } else if (split) {
+            // the merging split: the other splits' partial sums, then the outputs
+            for (int c = 0; c < D.ksplit - 1 && ok; ++c)
+              for (int r = 0; r < B && ok; ++r)
+                for (int row = T.row0; row < T.row0 + T.nrows && ok; ++row)
+                  ok = take(sim->op_words[T.op], TAG_OP + T.op, ((size_t)c * B + r) * D.n_out + row, st, tid, s,
+                            false);
+            if (!ok) return;
+            for (int r = 0; r < B; ++r)
+              for (int row = T.row0; row < T.row0 + T.nrows; ++row)
+                put(sim->tensor_words[O.out[0]], (uint32_t)O.out[0], (size_t)r * D.n_out + row, st);
+          } else if (T.kind == MPK_TK_LMHEAD) {
             if (!(cfg->fault == MPK_SIM_FAULT_DROP_PUBLISH && T.tile == 0))
               for (int r = 0; r < B; ++r)
                 for (int j = 0; j < 2; ++j)

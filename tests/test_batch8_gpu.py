@@ -294,3 +294,42 @@ def test_batch8_one_layer_matches_oracle(rocm_device, positions):
     log("one layer at batch 8 (positions %s): h max-abs err per request %s (|h| max %.3g)"
         % ([int(q) for q in pos], ["%.2g" % e for e in errs], float(np.abs(h_gpu).max())))
     sess.close()
+
+
+def test_batch8_split_k_layer_persistent_equals_per_op(rocm_device):
+    """The split-K down projection (FFN 12288: three 4096-column splits per
+    row group, the last one adding the others' partial sums in split order):
+    one Qwen3-8B-shaped layer at batch 8, each request at its own position.
+    The persistent kernel equals the one-launch-per-operator path and itself
+    on a second run, bit for bit (output h and the K/V rows written)."""
+    import torch
+    from persistent_task_runtime_amd import runner
+
+    B = 8
+    sh = synth.ModelShape(1, 4096, 32, 8, 128, 12288, 151936)
+    pos = np.array([300 - 30 * r for r in range(B)], np.int32)
+    n_fill = int(pos.max())
+    w = synth.Workload("split_k_b8", sh, B, 1, 514, pos + 1, pos, kv_prefill=n_fill)
+    weights = synth.make_model(sh, seed=0, with_embedding=False)
+    x = torch.from_numpy(synth.normal_f32(0, "split_k_b8.h", (B, sh.hidden), 1.0)).to("cuda:0")
+    K, V = synth.make_kv_prefill(sh, B, w.max_seq, n_fill, seed=0)
+    model = runner.DeviceModel(sh, weights=weights)
+    outs = []
+    for per_op in (False, True, False):
+        log("split-K layer at batch 8: %s" % ("per operator" if per_op else "persistent"))
+        sess = runner.Session(w, model, kv=(K, V), x_in=x)
+        if not outs:
+            info = mpk.mpk_get_graph_info(sess.exe.graph)
+            tasks = [info.tasks[i] for i in range(info.num_tasks)]
+            kinds = [o.kind for o in sess.exe.spec.ops]
+            down = [i for i, k in enumerate(kinds) if k == mpk.MPK_OP_LINEAR_RESIDUAL][-1]
+            assert {t.split for t in tasks if t.op == down} == {0, 1, 2}
+        sess.run(1, per_op=per_op)
+        torch.cuda.synchronize()
+        sess.check_status()
+        l = model.layer_ids[0]
+        outs.append((sess.x_out.cpu().numpy().view(np.uint32), sess.kc[l].cpu().numpy(), sess.vc[l].cpu().numpy()))
+        sess.close()
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert np.array_equal(a, b)

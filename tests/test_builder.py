@@ -360,9 +360,9 @@ def test_gemv_after_attention_avoids_merging_splits():
 
 
 def test_batch8_tiles_and_refusals():
-    """Batch 8 (the MFMA linear tasks): the same row tiles as batch 1 (QKV 24
-    rows = two 16-row blocks, down 16, gate/up 48 pairs, LM head 593/594; o
-    off the merging splits' CUs),
+    """Batch 8 (the MFMA linear tasks): the same row tiles as batch 1 for QKV
+    (24 rows = two 16-row blocks), gate/up (48 pairs) and the LM head
+    (593/594); o off the merging splits' CUs; down split in K three ways,
     attention 8 requests x 8 kv heads x 4 splits = 256 tasks; input widths
     must be multiples of 4096 (the 256-wide tiny decoder is refused), and
     batch sizes other than 1, 2 and 8 are refused."""
@@ -381,11 +381,20 @@ def test_batch8_tiles_and_refusals():
         assert len(attn) == 256 and {t.row0 for t in attn} == set(range(8))
         assert {t.split for t in attn} == {0, 1, 2, 3}
         # o (after the attention) avoids the 64 merging splits' CUs: 192
-        # tiles of 21-22 rows; down keeps 256 tiles of 16
+        # tiles of 21-22 rows; down (K = 12288) splits K in three: 85 row
+        # groups of 48-49 rows x splits 0, 1, 2 (one 4096-column pass each)
         o_ops = {i for i, k in enumerate(kinds) if k == mpk.MPK_OP_LINEAR_RESIDUAL and kinds[i - 1] == mpk.MPK_OP_ATTENTION}
         down_ops = {i for i, k in enumerate(kinds) if k == mpk.MPK_OP_LINEAR_RESIDUAL} - o_ops
         assert {t.nrows for t in tasks if t.op in o_ops} == {21, 22}
-        assert {t.nrows for t in tasks if t.op in down_ops} == {16}
+        assert {t.split for t in tasks if t.op in o_ops} == {-1}
+        for op in down_ops:
+            dt = [t for t in tasks if t.op == op]
+            assert len(dt) == 255 and {t.nrows for t in dt} == {48, 49}
+            groups = {}
+            for t in dt:
+                groups.setdefault((t.row0, t.nrows), []).append(t.split)
+            assert len(groups) == 85 and all(sorted(v) == [0, 1, 2] for v in groups.values())
+            assert sum(n for _, n in groups) == 4096 and len({t.worker for t in dt}) == 255
         owners = {t.worker for t in attn if t.split == 3}
         assert len(owners) == 64 and not owners & {t.worker for t in tasks if t.op in o_ops}
     finally:

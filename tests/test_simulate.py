@@ -139,3 +139,40 @@ def test_start_of_run_rule_applies(sim):
     with pytest.raises(mpk.MPKError) as e:
         _run(g, s, WIDTH, 10)
     assert e.value.code == mpk.MPK_ERR_SHAPE
+
+
+def test_batch8_split_k_graph_runs_under_jitter():
+    """Batch 8 with the down projection split in K (FFN 12288: three
+    4096-column splits per row group, the last one merging the others'
+    partial sums): one decoder layer on 256 CUs, 8 requests at their own
+    positions, three iterations under random per-task jitter.  Every task
+    runs once per iteration (the merging splits wait for the partials, none
+    takes a stale word), and step and tokens advance."""
+    sh = synth.ModelShape(1, 4096, 32, 8, 128, 12288, 4096)
+    B, width = 8, 40
+    g, spec = build(sh, B=B, num_cus=256, tokens_width=width, max_seq=width)
+    try:
+        info, tasks, _, _, _ = info_arrays(g)
+        kinds = [o.kind for o in spec.ops]
+        down = [i for i, k in enumerate(kinds) if k == mpk.MPK_OP_LINEAR_RESIDUAL][-1]
+        assert {t.split for t in tasks if t.op == down} == {0, 1, 2}
+        step = np.arange(10, 10 + B, dtype=np.int32)
+        toks = np.full((B, width), -1, np.int32)
+        for r in range(B):
+            toks[r, :step[r] + 1] = synth.uniform_ids(0, "sim8.%d" % r, int(step[r]) + 1, sh.vocab)
+        plen = step + 1
+        s = mpk.mpk_sim_create(g, step, toks, plen, kv_filled=int(step.max()))
+        try:
+            n = 3
+            tr = mpk.mpk_simulate(s, info.num_tasks, n, 500, seed=3, jitter_us=100,
+                                  timeout_ms=60000).reshape(n, info.num_tasks)
+            assert (tr["task"] == np.arange(info.num_tasks)[None, :]).all()
+            st, tk = mpk.mpk_sim_read_meta(s, B, width)
+            assert np.array_equal(st, step + n)
+            for r in range(B):
+                gen = tk[r, int(step[r]) + 1:int(step[r]) + n + 1]
+                assert ((gen >= 0) & (gen < sh.vocab)).all()
+        finally:
+            mpk.mpk_sim_destroy(s)
+    finally:
+        mpk.mpk_destroy_graph(g)
