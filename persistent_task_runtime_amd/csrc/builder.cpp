@@ -170,9 +170,6 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
   g->dops.assign(n_ops, mpk_dev_op{});
   std::vector<std::vector<int>> reads(n_ops);  // f32 activations read
   std::vector<int> reads_meta(n_ops, 0);
-  // avoid_attn[i] = the attention operator whose merging splits' CUs the
-  // tiles of GEMV i stay off (-1: none)
-  std::vector<int> avoid_attn(n_ops, -1);
   int lm_op = -1;
 
   auto set_producer = [&](int op, int t) -> int {
@@ -287,28 +284,19 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
         // A GEMV reading an attention output waits for the whole attention
         // phase, which occupies only the attention tasks' workers: its tiles
         // go to the other workers, which stream ahead meanwhile.
-        // Otherwise (the attention on most workers) its tiles stay off the
-        // CUs of the attention's merging splits (each group's last task),
-        // which finish after the other splits: a tile queued there could
-        // only start once the merge is done.
-        int n_avoid = 0;
         {
           const int xp = g->producer[o.in[0]];
           if (xp >= 0 && g->dops[xp].kind == MPK_TK_ATTN && g->dops[xp].ntiles <= W / 2 && o.num_tiles <= 0 &&
-              !D.pairs && K == 4096 && B == 1 && U / (W - g->dops[xp].ntiles) >= 2 * MPK_NW) {
+              !D.pairs && K == 4096 && B == 1 && U / (W - g->dops[xp].ntiles) >= 2 * MPK_NW)
             D.worker_base = g->dops[xp].ntiles;
-          } else if (xp >= 0 && g->dops[xp].kind == MPK_TK_ATTN && g->dops[xp].nsplit > 1 && o.num_tiles <= 0) {
-            avoid_attn[i] = xp;
-            n_avoid = g->dops[xp].ntiles / g->dops[xp].nsplit;
-          }
         }
-        const int Wt = W - D.worker_base - n_avoid;  // workers this operator's tiles may use
+        const int Wt = W - D.worker_base;  // workers this operator's tiles may use
         // Batch 8, linear + residual over several 4096-column passes (the
         // down projection): split K, one pass per tile, so a CU gathers only
         // its columns of the 8 rows' x (down: 128 KB instead of 384 KB, as
         // much as its weights); each row group's last split merges.
         D.ksplit = B == MPK_MAX_BATCH && o.kind == MPK_OP_LINEAR_RESIDUAL && !D.res_embed && K > 4096 &&
-                           K <= 3 * 4096 && K % 4096 == 0 && o.num_tiles <= 0 && !D.worker_base && !n_avoid
+                           K <= 3 * 4096 && K % 4096 == 0 && o.num_tiles <= 0 && !D.worker_base
                        ? K / 4096
                        : 0;
         const int ks = std::max(1, (int)D.ksplit);
@@ -472,13 +460,6 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
     g->op_first_task[i] = (int)g->tasks.size();
     if (!D.kind) continue;
     g->op_ntasks[i] = D.ntiles;
-    // workers a GEMV's tiles may use when they avoid the merging splits
-    std::vector<int> avail;
-    if (i < n_ops && avoid_attn[i] >= 0) {
-      const mpk_dev_op& A = g->dops[avoid_attn[i]];
-      for (int w = 0; w < W; ++w)
-        if (!(w < A.ntiles && w % A.nsplit == A.nsplit - 1)) avail.push_back(w);
-    }
     for (int t = 0; t < D.ntiles; ++t) {
       mpk_dev_task T{};
       T.kind = D.kind;
@@ -487,8 +468,7 @@ extern "C" int mpk_build_graph(const mpk_model_cfg* model, const mpk_launch_cfg*
       // attention tasks take workers 0, 1, ... (one each); other tiles spread
       // evenly over their workers
       T.worker = D.kind == MPK_TK_ATTN ? t
-                 : !avail.empty()        ? avail[((int64_t)t * (int64_t)avail.size()) / D.ntiles]
-                                         : D.worker_base + (int)(((int64_t)t * (W - D.worker_base)) / D.ntiles);
+                                       : D.worker_base + (int)(((int64_t)t * (W - D.worker_base)) / D.ntiles);
       T.split = -1;
       if (D.kind == MPK_TK_ATTN) {
         int per_req = D.nkv * D.nsplit;

@@ -1562,10 +1562,8 @@ DEV int argmax_task(const mpk_kparams& P, cop& D, char* smem, int tid, int s, in
 // of q and k, RoPE at the request's position p, K/V of p into the caches
 // (by the split that owns p), then softmax(q K^T) V over this split's
 // positions on MFMA, and one merge across the wavefronts.  The context
-// [0, p] is cut into na = min(nsplit, ceil((p + 1) / 64)) pieces: pieces
-// 0 .. na - 2 go to splits 0 .. na - 2, the last piece (a quarter of the
-// others' share) to split nsplit - 1, which owns p; the other splits have
-// nothing to do this iteration.  With one split the task writes
+// [0, p] is cut into na = min(nsplit, ceil((p + 1) / 64)) splits; splits
+// c >= na have nothing to do this iteration.  With one split the task writes
 // the attention output of the group's query heads; with several, splits
 // publish stamped partials (m, l, acc) and the split that owns p merges them
 // into the output.  Returns -1 on stop.
@@ -1699,19 +1697,9 @@ DEV int attn_task(const mpk_kparams& P, ctask& T, cop& D, char* smem, int tid, b
   const int p = cur_pos(smem, r);
   const int nf = p - off;
   const int na = max(1, min(NS, (nf + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT));
-  // the split that adds positions p - off .. p and merges is always the
-  // group's last task (NS - 1, whatever na is), so the graph builder knows
-  // its CU; it folds the context's last piece (piece na - 1), splits c <
-  // na - 1 piece c, the others have nothing to do this iteration (uniform
-  // over the workgroup)
-  const bool owner = c == NS - 1;
-  if (!owner && c >= na - 1) return 0;
-  const int ci = owner ? na - 1 : c;
-  // the owner's piece is a quarter of another split's (it merges after the
-  // others: with less to fold it is waiting when their partials land): piece
-  // ci < na - 1 starts at 4 ci nf / (4 na - 3), the owner's ends at nf
-  const int64_t den = 4 * (int64_t)na - 3;
-  const int lo = (int)((4 * (int64_t)ci * nf) / den), hi = owner ? nf : (int)((4 * (int64_t)(ci + 1) * nf) / den);
+  if (c >= na) return 0;  // uniform over the workgroup: nothing to do this iteration
+  const int lo = (int)(((int64_t)c * nf) / na), hi = (int)(((int64_t)(c + 1) * nf) / na);
+  const bool owner = c == na - 1;  // the split that adds positions p - off .. p and merges
   const uint32_t st = stamp_of(P, s);
   const uint32_t lb = lds_addr(smem);
   float* qs = reinterpret_cast<float*>(smem + LDS_X);  // [G][DH], scaled for base-2 scores

@@ -348,13 +348,9 @@ extern "C" int mpk_simulate(mpk_sim_t sim, const mpk_sim_cfg* cfg, mpk_trace_rec
           // adds p (the device's split rule)
           const int p = pos0[r] + s, nf = p;
           const int na = std::max(1, std::min(NS, (nf + MPK_ATTN_SPLIT - 1) / MPK_ATTN_SPLIT));
-          // the owner is always split NS - 1 and folds the last piece, a
-          // quarter of another split's; splits c < na - 1 fold piece c
-          const bool owner = c == NS - 1;
-          if (owner || c < na - 1) {
-            const int ci = owner ? na - 1 : c;
-            const int64_t den = 4 * (int64_t)na - 3;
-            const int lo = (int)(4 * (int64_t)ci * nf / den), hi = owner ? nf : (int)(4 * (int64_t)(ci + 1) * nf / den);
+          if (c < na) {
+            const int lo = (int)((int64_t)c * nf / na), hi = (int)((int64_t)(c + 1) * nf / na);
+            const bool owner = c == na - 1;
             // q of the group's heads, k and v of kv head j
             Words& X = sim->tensor_words[O.in[0]];
             const int qkv_w = (D.nq + 2 * D.nkv) * d;

@@ -232,6 +232,13 @@ class PromptChunks:
         s = torch.cuda.current_stream() if stream is None else stream
         self.exe.run(n_iter, s.cuda_stream)
 
+    def check_status(self):
+        """Raises MPKError if the last chunk run stopped on the device (after
+        the stream has been synchronised)."""
+        code, it, task = self.exe.status()
+        if code != 0:
+            raise mpk.MPKError(code, "chunk run: device status at iteration %d task %d" % (it, task))
+
     def close(self):
         self.exe.close()
 

@@ -336,33 +336,10 @@ def test_rows_per_request_graph_and_run_rule():
     assert e.value.code == mpk.MPK_ERR_SHAPE
 
 
-def test_gemv_after_attention_avoids_merging_splits():
-    """Long context (K/V capacity past 32768 positions): the attention takes
-    all 256 workers (8 kv heads x 32 splits), the split that merges is each
-    group's last task (split 31), and the o projection's tiles stay off those
-    8 CUs (248 tiles of 16-17 rows), so none waits behind a merge."""
-    g, spec = build(synth.QWEN3_8B, B=1, tokens_width=32900, max_seq=32900)
-    try:
-        info, tasks, _, _, _ = info_arrays(g)
-        kinds = [o.kind for o in spec.ops]
-        attn_ops = [i for i, k in enumerate(kinds) if k == mpk.MPK_OP_ATTENTION]
-        for a in attn_ops:
-            at = [t for t in tasks if t.op == a]
-            assert len(at) == 256 and {t.split for t in at} == set(range(32))
-            owners = {t.worker for t in at if t.split == 31}
-            assert owners == {32 * j + 31 for j in range(8)}
-            o = [t for t in tasks if t.op == a + 1]
-            assert kinds[a + 1] == mpk.MPK_OP_LINEAR_RESIDUAL
-            assert len(o) == 248 and {t.nrows for t in o} == {16, 17} and sum(t.nrows for t in o) == 4096
-            assert not owners & {t.worker for t in o} and len({t.worker for t in o}) == 248
-    finally:
-        mpk.mpk_destroy_graph(g)
-
-
 def test_batch8_tiles_and_refusals():
     """Batch 8 (the MFMA linear tasks): the same row tiles as batch 1 for QKV
-    (24 rows = two 16-row blocks), gate/up (48 pairs) and the LM head
-    (593/594); o off the merging splits' CUs; down split in K three ways,
+    (24 rows = two 16-row blocks), o (16), gate/up (48 pairs) and the LM head
+    (593/594); down split in K three ways,
     attention 8 requests x 8 kv heads x 4 splits = 256 tasks; input widths
     must be multiples of 4096 (the 256-wide tiny decoder is refused), and
     batch sizes other than 1, 2 and 8 are refused."""
@@ -380,12 +357,11 @@ def test_batch8_tiles_and_refusals():
         attn = [t for t in tasks if t.op == 2]
         assert len(attn) == 256 and {t.row0 for t in attn} == set(range(8))
         assert {t.split for t in attn} == {0, 1, 2, 3}
-        # o (after the attention) avoids the 64 merging splits' CUs: 192
-        # tiles of 21-22 rows; down (K = 12288) splits K in three: 85 row
-        # groups of 48-49 rows x splits 0, 1, 2 (one 4096-column pass each)
+        # o: 256 tiles of 16 rows; down (K = 12288) splits K in three: 85
+        # row groups of 48-49 rows x splits 0, 1, 2 (one 4096-column pass each)
         o_ops = {i for i, k in enumerate(kinds) if k == mpk.MPK_OP_LINEAR_RESIDUAL and kinds[i - 1] == mpk.MPK_OP_ATTENTION}
         down_ops = {i for i, k in enumerate(kinds) if k == mpk.MPK_OP_LINEAR_RESIDUAL} - o_ops
-        assert {t.nrows for t in tasks if t.op in o_ops} == {21, 22}
+        assert {t.nrows for t in tasks if t.op in o_ops} == {16}
         assert {t.split for t in tasks if t.op in o_ops} == {-1}
         for op in down_ops:
             dt = [t for t in tasks if t.op == op]
@@ -395,8 +371,6 @@ def test_batch8_tiles_and_refusals():
                 groups.setdefault((t.row0, t.nrows), []).append(t.split)
             assert len(groups) == 85 and all(sorted(v) == [0, 1, 2] for v in groups.values())
             assert sum(n for _, n in groups) == 4096 and len({t.worker for t in dt}) == 255
-        owners = {t.worker for t in attn if t.split == 3}
-        assert len(owners) == 64 and not owners & {t.worker for t in tasks if t.op in o_ops}
     finally:
         mpk.mpk_destroy_graph(g)
     g, _ = build(synth.workload("narrow8").shape, B=8, tokens_width=26, max_seq=26)
