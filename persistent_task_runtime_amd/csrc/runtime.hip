@@ -2538,9 +2538,10 @@ DEV int gemv8_body(const mpk_kparams& P, ctask& T, cop& D, int s, int task_id, c
   const int wr = wave / WK, wk = wave % WK;
   const int nrows = uni(T.nrows), row0 = uni(T.row0);
   const int nblk = (nrows + 15) >> 4;
-  // split K: this tile's one pass is pass kc of the row (kc = 0: all passes)
-  const int kc = D.ksplit > 1 ? uni(T.split) : 0;
-  const int npass = D.ksplit > 1 ? 1 : uni(D.K / G8_PASS);
+  // split K: this tile's one pass is pass kc of the row (kc = 0: all passes;
+  // never in the LM head's body, NBW = 5, which keeps its plain addressing)
+  const int kc = NBW != 5 && D.ksplit > 1 ? uni(T.split) : 0;
+  const int npass = NBW != 5 && D.ksplit > 1 ? 1 : uni(D.K / G8_PASS);
   const int U = npass * KSW;  // this wave's k-steps over the task
   const uint32_t st = stamp_of(P, s);
   const uint32_t lb = lds_addr(smem);
