@@ -488,8 +488,10 @@ class Executable:
         self.exe = self.graph = 0
         _live.discard(self)
 
-    def __del__(self):
-        if sys.is_finalizing():
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # (bound at definition: module globals may already be cleared when
+        # an executable is collected during interpreter shutdown)
+        if _finalizing():
             return
         try:
             self.close()
