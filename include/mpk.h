@@ -87,6 +87,13 @@ typedef struct {
  *     The launch still covers every CU (the pages' split of the chip). */
 enum { MPK_SCHED_CORESIDENT = 0, MPK_SCHED_DEDICATED = 1 };
 
+/* Launch parameters.  Three knobs a launch description could carry are fixed
+ * by the kernels instead, because the task bodies are written for them: the
+ * workgroup is 576 threads (eight worker wavefronts and one scheduler
+ * wavefront, one workgroup per CU through 156 KB of dynamic LDS), attention
+ * splits hold 64 positions at full use (the split count follows the KV
+ * capacity, mpk_graph_info shows the tasks), and timing jitter exists only in
+ * the host model of the protocol (mpk_sim_cfg.jitter_us). */
 typedef struct {
   int32_t num_cus;         /* CUs of the target device (0 = query device 0 at build time) */
   int32_t num_workers;     /* 0 = num_cus */
