@@ -202,7 +202,7 @@ def parse_args(argv=None):
                     help="skip the prompt-ingestion comparison (one position per iteration vs chunks of 8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for profiles)")
-    ap.add_argument("--workload", choices=("qwen3_8b", "long", "b8"), default="qwen3_8b",
+    ap.add_argument("--workload", choices=("qwen3_8b", "long", "b8", "tiny", "one_layer"), default="qwen3_8b",
                     help="long: the same model with each layer's K/V cache pre-filled N(0,1) to "
                          "32768 positions, 128 decode iterations from there (attention-heavy); "
                          "b8: batch 8, prompt lengths uniform in [16, 512] ingested per request, "
@@ -282,6 +282,10 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     if args.workload == "long":
         return bench_long(args)
+    if args.workload == "tiny":
+        return bench_tiny(args)
+    if args.workload == "one_layer":
+        return bench_one_layer(args)
     if args.workload == "b8":
         return bench_b8(args)
     sh = synth.QWEN3_8B
@@ -620,6 +624,163 @@ def bench_b8(args):
         "kernel": "mpk_persistent<8>", "launch_ms": round(sum(launch_ms) / len(launches), 4),
         "bound_ms_per_iteration": round(bound_ms, 5), "frac_of_bound": round(bound_ms / ms_it, 4),
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+
+def timed_runs(sess, n_iter: int, reps: int, restart, per_op: bool = False):
+    """reps launches of n_iter iterations, each after restart() (stream-ordered
+    copies, outside the events); durations in ms from HIP events on the launch
+    stream."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    out = []
+    for _ in range(reps):
+        restart()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sess.run(n_iter, per_op=per_op)
+        b.record(stream)
+        b.synchronize()
+        sess.check_status()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def bench_tiny(args):
+    """The tiny decoder (2 layers, hidden 256, 4 q / 2 kv heads of 64, FFN
+    768, vocab 1024; 39-id prompt and 32 greedy tokens): its whole workload,
+    70 decode iterations, as one persistent launch, repeated.  Its 3.7 MB of
+    weights stay in the last-level cache, so this measures the runtime's
+    latency per operator phase (12 phases per iteration: 2 layers x 5, the LM
+    head and the argmax), not bandwidth."""
+    import numpy as np
+
+    import synth
+    from persistent_task_runtime_amd import runner
+
+    w = synth.workload("tiny")
+    sh, n = w.shape, w.n_iter
+    weights = synth.make_model(sh, seed=w.seed, gains=w.gains)
+    model = runner.DeviceModel(sh, weights=weights)
+    sess = runner.Session(w, model)
+    toks0 = sess.tokens.clone()
+
+    def restart():
+        sess.step.zero_()
+        sess.tokens.copy_(toks0)
+
+    timed_runs(sess, n, 1, restart)  # warm-up
+    reps = 9
+    ms = sorted(timed_runs(sess, n, reps, restart))
+    ms_it = ms[reps // 2] / n
+    per_op = sorted(timed_runs(sess, n, 3, restart, per_op=True))[1] / n
+    phases = sh.layers * 5 + 2
+    alg = sum(iteration_bytes(sh, p) for p in range(n)) / n
+    achieved = alg / (ms_it / 1e3) / 1e9
+    log("tiny: %.4f ms/iteration (median of %d launches of %d), %.2f us per phase; one launch per operator "
+        "%.4f ms/iteration" % (ms_it, reps, n, ms_it * 1e3 / phases, per_op))
+    sess.close()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        om = oracle.Model(sh, weights)
+        st = oracle.State(sh, synth.make_tokens(w), w.step0, w.prompt_len, w.max_seq)
+        t1 = time.time()
+        oracle.decode(om, st, n, want_logits=False)
+        dt = time.time() - t1
+        cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+        cpu = {"value": dt / n * 1e3, "unit": "ms/iteration", "cores": cores, "kind": "oracle",
+               "sample": "the whole 70-iteration workload, fp64 C oracle, OpenMP over output rows"}
+    out = {
+        "metric": "ms/iteration decode latency (tiny 2-layer decoder) + us per operator phase",
+        "value": round(ms_it, 5), "unit": "ms/iteration", "n_gpus": 1, "steps": n * reps, "warmup": n,
+        "ms_per_step": round(ms_it, 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "tiny_2layer_prompt39_greedy32", "layers": sh.layers, "hidden": sh.hidden,
+                   "q_heads": sh.n_q, "kv_heads": sh.n_kv, "head_dim": sh.head_dim, "ffn": sh.ffn,
+                   "vocab": sh.vocab, "tied_lm_head": True, "batch": 1, "iterations_per_launch": n,
+                   "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None},
+        "note": "latency-bound: the weights stay in the last-level cache; us_per_phase is the figure of merit",
+        "phases_per_iteration": phases, "us_per_phase": round(ms_it * 1e3 / phases, 3),
+        "per_op_ms_per_iteration": round(per_op, 5), "speedup_vs_per_op": round(per_op / ms_it, 3),
+        "kernel": "mpk_persistent<1>", "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def layer_bytes(sh, p: int) -> int:
+    """Algorithmic HBM bytes of one decoder layer's decode step at position p
+    (batch 1): the layer's weights once, K/V rows 0 .. p - 1 read and row p
+    written."""
+    return sh.layer_weight_bytes() + sh.n_kv * sh.head_dim * 2 * 2 * (p + 1)
+
+
+def bench_one_layer(args):
+    """One Qwen3-8B-shaped decoder layer (hidden 4096, 32 q / 8 kv heads of
+    128, FFN 12288, bf16 weights), K/V pre-filled N(0,1) to 512 positions,
+    input h ~ N(0,1): the layer's decode step at positions 512 .. 575 as 64
+    iterations of one persistent launch (each iteration attends to the
+    positions before it and writes its own K/V row; the 385.9 MB of weights
+    exceed the 256 MB last-level cache and are streamed with nontemporal
+    loads, so every iteration reads them from HBM)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from persistent_task_runtime_amd import runner
+
+    sh = synth.ModelShape(1, 4096, 32, 8, 128, 12288, 151936)
+    n, p0 = 64, 512
+    w = synth.Workload("one_layer_bench", sh, 1, n, p0 + n + 2, np.array([p0 + 1], np.int32),
+                       np.array([p0], np.int32), kv_prefill=p0)
+    weights = synth.make_model(sh, seed=0, with_embedding=False)
+    x = torch.from_numpy(synth.normal_f32(0, "one_layer_bench.h", (1, sh.hidden), 1.0)).to("cuda:0")
+    K, V = synth.make_kv_prefill(sh, 1, w.max_seq, p0, seed=0)
+    model = runner.DeviceModel(sh, weights=weights)
+    sess = runner.Session(w, model, kv=(K, V), x_in=x)
+
+    def restart():  # no argmax in the graph: step stays at 512, every launch covers 512 .. 575
+        pass
+
+    timed_runs(sess, n, 1, restart)  # warm-up
+    reps = 5
+    ms = sorted(timed_runs(sess, n, reps, restart))
+    ms_med = ms[reps // 2]
+    us_it = ms_med * 1e3 / n
+    per_op = sorted(timed_runs(sess, n, 3, restart, per_op=True))[1] * 1e3 / n
+    alg = sum(layer_bytes(sh, p0 + i) for i in range(n))
+    achieved = alg / (ms_med / 1e3) / 1e9
+    bound_us = alg / n / (HBM_PEAK_GBS * 1e9) * 1e6
+    log("one layer: %.2f us/iteration (median of %d launches of %d), %.1f GB/s algorithmic (%.1f%% of %.0f "
+        "GB/s), bound %.2f us; one launch per operator %.2f us" % (us_it, reps, n, achieved,
+                                                               100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS,
+                                                               bound_us, per_op))
+    sess.close()
+    del sess, model
+    torch.cuda.synchronize()
+    ceiling = None if args.no_ceiling else stream_ceiling()
+    out = {
+        "metric": "us per decode step of one Qwen3-8B-shaped layer + % of HBM roofline",
+        "value": round(us_it, 3), "unit": "us/iteration", "n_gpus": 1, "steps": n * reps, "warmup": n,
+        "ms_per_step": round(us_it / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "qwen3_8b_one_layer_kv512", "hidden": sh.hidden, "q_heads": sh.n_q,
+                   "kv_heads": sh.n_kv, "head_dim": sh.head_dim, "ffn": sh.ffn, "batch": 1,
+                   "positions": [p0, p0 + n - 1], "iterations_per_launch": n,
+                   "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16, N(0,1) pre-filled to 512",
+                   "input": "h ~ N(0,1)"},
+        "roofline": with_ceiling({"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                                 ceiling),
+        "kernel": "mpk_persistent<1>", "bound_us_per_iteration": round(bound_us, 3),
+        "frac_of_bound": round(bound_us / us_it, 4), "per_op_us_per_iteration": round(per_op, 3),
+        "speedup_vs_per_op": round(per_op / us_it, 3), "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 

@@ -36,3 +36,19 @@ def test_driver_argv_parses_and_plans():
     assert sum(launches) == 512 and launches == [64] * 8
     # the committed traffic figure applies to 64-iteration launches
     assert launches[0] == bench.TRAFFIC["iters_per_launch"]
+
+
+def test_every_configuration_has_a_workload():
+    """The five configurations: tiny decoder, one layer, the full model at
+    batch 1 (default), batch 8 and long context."""
+    for wl in ("tiny", "one_layer", "qwen3_8b", "b8", "long"):
+        assert bench.parse_args(["--workload", wl]).workload == wl
+
+
+def test_one_layer_bytes_per_step():
+    import synth
+
+    sh = synth.ModelShape(1, 4096, 32, 8, 128, 12288, 151936)
+    # 385.9 MB of weights; K/V: 8 kv heads x 128 dims x bf16 x (K, V) per position
+    assert sh.layer_weight_bytes() == 2 * (4096 * 6144 + 4096 * 4096 + 3 * 12288 * 4096) + 2 * (2 * 4096 + 2 * 128)
+    assert bench.layer_bytes(sh, 512) - sh.layer_weight_bytes() == 513 * 8 * 128 * 4
