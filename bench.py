@@ -14,8 +14,8 @@ iterations through the one-launch-per-operator path (untimed, whatever
 --warmup says: the prompt is input, not the measured work), then the timed
 generating iterations as persistent launches of --launch-iters iterations
 (the last launch takes the remainder).  The timed region covers the whole
-configured generation: max(--steps, 512) tokens, so the driver's short
---steps still measures the 512-token workload; "steps" in the output is the
+configured generation: max(--steps, 512) tokens, so a short --steps
+(say 20) still measures the 512-token workload; "steps" in the output is the
 number of iterations actually timed.
 
 Prints one JSON line on stdout; progress goes to stderr.

@@ -1,4 +1,4 @@
-"""bench.py's launch planning under the driver's command line
+"""bench.py's launch planning under a short command line
 (``bench.py --gpus 1 --steps 20 --warmup 5``): any --steps is accepted, the
 timed region is the configured 512-token generation split into persistent
 launches (the last one takes the remainder), and the prompt is ingested
@@ -20,15 +20,15 @@ def test_plan_covers_every_iteration_with_a_remainder_launch():
         bench.plan_launches(0, 64)
 
 
-def test_driver_command_times_the_configured_generation():
-    # the driver's --steps 20 still times all 512 generated tokens
+def test_short_command_times_the_configured_generation():
+    # --steps 20 still times all 512 generated tokens
     assert bench.timed_tokens(20) == 512
     assert bench.timed_tokens(512) == 512
     assert bench.timed_tokens(600) == 600
     assert bench.plan_launches(bench.timed_tokens(20), 64) == [64] * 8
 
 
-def test_driver_argv_parses_and_plans():
+def test_short_argv_parses_and_plans():
     a = bench.parse_args(["--gpus", "1", "--steps", "20", "--warmup", "5"])
     assert (a.gpus, a.steps, a.warmup, a.workload) == (1, 20, 5, "qwen3_8b")
     K = bench.timed_tokens(a.steps)
