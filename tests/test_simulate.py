@@ -176,3 +176,41 @@ def test_batch8_split_k_graph_runs_under_jitter():
             mpk.mpk_sim_destroy(s)
     finally:
         mpk.mpk_destroy_graph(g)
+
+
+def test_batch2_hidden640_graph_runs_under_jitter():
+    """The decoder of the hidden-640 GPU parity case at batch 2 (10 q / 5 kv
+    heads, FFN 1920, 2 layers, 256 CUs): both requests from position 0 (prompts
+    of 12 and 9 ids), 24 iterations under random per-task jitter, then a second
+    launch on the same buffers with the stamp base advanced.  Every task runs
+    once per iteration with no stale word accepted, and step and the tokens
+    past each prompt advance."""
+    sh = synth.ModelShape(layers=2, hidden=640, n_q=10, n_kv=5, head_dim=64, ffn=1920, vocab=1024)
+    B, width = 2, 40
+    g, spec = build(sh, B=B, num_cus=256, tokens_width=width, max_seq=width)
+    try:
+        info = mpk.mpk_get_graph_info(g)
+        plen = np.array([12, 9], np.int32)
+        step = np.zeros(B, np.int32)
+        toks = np.full((B, width), -1, np.int32)
+        for r in range(B):
+            toks[r, :plen[r]] = synth.uniform_ids(0, "sim640.%d" % r, int(plen[r]), sh.vocab)
+        s = mpk.mpk_sim_create(g, step, toks, plen, kv_filled=0)
+        try:
+            base = 3000
+            for n, seed in ((24, 11), (8, 12)):
+                tr = mpk.mpk_simulate(s, info.num_tasks, n, base, seed=seed, jitter_us=60,
+                                      timeout_ms=60000).reshape(n, info.num_tasks)
+                assert (tr["task"] == np.arange(info.num_tasks)[None, :]).all()
+                base += n
+            st, tk = mpk.mpk_sim_read_meta(s, B, width)
+            assert np.array_equal(st, step + 32)
+            for r in range(B):
+                assert np.array_equal(tk[r, :plen[r]], toks[r, :plen[r]]), "prompt slots unchanged"
+                gen = tk[r, int(plen[r]):33]
+                assert ((gen >= 0) & (gen < sh.vocab)).all()
+                assert (tk[r, 33:] == -1).all()
+        finally:
+            mpk.mpk_sim_destroy(s)
+    finally:
+        mpk.mpk_destroy_graph(g)
