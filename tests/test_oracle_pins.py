@@ -424,3 +424,115 @@ def test_layer_wiring_from_pinned_components():
     gg, uu = f("wg") @ b, f("wu") @ b
     ref = h1 + f("wd") @ (gg * expit(gg) * uu)
     np.testing.assert_allclose(h, ref, rtol=1e-10, atol=1e-12)
+
+
+# ---- symmetries of the composed decoder --------------------------------------
+# Relabelling that the definition says cannot matter: FFN units, kv heads with
+# their query groups, query heads within a group, hidden dimensions.  The
+# whole multi-layer decoder must give the same logits (fp64; only the order of
+# a few sums changes).  A wrong GQA grouping, a transposed projection, a gain
+# applied to the wrong axis or gate/up paired with the wrong down column breaks
+# one of them.
+
+def _scaled(bits, k):
+    """bf16 bits times 2**k, exactly (only the exponent moves)."""
+    f = synth.bf16_bits_to_f32(bits).astype(np.float32) * np.float32(2.0 ** k)
+    out = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(synth.bf16_bits_to_f32(out), f)
+    return out
+
+
+def _mixing_model(shape, seed):
+    # sharper attention and a stronger FFN than N(0, 0.02) gives, so that the
+    # permutations act on a decoder far from linear
+    w = synth.make_model(shape, seed=seed, gains="random")
+    for l in range(shape.layers):
+        for key_, k in (("wq", 3), ("wk", 3), ("wg", 2), ("wu", 2), ("wo", 1), ("wd", 1)):
+            n = "l%d.%s" % (l, key_)
+            w[n] = _scaled(w[n], k)
+    return w
+
+
+def _prompt_logits(shape, w, seed, n=10):
+    prompt = synth.uniform_ids(seed, "sym", n, shape.vocab)
+    st = _tiny_state(shape, prompt, n + 2)
+    logits, _, _ = oracle.decode(oracle.Model(shape, w), st, n - 1)
+    return logits[:, 0]
+
+
+def _heads(a, d, order):
+    """Row blocks of d rows, taken in `order`."""
+    return np.ascontiguousarray(np.concatenate([a[h * d:(h + 1) * d] for h in order], axis=0))
+
+
+SYM_SHAPES = [synth.ModelShape(2, 256, 4, 2, 64, 768, 1024), synth.ModelShape(2, 192, 6, 2, 64, 320, 512)]
+
+
+@pytest.mark.parametrize("shape", SYM_SHAPES, ids=["tiny", "q_rows_ne_hidden"])
+def test_decoder_invariant_under_ffn_unit_permutation(shape):
+    w = _mixing_model(shape, 21)
+    ref = _prompt_logits(shape, w, 21)
+    p = np.random.default_rng(5).permutation(shape.ffn)
+    v = dict(w)
+    for l in range(shape.layers):
+        v["l%d.wg" % l] = np.ascontiguousarray(w["l%d.wg" % l][p])
+        v["l%d.wu" % l] = np.ascontiguousarray(w["l%d.wu" % l][p])
+        v["l%d.wd" % l] = np.ascontiguousarray(w["l%d.wd" % l][:, p])
+    np.testing.assert_allclose(_prompt_logits(shape, v, 21), ref, rtol=0, atol=1e-9 * np.abs(ref).max())
+    # the same permutation on the gate rows alone is not a symmetry
+    u = dict(w)
+    u["l0.wg"] = np.ascontiguousarray(w["l0.wg"][p])
+    assert np.abs(_prompt_logits(shape, u, 21) - ref).max() > 1e-4 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("shape", SYM_SHAPES, ids=["tiny", "q_rows_ne_hidden"])
+def test_decoder_invariant_under_head_relabelling(shape):
+    # kv head j' of the new model is old kv head sig[j'], with its query group;
+    # inside every group the query heads are taken in the order tau
+    d, G = shape.head_dim, shape.n_q // shape.n_kv
+    w = _mixing_model(shape, 22)
+    ref = _prompt_logits(shape, w, 22)
+    rng = np.random.default_rng(6)
+    sig = rng.permutation(shape.n_kv)
+    while shape.n_kv > 1 and (sig == np.arange(shape.n_kv)).all():
+        sig = rng.permutation(shape.n_kv)
+    tau = rng.permutation(G)
+    qorder = [int(sig[j]) * G + int(tau[i]) for j in range(shape.n_kv) for i in range(G)]
+    v = dict(w)
+    for l in range(shape.layers):
+        v["l%d.wq" % l] = _heads(w["l%d.wq" % l], d, qorder)
+        v["l%d.wk" % l] = _heads(w["l%d.wk" % l], d, sig)
+        v["l%d.wv" % l] = _heads(w["l%d.wv" % l], d, sig)
+        v["l%d.wo" % l] = np.ascontiguousarray(_heads(w["l%d.wo" % l].T, d, qorder).T)
+    np.testing.assert_allclose(_prompt_logits(shape, v, 22), ref, rtol=0, atol=1e-9 * np.abs(ref).max())
+    # moving the query heads without their kv heads changes the result
+    u = dict(w)
+    for l in range(shape.layers):
+        u["l%d.wq" % l] = v["l%d.wq" % l]
+        u["l%d.wo" % l] = v["l%d.wo" % l]
+    assert np.abs(_prompt_logits(shape, u, 22) - ref).max() > 1e-4 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("shape", SYM_SHAPES, ids=["tiny", "q_rows_ne_hidden"])
+def test_decoder_invariant_under_hidden_permutation(shape):
+    # the residual stream's coordinates relabelled everywhere they appear:
+    # embedding columns, every RMSNorm gain over the hidden axis, the input
+    # columns of q/k/v/gate/up and the output rows of o/down
+    w = _mixing_model(shape, 23)
+    ref = _prompt_logits(shape, w, 23)
+    r = np.random.default_rng(7).permutation(shape.hidden)
+    v = dict(w)
+    v["E"] = np.ascontiguousarray(w["E"][:, r])
+    v["final_norm"] = np.ascontiguousarray(w["final_norm"][r])
+    for l in range(shape.layers):
+        for key_ in ("attn_norm", "ffn_norm"):
+            v["l%d.%s" % (l, key_)] = np.ascontiguousarray(w["l%d.%s" % (l, key_)][r])
+        for key_ in ("wq", "wk", "wv", "wg", "wu"):
+            v["l%d.%s" % (l, key_)] = np.ascontiguousarray(w["l%d.%s" % (l, key_)][:, r])
+        for key_ in ("wo", "wd"):
+            v["l%d.%s" % (l, key_)] = np.ascontiguousarray(w["l%d.%s" % (l, key_)][r])
+    np.testing.assert_allclose(_prompt_logits(shape, v, 23), ref, rtol=0, atol=1e-9 * np.abs(ref).max())
+    # the permutation left out of one gain vector is not a symmetry
+    u = dict(v)
+    u["l1.ffn_norm"] = w["l1.ffn_norm"]
+    assert np.abs(_prompt_logits(shape, u, 23) - ref).max() > 1e-4 * np.abs(ref).max()
