@@ -214,3 +214,36 @@ def test_batch2_hidden640_graph_runs_under_jitter():
             mpk.mpk_sim_destroy(s)
     finally:
         mpk.mpk_destroy_graph(g)
+
+
+def test_full_qwen3_8b_graph_runs_under_jitter():
+    """The benchmark's own graph at full size (36 layers, 151936-id LM head,
+    batch 1, 256 CUs: 37121 tasks per iteration) across the end of a
+    39-token prompt: position 37 consumes a prompt id, 38 the last one and
+    writes the first generated id, 39 the next; then one more launch (position
+    40) with the stamp base advanced.  Every task runs once per iteration and no stale word is
+    accepted."""
+    sh = synth.QWEN3_8B
+    width, P = 64, 39
+    g, spec = build(sh, B=1, num_cus=256, tokens_width=width, max_seq=width)
+    try:
+        info = mpk.mpk_get_graph_info(g)
+        toks = np.full((1, width), -1, np.int32)
+        toks[0, :P] = synth.uniform_ids(0, "simfull", P, sh.vocab)
+        s = mpk.mpk_sim_create(g, np.array([P - 2], np.int32), toks, np.array([P], np.int32), kv_filled=P - 2)
+        try:
+            base = 7000
+            for n, seed in ((3, 5), (1, 6)):
+                tr = mpk.mpk_simulate(s, info.num_tasks, n, base, seed=seed, jitter_us=20,
+                                      timeout_ms=120000).reshape(n, info.num_tasks)
+                assert (tr["task"] == np.arange(info.num_tasks)[None, :]).all()
+                base += n
+            st, tk = mpk.mpk_sim_read_meta(s, 1, width)
+            assert st[0] == P + 2
+            assert np.array_equal(tk[0, :P], toks[0, :P])
+            assert ((tk[0, P:P + 3] >= 0) & (tk[0, P:P + 3] < sh.vocab)).all()
+            assert (tk[0, P + 3:] == -1).all()
+        finally:
+            mpk.mpk_sim_destroy(s)
+    finally:
+        mpk.mpk_destroy_graph(g)
