@@ -247,3 +247,37 @@ def test_full_qwen3_8b_graph_runs_under_jitter():
             mpk.mpk_sim_destroy(s)
     finally:
         mpk.mpk_destroy_graph(g)
+
+
+def test_long_context_graph_runs_under_jitter():
+    """The long-context benchmark's graph (full model, K/V filled to 32768
+    positions, 256 CUs): every layer's attention runs 32 splits per kv head,
+    the owner split gathering the other 31 partials.  Three iterations from
+    position 32768 under jitter: every attention split runs in every
+    iteration, no stale word is accepted, step and tokens advance."""
+    sh = synth.QWEN3_8B
+    width, P0 = 32800, 32768
+    g, spec = build(sh, B=1, num_cus=256, tokens_width=width, max_seq=width)
+    try:
+        info, tasks, _, _, _ = info_arrays(g)
+        kinds = [o.kind for o in spec.ops]
+        att = [i for i, t in enumerate(tasks) if t.op < len(kinds) and kinds[t.op] == mpk.MPK_OP_ATTENTION]
+        assert len(att) == sh.layers * sh.n_kv * 32
+        toks = np.full((1, width), -1, np.int32)
+        toks[0, :P0 + 1] = synth.uniform_ids(0, "simlong", P0 + 1, sh.vocab)
+        s = mpk.mpk_sim_create(g, np.array([P0], np.int32), toks, np.array([20], np.int32), kv_filled=P0)
+        try:
+            n = 3
+            tr = mpk.mpk_simulate(s, info.num_tasks, n, 9000, seed=8, jitter_us=20,
+                                  timeout_ms=120000).reshape(n, info.num_tasks)
+            assert (tr["task"] == np.arange(info.num_tasks)[None, :]).all()
+            assert (tr["start_ticket"][:, att] != NONE).all()
+            st, tk = mpk.mpk_sim_read_meta(s, 1, width)
+            assert st[0] == P0 + n
+            assert np.array_equal(tk[0, :P0 + 1], toks[0, :P0 + 1])
+            assert ((tk[0, P0 + 1:P0 + n + 1] >= 0) & (tk[0, P0 + 1:P0 + n + 1] < sh.vocab)).all()
+            assert (tk[0, P0 + n + 1:] == -1).all()
+        finally:
+            mpk.mpk_sim_destroy(s)
+    finally:
+        mpk.mpk_destroy_graph(g)
