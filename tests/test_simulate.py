@@ -281,3 +281,38 @@ def test_long_context_graph_runs_under_jitter():
             mpk.mpk_sim_destroy(s)
     finally:
         mpk.mpk_destroy_graph(g)
+
+
+def test_batch8_full_graph_runs_under_jitter():
+    """The batch-8 benchmark's graph at full size (36 layers, down projection
+    split in K, 256 CUs: 46301 tasks per iteration), eight requests each at
+    the last position of its own prompt (lengths 16 to 512): two iterations
+    under jitter write every request's first two generated ids; no stale word
+    is accepted."""
+    sh = synth.QWEN3_8B
+    B, width = 8, 600
+    g, spec = build(sh, B=B, num_cus=256, tokens_width=width, max_seq=width)
+    try:
+        info = mpk.mpk_get_graph_info(g)
+        plen = np.array([16, 512, 100, 37, 250, 64, 65, 400], np.int32)
+        step = plen - 1
+        toks = np.full((B, width), -1, np.int32)
+        for r in range(B):
+            toks[r, :plen[r]] = synth.uniform_ids(0, "simb8.%d" % r, int(plen[r]), sh.vocab)
+        s = mpk.mpk_sim_create(g, step, toks, plen, kv_filled=int(step.max()))
+        try:
+            n = 2
+            tr = mpk.mpk_simulate(s, info.num_tasks, n, 12000, seed=9, jitter_us=20,
+                                  timeout_ms=120000).reshape(n, info.num_tasks)
+            assert (tr["task"] == np.arange(info.num_tasks)[None, :]).all()
+            st, tk = mpk.mpk_sim_read_meta(s, B, width)
+            assert np.array_equal(st, step + n)
+            for r in range(B):
+                p = int(plen[r])
+                assert np.array_equal(tk[r, :p], toks[r, :p])
+                assert ((tk[r, p:p + n] >= 0) & (tk[r, p:p + n] < sh.vocab)).all()
+                assert (tk[r, p + n:] == -1).all()
+        finally:
+            mpk.mpk_sim_destroy(s)
+    finally:
+        mpk.mpk_destroy_graph(g)
